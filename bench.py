@@ -1,0 +1,379 @@
+#!/usr/bin/env python3
+"""SGEMM benchmark on one MI355X: GFLOPS at M=N=K=4096 (C = alpha*A*B + beta*C,
+row-major FP32, alpha=1, beta=0), as a fraction of measured and published
+FP32 peaks.
+
+Default run (the contract): ``python bench.py [--gpus 1] [--steps K] [--warmup W]``
+prints ONE JSON line.  A "step" is one sgemm() call on the 4096^3 problem, with
+A, B and C already resident in device memory.  After W untimed steps (and a
+clock-waking burst, see ``wake``), exactly K steps are timed between two device
+synchronisations; each launch is also bracketed by HIP events on the stream it
+is launched on, which gives the average kernel duration for the roofline.
+
+Other modes (one JSON line per result, not the contract line):
+  --sweep            every square size and rectangular shape, auto choice
+  --variants         every kernel variant on the 4096^3 problem
+  --shape M N K      a single shape (with --variant V to force a variant)
+  --profile          only the timed steps, no ceilings or CPU baseline: the
+                     command to run under rocprofv3
+
+Accounting (as on the pages): FLOPs = 2*M*N*K, the epilogue is not counted
+("Optimizing SGEMM in CUDA" and "The road to a fast GEMM", section "The
+problem and the ceiling"); algorithmic bytes = 4*(M*K + K*N + M*N), plus
+4*M*N when beta != 0 (C read and written).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published figures (AMD datasheet): dense FP32 matrix and vector
+# 157.3 TFLOP/s, HBM3E 8 TB/s; 256 CUs.
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+NUM_CUS = 256
+
+METRIC = "SGEMM GFLOPS at M=N=K=4096 on 1 MI355X; % of measured FP32 peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_4096.json")
+
+
+def flops(M: int, N: int, K: int) -> float:
+    """Floating-point operations of one GEMM: 2*M*N*K."""
+    return 2.0 * M * N * K
+
+
+def min_bytes(M: int, N: int, K: int, beta: float = 0.0) -> float:
+    """Bytes a GEMM must move at least: read A and B, write C, and read C
+    too when beta != 0."""
+    b = 4.0 * (M * K + K * N + M * N)
+    if beta != 0.0:
+        b += 4.0 * M * N
+    return b
+
+
+def arithmetic_intensity(M, N, K, beta=0.0) -> float:
+    return flops(M, N, K) / min_bytes(M, N, K, beta)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, so stored counter readings can be matched to
+    the kernels they were taken from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_fp32_gemm_sgemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- GPU side
+
+def _torch():
+    import torch
+    return torch
+
+
+def wake(seconds: float, fn):
+    """Run `fn` back to back for about `seconds` so the clocks are up before
+    timing (the Tinyforge README's benchmark-hygiene note: short kernels after
+    host work run at idle clocks)."""
+    torch = _torch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_steps(fn, steps: int, stream):
+    """Times `steps` calls of fn: returns (total ms from the first event to the
+    last, list of per-launch ms from events around each launch)."""
+    torch = _torch()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total = starts[0].elapsed_time(ends[-1])
+    return total, per
+
+
+class Problem:
+    """Device buffers of one GEMM and a zero-overhead launcher."""
+
+    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real"):
+        torch = _torch()
+        from workloads import draw
+        self.M, self.N, self.K, self.alpha, self.beta = M, N, K, alpha, beta
+        A, B, C = draw(M, N, K, seed=seed, kind=kind, with_c=(beta != 0.0))
+        self.host = (A, B, C)
+        self.A = torch.from_numpy(A).cuda()
+        self.B = torch.from_numpy(B).cuda()
+        self.C = (torch.from_numpy(C).cuda() if C is not None
+                  else torch.zeros((M, N), dtype=torch.float32, device="cuda"))
+        self.stream = torch.cuda.current_stream()
+
+    def launcher(self, variant=-1):
+        import dense_fp32_gemm_sgemm_amd as sg
+        args = (self.M, self.N, self.K, float(self.alpha), self.A.data_ptr(), max(1, self.K),
+                self.B.data_ptr(), max(1, self.N), float(self.beta), self.C.data_ptr(),
+                max(1, self.N), self.stream.cuda_stream, variant)
+        fn_ex = sg.load().sgemm_ex
+
+        def fn():
+            st = fn_ex(*args)
+            if st != 0:
+                raise RuntimeError("sgemm status %d: %s" % (st, sg.sgemm_status_string(st)))
+        return fn
+
+    def variant_name(self, variant=-1):
+        import dense_fp32_gemm_sgemm_amd as sg
+        if variant >= 0:
+            return sg.sgemm_variant_name(variant)
+        v = sg.sgemm_select_variant(self.M, self.N, self.K, self.alpha, 1, max(1, self.K), 1,
+                                    max(1, self.N), self.beta, 1, max(1, self.N))
+        return sg.sgemm_variant_name(v) if v >= 0 else "none"
+
+
+def measure_ceilings(samples: int = 7):
+    """Measured FP32 matrix-core, FP32 vector and HBM copy rates."""
+    torch = _torch()
+    import dense_fp32_gemm_sgemm_amd as sg
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    blocks = NUM_CUS * 8
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    out = {}
+
+    def rate(launch, target_ms=20.0):
+        # calibrate the iteration count to about target_ms per launch
+        iters = 256
+        while True:
+            st, fl = launch(iters)
+            assert st == 0
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            launch(iters)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            if ms >= target_ms * 0.5 or iters >= 1 << 22:
+                break
+            iters = int(iters * max(2.0, target_ms / max(ms, 1e-3)))
+        wake(0.3, lambda: launch(iters))
+        vals = []
+        for _ in range(samples):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            _, fl = launch(iters)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            vals.append(fl / (t0.elapsed_time(t1) * 1e-3) / 1e12)
+        return statistics.median(vals), vals
+
+    out["mfma_f32_32x32x2_tflops"], _ = rate(lambda it: sg.sgemm_ceiling_mfma(32, blocks, it, sink.data_ptr(), h))
+    out["mfma_f32_16x16x4_tflops"], _ = rate(lambda it: sg.sgemm_ceiling_mfma(16, blocks, it, sink.data_ptr(), h))
+    out["valu_fma_f32_tflops"], _ = rate(lambda it: sg.sgemm_ceiling_fma(blocks, it, sink.data_ptr(), h))
+    n = 256 * 1024 * 1024  # 1 GiB per buffer
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    cp = lambda: sg.sgemm_ceiling_copy(src.data_ptr(), dst.data_ptr(), n, NUM_CUS * 16, h)
+    wake(0.2, cp)
+    vals = []
+    for _ in range(samples):
+        total, _ = time_steps(cp, 1, stream)
+        vals.append(2 * 4 * n / (total * 1e-3) / 1e9)
+    out["hbm_copy_gbs"] = statistics.median(vals)
+    del src, dst
+    return out
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The oracle (as it stands) on a bounded row sample of the 4096^3
+    workload, on the host cores."""
+    import numpy as np
+    import oracle
+    from workloads import HEADLINE, draw_workload
+    A, B, _ = draw_workload(HEADLINE)
+    oracle.load()
+    rows = 32
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    nrows = int(min(HEADLINE.M, max(rows, rows * target_s / max(dt, 1e-6))))
+    sel = np.arange(nrows)
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, rows=sel)
+    dt = time.perf_counter() - t0
+    gfl = flops(nrows, HEADLINE.N, HEADLINE.K) / dt / 1e9
+    return {"value": round(gfl, 3), "unit": "GFLOPS", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "first %d of 4096 output rows of the 4096^3 workload (fp64 i-k-j "
+                      "oracle, OpenMP over rows), %.1f s" % (nrows, dt)}
+
+
+def stored_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def bench_problem(prob: Problem, steps: int, warmup: int, variant=-1):
+    fn = prob.launcher(variant)
+    for _ in range(warmup):
+        fn()
+    wake(0.25, fn)
+    total, per = time_steps(fn, steps, prob.stream)
+    return total, per
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--variant", type=int, default=-1)
+    ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"))
+    ap.add_argument("--beta", type=float, default=0.0)
+    ap.add_argument("--alpha", type=float, default=1.0)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--variants", action="store_true")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this SGEMM runs whole on a single MI355X and "
+              "--gpus %d is not supported (the sharded design is described, not built)"
+              % args.gpus, file=sys.stderr)
+        return 2
+
+    torch = _torch()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    import dense_fp32_gemm_sgemm_amd as sg
+    sg.load()
+
+    if args.sweep or args.variants or args.shape or args.profile:
+        return run_modes(args)
+
+    M = N = K = 4096
+    prob = Problem(M, N, K, 1.0, 0.0, seed=0)
+    vname = prob.variant_name(args.variant)
+    total, per = bench_problem(prob, args.steps, args.warmup, args.variant)
+    ms_step = total / args.steps
+    kern_ms = statistics.mean(per)
+    value = flops(M, N, K) / (ms_step * 1e-3) / 1e9
+    achieved = flops(M, N, K) / (kern_ms * 1e-3) / 1e12
+
+    ceilings = None if args.no_ceilings else measure_ceilings()
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    traffic = stored_traffic()
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sgemm M=N=K=4096 alpha=1 beta=0 row-major fp32, A,B uniform[-1,1] seed 0",
+                   "M": M, "N": N, "K": K, "alpha": 1.0, "beta": 0.0, "variant": vname,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
+                     "kernel_ms_max": round(max(per), 5)},
+        "cpu_baseline": cpu,
+    }
+    if ceilings:
+        mf = ceilings["mfma_f32_32x32x2_tflops"]
+        line["measured_ceilings"] = {k: round(v, 2) for k, v in ceilings.items()}
+        line["pct_of_measured_mfma_f32"] = round(100.0 * value / 1e3 / mf, 2)
+        line["pct_of_measured_valu_f32"] = round(100.0 * value / 1e3 / ceilings["valu_fma_f32_tflops"], 2)
+        line["pct_of_datasheet_fp32"] = round(100.0 * value / 1e3 / PEAK_FP32_TFLOPS, 2)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_modes(args):
+    from workloads import RAGGED_SHAPES, SWEEP_SIZES
+    import dense_fp32_gemm_sgemm_amd as sg
+    jobs = []
+    if args.profile:
+        shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
+        prob = Problem(*shape, args.alpha, args.beta, seed=0)
+        total, per = bench_problem(prob, args.steps, args.warmup, args.variant)
+        kern_ms = statistics.mean(per)
+        print(json.dumps({"mode": "profile", "shape": shape, "variant": prob.variant_name(args.variant),
+                          "steps": args.steps, "kernel_ms_mean": round(kern_ms, 5),
+                          "tflops": round(flops(*shape) / (kern_ms * 1e-3) / 1e12, 2)}), flush=True)
+        return 0
+    if args.sweep:
+        jobs = [((n, n, n), -1) for n in SWEEP_SIZES] + [(s, -1) for s in RAGGED_SHAPES]
+    elif args.variants:
+        shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
+        jobs = [(shape, v) for v in range(sg.sgemm_num_variants())]
+    elif args.shape:
+        jobs = [(tuple(args.shape), args.variant)]
+    for shape, v in jobs:
+        M, N, K = shape
+        prob = Problem(M, N, K, args.alpha, args.beta, seed=0)
+        name = prob.variant_name(v)
+        work = flops(M, N, K)
+        steps = max(5, min(args.steps, int(2e12 / max(work, 1.0))))
+        if name == "simple" and work > 1e11:
+            steps = 3
+        total, per = bench_problem(prob, steps, min(args.warmup, steps), v)
+        kern_ms = statistics.median(per)
+        rec = {"mode": "sweep" if args.sweep else "variant", "M": M, "N": N, "K": K,
+               "beta": args.beta, "variant": name, "steps": steps,
+               "kernel_ms_median": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
+               "gflops": round(work / (kern_ms * 1e-3) / 1e9, 1),
+               "frac_fp32_peak": round(work / (kern_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+               "ai_flop_per_byte": round(arithmetic_intensity(M, N, K, args.beta), 2),
+               "hbm_gbs_at_min_bytes": round(min_bytes(M, N, K, args.beta) / (kern_ms * 1e-3) / 1e9, 1)}
+        print(json.dumps(rec), flush=True)
+        del prob
+        _torch().cuda.empty_cache()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

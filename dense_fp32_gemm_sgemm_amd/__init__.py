@@ -1,0 +1,89 @@
+"""Strict-FP32 SGEMM for AMD Instinct MI355X (gfx950): C = alpha*A*B + beta*C.
+
+The computation runs in the HIP library ``libsgemm_gfx950.so`` (sources in
+``csrc/``, C interface in ``include/sgemm.h``).  This package is its thin
+Python binding:
+
+* ``sgemm``, ``sgemm_ex`` and the other ``sgemm_*`` functions take exactly the
+  C arguments (device pointers as ints, ``stream`` as a ``hipStream_t`` int);
+* ``gemm(A, B, C, alpha, beta)`` marshals torch tensors into that call --
+  shapes, leading dimensions from the row strides, data pointers and the
+  current torch stream -- and raises on a non-zero status.
+
+PyTorch only supplies device memory and streams; there is no fallback path,
+and the functions raise ``LibraryMissing`` when the library is not built.
+"""
+from __future__ import annotations
+
+from ._lib import (EXPORTS, LIBRARY, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM,  # noqa: F401
+                   SGEMM_ERR_LAUNCH, SGEMM_ERR_LD, SGEMM_ERR_PTR, SGEMM_ERR_VARIANT,
+                   SGEMM_NO_KERNEL, SGEMM_OK, LibraryMissing, load, sgemm,
+                   sgemm_ceiling_copy, sgemm_ceiling_fma, sgemm_ceiling_mfma, sgemm_ex,
+                   sgemm_num_variants, sgemm_select_variant, sgemm_status_string,
+                   sgemm_variant_name, sgemm_version)
+
+__all__ = ["gemm", "variant_names", "sgemm", "sgemm_ex", "sgemm_num_variants",
+           "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
+           "sgemm_version", "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
+           "LibraryMissing", "SgemmError"]
+
+
+class SgemmError(RuntimeError):
+    """A non-zero status from the C library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__("sgemm status %d: %s" % (status, sgemm_status_string(status)))
+
+
+def variant_names():
+    return [sgemm_variant_name(i) for i in range(sgemm_num_variants())]
+
+
+def _leading_dim(t, rows, cols, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on a HIP device" % name)
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (rows, cols)))
+    if rows > 1 and cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s must be row-major (stride(1) == 1)" % name)
+    if rows <= 1:
+        return max(1, cols)
+    if cols == 1 and t.stride(1) != 1:
+        return max(1, t.stride(0))
+    return t.stride(0)
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, variant: int = -1, stream=None):
+    """C = alpha * A @ B + beta * C in place on float32 HIP tensors; returns C.
+
+    A is (M, K), B is (K, N), C is (M, N), each row-major (unit column
+    stride; the row stride is the leading dimension).  The call is enqueued on
+    ``stream`` (default: the current torch stream) and does not synchronise."""
+    import torch
+    M, K = int(A.shape[0]), int(A.shape[1])
+    N = int(B.shape[1])
+    if B.shape[0] != K:
+        raise ValueError("inner dimensions differ: A %s, B %s" % (tuple(A.shape), tuple(B.shape)))
+    lda = _leading_dim(A, M, K, "A")
+    ldb = _leading_dim(B, K, N, "B")
+    ldc = _leading_dim(C, M, N, "C")
+    devs = {t.device for t in (A, B, C)}
+    if len(devs) != 1:
+        raise ValueError("A, B and C must be on the same device")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(C.device):
+        st = sgemm_ex(M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
+                      float(beta), C.data_ptr() or None, ldc, handle, variant)
+    if st != SGEMM_OK:
+        raise SgemmError(st)
+    return C

@@ -1,0 +1,126 @@
+"""ctypes binding of ``libsgemm_gfx950.so`` -- argument marshalling only.
+
+Every function here has the name and arguments of the C entry point it wraps
+(declared in ``include/sgemm.h`` and ``include/sgemm_ceiling.h``): sizes and
+scalars are passed through, matrices are device pointers given as Python ints,
+and ``stream`` is a ``hipStream_t`` as an int (0 = default stream).  No step of
+the computation runs in Python, and there is no fallback: if the library is
+missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgemm_gfx950.so")
+
+SGEMM_OK = 0
+SGEMM_ERR_DIM = -1
+SGEMM_ERR_LD = -2
+SGEMM_ERR_PTR = -3
+SGEMM_ERR_LAUNCH = -4
+SGEMM_ERR_DEVICE = -5
+SGEMM_ERR_VARIANT = -6
+SGEMM_NO_KERNEL = -100
+
+# Every exported symbol, as declared in include/*.h.
+EXPORTS = ("sgemm", "sgemm_ex", "sgemm_num_variants", "sgemm_variant_name",
+           "sgemm_select_variant", "sgemm_status_string", "sgemm_version",
+           "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    """The HIP library has not been built (run ``__graft_entry__.build()``)."""
+
+
+def _declare(lib):
+    c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    gemm_args = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int, c_float, vp, c_int, vp]
+    lib.sgemm.argtypes = gemm_args
+    lib.sgemm.restype = c_int
+    lib.sgemm_ex.argtypes = gemm_args + [c_int]
+    lib.sgemm_ex.restype = c_int
+    lib.sgemm_num_variants.argtypes = []
+    lib.sgemm_num_variants.restype = c_int
+    lib.sgemm_variant_name.argtypes = [c_int]
+    lib.sgemm_variant_name.restype = ctypes.c_char_p
+    lib.sgemm_select_variant.argtypes = [c_int, c_int, c_int, c_float, vp, c_int, vp, c_int,
+                                         c_float, vp, c_int]
+    lib.sgemm_select_variant.restype = c_int
+    lib.sgemm_status_string.argtypes = [c_int]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_version.argtypes = []
+    lib.sgemm_version.restype = c_int
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.sgemm_ceiling_mfma.argtypes = [c_int, c_int, c_int, vp, vp, dp]
+    lib.sgemm_ceiling_mfma.restype = c_int
+    lib.sgemm_ceiling_fma.argtypes = [c_int, c_int, vp, vp, dp]
+    lib.sgemm_ceiling_fma.restype = c_int
+    lib.sgemm_ceiling_copy.argtypes = [vp, vp, ctypes.c_longlong, c_int, vp]
+    lib.sgemm_ceiling_copy.restype = c_int
+    return lib
+
+
+def load():
+    """The loaded library; raises LibraryMissing if it was never built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                raise LibraryMissing(
+                    "%s not found: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                    % LIBRARY)
+            _lib = _declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C = alpha*A*B + beta*C on ``stream``; returns the C status code."""
+    return load().sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, variant=-1) -> int:
+    """As ``sgemm`` with an explicit kernel variant (-1 = automatic)."""
+    return load().sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
+
+
+def sgemm_num_variants() -> int:
+    return load().sgemm_num_variants()
+
+
+def sgemm_variant_name(variant: int) -> str:
+    return load().sgemm_variant_name(variant).decode()
+
+
+def sgemm_select_variant(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
+    return load().sgemm_select_variant(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+
+
+def sgemm_status_string(status: int) -> str:
+    return load().sgemm_status_string(status).decode()
+
+
+def sgemm_version() -> int:
+    return load().sgemm_version()
+
+
+def sgemm_ceiling_mfma(shape, blocks, iters, sink, stream=0):
+    """Returns (status, flops of the launch)."""
+    flops = ctypes.c_double(0.0)
+    st = load().sgemm_ceiling_mfma(shape, blocks, iters, sink, stream, ctypes.byref(flops))
+    return st, flops.value
+
+
+def sgemm_ceiling_fma(blocks, iters, sink, stream=0):
+    """Returns (status, flops of the launch)."""
+    flops = ctypes.c_double(0.0)
+    st = load().sgemm_ceiling_fma(blocks, iters, sink, stream, ctypes.byref(flops))
+    return st, flops.value
+
+
+def sgemm_ceiling_copy(src, dst, n, blocks, stream=0) -> int:
+    return load().sgemm_ceiling_copy(src, dst, n, blocks, stream)

@@ -1,0 +1,161 @@
+// sgemm_api.hip -- the C entry points: argument checks, variant table and the
+// per-shape choice of kernel.
+//
+// Everything here runs on the host.  Argument errors are found before any HIP
+// call; the only HIP calls are the device check (once per device), the kernel
+// launch(es) and hipGetLastError.
+#include "../../include/sgemm.h"
+#include "sgemm_common.hpp"
+#include "sgemm_launch.hpp"
+
+#include <atomic>
+#include <climits>
+#include <cstring>
+
+namespace sg950 {
+namespace {
+
+typedef int (*Launcher)(const Problem &, hipStream_t);
+
+struct Variant {
+  const char *name;
+  Launcher launch;
+};
+
+// Stable order: tests and benchmarks address variants by index and name.
+const Variant kVariants[] = {
+    {"simple", launch_simple},
+    {"valu_128x128x16", launch_valu_128x128},
+    {"mfma32_128x128x16_2x2", launch_mfma32_128x128x16_2x2},
+    {"mfma32_128x128x32_2x2", launch_mfma32_128x128x32_2x2},
+    {"mfma32_256x128x16_2x2", launch_mfma32_256x128x16_2x2},
+    {"mfma32_256x256x16_2x2", launch_mfma32_256x256x16_2x2},
+    {"mfma32_64x64x16_1x1", launch_mfma32_64x64x16_1x1},
+    {"mfma16_128x128x16_2x2", launch_mfma16_128x128x16_2x2},
+    {"mfma16_64x64x16_2x2", launch_mfma16_64x64x16_2x2},
+};
+constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+
+enum VariantId {
+  kSimple = 0,
+  kValu128 = 1,
+  kMfma32_128x128x16 = 2,
+  kMfma32_128x128x32 = 3,
+  kMfma32_256x128x16 = 4,
+  kMfma32_256x256x16 = 5,
+  kMfma32_64x64x16 = 6,
+  kMfma16_128x128x16 = 7,
+  kMfma16_64x64x16 = 8,
+};
+
+constexpr int kNoKernel = -100;
+
+// Argument checks shared by every entry point (BLAS order: sizes, then leading
+// dimensions, then pointers).
+int check_args(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+               float beta, const float *C, int ldc) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return SGEMM_ERR_LD;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  if (C == nullptr) return SGEMM_ERR_PTR;
+  if (alpha != 0.0f && K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_PTR;
+  (void)beta;
+  return SGEMM_OK;
+}
+
+// The per-shape table.  Filled from measured sweeps on an MI355X; every entry
+// names a variant that handles any shape, so the table only trades speed.
+int choose_variant(const Problem &p) {
+  const long long mn = (long long)p.M * p.N;
+  const long long work = mn * p.K;
+  if (work <= 64LL * 64 * 64 || p.M < 8 || p.N < 8) return kSimple;
+  if (mn <= 512LL * 512) return kMfma16_64x64x16;
+  return kMfma32_128x128x16;
+}
+
+std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return SGEMM_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SGEMM_ERR_DEVICE;
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? SGEMM_OK : SGEMM_ERR_DEVICE;
+}
+
+int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+        float beta, float *C, int ldc, void *stream, int variant) {
+  int st = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (variant < -1 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  const bool no_product = (alpha == 0.0f || K == 0);
+  if (no_product && beta == 1.0f) return SGEMM_OK;
+  st = check_device();
+  if (st != SGEMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int rc;
+  if (no_product) {
+    rc = launch_scale(M, N, beta, C, ldc, s);
+  } else {
+    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    const int v = (variant >= 0) ? variant : choose_variant(p);
+    rc = kVariants[v].launch(p, s);
+  }
+  if (rc != 0) return SGEMM_ERR_DIM;
+  return (hipGetLastError() == hipSuccess) ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace sg950
+
+extern "C" {
+
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+          float beta, float *C, int ldc, void *stream) {
+  return sg950::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream, int variant) {
+  return sg950::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+int sgemm_num_variants(void) { return sg950::kNumVariants; }
+
+const char *sgemm_variant_name(int variant) {
+  if (variant < 0 || variant >= sg950::kNumVariants) return "";
+  return sg950::kVariants[variant].name;
+}
+
+int sgemm_select_variant(int M, int N, int K, float alpha, const float *A, int lda,
+                         const float *B, int ldb, float beta, const float *C, int ldc) {
+  const int st = sg950::check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0 || alpha == 0.0f || K == 0) return sg950::kNoKernel;
+  const sg950::Problem p{M, N, K, alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc};
+  return sg950::choose_variant(p);
+}
+
+const char *sgemm_status_string(int status) {
+  switch (status) {
+    case SGEMM_OK: return "success";
+    case SGEMM_ERR_DIM: return "invalid dimension (negative M, N or K, or grid too large)";
+    case SGEMM_ERR_LD: return "invalid leading dimension (lda < max(1,K), ldb or ldc < max(1,N))";
+    case SGEMM_ERR_PTR: return "NULL matrix pointer";
+    case SGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case SGEMM_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
+    case SGEMM_ERR_VARIANT: return "variant index out of range";
+    default: return "unknown status";
+  }
+}
+
+int sgemm_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// sgemm_common.hpp -- types and small device helpers shared by the SGEMM kernels.
+//
+// Written for gfx950 (CDNA4): 64-lane wavefronts, 256 compute units in 8
+// accelerator complex dies (XCDs) with a separate L2 each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sg950 {
+
+// The GEMM problem C = alpha*A*B + beta*C, row-major, as one kernel argument.
+struct Problem {
+  int M, N, K;
+  float alpha, beta;
+  const float *A;
+  int lda;
+  const float *B;
+  int ldb;
+  float *C;
+  int ldc;
+};
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kNumXcds = 8;
+
+// Workgroups are handed to the XCDs round-robin (workgroup w runs on XCD
+// w % 8).  This remaps the hardware order so that XCD x receives a contiguous
+// run of logical tile ids; with the grouped tile order below, the tiles that
+// share one L2 then share rows of A and columns of B.
+__device__ __forceinline__ int xcd_remap(int wg, int num_wg) {
+  const int per_xcd = (num_wg + kNumXcds - 1) / kNumXcds;
+  const int tall = num_wg - (per_xcd - 1) * kNumXcds;  // XCDs holding per_xcd ids
+  const int xcd = wg % kNumXcds;
+  const int local = wg / kNumXcds;
+  return (xcd < tall) ? xcd * per_xcd + local
+                      : tall * per_xcd + (xcd - tall) * (per_xcd - 1) + local;
+}
+
+// Grouped tile order: consecutive logical ids walk down `group_m` tile rows
+// before moving one tile column right, so a window of consecutive ids covers a
+// compact block of C.
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int group_m,
+                                             int &tm, int &tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = id / per_group;
+  const int first_m = g * group_m;
+  const int rows = min(tiles_m - first_m, group_m);
+  const int in_group = id - g * per_group;
+  tm = first_m + in_group % rows;
+  tn = in_group / rows;
+}
+
+// Epilogue for one element: alpha*acc (+ beta*C when beta != 0; C is not read
+// otherwise).
+__device__ __forceinline__ void store_out(float *c, float acc, float alpha, float beta) {
+  float v = alpha * acc;
+  if (beta != 0.0f) v = fmaf(beta, *c, v);
+  *c = v;
+}
+
+}  // namespace sg950

@@ -1,0 +1,44 @@
+// sgemm_launch.hpp -- host-side launchers of the SGEMM kernel families.
+//
+// Each launcher enqueues one GEMM on `stream` and returns 0, or -1 when the
+// problem's grid would exceed the launch limits.  Arguments are already
+// validated by the C entry points (sizes >= 1, leading dimensions in range,
+// pointers non-NULL, alpha != 0, K >= 1).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "sgemm_common.hpp"
+
+namespace sg950 {
+
+int launch_simple(const Problem &p, hipStream_t stream);
+int launch_scale(int M, int N, float beta, float *C, int ldc, hipStream_t stream);
+
+// Register-tiled VALU kernel: 128x128 tile, 8x8 outputs per thread.
+int launch_valu_128x128(const Problem &p, hipStream_t stream);
+
+// Matrix-core kernels, named <instruction>_<BM>x<BN>x<BK>_<waves M>x<waves N>.
+int launch_mfma32_128x128x16_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_128x128x32_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_256x128x16_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_256x256x16_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_64x64x16_1x1(const Problem &p, hipStream_t stream);
+int launch_mfma16_128x128x16_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t stream);
+
+// Operand alignment classes: a matrix may be read with 16-byte vector loads
+// when its base is 16-byte aligned and its leading dimension is a multiple of
+// four (for B the row length N must be one too, so a vector never straddles
+// the end of a row).
+inline bool a_vec_ok(const Problem &p) {
+  return ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && (p.lda % 4 == 0);
+}
+inline bool b_vec_ok(const Problem &p) {
+  return ((reinterpret_cast<uintptr_t>(p.B) & 15) == 0) && (p.ldb % 4 == 0) && (p.N % 4 == 0);
+}
+inline bool c_vec_ok(const Problem &p) {
+  return ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0) && (p.N % 4 == 0);
+}
+
+}  // namespace sg950

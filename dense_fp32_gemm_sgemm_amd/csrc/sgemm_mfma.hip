@@ -1,0 +1,241 @@
+// sgemm_mfma.hip -- strict-FP32 SGEMM on the CDNA4 matrix cores.
+//
+// SGEMM is a dense contraction, so on gfx950 its inner product belongs on the
+// matrix cores.  The instructions used take FP32 operands and accumulate in
+// FP32 -- no input is rounded to a narrower format:
+//   v_mfma_f32_32x32x2f32: a 32x32 block of C += (32x2 of A) x (2x32 of B)
+//   v_mfma_f32_16x16x4f32: a 16x16 block of C += (16x4 of A) x (4x16 of B)
+// Each is 64 FLOP per matrix-core clock per SIMD, the same peak as packed
+// FP32 vector FMA and twice that of plain v_fma_f32.
+//
+// Structure (the tiling hierarchy of "The road to a fast GEMM", sections
+// "v2: shared-memory tiling", "v4: two-dimensional register tiling" and "Where
+// to go next" -- block tile, warp tile, matrix instruction -- re-sized for
+// wave64 and the CDNA4 LDS):
+//   * a workgroup owns a BM x BN tile of C and walks K in slabs of BK;
+//   * its WAVES_M x WAVES_N wavefronts each own a (BM/WAVES_M) x (BN/WAVES_N)
+//     wave tile, held as FM x FN matrix-core blocks in accumulator registers;
+//   * each slab of A and B is read from global memory with 16-byte loads and
+//     staged in LDS; two LDS buffers alternate so the global loads of slab
+//     t+1 are in flight while slab t is multiplied, with one barrier per slab
+//     (the double-buffering exercise of "The road to a fast GEMM").
+//
+// Operand layout.  For the 32x32x2 instruction lane l supplies A[l%32][k] and
+// B[k][l%32] with k = l/32 (the 16x16x4 one: A[l%16][l/16], B[l/16][l%16]).
+// Which k of the slab a lane group stands for is free, as long as A and B
+// agree, so lane group g takes the KPG = BK/(64/MI) consecutive k values
+// [g*KPG, (g+1)*KPG): its A operands for a whole slab are then contiguous in a
+// row of the A tile and come out of LDS as 16-byte reads.  A is kept
+// row-major in LDS with a 4-float pad per row (row pitch BK+4), which puts the
+// 16-byte reads of 8 (or 16) consecutive rows on disjoint banks; B stays
+// row-major, where each 32-lane half reads 32 consecutive floats.
+//
+// Output layout.  Lane l of a 32x32 block holds column l%32 and, in register
+// r, row 8*(r/4) + 4*(l/32) + r%4; of a 16x16 block, row 4*(l/16) + r.
+#include "sgemm_common.hpp"
+#include "sgemm_launch.hpp"
+#include "sgemm_tiles.hpp"
+
+#include <climits>
+#include <type_traits>
+
+namespace sg950 {
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+struct MfmaTile {
+  static constexpr int kThreads = WAVES_M * WAVES_N * 64;
+  static constexpr int WTM = BM / WAVES_M;  // wave tile rows
+  static constexpr int WTN = BN / WAVES_N;  // wave tile columns
+  static constexpr int FM = WTM / MI;       // matrix-core blocks per wave, M
+  static constexpr int FN = WTN / MI;       // matrix-core blocks per wave, N
+  static constexpr int KG = 64 / MI;        // lane groups along k
+  static constexpr int KPG = BK / KG;       // consecutive k per lane group and slab
+  static constexpr int APITCH = BK + 4;     // A row pitch in LDS (floats)
+  static constexpr int BPITCH = BN;         // B row pitch in LDS (floats)
+  static constexpr int A_STAGE = BM * APITCH;
+  static constexpr int B_STAGE = BK * BPITCH;
+  static_assert(MI == 32 || MI == 16, "32x32x2 or 16x16x4 instruction");
+  static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole blocks");
+  static_assert(KPG % 4 == 0, "A operands are read from LDS 4 at a time");
+};
+
+__device__ __forceinline__ floatx16 mfma_step(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma_step(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Row inside an MI x MI block of accumulator register r of lane group g.
+template <int MI>
+__device__ __forceinline__ int acc_row(int g, int r) {
+  if constexpr (MI == 32) {
+    return 8 * (r / 4) + 4 * g + (r % 4);
+  } else {
+    return 4 * g + r;
+  }
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VA, bool VB>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void mfma_kernel(Problem p, int tiles_m,
+                                                                        int tiles_n, int group_m) {
+  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N>;
+  using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
+  constexpr int kRegs = MI * MI / 64;
+
+  __shared__ __attribute__((aligned(16))) float As[2 * T::A_STAGE];
+  __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_STAGE];
+
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int g = lane / MI;
+  const int li = lane % MI;
+
+  ATileLoader<BM, BK, T::kThreads, VA> la;
+  BTileLoader<BK, BN, T::kThreads, VB> lb;
+  la.init(p, m0, tid);
+  lb.init(p, n0, tid);
+
+  Acc acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) acc[i][j][r] = 0.0f;
+
+  const int K = p.K;
+  const int nk = (K + BK - 1) / BK;
+  const bool ragged = (K % BK) != 0;
+
+  // LDS offsets of this thread's stores and of its wave's operand reads.
+  int a_st[decltype(la)::kVecs];
+  int b_st[decltype(lb)::kVecs];
+#pragma unroll
+  for (int i = 0; i < decltype(la)::kVecs; ++i)
+    a_st[i] = decltype(la)::row_of(tid, i) * T::APITCH + decltype(la)::col_of(tid, i);
+#pragma unroll
+  for (int i = 0; i < decltype(lb)::kVecs; ++i)
+    b_st[i] = decltype(lb)::row_of(tid, i) * T::BPITCH + decltype(lb)::col_of(tid, i);
+  const int a_rd = (wm * T::WTM + li) * T::APITCH + g * T::KPG;
+  const int b_rd = (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
+
+  if (ragged && nk == 1) {
+    la.template load<true>(0, K);
+    lb.template load<true>(0, K);
+  } else {
+    la.template load<false>(0, K);
+    lb.template load<false>(0, K);
+  }
+#pragma unroll
+  for (int i = 0; i < decltype(la)::kVecs; ++i) *reinterpret_cast<floatx4 *>(As + a_st[i]) = la.v[i];
+#pragma unroll
+  for (int i = 0; i < decltype(lb)::kVecs; ++i) *reinterpret_cast<floatx4 *>(Bs + b_st[i]) = lb.v[i];
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool has_next = kt + 1 < nk;
+    if (has_next) {
+      const int k1 = (kt + 1) * BK;
+      if (ragged && kt + 2 == nk) {
+        la.template load<true>(k1, K);
+        lb.template load<true>(k1, K);
+      } else {
+        la.template load<false>(k1, K);
+        lb.template load<false>(k1, K);
+      }
+    }
+
+    const float *as = As + cur * T::A_STAGE + a_rd;
+    const float *bs = Bs + cur * T::B_STAGE + b_rd;
+#pragma unroll
+    for (int q = 0; q < T::KPG / 4; ++q) {
+      floatx4 av[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+        av[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
+      float bv[T::FN][4];
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma_step(av[i][e], bv[j][e], acc[i][j]);
+    }
+
+    if (has_next) {
+      float *an = As + (cur ^ 1) * T::A_STAGE;
+      float *bn = Bs + (cur ^ 1) * T::B_STAGE;
+#pragma unroll
+      for (int i = 0; i < decltype(la)::kVecs; ++i) *reinterpret_cast<floatx4 *>(an + a_st[i]) = la.v[i];
+#pragma unroll
+      for (int i = 0; i < decltype(lb)::kVecs; ++i) *reinterpret_cast<floatx4 *>(bn + b_st[i]) = lb.v[i];
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: C = alpha*acc + beta*C for the in-range elements.  For a fixed
+  // register, the MI lanes of a group write MI consecutive floats of one row.
+  const int row0 = m0 + wm * T::WTM;
+  const int col0 = n0 + wn * T::WTN + li;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int col = col0 + j * MI;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) {
+        const int row = row0 + i * MI + acc_row<MI>(g, r);
+        if (row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
+      }
+    }
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+static int launch_mfma(const Problem &p, hipStream_t stream) {
+  const long long tiles_m = ((long long)p.M + BM - 1) / BM;
+  const long long tiles_n = ((long long)p.N + BN - 1) / BN;
+  if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
+  const int group_m = 8;
+  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const dim3 block(WAVES_M * WAVES_N * 64);
+  const int tm = (int)tiles_m, tn = (int)tiles_n;
+  const bool va = a_vec_ok(p), vb = b_vec_ok(p);
+  if (va && vb) {
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, true, true>), grid, block, 0,
+                       stream, p, tm, tn, group_m);
+  } else if (va) {
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, true, false>), grid, block, 0,
+                       stream, p, tm, tn, group_m);
+  } else if (vb) {
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, false, true>), grid, block, 0,
+                       stream, p, tm, tn, group_m);
+  } else {
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, false, false>), grid, block, 0,
+                       stream, p, tm, tn, group_m);
+  }
+  return 0;
+}
+
+int launch_mfma32_128x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 128, 128, 16, 2, 2>(p, s); }
+int launch_mfma32_128x128x32_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 128, 128, 32, 2, 2>(p, s); }
+int launch_mfma32_256x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 256, 128, 16, 2, 2>(p, s); }
+int launch_mfma32_256x256x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 256, 256, 16, 2, 2>(p, s); }
+int launch_mfma32_64x64x16_1x1(const Problem &p, hipStream_t s) { return launch_mfma<32, 64, 64, 16, 1, 1>(p, s); }
+int launch_mfma16_128x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<16, 128, 128, 16, 2, 2>(p, s); }
+int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<16, 64, 64, 16, 2, 2>(p, s); }
+
+}  // namespace sg950

@@ -1,0 +1,71 @@
+// sgemm_simple.hip -- one output element per lane, and the C = beta*C kernel.
+//
+// The one-thread-per-output kernel is the starting point of every page ("The
+// road to a fast GEMM", sections "v0 to v1: the naive version and
+// coalescing"; "Optimizing SGEMM in CUDA", "Kernel 1"): a thread walks a row
+// of A and a column of B.  What decides its speed is which matrix index runs
+// along the lanes of a wavefront: here the 64 lanes of a wave take 64
+// consecutive columns of one row of C, so each load of B and each store of C
+// is one contiguous 256-byte access, and the load of A is a single address
+// broadcast to all lanes.  It handles any shape, leading dimension and
+// alignment and serves the tiny problems where a tiled kernel would leave most
+// of its tile empty.
+#include "sgemm_common.hpp"
+#include "sgemm_launch.hpp"
+
+namespace sg950 {
+
+constexpr int kSimpleCols = 64;  // one wave along N
+constexpr int kSimpleRows = 4;   // four waves per workgroup, one row each
+
+__global__ __launch_bounds__(kSimpleCols *kSimpleRows) void simple_kernel(Problem p) {
+  const int col = blockIdx.y * kSimpleCols + (threadIdx.x & (kSimpleCols - 1));
+  const int row = blockIdx.x * kSimpleRows + (threadIdx.x >> 6);
+  if (row >= p.M || col >= p.N) return;  // no barrier in this kernel
+  const float *a = p.A + (size_t)row * p.lda;
+  const float *b = p.B + col;
+  const size_t ldb = (size_t)p.ldb;
+  float acc = 0.0f;
+  int k = 0;
+  // Four independent partial sums hide the FMA latency; they are combined in a
+  // fixed order, so the result is still a plain fp32 sum of the K products.
+  float acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+  for (; k + 4 <= p.K; k += 4) {
+    acc = fmaf(a[k], b[(size_t)k * ldb], acc);
+    acc1 = fmaf(a[k + 1], b[(size_t)(k + 1) * ldb], acc1);
+    acc2 = fmaf(a[k + 2], b[(size_t)(k + 2) * ldb], acc2);
+    acc3 = fmaf(a[k + 3], b[(size_t)(k + 3) * ldb], acc3);
+  }
+  for (; k < p.K; ++k) acc = fmaf(a[k], b[(size_t)k * ldb], acc);
+  acc = (acc + acc1) + (acc2 + acc3);
+  store_out(p.C + (size_t)row * p.ldc + col, acc, p.alpha, p.beta);
+}
+
+// C = beta * C (beta == 0 writes zeros without reading C).
+__global__ __launch_bounds__(256) void scale_kernel(int M, int N, float beta, float *C, int ldc) {
+  const int col = blockIdx.y * 64 + (threadIdx.x & 63);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M || col >= N) return;
+  float *c = C + (size_t)row * ldc + col;
+  *c = (beta == 0.0f) ? 0.0f : beta * *c;
+}
+
+int launch_simple(const Problem &p, hipStream_t stream) {
+  const long long gx = ((long long)p.M + kSimpleRows - 1) / kSimpleRows;
+  const long long gy = ((long long)p.N + kSimpleCols - 1) / kSimpleCols;
+  if (gx > 0x7fffffffLL || gy > 65535) return -1;
+  hipLaunchKernelGGL(simple_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kSimpleCols * kSimpleRows),
+                     0, stream, p);
+  return 0;
+}
+
+int launch_scale(int M, int N, float beta, float *C, int ldc, hipStream_t stream) {
+  const long long gx = ((long long)M + 3) / 4;
+  const long long gy = ((long long)N + 63) / 64;
+  if (gx > 0x7fffffffLL || gy > 65535) return -1;
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, M, N,
+                     beta, C, ldc);
+  return 0;
+}
+
+}  // namespace sg950

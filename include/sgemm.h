@@ -1,0 +1,109 @@
+/*
+ * sgemm.h -- single-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined in "The road to a fast GEMM" (section "The
+ * problem and the ceiling"):
+ *
+ *     C = alpha * A * B + beta * C
+ *
+ * with A of size MxK, B of size KxN and C of size MxN, every matrix row-major
+ * FP32.  Each C[i,j] is the dot product of row i of A and column j of B
+ * ("Optimizing SGEMM in CUDA", section "What is a SGEMM?").  The pages' kernels
+ * take (M, N, K, alpha, A, B, beta, C) with packed rows; this interface adds a
+ * leading dimension per matrix, as the vendor call on those pages does
+ * ("Optimizing SGEMM in CUDA", section "cuBLAS implementation"), and a stream.
+ *
+ * Layout.  Element (i,k) of A is A[i*lda + k], element (k,j) of B is
+ * B[k*ldb + j], element (i,j) of C is C[i*ldc + j].  Elements in the gap between
+ * a row's length and its leading dimension are never read or written.
+ *
+ * Ownership.  Every matrix pointer is a device pointer on the calling thread's
+ * current HIP device, owned by the caller.  The library allocates no device
+ * memory, keeps no per-call state and may be called from several threads.
+ *
+ * Asynchrony.  A call validates its arguments on the host, enqueues its
+ * kernel(s) on `stream` (a hipStream_t; NULL means the default stream) and
+ * returns without synchronising.  C must not overlap A or B.
+ *
+ * Arithmetic.  Strict FP32: products and sums are IEEE single precision with
+ * round-to-nearest-even (fused multiply-add where the hardware fuses); no input
+ * is rounded to a narrower format.  The order of the K-sum is unspecified, so
+ * results on real-valued data may differ from another correct implementation
+ * by rounding; on integer-valued data whose partial sums stay below 2^24 they
+ * are exact.
+ *
+ * Special cases (BLAS conventions; the pages are silent on them):
+ *   - M == 0 or N == 0: nothing is done.
+ *   - alpha == 0 or K == 0: A and B are not read; C = beta * C.
+ *   - beta == 0: C is not read, so NaN or Inf already in C does not propagate.
+ *   - beta == 1 with alpha == 0 or K == 0: nothing is enqueued.
+ *
+ * Errors.  Every function returns SGEMM_OK (0) or a negative status; nothing
+ * aborts or prints.  Argument errors are detected before any HIP call.
+ */
+#ifndef SGEMM_GFX950_H
+#define SGEMM_GFX950_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_OK 0
+#define SGEMM_ERR_DIM (-1)     /* M, N or K negative, or a grid too large */
+#define SGEMM_ERR_LD (-2)      /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define SGEMM_ERR_PTR (-3)     /* a matrix that must be read or written is NULL */
+#define SGEMM_ERR_LAUNCH (-4)  /* the HIP runtime rejected a kernel launch */
+#define SGEMM_ERR_DEVICE (-5)  /* the current device is not gfx950, or no device */
+#define SGEMM_ERR_VARIANT (-6) /* sgemm_ex: variant index out of range */
+
+/*
+ * C = alpha * A * B + beta * C on `stream`, with the kernel variant and tile
+ * configuration chosen from the shape, the operands' alignment and beta.
+ *
+ *   M, N, K   matrix sizes (>= 0)
+ *   alpha     scale of A*B
+ *   A, lda    MxK matrix, row stride lda >= max(1, K) elements
+ *   B, ldb    KxN matrix, row stride ldb >= max(1, N) elements
+ *   beta      scale of the incoming C
+ *   C, ldc    MxN matrix, read (when beta != 0) and written, ldc >= max(1, N)
+ *   stream    hipStream_t to enqueue on; NULL = default stream
+ *
+ * Returns SGEMM_OK or a negative SGEMM_ERR_* status.
+ */
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+          const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+
+/*
+ * As sgemm(), but runs kernel variant `variant` (0 <= variant <
+ * sgemm_num_variants()); -1 means the automatic choice.  Every variant accepts
+ * every valid problem (any shape, leading dimension and alignment), so the
+ * variants can be compared on the same inputs.
+ */
+int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc,
+             void *stream, int variant);
+
+/* Number of kernel variants, and a stable name for each ("" when out of range). */
+int sgemm_num_variants(void);
+const char *sgemm_variant_name(int variant);
+
+/*
+ * The variant sgemm() would run for this problem (no launch, no HIP call), or
+ * a negative SGEMM_ERR_* status for invalid arguments.  Returns -100 when the
+ * problem needs no GEMM kernel (M or N zero, or alpha == 0 or K == 0).
+ */
+int sgemm_select_variant(int M, int N, int K, float alpha, const float *A,
+                         int lda, const float *B, int ldb, float beta,
+                         const float *C, int ldc);
+
+/* Short English description of a status code (never NULL). */
+const char *sgemm_status_string(int status);
+
+/* Interface version, currently 1. */
+int sgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_GFX950_H */

@@ -1,0 +1,143 @@
+"""CPU tests of the C boundary: the library loads, exports what the headers
+declare, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import dense_fp32_gemm_sgemm_amd as sg
+from dense_fp32_gemm_sgemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("sgemm.h", "sgemm_ceiling.h")]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY):
+        from dense_fp32_gemm_sgemm_amd import _build
+        _build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(sgemm\w*)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_headers_declare_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_symbol_exported(lib, name):
+    assert hasattr(lib, name), name
+
+
+def test_exported_symbols_are_c_linkage(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (sgemm\w*)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_variant_registry(lib):
+    n = sg.sgemm_num_variants()
+    names = sg.variant_names()
+    assert n == len(names) >= 3 and len(set(names)) == n
+    assert names[0] == "simple"
+    assert any(x.startswith("mfma32") for x in names) and any(x.startswith("valu") for x in names)
+    assert sg.sgemm_variant_name(n) == "" and sg.sgemm_variant_name(-1) == ""
+    assert sg.sgemm_version() == 1
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails or returns before any HIP call
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_DIM),
+    ((4, -1, 4, 1.0, FAKE, 4, FAKE, 1, 0.0, FAKE, 1), sg.SGEMM_ERR_DIM),
+    ((4, 4, -2, 1.0, FAKE, 1, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_DIM),
+    ((4, 4, 8, 1.0, FAKE, 7, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_LD),
+    ((4, 4, 8, 1.0, FAKE, 8, FAKE, 3, 0.0, FAKE, 4), sg.SGEMM_ERR_LD),
+    ((4, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 3), sg.SGEMM_ERR_LD),
+    ((4, 4, 0, 1.0, None, 0, None, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_LD),   # lda >= 1
+    ((4, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, None, 4), sg.SGEMM_ERR_PTR),
+    ((4, 4, 8, 1.0, None, 8, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_PTR),
+    ((4, 4, 8, 1.0, FAKE, 8, None, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_PTR),
+    ((0, 4, 8, 1.0, None, 8, None, 4, 0.0, None, 4), sg.SGEMM_OK),      # M == 0: no-op
+    ((4, 0, 8, 1.0, None, 8, None, 1, 0.0, None, 1), sg.SGEMM_OK),      # N == 0: no-op
+    ((4, 4, 8, 0.0, None, 8, None, 4, 1.0, FAKE, 4), sg.SGEMM_OK),      # alpha 0, beta 1
+    ((4, 4, 0, 2.0, None, 1, None, 4, 1.0, FAKE, 4), sg.SGEMM_OK),      # K 0, beta 1
+])
+def test_argument_checks_before_any_hip_call(lib, args, status):
+    assert sg.sgemm(*args, 0) == status
+    assert sg.sgemm_ex(*args, 0, -1) == status
+
+
+def test_variant_index_checked(lib):
+    args = (4, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 4)
+    n = sg.sgemm_num_variants()
+    assert sg.sgemm_ex(*args, 0, n) == sg.SGEMM_ERR_VARIANT
+    assert sg.sgemm_ex(*args, 0, -2) == sg.SGEMM_ERR_VARIANT
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        s = sg.sgemm_status_string(st)
+        assert s and s != "unknown status"
+    assert sg.sgemm_status_string(12345) == "unknown status"
+
+
+def test_select_variant_is_pure(lib):
+    # No launch, no HIP call: usable without a GPU.
+    big = sg.sgemm_select_variant(4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE, 4096)
+    assert sg.sgemm_variant_name(big).startswith("mfma32")
+    tiny = sg.sgemm_select_variant(3, 5, 7, 1.0, FAKE, 7, FAKE, 5, 0.0, FAKE, 5)
+    assert sg.sgemm_variant_name(tiny) == "simple"
+    assert sg.sgemm_select_variant(0, 5, 7, 1.0, None, 7, None, 5, 0.0, None, 5) == sg.SGEMM_NO_KERNEL
+    assert sg.sgemm_select_variant(3, 5, 7, 0.0, None, 7, None, 5, 0.5, FAKE, 5) == sg.SGEMM_NO_KERNEL
+    assert sg.sgemm_select_variant(3, 5, 7, 1.0, FAKE, 6, FAKE, 5, 0.0, FAKE, 5) == sg.SGEMM_ERR_LD
+    for shape in ((4095, 4097, 1023), (127, 129, 17), (1, 4096, 4096), (8192, 1024, 8192)):
+        M, N, K = shape
+        v = sg.sgemm_select_variant(M, N, K, 1.0, FAKE, K, FAKE, N, 0.0, FAKE, N)
+        assert 0 <= v < sg.sgemm_num_variants()
+
+
+def test_ceiling_argument_checks(lib):
+    assert sg.sgemm_ceiling_mfma(8, 1, 1, FAKE)[0] == -1
+    assert sg.sgemm_ceiling_mfma(32, 0, 1, FAKE)[0] == -1
+    assert sg.sgemm_ceiling_fma(1, 0, FAKE)[0] == -1
+    assert sg.sgemm_ceiling_copy(FAKE, FAKE, 6, 1) == -1
+    assert sg.sgemm_ceiling_copy(FAKE + 4, FAKE, 8, 1) == -1
+
+
+def test_no_device_is_reported_not_crashed(lib):
+    """On a machine without a gfx950 GPU a valid call returns
+    SGEMM_ERR_DEVICE (run in a child process; skipped when a GPU is present)."""
+    code = (
+        "import torch, sys\n"
+        "if torch.cuda.is_available(): sys.exit(3)\n"
+        "import dense_fp32_gemm_sgemm_amd as sg\n"
+        "st = sg.sgemm(4, 4, 4, 1.0, 0x1000, 4, 0x1000, 4, 0.0, 0x1000, 4, 0)\n"
+        "sys.exit(0 if st == sg.SGEMM_ERR_DEVICE else 1)\n")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    if res.returncode == 3:
+        pytest.skip("a GPU is visible")
+    assert res.returncode == 0, res.stdout + res.stderr
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIBRARY", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()

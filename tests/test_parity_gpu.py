@@ -1,0 +1,290 @@
+"""GPU parity: the HIP SGEMM against the fp64 CPU oracle, through the C ABI.
+
+Bars (from the operation's definition and the tolerance it is held to):
+  * integer inputs in {-4..4}: every partial sum is an integer below 2^24, so
+    the fp32 result must equal the oracle exactly;
+  * real inputs: max |C - C_ref| / (sum_k |A_ik||B_kj| + |beta C_ij|) <= 1e-5;
+  * permutation inputs: the product only moves values, so it is exact and
+    pins the matrix-core lane maps.
+Every kernel variant is checked on small shapes that span several tiles and a
+ragged tail; the full-size workloads run through the automatic choice, which
+is the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import dense_fp32_gemm_sgemm_amd as sg  # noqa: E402
+from tests.gpu_util import run  # noqa: E402
+from workloads import (ACCUM, ACCUM_INT, HEADLINE, SMALL, SMALL_INT, draw,  # noqa: E402
+                       draw_workload, ragged_workloads, sweep_workloads)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+VARIANTS = list(range(sg.sgemm_num_variants())) if True else []
+VNAMES = [sg.sgemm_variant_name(v) for v in VARIANTS]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_real(C, A, B, Cin, alpha, beta, what):
+    ref, den = oracle.gemm(A, B, Cin, alpha, beta)
+    err = oracle.normalized_error(C, ref, den)
+    assert err <= TOL, "%s: normalized error %.3g > %g" % (what, err, TOL)
+    return err
+
+
+def check_exact(C, A, B, Cin, alpha, beta, what):
+    ref, _ = oracle.gemm(A, B, Cin, alpha, beta)
+    bad = np.argwhere(C.astype(np.float64) != ref)
+    assert bad.size == 0, "%s: %d mismatches, first at %s (%r vs %r)" % (
+        what, len(bad), tuple(bad[0]), C[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+# ---------------------------------------------------------------- every variant
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_permutation_pins_lane_maps(variant):
+    """A = P (a row permutation) gives P@B exactly; B = Q permutes columns."""
+    rng = np.random.default_rng(31)
+    M = K = 200
+    N = 328
+    perm = rng.permutation(K)
+    P = np.zeros((M, K), np.float32)
+    P[np.arange(M), perm] = 1.0
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    say("perm rows", VNAMES[variant])
+    C = run(P, B, variant=variant)
+    assert np.array_equal(C, B[perm]), VNAMES[variant]
+    q = rng.permutation(N)
+    Q = np.zeros((N, N), np.float32)
+    Q[q, np.arange(N)] = 1.0
+    A = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+    say("perm cols", VNAMES[variant])
+    C = run(A, Q, variant=variant)
+    assert np.array_equal(C, A[:, q]), VNAMES[variant]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_small_config_every_variant(variant):
+    """256^3, alpha=1, beta=0: real inputs to 1e-5, integer copy exact."""
+    A, B, _ = draw_workload(SMALL)
+    say("small real", VNAMES[variant])
+    C = run(A, B, variant=variant)
+    check_real(C, A, B, None, 1.0, 0.0, VNAMES[variant])
+    Ai, Bi, _ = draw_workload(SMALL_INT)
+    say("small int", VNAMES[variant])
+    C = run(Ai, Bi, variant=variant)
+    check_exact(C, Ai, Bi, None, 1.0, 0.0, VNAMES[variant])
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+@pytest.mark.parametrize("shape", [(300, 200, 100), (129, 257, 33), (64, 64, 64), (65, 63, 17),
+                                   (520, 130, 1000)])
+def test_ragged_every_variant(variant, shape):
+    """Shapes that cut tiles in M, N and K; accumulate form (alpha, beta)."""
+    M, N, K = shape
+    A, B, Cin = draw(M, N, K, seed=M + N + K, with_c=True)
+    say("ragged", shape, VNAMES[variant])
+    C = run(A, B, Cin, 1.5, 0.5, variant=variant, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "%s %s" % (VNAMES[variant], shape))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=variant)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s int" % (VNAMES[variant], shape))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_bruteforce_tiny_shapes(variant):
+    """Every (M,N,K) in [1..9]^3 and {63,64,65}^3, integer data, exact."""
+    shapes = [(m, n, k) for m in range(1, 10) for n in range(1, 10) for k in range(1, 10)]
+    shapes += [(m, n, k) for m in (63, 64, 65) for n in (63, 64, 65) for k in (63, 64, 65)]
+    say("bruteforce", VNAMES[variant], len(shapes), "shapes")
+    for (M, N, K) in shapes:
+        A, B, Cin = draw(M, N, K, seed=1000 + M * 100 + N * 10 + K, kind="int", with_c=True)
+        C = run(A, B, Cin, 1.0, 1.0, variant=variant)
+        check_exact(C, A, B, Cin, 1.0, 1.0, "%s (%d,%d,%d)" % (VNAMES[variant], M, N, K))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_leading_dims_alignment_and_canaries(variant):
+    """Padded leading dimensions with NaN gaps, misaligned bases; nothing
+    outside C's elements is written and no gap is read."""
+    M, N, K = 150, 140, 70
+    A, B, Cin = draw(M, N, K, seed=77, kind="int", with_c=True)
+    cases = [((K + 5, N + 3, N + 7), (0, 0, 0)),
+             ((K + 4, N + 4, N + 4), (0, 0, 0)),
+             ((K, N, N), (1, 2, 3)),
+             ((K + 3, N + 1, N + 2), (3, 1, 2))]
+    for lds, offs in cases:
+        say("ld/offset", VNAMES[variant], lds, offs)
+        C = run(A, B, Cin, 1.0, 1.0, variant=variant, lds=lds, offsets=offs, check_outside=True)
+        check_exact(C, A, B, Cin, 1.0, 1.0, "%s lds=%s offs=%s" % (VNAMES[variant], lds, offs))
+
+
+# ---------------------------------------------------------------- special cases
+
+def test_beta_zero_ignores_nan_in_c():
+    A, B, _ = draw(200, 180, 90, seed=5)
+    say("beta=0 with NaN C")
+    C = run(A, B, None, 1.0, 0.0)
+    assert np.all(np.isfinite(C))
+    check_real(C, A, B, None, 1.0, 0.0, "beta=0")
+
+
+def test_alpha_zero_and_k_zero_scale_c():
+    rng = np.random.default_rng(6)
+    Cin = rng.integers(-4, 5, (70, 90)).astype(np.float32)
+    A = np.full((70, 30), np.nan, np.float32)   # must not be read
+    B = np.full((30, 90), np.nan, np.float32)
+    say("alpha=0")
+    C = run(A, B, Cin, 0.0, 0.5)
+    assert np.array_equal(C, 0.5 * Cin)
+    C = run(A, B, Cin, 0.0, 0.0)
+    assert np.all(C == 0)
+    C = run(A, B, Cin, 0.0, 1.0)
+    assert np.array_equal(C, Cin)
+    say("K=0")
+    C = run(np.zeros((70, 0), np.float32), np.zeros((0, 90), np.float32), Cin, 2.0, -1.5)
+    assert np.array_equal(C, -1.5 * Cin)
+
+
+def test_empty_problems_are_noops():
+    for (M, N, K) in ((0, 5, 5), (5, 0, 5), (0, 0, 0)):
+        A, B, _ = draw(M, N, K, seed=1)
+        C = run(A, B, np.ones((M, N), np.float32), 1.0, 1.0)
+        assert C.shape == (M, N)
+
+
+def test_nan_in_a_poisons_its_row_only():
+    A, B, _ = draw(130, 140, 60, seed=8)
+    A[7, 13] = np.nan
+    say("NaN in A")
+    C = run(A, B, np.zeros((130, 140), np.float32), 1.0, 0.0)
+    assert np.all(np.isnan(C[7]))
+    rest = np.delete(C, 7, axis=0)
+    assert np.all(np.isfinite(rest))
+
+
+def test_repeatable_bitwise():
+    A, B, Cin = draw(1000, 1000, 1000, seed=12, with_c=True)
+    say("repeatability")
+    C1 = run(A, B, Cin, 1.5, 0.5)
+    C2 = run(A, B, Cin, 1.5, 0.5)
+    assert np.array_equal(C1, C2)
+
+
+def test_runs_on_a_side_stream():
+    A, B, _ = draw(512, 384, 256, seed=13)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.full((512, 384), float("nan"), device="cuda")
+    s = torch.cuda.Stream()
+    say("side stream")
+    with torch.cuda.stream(s):
+        sg.gemm(dA, dB, dC, 1.0, 0.0)
+    s.synchronize()
+    check_real(dC.cpu().numpy(), A, B, None, 1.0, 0.0, "side stream")
+
+
+def test_error_status_raised_from_python():
+    dA = torch.zeros((4, 8), device="cuda")
+    dB = torch.zeros((8, 4), device="cuda")
+    dC = torch.zeros((4, 4), device="cuda")
+    with pytest.raises(sg.SgemmError):
+        sg.gemm(dA, dB, dC, variant=sg.sgemm_num_variants())
+    with pytest.raises(TypeError):
+        sg.gemm(dA.double(), dB, dC)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+_cache = {}
+
+
+def _ref(key, fn):
+    if key not in _cache:
+        _cache[key] = fn()
+    return _cache[key]
+
+
+def test_headline_4096_full_check():
+    """M=N=K=4096, alpha=1, beta=0 through the automatic choice; every
+    element checked."""
+    A, B, _ = draw_workload(HEADLINE)
+    say("headline 4096^3 variant", sg.sgemm_variant_name(
+        sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 1, 4096, 1, 4096, 0.0, 1, 4096)))
+    C = run(A, B)
+    err = check_real(C, A, B, None, 1.0, 0.0, "4096^3")
+    say("headline normalized error %.3g" % err)
+
+
+def test_accumulate_4096_full_check_and_integer_copy():
+    A, B, Cin = draw_workload(ACCUM)
+    say("accumulate 4096^3 real")
+    C = run(A, B, Cin, ACCUM.alpha, ACCUM.beta)
+    err = check_real(C, A, B, Cin, ACCUM.alpha, ACCUM.beta, "4096^3 accumulate")
+    say("accumulate normalized error %.3g" % err)
+    Ai, Bi, Ci = draw_workload(ACCUM_INT)
+    say("accumulate 4096^3 int")
+    C = run(Ai, Bi, Ci, ACCUM_INT.alpha, ACCUM_INT.beta)
+    check_exact(C, Ai, Bi, Ci, ACCUM_INT.alpha, ACCUM_INT.beta, "4096^3 accumulate int")
+    # dyadic scalars on integer data stay exact too
+    C = run(Ai, Bi, Ci, 1.5, 0.5)
+    check_exact(C, Ai, Bi, Ci, 1.5, 0.5, "4096^3 int alpha=1.5 beta=0.5")
+
+
+@pytest.mark.parametrize("w", [w for w in sweep_workloads() if w.M < 8192], ids=lambda w: w.name)
+def test_sweep_full_check(w):
+    A, B, _ = draw_workload(w)
+    say("sweep", w.name)
+    C = run(A, B)
+    check_real(C, A, B, None, 1.0, 0.0, w.name)
+    Ai, Bi, _ = draw(w.M, w.N, w.K, seed=w.seed, kind="int")
+    C = run(Ai, Bi)
+    check_exact(C, Ai, Bi, None, 1.0, 0.0, w.name + " int")
+
+
+def _sampled_check(A, B, C, alpha, beta, Cin, nrows, ncols, seed, what):
+    rng = np.random.default_rng(seed)
+    M, N = C.shape
+    rows = np.sort(rng.choice(M, size=min(nrows, M), replace=False))
+    cols = np.sort(rng.choice(N, size=min(ncols, N), replace=False))
+    ref, den = oracle.gemm(A, B, Cin, alpha, beta, rows=rows)
+    err_r = oracle.normalized_error(C[rows], ref, den)
+    ref, den = oracle.gemm(A, B, Cin, alpha, beta, cols=cols)
+    err_c = oracle.normalized_error(C[:, cols], ref, den)
+    assert max(err_r, err_c) <= TOL, "%s: sampled normalized error %.3g" % (what, max(err_r, err_c))
+
+
+def test_sweep_8192_sampled():
+    """8192^3: 256 whole rows and 256 whole columns (each crosses every tile
+    boundary along its length) against the oracle."""
+    w = [w for w in sweep_workloads() if w.M == 8192][0]
+    A, B, _ = draw_workload(w)
+    say("sweep 8192^3")
+    C = run(A, B)
+    _sampled_check(A, B, C, 1.0, 0.0, None, 256, 256, 8192, w.name)
+
+
+@pytest.mark.parametrize("w", ragged_workloads(), ids=lambda w: w.name)
+def test_rectangular_and_ragged(w):
+    A, B, _ = draw_workload(w)
+    say("shape", w.name)
+    C = run(A, B)
+    if w.M * w.N * w.K > 2 ** 36:
+        _sampled_check(A, B, C, 1.0, 0.0, None, 256, 256, w.seed, w.name)
+    else:
+        check_real(C, A, B, None, 1.0, 0.0, w.name)
+    Ai, Bi, _ = draw(w.M, w.N, w.K, seed=w.seed, kind="int")
+    C = run(Ai, Bi)
+    if w.M * w.N * w.K > 2 ** 36:
+        rows = np.arange(0, w.M, max(1, w.M // 128))
+        ref, _ = oracle.gemm(Ai, Bi, rows=rows)
+        assert oracle.exact_match(C[rows], ref), w.name + " int"
+    else:
+        check_exact(C, Ai, Bi, None, 1.0, 0.0, w.name + " int")
