@@ -64,16 +64,71 @@ def arithmetic_intensity(M, N, K, beta=0.0) -> float:
     return flops(M, N, K) / min_bytes(M, N, K, beta)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources, so stored counter readings can be matched to
-    the kernels they were taken from."""
+def tile_global_bytes(M: int, N: int, K: int, BM: int, BN: int) -> float:
+    """Bytes a tiled kernel loads from global memory (L2 or HBM) for A and B:
+    each of the ceil(M/BM)*ceil(N/BN) tiles reads BM rows of A and BN columns
+    of B over the whole of K ("The road to a fast GEMM", Exercise 1)."""
+    tiles = -(-M // BM) * -(-N // BN)
+    return tiles * 4.0 * (BM + BN) * K
+
+
+def lds_reads_per_fma(TM: int, TN: int) -> float:
+    """Operand reads per multiply-add for a TM x TN register tile: an outer
+    product of TM values of A and TN of B feeds TM*TN multiply-adds."""
+    return (TM + TN) / float(TM * TN)
+
+
+# The sources that define the matrix-core kernel whose counters are stored.
+KERNEL_FILES = ("sgemm_mfma.hip", "sgemm_tiles.hpp", "sgemm_common.hpp")
+
+
+def kernel_source_hash(files=KERNEL_FILES) -> str:
+    """Hash of the kernel's HIP sources, so stored counter readings can be
+    matched to the code they were taken from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_gemm_sgemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(files):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def _counter_means(path, kernel_prefix):
+    """Mean counter value per counter name over the dispatches of kernels whose
+    name starts with kernel_prefix, from a rocprofv3 counter_collection.csv."""
+    import csv
+    vals = {}
+    names = set()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Kernel_Name"].startswith(kernel_prefix):
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                names.add(r["Kernel_Name"])
+    return {k: sum(v) / len(v) for k, v in vals.items()}, sorted(names), {k: len(v) for k, v in vals.items()}
+
+
+def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, variant,
+                          copy_bytes=256 * 1024 * 1024):
+    """HBM-side bytes per launch of the GEMM kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a streaming copy that reads and writes copy_bytes."""
+    gemm_prefix = "void sg950::mfma_kernel"
+    f, fnames, fn = _counter_means(fetch_csv, gemm_prefix)
+    w, _, wn = _counter_means(write_csv, gemm_prefix)
+    cf, _, _ = _counter_means(copy_fetch_csv, "sg950::copy_kernel")
+    cw, _, _ = _counter_means(copy_write_csv, "sg950::copy_kernel")
+    fetch_scale = copy_bytes / (cf["FETCH_SIZE"] * 1024.0)
+    write_scale = copy_bytes / (cw["WRITE_SIZE"] * 1024.0)
+    fetch_b = f["FETCH_SIZE"] * 1024.0 * fetch_scale
+    write_b = w["WRITE_SIZE"] * 1024.0 * write_scale
+    return {"variant": variant, "kernel": fnames, "source_hash": kernel_source_hash(),
+            "fetch_kib_raw": f["FETCH_SIZE"], "write_kib_raw": w["WRITE_SIZE"],
+            "dispatches": {"fetch": fn["FETCH_SIZE"], "write": wn["WRITE_SIZE"]},
+            "copy_fetch_kib_raw": cf["FETCH_SIZE"], "copy_write_kib_raw": cw["WRITE_SIZE"],
+            "fetch_scale": fetch_scale, "write_scale": write_scale,
+            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+            "bytes_per_launch": fetch_b + write_b,
+            "algorithmic_bytes_per_launch": min_bytes(4096, 4096, 4096, 0.0)}
 
 
 # ---------------------------------------------------------------- GPU side
@@ -230,9 +285,9 @@ def cpu_baseline(target_s: float = 12.0):
                       "oracle, OpenMP over rows), %.1f s" % (nrows, dt)}
 
 
-def stored_traffic():
+def stored_traffic(variant: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources."""
+    were taken on the current kernel sources and the same variant."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
@@ -240,9 +295,9 @@ def stored_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("variant") != variant:
         return None
-    return t.get("bytes_per_launch")
+    return round(t.get("bytes_per_launch"))
 
 
 def bench_problem(prob: Problem, steps: int, warmup: int, variant=-1):
@@ -266,9 +321,27 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--variants", action="store_true")
     ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--matrix", action="store_true",
+                    help="every variant on every sweep and rectangular shape")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the stored traffic figure from four counter_collection.csv files")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="one 256 MiB streaming copy (to scale HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     args = ap.parse_args(argv)
+
+    if args.traffic_from:
+        from_ = args.traffic_from
+        # the variant the automatic choice runs on the 4096^3 problem (no GPU needed)
+        import dense_fp32_gemm_sgemm_amd as sg
+        v = sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 1, 4096, 1, 4096, 0.0, 1, 4096)
+        t = traffic_from_counters(*from_, variant=sg.sgemm_variant_name(v))
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this SGEMM runs whole on a single MI355X and "
@@ -283,7 +356,7 @@ def main(argv=None):
     import dense_fp32_gemm_sgemm_amd as sg
     sg.load()
 
-    if args.sweep or args.variants or args.shape or args.profile:
+    if args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib:
         return run_modes(args)
 
     M = N = K = 4096
@@ -297,7 +370,7 @@ def main(argv=None):
 
     ceilings = None if args.no_ceilings else measure_ceilings()
     cpu = None if args.no_cpu_baseline else cpu_baseline()
-    traffic = stored_traffic()
+    traffic = stored_traffic(vname)
 
     line = {
         "metric": METRIC,
@@ -336,6 +409,18 @@ def run_modes(args):
     from workloads import RAGGED_SHAPES, SWEEP_SIZES
     import dense_fp32_gemm_sgemm_amd as sg
     jobs = []
+    if args.copy_calib:
+        torch = _torch()
+        n = 64 * 1024 * 1024  # 256 MiB per buffer
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty(n, dtype=torch.float32, device="cuda")
+        h = torch.cuda.current_stream().cuda_stream
+        for _ in range(3):
+            assert sg.sgemm_ceiling_copy(src.data_ptr(), dst.data_ptr(), n, NUM_CUS * 16, h) == 0
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy-calib", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "dispatches": 3}), flush=True)
+        return 0
     if args.profile:
         shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
         prob = Problem(*shape, args.alpha, args.beta, seed=0)
@@ -347,6 +432,10 @@ def run_modes(args):
         return 0
     if args.sweep:
         jobs = [((n, n, n), -1) for n in SWEEP_SIZES] + [(s, -1) for s in RAGGED_SHAPES]
+    elif args.matrix:
+        shapes = [(n, n, n) for n in SWEEP_SIZES] + list(RAGGED_SHAPES)
+        jobs = [(sh, v) for sh in shapes for v in range(sg.sgemm_num_variants())
+                if not (sg.sgemm_variant_name(v) == "simple" and flops(*sh) > 2e10)]
     elif args.variants:
         shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
         jobs = [(shape, v) for v in range(sg.sgemm_num_variants())]
@@ -362,7 +451,7 @@ def run_modes(args):
             steps = 3
         total, per = bench_problem(prob, steps, min(args.warmup, steps), v)
         kern_ms = statistics.median(per)
-        rec = {"mode": "sweep" if args.sweep else "variant", "M": M, "N": N, "K": K,
+        rec = {"mode": "sweep" if args.sweep else ("matrix" if args.matrix else "variant"), "M": M, "N": N, "K": K,
                "beta": args.beta, "variant": name, "steps": steps,
                "kernel_ms_median": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
                "gflops": round(work / (kern_ms * 1e-3) / 1e9, 1),

@@ -28,8 +28,11 @@ const Variant kVariants[] = {
     {"valu_128x128x16", launch_valu_128x128},
     {"mfma32_128x128x16_2x2", launch_mfma32_128x128x16_2x2},
     {"mfma32_128x128x32_2x2", launch_mfma32_128x128x32_2x2},
-    {"mfma32_256x128x16_2x2", launch_mfma32_256x128x16_2x2},
+    {"mfma32_128x128x16_2x2_w4", launch_mfma32_128x128x16_2x2_w4},
+    {"mfma32_256x128x16_2x2_w2", launch_mfma32_256x128x16_2x2_w2},
+    {"mfma32_128x256x16_2x2_w2", launch_mfma32_128x256x16_2x2_w2},
     {"mfma32_256x256x16_2x2", launch_mfma32_256x256x16_2x2},
+    {"mfma32_256x256x16_4x2_w2", launch_mfma32_256x256x16_4x2_w2},
     {"mfma32_64x64x16_1x1", launch_mfma32_64x64x16_1x1},
     {"mfma16_128x128x16_2x2", launch_mfma16_128x128x16_2x2},
     {"mfma16_64x64x16_2x2", launch_mfma16_64x64x16_2x2},
@@ -41,11 +44,14 @@ enum VariantId {
   kValu128 = 1,
   kMfma32_128x128x16 = 2,
   kMfma32_128x128x32 = 3,
-  kMfma32_256x128x16 = 4,
-  kMfma32_256x256x16 = 5,
-  kMfma32_64x64x16 = 6,
-  kMfma16_128x128x16 = 7,
-  kMfma16_64x64x16 = 8,
+  kMfma32_128x128x16_w4 = 4,
+  kMfma32_256x128x16_w2 = 5,
+  kMfma32_128x256x16_w2 = 6,
+  kMfma32_256x256x16 = 7,
+  kMfma32_256x256x16_8w = 8,
+  kMfma32_64x64x16 = 9,
+  kMfma16_128x128x16 = 10,
+  kMfma16_64x64x16 = 11,
 };
 
 constexpr int kNoKernel = -100;
@@ -63,14 +69,29 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda, const 
   return SGEMM_OK;
 }
 
-// The per-shape table.  Filled from measured sweeps on an MI355X; every entry
-// names a variant that handles any shape, so the table only trades speed.
+// The per-shape table.  Every entry names a variant that handles any shape,
+// so the table only trades speed; the thresholds come from a measured sweep
+// of every variant over the square sizes 128..8192 and the rectangular shapes
+// on an MI355X.
+//   * tiny problems are launch-latency bound: one lane per output wins;
+//   * 256x256 tiles (eight waves, one workgroup per CU) are fastest when the
+//     tile count fills the 256 CUs in whole rounds (little tail);
+//   * 128x128 tiles with a 32-deep K slab when there are at least as many
+//     tiles as CUs;
+//   * otherwise 64x64 tiles on the 16x16x4 instruction, which keep the most
+//     CUs busy on small grids.
 int choose_variant(const Problem &p) {
-  const long long mn = (long long)p.M * p.N;
-  const long long work = mn * p.K;
-  if (work <= 64LL * 64 * 64 || p.M < 8 || p.N < 8) return kSimple;
-  if (mn <= 512LL * 512) return kMfma16_64x64x16;
-  return kMfma32_128x128x16;
+  const long long work = (long long)p.M * p.N * p.K;
+  if (p.M < 16 || p.N < 16 || work <= 256LL * 256 * 256) return kSimple;
+  const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256);
+  const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128);
+  const long long cus = 256;
+  if (t256 >= cus) {
+    const long long tail = t256 % cus;
+    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x16_8w;
+  }
+  if (t128 >= cus) return kMfma32_128x128x32;
+  return kMfma16_64x64x16;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other

@@ -76,9 +76,11 @@ __device__ __forceinline__ int acc_row(int g, int r) {
   }
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool VA, bool VB>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void mfma_kernel(Problem p, int tiles_m,
-                                                                        int tiles_n, int group_m) {
+// MINW is the minimum number of waves per SIMD the register allocation must
+// leave room for (two workgroups per CU need MINW = 2 with four-wave groups).
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, bool VA, bool VB>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Problem p, int tiles_m,
+                                                                              int tiles_n, int group_m) {
   using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N>;
   using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
   constexpr int kRegs = MI * MI / 64;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void mfma_kernel(Problem p, 
     }
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW>
 static int launch_mfma(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
@@ -215,27 +217,37 @@ static int launch_mfma(const Problem &p, hipStream_t stream) {
   const int tm = (int)tiles_m, tn = (int)tiles_n;
   const bool va = a_vec_ok(p), vb = b_vec_ok(p);
   if (va && vb) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, true, true>), grid, block, 0,
-                       stream, p, tm, tn, group_m);
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, true, true>), grid, block,
+                       0, stream, p, tm, tn, group_m);
   } else if (va) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, true, false>), grid, block, 0,
-                       stream, p, tm, tn, group_m);
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, true, false>), grid, block,
+                       0, stream, p, tm, tn, group_m);
   } else if (vb) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, false, true>), grid, block, 0,
-                       stream, p, tm, tn, group_m);
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, false, true>), grid, block,
+                       0, stream, p, tm, tn, group_m);
   } else {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, false, false>), grid, block, 0,
-                       stream, p, tm, tn, group_m);
+    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, false, false>), grid, block,
+                       0, stream, p, tm, tn, group_m);
   }
   return 0;
 }
 
-int launch_mfma32_128x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 128, 128, 16, 2, 2>(p, s); }
-int launch_mfma32_128x128x32_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 128, 128, 32, 2, 2>(p, s); }
-int launch_mfma32_256x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 256, 128, 16, 2, 2>(p, s); }
-int launch_mfma32_256x256x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<32, 256, 256, 16, 2, 2>(p, s); }
-int launch_mfma32_64x64x16_1x1(const Problem &p, hipStream_t s) { return launch_mfma<32, 64, 64, 16, 1, 1>(p, s); }
-int launch_mfma16_128x128x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<16, 128, 128, 16, 2, 2>(p, s); }
-int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t s) { return launch_mfma<16, 64, 64, 16, 2, 2>(p, s); }
+#define SG950_MFMA_LAUNCHER(name, MI, BM, BN, BK, WM, WN, MINW) \
+  int launch_##name(const Problem &p, hipStream_t s) {        \
+    return launch_mfma<MI, BM, BN, BK, WM, WN, MINW>(p, s);     \
+  }
+
+SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2, 32, 128, 128, 16, 2, 2, 1)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2, 32, 128, 128, 32, 2, 2, 1)
+SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2_w4, 32, 128, 128, 16, 2, 2, 4)
+SG950_MFMA_LAUNCHER(mfma32_256x128x16_2x2_w2, 32, 256, 128, 16, 2, 2, 2)
+SG950_MFMA_LAUNCHER(mfma32_128x256x16_2x2_w2, 32, 128, 256, 16, 2, 2, 2)
+SG950_MFMA_LAUNCHER(mfma32_256x256x16_2x2, 32, 256, 256, 16, 2, 2, 1)
+SG950_MFMA_LAUNCHER(mfma32_256x256x16_4x2_w2, 32, 256, 256, 16, 4, 2, 2)
+SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1, 32, 64, 64, 16, 1, 1, 1)
+SG950_MFMA_LAUNCHER(mfma16_128x128x16_2x2, 16, 128, 128, 16, 2, 2, 1)
+SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2, 16, 64, 64, 16, 2, 2, 1)
+
+#undef SG950_MFMA_LAUNCHER
 
 }  // namespace sg950
