@@ -26,13 +26,11 @@ struct Variant {
 const Variant kVariants[] = {
     {"simple", launch_simple},
     {"valu_128x128x16", launch_valu_128x128},
-    {"mfma32_128x128x16_2x2", launch_mfma32_128x128x16_2x2},
+    {"mfma32_256x256x32_4x2", launch_mfma32_256x256x32_4x2},
+    {"mfma32_256x256x16_4x2", launch_mfma32_256x256x16_4x2},
     {"mfma32_128x128x32_2x2", launch_mfma32_128x128x32_2x2},
+    {"mfma32_128x128x32_2x2_pipe", launch_mfma32_128x128x32_2x2_pipe},
     {"mfma32_128x128x16_2x2_w4", launch_mfma32_128x128x16_2x2_w4},
-    {"mfma32_256x128x16_2x2_w2", launch_mfma32_256x128x16_2x2_w2},
-    {"mfma32_128x256x16_2x2_w2", launch_mfma32_128x256x16_2x2_w2},
-    {"mfma32_256x256x16_2x2", launch_mfma32_256x256x16_2x2},
-    {"mfma32_256x256x16_4x2_w2", launch_mfma32_256x256x16_4x2_w2},
     {"mfma32_64x64x16_1x1", launch_mfma32_64x64x16_1x1},
     {"mfma16_128x128x16_2x2", launch_mfma16_128x128x16_2x2},
     {"mfma16_64x64x16_2x2", launch_mfma16_64x64x16_2x2},
@@ -42,16 +40,14 @@ constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 enum VariantId {
   kSimple = 0,
   kValu128 = 1,
-  kMfma32_128x128x16 = 2,
-  kMfma32_128x128x32 = 3,
-  kMfma32_128x128x16_w4 = 4,
-  kMfma32_256x128x16_w2 = 5,
-  kMfma32_128x256x16_w2 = 6,
-  kMfma32_256x256x16 = 7,
-  kMfma32_256x256x16_8w = 8,
-  kMfma32_64x64x16 = 9,
-  kMfma16_128x128x16 = 10,
-  kMfma16_64x64x16 = 11,
+  kMfma32_256x256x32 = 2,
+  kMfma32_256x256x16 = 3,
+  kMfma32_128x128x32 = 4,
+  kMfma32_128x128x32_pipe = 5,
+  kMfma32_128x128x16_w4 = 6,
+  kMfma32_64x64x16 = 7,
+  kMfma16_128x128x16 = 8,
+  kMfma16_64x64x16 = 9,
 };
 
 constexpr int kNoKernel = -100;
@@ -74,10 +70,10 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda, const 
 // of every variant over the square sizes 128..8192 and the rectangular shapes
 // on an MI355X.
 //   * tiny problems are launch-latency bound: one lane per output wins;
-//   * 256x256 tiles (eight waves, one workgroup per CU) are fastest when the
-//     tile count fills the 256 CUs in whole rounds (little tail);
-//   * 128x128 tiles with a 32-deep K slab when there are at least as many
-//     tiles as CUs;
+//   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
+//     fastest when the tile count fills the 256 CUs in whole rounds;
+//   * 128x128x32 tiles when there are at least as many tiles as CUs, with the
+//     pinned software pipeline when the K loop is long;
 //   * otherwise 64x64 tiles on the 16x16x4 instruction, which keep the most
 //     CUs busy on small grids.
 int choose_variant(const Problem &p) {
@@ -88,9 +84,9 @@ int choose_variant(const Problem &p) {
   const long long cus = 256;
   if (t256 >= cus) {
     const long long tail = t256 % cus;
-    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x16_8w;
+    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32;
   }
-  if (t128 >= cus) return kMfma32_128x128x32;
+  if (t128 >= cus) return (p.K >= 4096) ? kMfma32_128x128x32_pipe : kMfma32_128x128x32;
   return kMfma16_64x64x16;
 }
 

@@ -18,15 +18,14 @@ int launch_scale(int M, int N, float beta, float *C, int ldc, hipStream_t stream
 // Register-tiled VALU kernel: 128x128 tile, 8x8 outputs per thread.
 int launch_valu_128x128(const Problem &p, hipStream_t stream);
 
-// Matrix-core kernels, named <instruction>_<BM>x<BN>x<BK>_<waves M>x<waves N>
-// with _w<n> when the register budget is capped for n waves per SIMD.
-int launch_mfma32_128x128x16_2x2(const Problem &p, hipStream_t stream);
+// Matrix-core kernels, named <instruction>_<BM>x<BN>x<BK>_<waves M>x<waves N>;
+// _pipe: software-pipelined slab order; _w4: registers capped for four waves
+// per SIMD.
+int launch_mfma32_256x256x32_4x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_256x256x16_4x2(const Problem &p, hipStream_t stream);
 int launch_mfma32_128x128x32_2x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_128x128x32_2x2_pipe(const Problem &p, hipStream_t stream);
 int launch_mfma32_128x128x16_2x2_w4(const Problem &p, hipStream_t stream);
-int launch_mfma32_256x128x16_2x2_w2(const Problem &p, hipStream_t stream);
-int launch_mfma32_128x256x16_2x2_w2(const Problem &p, hipStream_t stream);
-int launch_mfma32_256x256x16_2x2(const Problem &p, hipStream_t stream);
-int launch_mfma32_256x256x16_4x2_w2(const Problem &p, hipStream_t stream);
 int launch_mfma32_64x64x16_1x1(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x128x16_2x2(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t stream);

@@ -41,7 +41,7 @@
 
 namespace sg950 {
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int BPAD>
 struct MfmaTile {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int WTM = BM / WAVES_M;  // wave tile rows
@@ -50,13 +50,15 @@ struct MfmaTile {
   static constexpr int FN = WTN / MI;       // matrix-core blocks per wave, N
   static constexpr int KG = 64 / MI;        // lane groups along k
   static constexpr int KPG = BK / KG;       // consecutive k per lane group and slab
+  static constexpr int NQ = KPG / 4;        // 4-deep operand groups per slab
   static constexpr int APITCH = BK + 4;     // A row pitch in LDS (floats)
-  static constexpr int BPITCH = BN;         // B row pitch in LDS (floats)
+  static constexpr int BPITCH = BN + BPAD;  // B row pitch in LDS (floats)
   static constexpr int A_STAGE = BM * APITCH;
   static constexpr int B_STAGE = BK * BPITCH;
   static_assert(MI == 32 || MI == 16, "32x32x2 or 16x16x4 instruction");
   static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole blocks");
   static_assert(KPG % 4 == 0, "A operands are read from LDS 4 at a time");
+  static_assert(BPAD % 4 == 0, "B rows must stay 16-byte aligned");
 };
 
 __device__ __forceinline__ floatx16 mfma_step(float a, float b, floatx16 c) {
@@ -76,12 +78,55 @@ __device__ __forceinline__ int acc_row(int g, int r) {
   }
 }
 
+// One 4-deep group of matrix-core operands of a wave: per MI-row block of A a
+// 16-byte vector (four consecutive k), per MI-column block of B four scalars.
+template <class T>
+struct Operands {
+  floatx4 a[T::FM];
+  float b[T::FN][4];
+};
+
+// Reads operand group q of a slab; `as` / `bs` already point at this lane's
+// first A element and first B element in the stage.
+template <int MI, class T>
+__device__ __forceinline__ void read_operands(Operands<T> &o, const float *as, const float *bs, int q) {
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+    o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.b[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
+}
+
+template <class T, class Acc>
+__device__ __forceinline__ void multiply(Acc (&acc)[T::FM][T::FN], const Operands<T> &o) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma_step(o.a[i][e], o.b[j][e], acc[i][j]);
+}
+
 // MINW is the minimum number of waves per SIMD the register allocation must
-// leave room for (two workgroups per CU need MINW = 2 with four-wave groups).
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, bool VA, bool VB>
+// leave room for (two waves per SIMD for the eight-wave 256x256 tile).
+//
+// Two LDS stages alternate: slab t+1 is loaded from global memory while slab
+// t is multiplied and stored to the other stage after it; one barrier per
+// slab.  With PIPE the order inside a slab is pinned by scheduling barriers:
+// operand group q+1 is read before group q is multiplied, the next slab's
+// registers are stored to the free stage in mid-slab, and the last group of a
+// slab is multiplied after the barrier, behind the first reads of the next
+// slab.  The store and that read are unconditional: on the last slab they only
+// touch the stage nobody reads any more.  PIPE pays off on long K loops with
+// 128x128 tiles; the plain order (left to the compiler, which interleaves the
+// operand reads finely with the matrix instructions) is faster elsewhere.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
+          bool VA, bool VB>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Problem p, int tiles_m,
                                                                               int tiles_n, int group_m) {
-  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N>;
+  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD>;
   using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
   constexpr int kRegs = MI * MI / 64;
 
@@ -100,8 +145,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   const int g = lane / MI;
   const int li = lane % MI;
 
-  ATileLoader<BM, BK, T::kThreads, VA> la;
-  BTileLoader<BK, BN, T::kThreads, VB> lb;
+  using LA = ATileLoader<BM, BK, T::kThreads, VA>;
+  using LB = BTileLoader<BK, BN, T::kThreads, VB>;
+  LA la;
+  LB lb;
   la.init(p, m0, tid);
   lb.init(p, n0, tid);
 
@@ -118,74 +165,84 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   const bool ragged = (K % BK) != 0;
 
   // LDS offsets of this thread's stores and of its wave's operand reads.
-  int a_st[decltype(la)::kVecs];
-  int b_st[decltype(lb)::kVecs];
+  int a_st[LA::kVecs];
+  int b_st[LB::kVecs];
 #pragma unroll
-  for (int i = 0; i < decltype(la)::kVecs; ++i)
-    a_st[i] = decltype(la)::row_of(tid, i) * T::APITCH + decltype(la)::col_of(tid, i);
+  for (int i = 0; i < LA::kVecs; ++i) a_st[i] = LA::row_of(tid, i) * T::APITCH + LA::col_of(tid, i);
 #pragma unroll
-  for (int i = 0; i < decltype(lb)::kVecs; ++i)
-    b_st[i] = decltype(lb)::row_of(tid, i) * T::BPITCH + decltype(lb)::col_of(tid, i);
+  for (int i = 0; i < LB::kVecs; ++i) b_st[i] = LB::row_of(tid, i) * T::BPITCH + LB::col_of(tid, i);
   const int a_rd = (wm * T::WTM + li) * T::APITCH + g * T::KPG;
   const int b_rd = (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
 
-  if (ragged && nk == 1) {
-    la.template load<true>(0, K);
-    lb.template load<true>(0, K);
-  } else {
-    la.template load<false>(0, K);
-    lb.template load<false>(0, K);
-  }
+  // Loads slab `slab` into the loaders' registers (zero-filled K tail).
+  auto load = [&](int slab) {
+    const int k0 = slab * BK;
+    if (ragged && slab == nk - 1) {
+      la.template load<true>(k0, K);
+      lb.template load<true>(k0, K);
+    } else {
+      la.template load<false>(k0, K);
+      lb.template load<false>(k0, K);
+    }
+  };
+  auto store = [&](int stage) {
+    float *an = As + stage * T::A_STAGE;
+    float *bn = Bs + stage * T::B_STAGE;
 #pragma unroll
-  for (int i = 0; i < decltype(la)::kVecs; ++i) *reinterpret_cast<floatx4 *>(As + a_st[i]) = la.v[i];
+    for (int i = 0; i < LA::kVecs; ++i) *reinterpret_cast<floatx4 *>(an + a_st[i]) = la.v[i];
 #pragma unroll
-  for (int i = 0; i < decltype(lb)::kVecs; ++i) *reinterpret_cast<floatx4 *>(Bs + b_st[i]) = lb.v[i];
+    for (int i = 0; i < LB::kVecs; ++i) *reinterpret_cast<floatx4 *>(bn + b_st[i]) = lb.v[i];
+  };
+
+  load(0);
+  store(0);
   __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool has_next = kt + 1 < nk;
-    if (has_next) {
-      const int k1 = (kt + 1) * BK;
-      if (ragged && kt + 2 == nk) {
-        la.template load<true>(k1, K);
-        lb.template load<true>(k1, K);
-      } else {
-        la.template load<false>(k1, K);
-        lb.template load<false>(k1, K);
+  if constexpr (PIPE) {
+    Operands<T> o;
+    read_operands<MI>(o, As + a_rd, Bs + b_rd, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) load(kt + 1);
+      const float *as = As + cur * T::A_STAGE + a_rd;
+      const float *bs = Bs + cur * T::B_STAGE + b_rd;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q + 1 < T::NQ; ++q) {
+        Operands<T> nxt;
+        read_operands<MI>(nxt, as, bs, q + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q == T::NQ / 2 - 1) {
+          store(cur ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        multiply<T>(acc, o);
+        o = nxt;
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (T::NQ == 1) store(cur ^ 1);
+      __syncthreads();
+      Operands<T> nxt;
+      read_operands<MI>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd, Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply<T>(acc, o);
+      o = nxt;
     }
-
-    const float *as = As + cur * T::A_STAGE + a_rd;
-    const float *bs = Bs + cur * T::B_STAGE + b_rd;
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool has_next = kt + 1 < nk;
+      if (has_next) load(kt + 1);
+      const float *as = As + cur * T::A_STAGE + a_rd;
+      const float *bs = Bs + cur * T::B_STAGE + b_rd;
 #pragma unroll
-    for (int q = 0; q < T::KPG / 4; ++q) {
-      floatx4 av[T::FM];
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-        av[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
-      float bv[T::FN][4];
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma_step(av[i][e], bv[j][e], acc[i][j]);
+      for (int q = 0; q < T::NQ; ++q) {
+        Operands<T> o;
+        read_operands<MI>(o, as, bs, q);
+        multiply<T>(acc, o);
+      }
+      if (has_next) store(cur ^ 1);
+      __syncthreads();
     }
-
-    if (has_next) {
-      float *an = As + (cur ^ 1) * T::A_STAGE;
-      float *bn = Bs + (cur ^ 1) * T::B_STAGE;
-#pragma unroll
-      for (int i = 0; i < decltype(la)::kVecs; ++i) *reinterpret_cast<floatx4 *>(an + a_st[i]) = la.v[i];
-#pragma unroll
-      for (int i = 0; i < decltype(lb)::kVecs; ++i) *reinterpret_cast<floatx4 *>(bn + b_st[i]) = lb.v[i];
-    }
-    __syncthreads();
   }
 
   // Epilogue: C = alpha*acc + beta*C for the in-range elements.  For a fixed
@@ -206,7 +263,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
     }
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE>
 static int launch_mfma(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
@@ -216,37 +273,35 @@ static int launch_mfma(const Problem &p, hipStream_t stream) {
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n;
   const bool va = a_vec_ok(p), vb = b_vec_ok(p);
+#define SG950_LAUNCH(VA_, VB_)                                                                   \
+  hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, VA_, VB_>), \
+                     grid, block, 0, stream, p, tm, tn, group_m)
   if (va && vb) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, true, true>), grid, block,
-                       0, stream, p, tm, tn, group_m);
+    SG950_LAUNCH(true, true);
   } else if (va) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, true, false>), grid, block,
-                       0, stream, p, tm, tn, group_m);
+    SG950_LAUNCH(true, false);
   } else if (vb) {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, false, true>), grid, block,
-                       0, stream, p, tm, tn, group_m);
+    SG950_LAUNCH(false, true);
   } else {
-    hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, false, false>), grid, block,
-                       0, stream, p, tm, tn, group_m);
+    SG950_LAUNCH(false, false);
   }
+#undef SG950_LAUNCH
   return 0;
 }
 
-#define SG950_MFMA_LAUNCHER(name, MI, BM, BN, BK, WM, WN, MINW) \
-  int launch_##name(const Problem &p, hipStream_t s) {        \
-    return launch_mfma<MI, BM, BN, BK, WM, WN, MINW>(p, s);     \
+#define SG950_MFMA_LAUNCHER(name, MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE) \
+  int launch_##name(const Problem &p, hipStream_t s) {                      \
+    return launch_mfma<MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE>(p, s);     \
   }
 
-SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2, 32, 128, 128, 16, 2, 2, 1)
-SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2, 32, 128, 128, 32, 2, 2, 1)
-SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2_w4, 32, 128, 128, 16, 2, 2, 4)
-SG950_MFMA_LAUNCHER(mfma32_256x128x16_2x2_w2, 32, 256, 128, 16, 2, 2, 2)
-SG950_MFMA_LAUNCHER(mfma32_128x256x16_2x2_w2, 32, 128, 256, 16, 2, 2, 2)
-SG950_MFMA_LAUNCHER(mfma32_256x256x16_2x2, 32, 256, 256, 16, 2, 2, 1)
-SG950_MFMA_LAUNCHER(mfma32_256x256x16_4x2_w2, 32, 256, 256, 16, 4, 2, 2)
-SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1, 32, 64, 64, 16, 1, 1, 1)
-SG950_MFMA_LAUNCHER(mfma16_128x128x16_2x2, 16, 128, 128, 16, 2, 2, 1)
-SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2, 16, 64, 64, 16, 2, 2, 1)
+SG950_MFMA_LAUNCHER(mfma32_256x256x32_4x2, 32, 256, 256, 32, 4, 2, 2, 4, false)
+SG950_MFMA_LAUNCHER(mfma32_256x256x16_4x2, 32, 256, 256, 16, 4, 2, 2, 0, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2, 32, 128, 128, 32, 2, 2, 1, 4, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2_pipe, 32, 128, 128, 32, 2, 2, 1, 4, true)
+SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2_w4, 32, 128, 128, 16, 2, 2, 4, 0, false)
+SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1, 32, 64, 64, 16, 1, 1, 1, 0, false)
+SG950_MFMA_LAUNCHER(mfma16_128x128x16_2x2, 16, 128, 128, 16, 2, 2, 1, 0, false)
+SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2, 16, 64, 64, 16, 2, 2, 1, 0, false)
 
 #undef SG950_MFMA_LAUNCHER
 
