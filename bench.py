@@ -200,8 +200,9 @@ class Problem:
         import dense_fp32_gemm_sgemm_amd as sg
         if variant >= 0:
             return sg.sgemm_variant_name(variant)
-        v = sg.sgemm_select_variant(self.M, self.N, self.K, self.alpha, 1, max(1, self.K), 1,
-                                    max(1, self.N), self.beta, 1, max(1, self.N))
+        v = sg.sgemm_select_variant(self.M, self.N, self.K, self.alpha, self.A.data_ptr(),
+                                    max(1, self.K), self.B.data_ptr(), max(1, self.N), self.beta,
+                                    self.C.data_ptr(), max(1, self.N))
         return sg.sgemm_variant_name(v) if v >= 0 else "none"
 
 
@@ -335,7 +336,7 @@ def main(argv=None):
         from_ = args.traffic_from
         # the variant the automatic choice runs on the 4096^3 problem (no GPU needed)
         import dense_fp32_gemm_sgemm_amd as sg
-        v = sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 1, 4096, 1, 4096, 0.0, 1, 4096)
+        v = sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 256, 4096, 256, 4096, 0.0, 256, 4096)
         t = traffic_from_counters(*from_, variant=sg.sgemm_variant_name(v))
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:

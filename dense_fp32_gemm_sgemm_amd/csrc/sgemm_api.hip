@@ -17,6 +17,20 @@ namespace {
 
 typedef int (*Launcher)(const Problem &, hipStream_t);
 
+// The few-rows kernel covers M <= 8; as a forced variant on a taller problem
+// it runs on row blocks of 8 so that every variant accepts every problem.
+int launch_skinny_any(const Problem &p, hipStream_t s) {
+  for (int r = 0; r < p.M; r += 8) {
+    Problem q = p;
+    q.M = (p.M - r < 8) ? p.M - r : 8;
+    q.A = p.A + (size_t)r * (size_t)p.lda;
+    q.C = p.C + (size_t)r * (size_t)p.ldc;
+    const int rc = launch_skinny(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 struct Variant {
   const char *name;
   Launcher launch;
@@ -34,6 +48,10 @@ const Variant kVariants[] = {
     {"mfma32_64x64x16_1x1", launch_mfma32_64x64x16_1x1},
     {"mfma16_128x128x16_2x2", launch_mfma16_128x128x16_2x2},
     {"mfma16_64x64x16_2x2", launch_mfma16_64x64x16_2x2},
+    {"mfma32_128x128x32_2x2_splitk", launch_mfma32_128x128x32_2x2_splitk},
+    {"mfma16_64x64x16_2x2_splitk", launch_mfma16_64x64x16_2x2_splitk},
+    {"mfma32_64x64x16_1x1_splitk", launch_mfma32_64x64x16_1x1_splitk},
+    {"skinny_m8", launch_skinny_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -48,6 +66,10 @@ enum VariantId {
   kMfma32_64x64x16 = 7,
   kMfma16_128x128x16 = 8,
   kMfma16_64x64x16 = 9,
+  kMfma32_128x128x32_splitk = 10,
+  kMfma16_64x64x16_splitk = 11,
+  kMfma32_64x64x16_splitk = 12,
+  kSkinny = 13,
 };
 
 constexpr int kNoKernel = -100;
@@ -70,15 +92,20 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda, const 
 // of every variant over the square sizes 128..8192 and the rectangular shapes
 // on an MI355X.
 //   * tiny problems are launch-latency bound: one lane per output wins;
+//   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
 //     fastest when the tile count fills the 256 CUs in whole rounds;
-//   * 128x128x32 tiles when there are at least as many tiles as CUs, with the
-//     pinned software pipeline when the K loop is long;
-//   * otherwise 64x64 tiles on the 16x16x4 instruction, which keep the most
-//     CUs busy on small grids.
+//   * 128x128x32 tiles when there are at least as many tiles as CUs and both
+//     operands allow 16-byte loads, with the pinned software pipeline when the
+//     K loop is long;
+//   * otherwise 64x64 tiles on the 16x16x4 instruction, splitting K over
+//     workgroups when even those tiles cannot give every CU one workgroup.
 int choose_variant(const Problem &p) {
   const long long work = (long long)p.M * p.N * p.K;
-  if (p.M < 16 || p.N < 16 || work <= 256LL * 256 * 256) return kSimple;
+  const long long nk = (long long)p.N * p.K;
+  if (p.M <= 2 && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
+  if (work <= 256LL * 256 * 256 || p.N < 16) return kSimple;
+  if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256);
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128);
   const long long cus = 256;
@@ -86,8 +113,11 @@ int choose_variant(const Problem &p) {
     const long long tail = t256 % cus;
     if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32;
   }
-  if (t128 >= cus) return (p.K >= 4096) ? kMfma32_128x128x32_pipe : kMfma32_128x128x32;
-  return kMfma16_64x64x16;
+  // Operands that need scalar loads (unaligned base or leading dimension)
+  // favour the smaller tiles, whose many workgroups hide the longer loads.
+  if (t128 >= cus && a_vec_ok(p) && b_vec_ok(p))
+    return (p.K >= 4096) ? kMfma32_128x128x32_pipe : kMfma32_128x128x32;
+  return kMfma16_64x64x16_splitk;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other

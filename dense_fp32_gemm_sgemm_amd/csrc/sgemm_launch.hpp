@@ -29,6 +29,17 @@ int launch_mfma32_128x128x16_2x2_w4(const Problem &p, hipStream_t stream);
 int launch_mfma32_64x64x16_1x1(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x128x16_2x2(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t stream);
+// _splitk: K split over blockIdx.y when the tiles alone cannot fill the GPU;
+// C is scaled by beta first and the partial products are added with float
+// atomics (summation order of the splits unspecified).
+int launch_mfma32_128x128x32_2x2_splitk(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x16_2x2_splitk(const Problem &p, hipStream_t stream);
+int launch_mfma32_64x64x16_1x1_splitk(const Problem &p, hipStream_t stream);
+
+// Few rows of C (M <= 8): streams B across every CU, K split over
+// workgroups, float atomics into C (scaled by beta first).  Returns -1 for
+// M > 8.
+int launch_skinny(const Problem &p, hipStream_t stream);
 
 // Operand alignment classes: a matrix may be read with 16-byte vector loads
 // when its base is 16-byte aligned and its leading dimension is a multiple of

@@ -122,10 +122,22 @@ __device__ __forceinline__ void multiply(Acc (&acc)[T::FM][T::FN], const Operand
 // touch the stage nobody reads any more.  PIPE pays off on long K loops with
 // 128x128 tiles; the plain order (left to the compiler, which interleaves the
 // operand reads finely with the matrix instructions) is faster elsewhere.
+//
+// SPLITK: blockIdx.y selects a range of k_per_split values of K (a multiple
+// of BK); the workgroup multiplies only that range and adds alpha times its
+// partial product into C with float atomics (C was scaled by beta before the
+// launch).  This fills the GPU when there are too few output tiles.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
-          bool VA, bool VB>
+          bool SPLITK, bool VA, bool VB>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Problem p, int tiles_m,
-                                                                              int tiles_n, int group_m) {
+                                                                              int tiles_n, int group_m,
+                                                                              int k_per_split) {
+  if constexpr (SPLITK) {
+    const int kb = blockIdx.y * k_per_split;  // < K by construction of the grid
+    p.A += kb;
+    p.B += (size_t)kb * (size_t)p.ldb;
+    p.K = min(p.K - kb, k_per_split);
+  }
   using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD>;
   using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
   constexpr int kRegs = MI * MI / 64;
@@ -258,50 +270,93 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
 #pragma unroll
       for (int r = 0; r < kRegs; ++r) {
         const int row = row0 + i * MI + acc_row<MI>(g, r);
-        if (row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
+        if (row >= p.M) continue;
+        float *c = p.C + (size_t)row * (size_t)p.ldc + col;
+        if constexpr (SPLITK) {
+          atomicAdd(c, p.alpha * acc[i][j][r]);
+        } else {
+          store_out(c, acc[i][j][r], p.alpha, p.beta);
+        }
       }
     }
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE>
+// Number of K splits for a grid of `tiles` output tiles: none when the tiles
+// alone give every CU a workgroup, otherwise enough for about two workgroups
+// per CU, each split at least four slabs deep.
+template <int BK>
+static int choose_splits(long long tiles, int K, int &k_per_split) {
+  const long long cus = 256, target = 512;
+  long long splits = (tiles >= cus) ? 1 : (target + tiles - 1) / tiles;
+  const long long max_splits = K / (4 * BK);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 2) {
+    k_per_split = K;
+    return 1;
+  }
+  long long kps = ((long long)K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  k_per_split = (int)kps;
+  return (int)(((long long)K + kps - 1) / kps);
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
+          bool SPLITK>
 static int launch_mfma(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
+  int k_per_split = p.K;
+  const int splits = SPLITK ? choose_splits<BK>(tiles_m * tiles_n, p.K, k_per_split) : 1;
+  if (SPLITK && splits > 1) {
+    if (splits > 65535) return -1;
+    // C = beta*C first; the split workgroups then add into it.
+    if (p.beta != 1.0f && launch_scale(p.M, p.N, p.beta, p.C, p.ldc, stream) != 0) return -1;
+  }
   const int group_m = 8;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n;
   const bool va = a_vec_ok(p), vb = b_vec_ok(p);
-#define SG950_LAUNCH(VA_, VB_)                                                                   \
-  hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, VA_, VB_>), \
-                     grid, block, 0, stream, p, tm, tn, group_m)
-  if (va && vb) {
-    SG950_LAUNCH(true, true);
-  } else if (va) {
-    SG950_LAUNCH(true, false);
-  } else if (vb) {
-    SG950_LAUNCH(false, true);
-  } else {
-    SG950_LAUNCH(false, false);
+#define SG950_LAUNCH(SK_, VA_, VB_)                                                                  \
+  hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SK_, VA_, VB_>), \
+                     grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
+#define SG950_LAUNCH_ALIGN(SK_)        \
+  if (va && vb) {                      \
+    SG950_LAUNCH(SK_, true, true);     \
+  } else if (va) {                     \
+    SG950_LAUNCH(SK_, true, false);    \
+  } else if (vb) {                     \
+    SG950_LAUNCH(SK_, false, true);    \
+  } else {                             \
+    SG950_LAUNCH(SK_, false, false);   \
   }
+  if (SPLITK && splits > 1) {
+    SG950_LAUNCH_ALIGN(SPLITK)
+  } else {
+    SG950_LAUNCH_ALIGN(false)
+  }
+#undef SG950_LAUNCH_ALIGN
 #undef SG950_LAUNCH
   return 0;
 }
 
-#define SG950_MFMA_LAUNCHER(name, MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE) \
-  int launch_##name(const Problem &p, hipStream_t s) {                      \
-    return launch_mfma<MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE>(p, s);     \
+#define SG950_MFMA_LAUNCHER(name, MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE, SPLITK) \
+  int launch_##name(const Problem &p, hipStream_t s) {                              \
+    return launch_mfma<MI, BM, BN, BK, WM, WN, MINW, BPAD, PIPE, SPLITK>(p, s);     \
   }
 
-SG950_MFMA_LAUNCHER(mfma32_256x256x32_4x2, 32, 256, 256, 32, 4, 2, 2, 4, false)
-SG950_MFMA_LAUNCHER(mfma32_256x256x16_4x2, 32, 256, 256, 16, 4, 2, 2, 0, false)
-SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2, 32, 128, 128, 32, 2, 2, 1, 4, false)
-SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2_pipe, 32, 128, 128, 32, 2, 2, 1, 4, true)
-SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2_w4, 32, 128, 128, 16, 2, 2, 4, 0, false)
-SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1, 32, 64, 64, 16, 1, 1, 1, 0, false)
-SG950_MFMA_LAUNCHER(mfma16_128x128x16_2x2, 16, 128, 128, 16, 2, 2, 1, 0, false)
-SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2, 16, 64, 64, 16, 2, 2, 1, 0, false)
+SG950_MFMA_LAUNCHER(mfma32_256x256x32_4x2, 32, 256, 256, 32, 4, 2, 2, 4, false, false)
+SG950_MFMA_LAUNCHER(mfma32_256x256x16_4x2, 32, 256, 256, 16, 4, 2, 2, 0, false, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2, 32, 128, 128, 32, 2, 2, 1, 4, false, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2_pipe, 32, 128, 128, 32, 2, 2, 1, 4, true, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x16_2x2_w4, 32, 128, 128, 16, 2, 2, 4, 0, false, false)
+SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1, 32, 64, 64, 16, 1, 1, 1, 0, false, false)
+SG950_MFMA_LAUNCHER(mfma16_128x128x16_2x2, 16, 128, 128, 16, 2, 2, 1, 0, false, false)
+SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2, 16, 64, 64, 16, 2, 2, 1, 0, false, false)
+SG950_MFMA_LAUNCHER(mfma32_128x128x32_2x2_splitk, 32, 128, 128, 32, 2, 2, 1, 4, false, true)
+SG950_MFMA_LAUNCHER(mfma16_64x64x16_2x2_splitk, 16, 64, 64, 16, 2, 2, 1, 0, false, true)
+SG950_MFMA_LAUNCHER(mfma32_64x64x16_1x1_splitk, 32, 64, 64, 16, 1, 1, 1, 0, false, true)
 
 #undef SG950_MFMA_LAUNCHER
 

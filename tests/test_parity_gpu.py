@@ -24,7 +24,7 @@ from workloads import (ACCUM, ACCUM_INT, HEADLINE, SMALL, SMALL_INT, draw,  # no
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-VARIANTS = list(range(sg.sgemm_num_variants())) if True else []
+VARIANTS = list(range(sg.sgemm_num_variants()))
 VNAMES = [sg.sgemm_variant_name(v) for v in VARIANTS]
 
 
@@ -170,12 +170,55 @@ def test_nan_in_a_poisons_its_row_only():
     assert np.all(np.isfinite(rest))
 
 
-def test_repeatable_bitwise():
-    A, B, Cin = draw(1000, 1000, 1000, seed=12, with_c=True)
-    say("repeatability")
-    C1 = run(A, B, Cin, 1.5, 0.5)
-    C2 = run(A, B, Cin, 1.5, 0.5)
+# Variants whose K-sum order is fixed; the split-K and few-rows variants add
+# partial sums with atomics in an order the hardware chooses.
+DETERMINISTIC = [v for v in VARIANTS if not (VNAMES[v].endswith("_splitk") or VNAMES[v].startswith("skinny"))]
+UNORDERED = [v for v in VARIANTS if v not in DETERMINISTIC]
+
+
+@pytest.mark.parametrize("variant", DETERMINISTIC, ids=[VNAMES[v] for v in DETERMINISTIC])
+def test_repeatable_bitwise(variant):
+    A, B, Cin = draw(700, 600, 900, seed=12, with_c=True)
+    say("repeatability", VNAMES[variant])
+    C1 = run(A, B, Cin, 1.5, 0.5, variant=variant)
+    C2 = run(A, B, Cin, 1.5, 0.5, variant=variant)
     assert np.array_equal(C1, C2)
+
+
+def test_automatic_choice_repeatable_at_headline_size():
+    A, B, _ = draw(4096, 4096, 4096, seed=3)
+    say("repeatability 4096^3")
+    assert np.array_equal(run(A, B), run(A, B))
+
+
+@pytest.mark.parametrize("variant", UNORDERED, ids=[VNAMES[v] for v in UNORDERED])
+@pytest.mark.parametrize("shape", [(700, 600, 3000), (256, 256, 4096), (8, 1000, 2500), (1, 4097, 4096),
+                                   (3, 130, 777)])
+def test_split_reductions(variant, shape):
+    """Split-K and few-rows kernels: K split across workgroups, partial sums
+    added with atomics after C is scaled by beta."""
+    M, N, K = shape
+    A, B, Cin = draw(M, N, K, seed=M + N + K, with_c=True)
+    say("split", VNAMES[variant], shape)
+    C = run(A, B, Cin, 1.5, 0.5, variant=variant, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "%s %s" % (VNAMES[variant], shape))
+    C = run(A, B, None, 1.0, 0.0, variant=variant)   # beta = 0 over NaN-filled C
+    check_real(C, A, B, None, 1.0, 0.0, "%s %s beta=0" % (VNAMES[variant], shape))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=variant)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s int" % (VNAMES[variant], shape))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_few_rows_automatic(M):
+    """Matrix-vector-like shapes through the automatic choice, including a
+    misaligned B (ld not a multiple of 4)."""
+    A, B, Cin = draw(M, 3001, 2049, seed=M, with_c=True)
+    say("few rows", M)
+    C = run(A, B, Cin, 2.0, -1.0, check_outside=True)
+    check_real(C, A, B, Cin, 2.0, -1.0, "M=%d" % M)
+    C = run(A, B, Cin, 2.0, -1.0, lds=(2049 + 3, 3001 + 2, 3001 + 1), offsets=(1, 2, 3), check_outside=True)
+    check_real(C, A, B, Cin, 2.0, -1.0, "M=%d padded" % M)
 
 
 def test_runs_on_a_side_stream():
@@ -217,7 +260,7 @@ def test_headline_4096_full_check():
     element checked."""
     A, B, _ = draw_workload(HEADLINE)
     say("headline 4096^3 variant", sg.sgemm_variant_name(
-        sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 1, 4096, 1, 4096, 0.0, 1, 4096)))
+        sg.sgemm_select_variant(4096, 4096, 4096, 1.0, 256, 4096, 256, 4096, 0.0, 256, 4096)))
     C = run(A, B)
     err = check_real(C, A, B, None, 1.0, 0.0, "4096^3")
     say("headline normalized error %.3g" % err)
