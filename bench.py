@@ -171,24 +171,30 @@ def time_steps(fn, steps: int, stream):
 class Problem:
     """Device buffers of one GEMM and a zero-overhead launcher."""
 
-    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real"):
+    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real", ops="NN"):
         torch = _torch()
+        import numpy as np
         from workloads import draw
         self.M, self.N, self.K, self.alpha, self.beta = M, N, K, alpha, beta
+        self.ta, self.tb = ops[0] == "T", ops[1] == "T"
         A, B, C = draw(M, N, K, seed=seed, kind=kind, with_c=(beta != 0.0))
         self.host = (A, B, C)
-        self.A = torch.from_numpy(A).cuda()
-        self.B = torch.from_numpy(B).cuda()
+        # stored matrices: the transposes when the operation transposes them
+        As = np.ascontiguousarray(A.T) if self.ta else A
+        Bs = np.ascontiguousarray(B.T) if self.tb else B
+        self.lda, self.ldb = max(1, As.shape[1]), max(1, Bs.shape[1])
+        self.A = torch.from_numpy(As).cuda()
+        self.B = torch.from_numpy(Bs).cuda()
         self.C = (torch.from_numpy(C).cuda() if C is not None
                   else torch.zeros((M, N), dtype=torch.float32, device="cuda"))
         self.stream = torch.cuda.current_stream()
 
     def launcher(self, variant=-1):
         import dense_fp32_gemm_sgemm_amd as sg
-        args = (self.M, self.N, self.K, float(self.alpha), self.A.data_ptr(), max(1, self.K),
-                self.B.data_ptr(), max(1, self.N), float(self.beta), self.C.data_ptr(),
-                max(1, self.N), self.stream.cuda_stream, variant)
-        fn_ex = sg.load().sgemm_ex
+        args = (int(self.ta), int(self.tb), self.M, self.N, self.K, float(self.alpha),
+                self.A.data_ptr(), self.lda, self.B.data_ptr(), self.ldb, float(self.beta),
+                self.C.data_ptr(), max(1, self.N), self.stream.cuda_stream, variant)
+        fn_ex = sg.load().sgemm_op_ex
 
         def fn():
             st = fn_ex(*args)
@@ -200,9 +206,9 @@ class Problem:
         import dense_fp32_gemm_sgemm_amd as sg
         if variant >= 0:
             return sg.sgemm_variant_name(variant)
-        v = sg.sgemm_select_variant(self.M, self.N, self.K, self.alpha, self.A.data_ptr(),
-                                    max(1, self.K), self.B.data_ptr(), max(1, self.N), self.beta,
-                                    self.C.data_ptr(), max(1, self.N))
+        v = sg.sgemm_op_select_variant(int(self.ta), int(self.tb), self.M, self.N, self.K,
+                                       self.alpha, self.A.data_ptr(), self.lda, self.B.data_ptr(),
+                                       self.ldb, self.beta, self.C.data_ptr(), max(1, self.N))
         return sg.sgemm_variant_name(v) if v >= 0 else "none"
 
 
@@ -318,6 +324,8 @@ def main(argv=None):
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"))
     ap.add_argument("--beta", type=float, default=0.0)
+    ap.add_argument("--ops", default="NN", choices=["NN", "NT", "TN", "TT"],
+                    help="op(A) op(B) for the non-contract modes (T = transposed operand)")
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--variants", action="store_true")
@@ -424,7 +432,7 @@ def run_modes(args):
         return 0
     if args.profile:
         shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
-        prob = Problem(*shape, args.alpha, args.beta, seed=0)
+        prob = Problem(*shape, args.alpha, args.beta, seed=0, ops=args.ops)
         total, per = bench_problem(prob, args.steps, args.warmup, args.variant)
         kern_ms = statistics.mean(per)
         print(json.dumps({"mode": "profile", "shape": shape, "variant": prob.variant_name(args.variant),
@@ -444,7 +452,7 @@ def run_modes(args):
         jobs = [(tuple(args.shape), args.variant)]
     for shape, v in jobs:
         M, N, K = shape
-        prob = Problem(M, N, K, args.alpha, args.beta, seed=0)
+        prob = Problem(M, N, K, args.alpha, args.beta, seed=0, ops=args.ops)
         name = prob.variant_name(v)
         work = flops(M, N, K)
         steps = max(5, min(args.steps, int(2e12 / max(work, 1.0))))
@@ -452,7 +460,8 @@ def run_modes(args):
             steps = 3
         total, per = bench_problem(prob, steps, min(args.warmup, steps), v)
         kern_ms = statistics.median(per)
-        rec = {"mode": "sweep" if args.sweep else ("matrix" if args.matrix else "variant"), "M": M, "N": N, "K": K,
+        rec = {"mode": "sweep" if args.sweep else ("matrix" if args.matrix else "variant"),
+               "ops": args.ops, "M": M, "N": N, "K": K,
                "beta": args.beta, "variant": name, "steps": steps,
                "kernel_ms_median": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
                "gflops": round(work / (kern_ms * 1e-3) / 1e9, 1),

@@ -16,13 +16,15 @@ and the functions raise ``LibraryMissing`` when the library is not built.
 from __future__ import annotations
 
 from ._lib import (EXPORTS, LIBRARY, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM,  # noqa: F401
-                   SGEMM_ERR_LAUNCH, SGEMM_ERR_LD, SGEMM_ERR_PTR, SGEMM_ERR_VARIANT,
-                   SGEMM_NO_KERNEL, SGEMM_OK, LibraryMissing, load, sgemm,
-                   sgemm_ceiling_copy, sgemm_ceiling_fma, sgemm_ceiling_mfma, sgemm_ex,
-                   sgemm_num_variants, sgemm_select_variant, sgemm_status_string,
+                   SGEMM_ERR_LAUNCH, SGEMM_ERR_LD, SGEMM_ERR_OP, SGEMM_ERR_PTR,
+                   SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N, SGEMM_OP_T,
+                   LibraryMissing, load, sgemm, sgemm_ceiling_copy, sgemm_ceiling_fma,
+                   sgemm_ceiling_mfma, sgemm_ex, sgemm_num_variants, sgemm_op, sgemm_op_ex,
+                   sgemm_op_select_variant, sgemm_select_variant, sgemm_status_string,
                    sgemm_variant_name, sgemm_version)
 
-__all__ = ["gemm", "variant_names", "sgemm", "sgemm_ex", "sgemm_num_variants",
+__all__ = ["gemm", "variant_names", "sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex",
+           "sgemm_op_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
            "sgemm_version", "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
            "LibraryMissing", "SgemmError"]
@@ -61,19 +63,25 @@ def _leading_dim(t, rows, cols, name):
     return t.stride(0)
 
 
-def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, variant: int = -1, stream=None):
-    """C = alpha * A @ B + beta * C in place on float32 HIP tensors; returns C.
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
+         trans_b: bool = False, variant: int = -1, stream=None):
+    """C = alpha * op(A) @ op(B) + beta * C in place on float32 HIP tensors;
+    returns C.
 
-    A is (M, K), B is (K, N), C is (M, N), each row-major (unit column
-    stride; the row stride is the leading dimension).  The call is enqueued on
-    ``stream`` (default: the current torch stream) and does not synchronise."""
+    op(A) is A (M x K) or, with trans_a, the transpose of the K x M tensor A;
+    op(B) is B (K x N) or, with trans_b, the transpose of the N x K tensor B.
+    Every tensor is row-major (unit column stride; the row stride is the
+    leading dimension).  The call is enqueued on ``stream`` (default: the
+    current torch stream) and does not synchronise."""
     import torch
-    M, K = int(A.shape[0]), int(A.shape[1])
-    N = int(B.shape[1])
-    if B.shape[0] != K:
-        raise ValueError("inner dimensions differ: A %s, B %s" % (tuple(A.shape), tuple(B.shape)))
-    lda = _leading_dim(A, M, K, "A")
-    ldb = _leading_dim(B, K, N, "B")
+    M = int(A.shape[1] if trans_a else A.shape[0])
+    K = int(A.shape[0] if trans_a else A.shape[1])
+    N = int(B.shape[0] if trans_b else B.shape[1])
+    kb = int(B.shape[1] if trans_b else B.shape[0])
+    if kb != K:
+        raise ValueError("inner dimensions differ: op(A) has K=%d, op(B) has K=%d" % (K, kb))
+    lda = _leading_dim(A, K if trans_a else M, M if trans_a else K, "A")
+    ldb = _leading_dim(B, N if trans_b else K, K if trans_b else N, "B")
     ldc = _leading_dim(C, M, N, "C")
     devs = {t.device for t in (A, B, C)}
     if len(devs) != 1:
@@ -82,8 +90,9 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, variant: int = -1, s
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     with torch.cuda.device(C.device):
-        st = sgemm_ex(M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
-                      float(beta), C.data_ptr() or None, ldc, handle, variant)
+        st = sgemm_op_ex(SGEMM_OP_T if trans_a else SGEMM_OP_N, SGEMM_OP_T if trans_b else SGEMM_OP_N,
+                         M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
+                         float(beta), C.data_ptr() or None, ldc, handle, variant)
     if st != SGEMM_OK:
         raise SgemmError(st)
     return C

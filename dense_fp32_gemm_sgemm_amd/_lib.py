@@ -22,11 +22,15 @@ SGEMM_ERR_PTR = -3
 SGEMM_ERR_LAUNCH = -4
 SGEMM_ERR_DEVICE = -5
 SGEMM_ERR_VARIANT = -6
+SGEMM_ERR_OP = -7
 SGEMM_NO_KERNEL = -100
+SGEMM_OP_N = 0
+SGEMM_OP_T = 1
 
 # Every exported symbol, as declared in include/*.h.
-EXPORTS = ("sgemm", "sgemm_ex", "sgemm_num_variants", "sgemm_variant_name",
-           "sgemm_select_variant", "sgemm_status_string", "sgemm_version",
+EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_num_variants",
+           "sgemm_variant_name", "sgemm_select_variant", "sgemm_op_select_variant",
+           "sgemm_status_string", "sgemm_version",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy")
 
 _lock = threading.Lock()
@@ -44,6 +48,13 @@ def _declare(lib):
     lib.sgemm.restype = c_int
     lib.sgemm_ex.argtypes = gemm_args + [c_int]
     lib.sgemm_ex.restype = c_int
+    lib.sgemm_op.argtypes = [c_int, c_int] + gemm_args
+    lib.sgemm_op.restype = c_int
+    lib.sgemm_op_ex.argtypes = [c_int, c_int] + gemm_args + [c_int]
+    lib.sgemm_op_ex.restype = c_int
+    lib.sgemm_op_select_variant.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float, vp, c_int,
+                                            vp, c_int, c_float, vp, c_int]
+    lib.sgemm_op_select_variant.restype = c_int
     lib.sgemm_num_variants.argtypes = []
     lib.sgemm_num_variants.restype = c_int
     lib.sgemm_variant_name.argtypes = [c_int]
@@ -86,6 +97,21 @@ def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
 def sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, variant=-1) -> int:
     """As ``sgemm`` with an explicit kernel variant (-1 = automatic)."""
     return load().sgemm_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
+
+
+def sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C = alpha*op(A)*op(B) + beta*C; op is SGEMM_OP_N or SGEMM_OP_T."""
+    return load().sgemm_op(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_op_ex(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+                variant=-1) -> int:
+    return load().sgemm_op_ex(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                              variant)
+
+
+def sgemm_op_select_variant(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
+    return load().sgemm_op_select_variant(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
 
 
 def sgemm_num_variants() -> int:

@@ -23,7 +23,7 @@ int launch_skinny_any(const Problem &p, hipStream_t s) {
   for (int r = 0; r < p.M; r += 8) {
     Problem q = p;
     q.M = (p.M - r < 8) ? p.M - r : 8;
-    q.A = p.A + (size_t)r * (size_t)p.lda;
+    q.A = p.ta ? p.A + r : p.A + (size_t)r * (size_t)p.lda;
     q.C = p.C + (size_t)r * (size_t)p.ldc;
     const int rc = launch_skinny(q, s);
     if (rc != 0) return rc;
@@ -74,12 +74,17 @@ enum VariantId {
 
 constexpr int kNoKernel = -100;
 
-// Argument checks shared by every entry point (BLAS order: sizes, then leading
-// dimensions, then pointers).
-int check_args(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-               float beta, const float *C, int ldc) {
+// Argument checks shared by every entry point (BLAS order: operations, sizes,
+// then leading dimensions, then pointers).
+int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+               const float *B, int ldb, float beta, const float *C, int ldc) {
+  if ((opA != SGEMM_OP_N && opA != SGEMM_OP_T) || (opB != SGEMM_OP_N && opB != SGEMM_OP_T))
+    return SGEMM_ERR_OP;
   if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return SGEMM_ERR_LD;
+  const int a_row = opA == SGEMM_OP_T ? M : K;  // stored row length of A
+  const int b_row = opB == SGEMM_OP_T ? K : N;  // stored row length of B
+  if (lda < (a_row > 1 ? a_row : 1) || ldb < (b_row > 1 ? b_row : 1) || ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_LD;
   if (M == 0 || N == 0) return SGEMM_OK;
   if (C == nullptr) return SGEMM_ERR_PTR;
   if (alpha != 0.0f && K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_PTR;
@@ -91,7 +96,8 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda, const 
 // so the table only trades speed; the thresholds come from a measured sweep
 // of every variant over the square sizes 128..8192 and the rectangular shapes
 // on an MI355X.
-//   * tiny problems are launch-latency bound: one lane per output wins;
+//   * tiny problems (little work and little data) are launch-latency bound:
+//     one lane per output wins;
 //   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
 //     fastest when the tile count fills the 256 CUs in whole rounds;
@@ -103,8 +109,10 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda, const 
 int choose_variant(const Problem &p) {
   const long long work = (long long)p.M * p.N * p.K;
   const long long nk = (long long)p.N * p.K;
-  if (p.M <= 2 && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
-  if (work <= 256LL * 256 * 256 || p.N < 16) return kSimple;
+  if (p.M <= 2 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
+  if (p.N < 16) return kSimple;
+  // (the one-lane kernel reads a transposed B with a stride: small tiles then)
+  if (work <= 256LL * 256 * 256 && nk < (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
   if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256);
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128);
@@ -136,9 +144,9 @@ int check_device() {
   return state == 1 ? SGEMM_OK : SGEMM_ERR_DEVICE;
 }
 
-int run(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-        float beta, float *C, int ldc, void *stream, int variant) {
-  int st = check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+int run(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+        int ldb, float beta, float *C, int ldc, void *stream, int variant) {
+  int st = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
   if (st != SGEMM_OK) return st;
   if (variant < -1 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
   if (M == 0 || N == 0) return SGEMM_OK;
@@ -151,12 +159,22 @@ int run(int M, int N, int K, float alpha, const float *A, int lda, const float *
   if (no_product) {
     rc = launch_scale(M, N, beta, C, ldc, s);
   } else {
-    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T};
     const int v = (variant >= 0) ? variant : choose_variant(p);
     rc = kVariants[v].launch(p, s);
   }
   if (rc != 0) return SGEMM_ERR_DIM;
   return (hipGetLastError() == hipSuccess) ? SGEMM_OK : SGEMM_ERR_LAUNCH;
+}
+
+int select(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+           const float *B, int ldb, float beta, const float *C, int ldc) {
+  const int st = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0 || alpha == 0.0f || K == 0) return kNoKernel;
+  const Problem p{M,   N,   K,   alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc,
+                  opA == SGEMM_OP_T, opB == SGEMM_OP_T};
+  return choose_variant(p);
 }
 
 }  // namespace
@@ -166,12 +184,23 @@ extern "C" {
 
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, void *stream) {
-  return sg950::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
 }
 
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream, int variant) {
-  return sg950::run(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                    variant);
+}
+
+int sgemm_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+}
+
+int sgemm_op_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
 }
 
 int sgemm_num_variants(void) { return sg950::kNumVariants; }
@@ -183,26 +212,28 @@ const char *sgemm_variant_name(int variant) {
 
 int sgemm_select_variant(int M, int N, int K, float alpha, const float *A, int lda,
                          const float *B, int ldb, float beta, const float *C, int ldc) {
-  const int st = sg950::check_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-  if (st != SGEMM_OK) return st;
-  if (M == 0 || N == 0 || alpha == 0.0f || K == 0) return sg950::kNoKernel;
-  const sg950::Problem p{M, N, K, alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc};
-  return sg950::choose_variant(p);
+  return sg950::select(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+}
+
+int sgemm_op_select_variant(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                            int lda, const float *B, int ldb, float beta, const float *C, int ldc) {
+  return sg950::select(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
 }
 
 const char *sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
     case SGEMM_ERR_DIM: return "invalid dimension (negative M, N or K, or grid too large)";
-    case SGEMM_ERR_LD: return "invalid leading dimension (lda < max(1,K), ldb or ldc < max(1,N))";
+    case SGEMM_ERR_LD: return "invalid leading dimension (shorter than the stored row it spans)";
     case SGEMM_ERR_PTR: return "NULL matrix pointer";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     case SGEMM_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
     case SGEMM_ERR_VARIANT: return "variant index out of range";
+    case SGEMM_ERR_OP: return "invalid operation (opA and opB must be SGEMM_OP_N or SGEMM_OP_T)";
     default: return "unknown status";
   }
 }
 
-int sgemm_version(void) { return 1; }
+int sgemm_version(void) { return 2; }
 
 }  // extern "C"

@@ -9,7 +9,12 @@
 
 namespace sg950 {
 
-// The GEMM problem C = alpha*A*B + beta*C, row-major, as one kernel argument.
+// The GEMM problem C = alpha*op(A)*op(B) + beta*C, row-major, as one kernel
+// argument.  op(A) is M x K: A itself (element (i,k) at A[i*lda + k]) when
+// ta == 0, or the transpose of the K x M matrix A (element (i,k) at
+// A[k*lda + i]) when ta == 1; likewise op(B) is K x N, from B (element (k,j)
+// at B[k*ldb + j]) or, when tb == 1, from the N x K matrix B (element (k,j)
+// at B[j*ldb + k]).
 struct Problem {
   int M, N, K;
   float alpha, beta;
@@ -19,6 +24,7 @@ struct Problem {
   int ldb;
   float *C;
   int ldc;
+  int ta, tb;
 };
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));

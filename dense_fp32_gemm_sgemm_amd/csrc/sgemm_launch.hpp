@@ -41,15 +41,17 @@ int launch_mfma32_64x64x16_1x1_splitk(const Problem &p, hipStream_t stream);
 // M > 8.
 int launch_skinny(const Problem &p, hipStream_t stream);
 
-// Operand alignment classes: a matrix may be read with 16-byte vector loads
-// when its base is 16-byte aligned and its leading dimension is a multiple of
-// four (for B the row length N must be one too, so a vector never straddles
-// the end of a row).
+// Operand alignment classes: an operand may be read with 16-byte vector
+// loads when its base is 16-byte aligned and its leading dimension is a
+// multiple of four; when its rows run along M or N (A transposed, B not) the
+// row length must be one too, so a vector never crosses the end of a row.
 inline bool a_vec_ok(const Problem &p) {
-  return ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && (p.lda % 4 == 0);
+  return ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && (p.lda % 4 == 0) &&
+         (!p.ta || p.M % 4 == 0);
 }
 inline bool b_vec_ok(const Problem &p) {
-  return ((reinterpret_cast<uintptr_t>(p.B) & 15) == 0) && (p.ldb % 4 == 0) && (p.N % 4 == 0);
+  return ((reinterpret_cast<uintptr_t>(p.B) & 15) == 0) && (p.ldb % 4 == 0) &&
+         (p.tb || p.N % 4 == 0);
 }
 inline bool c_vec_ok(const Problem &p) {
   return ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0) && (p.N % 4 == 0);

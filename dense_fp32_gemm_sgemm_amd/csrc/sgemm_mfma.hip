@@ -24,11 +24,17 @@
 // B[k][l%32] with k = l/32 (the 16x16x4 one: A[l%16][l/16], B[l/16][l%16]).
 // Which k of the slab a lane group stands for is free, as long as A and B
 // agree, so lane group g takes the KPG = BK/(64/MI) consecutive k values
-// [g*KPG, (g+1)*KPG): its A operands for a whole slab are then contiguous in a
-// row of the A tile and come out of LDS as 16-byte reads.  A is kept
-// row-major in LDS with a 4-float pad per row (row pitch BK+4), which puts the
-// 16-byte reads of 8 (or 16) consecutive rows on disjoint banks; B stays
-// row-major, where each 32-lane half reads 32 consecutive floats.
+// [g*KPG, (g+1)*KPG).  Each operand tile is kept in LDS in the orientation it
+// has in memory:
+//   * k contiguous (A untransposed, B transposed): rows of BK+4 floats; a
+//     lane's four k values of an operand group are one 16-byte read, and the
+//     4-float pad puts the reads of 8 (or 16) consecutive rows on disjoint
+//     banks;
+//   * M or N contiguous (B untransposed, A transposed): rows along k, padded
+//     by 4 floats (BPAD for B); a lane reads its four k values as scalars, each
+//     32-lane half reading 32 consecutive floats.
+// With op(A), op(B) in {N, T} this gives the four transpose combinations from
+// one kernel template.
 //
 // Output layout.  Lane l of a 32x32 block holds column l%32 and, in register
 // r, row 8*(r/4) + 4*(l/32) + r%4; of a 16x16 block, row 4*(l/16) + r.
@@ -41,7 +47,7 @@
 
 namespace sg950 {
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int BPAD>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int BPAD, bool TA, bool TB>
 struct MfmaTile {
   static constexpr int kThreads = WAVES_M * WAVES_N * 64;
   static constexpr int WTM = BM / WAVES_M;  // wave tile rows
@@ -51,13 +57,14 @@ struct MfmaTile {
   static constexpr int KG = 64 / MI;        // lane groups along k
   static constexpr int KPG = BK / KG;       // consecutive k per lane group and slab
   static constexpr int NQ = KPG / 4;        // 4-deep operand groups per slab
-  static constexpr int APITCH = BK + 4;     // A row pitch in LDS (floats)
-  static constexpr int BPITCH = BN + BPAD;  // B row pitch in LDS (floats)
-  static constexpr int A_STAGE = BM * APITCH;
-  static constexpr int B_STAGE = BK * BPITCH;
+  // LDS row pitch (floats) and stage size of each operand tile.
+  static constexpr int APITCH = TA ? BM + 4 : BK + 4;
+  static constexpr int BPITCH = TB ? BK + 4 : BN + BPAD;
+  static constexpr int A_STAGE = TA ? BK * APITCH : BM * APITCH;
+  static constexpr int B_STAGE = TB ? BN * BPITCH : BK * BPITCH;
   static_assert(MI == 32 || MI == 16, "32x32x2 or 16x16x4 instruction");
   static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must hold whole blocks");
-  static_assert(KPG % 4 == 0, "A operands are read from LDS 4 at a time");
+  static_assert(KPG % 4 == 0, "operands are read from LDS 4 k at a time");
   static_assert(BPAD % 4 == 0, "B rows must stay 16-byte aligned");
 };
 
@@ -78,25 +85,36 @@ __device__ __forceinline__ int acc_row(int g, int r) {
   }
 }
 
-// One 4-deep group of matrix-core operands of a wave: per MI-row block of A a
-// 16-byte vector (four consecutive k), per MI-column block of B four scalars.
+// One 4-deep group of matrix-core operands of a wave: per MI-row block of
+// op(A) and per MI-column block of op(B), four consecutive k.
 template <class T>
 struct Operands {
   floatx4 a[T::FM];
-  float b[T::FN][4];
+  floatx4 b[T::FN];
 };
 
 // Reads operand group q of a slab; `as` / `bs` already point at this lane's
 // first A element and first B element in the stage.
-template <int MI, class T>
+template <int MI, bool TA, bool TB, class T>
 __device__ __forceinline__ void read_operands(Operands<T> &o, const float *as, const float *bs, int q) {
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-    o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
+  for (int i = 0; i < T::FM; ++i) {
+    if constexpr (!TA) {
+      o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
+    } else {
 #pragma unroll
-  for (int j = 0; j < T::FN; ++j)
+      for (int e = 0; e < 4; ++e) o.a[i][e] = as[(4 * q + e) * T::APITCH + i * MI];
+    }
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.b[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
+  for (int j = 0; j < T::FN; ++j) {
+    if constexpr (!TB) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o.b[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
+    } else {
+      o.b[j] = *reinterpret_cast<const floatx4 *>(bs + j * MI * T::BPITCH + 4 * q);
+    }
+  }
 }
 
 template <class T, class Acc>
@@ -128,17 +146,17 @@ __device__ __forceinline__ void multiply(Acc (&acc)[T::FM][T::FN], const Operand
 // partial product into C with float atomics (C was scaled by beta before the
 // launch).  This fills the GPU when there are too few output tiles.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
-          bool SPLITK, bool VA, bool VB>
+          bool SPLITK, bool TA, bool TB, bool VA, bool VB>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Problem p, int tiles_m,
                                                                               int tiles_n, int group_m,
                                                                               int k_per_split) {
   if constexpr (SPLITK) {
     const int kb = blockIdx.y * k_per_split;  // < K by construction of the grid
-    p.A += kb;
-    p.B += (size_t)kb * (size_t)p.ldb;
+    p.A += TA ? (size_t)kb * (size_t)p.lda : (size_t)kb;
+    p.B += TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb;
     p.K = min(p.K - kb, k_per_split);
   }
-  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD>;
+  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD, TA, TB>;
   using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
   constexpr int kRegs = MI * MI / 64;
 
@@ -157,12 +175,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   const int g = lane / MI;
   const int li = lane % MI;
 
-  using LA = ATileLoader<BM, BK, T::kThreads, VA>;
-  using LB = BTileLoader<BK, BN, T::kThreads, VB>;
+  using LA = typename std::conditional<TA, KRowTileLoader<BK, BM, T::kThreads, VA>,
+                                       RowTileLoader<BM, BK, T::kThreads, VA>>::type;
+  using LB = typename std::conditional<TB, RowTileLoader<BN, BK, T::kThreads, VB>,
+                                       KRowTileLoader<BK, BN, T::kThreads, VB>>::type;
   LA la;
   LB lb;
-  la.init(p, m0, tid);
-  lb.init(p, n0, tid);
+  la.init(p.A, p.lda, p.M, m0, tid);
+  lb.init(p.B, p.ldb, p.N, n0, tid);
 
   Acc acc[T::FM][T::FN];
 #pragma unroll
@@ -183,8 +203,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   for (int i = 0; i < LA::kVecs; ++i) a_st[i] = LA::row_of(tid, i) * T::APITCH + LA::col_of(tid, i);
 #pragma unroll
   for (int i = 0; i < LB::kVecs; ++i) b_st[i] = LB::row_of(tid, i) * T::BPITCH + LB::col_of(tid, i);
-  const int a_rd = (wm * T::WTM + li) * T::APITCH + g * T::KPG;
-  const int b_rd = (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
+  const int a_rd = TA ? (g * T::KPG) * T::APITCH + wm * T::WTM + li
+                      : (wm * T::WTM + li) * T::APITCH + g * T::KPG;
+  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::KPG
+                      : (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
 
   // Loads slab `slab` into the loaders' registers (zero-filled K tail).
   auto load = [&](int slab) {
@@ -211,7 +233,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   __syncthreads();
   if constexpr (PIPE) {
     Operands<T> o;
-    read_operands<MI>(o, As + a_rd, Bs + b_rd, 0);
+    read_operands<MI, TA, TB>(o, As + a_rd, Bs + b_rd, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < nk) load(kt + 1);
@@ -221,7 +243,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
 #pragma unroll
       for (int q = 0; q + 1 < T::NQ; ++q) {
         Operands<T> nxt;
-        read_operands<MI>(nxt, as, bs, q + 1);
+        read_operands<MI, TA, TB>(nxt, as, bs, q + 1);
         __builtin_amdgcn_sched_barrier(0);
         if (q == T::NQ / 2 - 1) {
           store(cur ^ 1);
@@ -234,7 +256,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
       if (T::NQ == 1) store(cur ^ 1);
       __syncthreads();
       Operands<T> nxt;
-      read_operands<MI>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd, Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
+      read_operands<MI, TA, TB>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd,
+                                Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
       __builtin_amdgcn_sched_barrier(0);
       multiply<T>(acc, o);
       o = nxt;
@@ -249,7 +272,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
 #pragma unroll
       for (int q = 0; q < T::NQ; ++q) {
         Operands<T> o;
-        read_operands<MI>(o, as, bs, q);
+        read_operands<MI, TA, TB>(o, as, bs, q);
         multiply<T>(acc, o);
       }
       if (has_next) store(cur ^ 1);
@@ -301,6 +324,46 @@ static int choose_splits(long long tiles, int K, int &k_per_split) {
 }
 
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
+          bool SPLITK, bool TA, bool TB>
+static void launch_mfma_aligned(const Problem &p, dim3 grid, dim3 block, hipStream_t stream, int tm,
+                                int tn, int group_m, int k_per_split) {
+  const bool va = a_vec_ok(p), vb = b_vec_ok(p);
+#define SG950_LAUNCH(VA_, VB_)                                                                        \
+  hipLaunchKernelGGL(                                                                                \
+      (mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SPLITK, TA, TB, VA_, VB_>), \
+      grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
+  if (va && vb) {
+    SG950_LAUNCH(true, true);
+  } else if (va) {
+    SG950_LAUNCH(true, false);
+  } else if (vb) {
+    SG950_LAUNCH(false, true);
+  } else {
+    SG950_LAUNCH(false, false);
+  }
+#undef SG950_LAUNCH
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
+          bool SPLITK>
+static void launch_mfma_split(const Problem &p, dim3 grid, dim3 block, hipStream_t stream, int tm,
+                              int tn, int group_m, int k_per_split) {
+#define SG950_LAUNCH_T(TA_, TB_)                                                                 \
+  launch_mfma_aligned<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SPLITK, TA_, TB_>(p, grid, \
+      block, stream, tm, tn, group_m, k_per_split)
+  if (!p.ta && !p.tb) {
+    SG950_LAUNCH_T(false, false);
+  } else if (!p.ta) {
+    SG950_LAUNCH_T(false, true);
+  } else if (!p.tb) {
+    SG950_LAUNCH_T(true, false);
+  } else {
+    SG950_LAUNCH_T(true, true);
+  }
+#undef SG950_LAUNCH_T
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,
           bool SPLITK>
 static int launch_mfma(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
@@ -313,31 +376,16 @@ static int launch_mfma(const Problem &p, hipStream_t stream) {
     // C = beta*C first; the split workgroups then add into it.
     if (p.beta != 1.0f && launch_scale(p.M, p.N, p.beta, p.C, p.ldc, stream) != 0) return -1;
   }
-  const int group_m = 8;
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
   const dim3 block(WAVES_M * WAVES_N * 64);
-  const int tm = (int)tiles_m, tn = (int)tiles_n;
-  const bool va = a_vec_ok(p), vb = b_vec_ok(p);
-#define SG950_LAUNCH(SK_, VA_, VB_)                                                                  \
-  hipLaunchKernelGGL((mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SK_, VA_, VB_>), \
-                     grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
-#define SG950_LAUNCH_ALIGN(SK_)        \
-  if (va && vb) {                      \
-    SG950_LAUNCH(SK_, true, true);     \
-  } else if (va) {                     \
-    SG950_LAUNCH(SK_, true, false);    \
-  } else if (vb) {                     \
-    SG950_LAUNCH(SK_, false, true);    \
-  } else {                             \
-    SG950_LAUNCH(SK_, false, false);   \
-  }
+  const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
   if (SPLITK && splits > 1) {
-    SG950_LAUNCH_ALIGN(SPLITK)
+    launch_mfma_split<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SPLITK>(
+        p, grid, block, stream, tm, tn, group_m, k_per_split);
   } else {
-    SG950_LAUNCH_ALIGN(false)
+    launch_mfma_split<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, false>(
+        p, grid, block, stream, tm, tn, group_m, k_per_split);
   }
-#undef SG950_LAUNCH_ALIGN
-#undef SG950_LAUNCH
   return 0;
 }
 

@@ -8,8 +8,8 @@
 // consecutive columns of one row of C, so each load of B and each store of C
 // is one contiguous 256-byte access, and the load of A is a single address
 // broadcast to all lanes.  It handles any shape, leading dimension and
-// alignment and serves the tiny problems where a tiled kernel would leave most
-// of its tile empty.
+// alignment (and either operand transposed, with strided reads) and serves
+// the tiny problems where a tiled kernel would leave most of its tile empty.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
 
@@ -22,21 +22,24 @@ __global__ __launch_bounds__(kSimpleCols *kSimpleRows) void simple_kernel(Proble
   const int col = blockIdx.y * kSimpleCols + (threadIdx.x & (kSimpleCols - 1));
   const int row = blockIdx.x * kSimpleRows + (threadIdx.x >> 6);
   if (row >= p.M || col >= p.N) return;  // no barrier in this kernel
-  const float *a = p.A + (size_t)row * p.lda;
-  const float *b = p.B + col;
-  const size_t ldb = (size_t)p.ldb;
+  // Element strides of op(A) along its rows / along K, and of op(B) along K /
+  // along its columns (transposed operands swap them).
+  const size_t sa_i = p.ta ? 1 : (size_t)p.lda, sa_k = p.ta ? (size_t)p.lda : 1;
+  const size_t sb_k = p.tb ? 1 : (size_t)p.ldb, sb_j = p.tb ? (size_t)p.ldb : 1;
+  const float *a = p.A + (size_t)row * sa_i;
+  const float *b = p.B + (size_t)col * sb_j;
   float acc = 0.0f;
   int k = 0;
   // Four independent partial sums hide the FMA latency; they are combined in a
   // fixed order, so the result is still a plain fp32 sum of the K products.
   float acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
   for (; k + 4 <= p.K; k += 4) {
-    acc = fmaf(a[k], b[(size_t)k * ldb], acc);
-    acc1 = fmaf(a[k + 1], b[(size_t)(k + 1) * ldb], acc1);
-    acc2 = fmaf(a[k + 2], b[(size_t)(k + 2) * ldb], acc2);
-    acc3 = fmaf(a[k + 3], b[(size_t)(k + 3) * ldb], acc3);
+    acc = fmaf(a[(size_t)k * sa_k], b[(size_t)k * sb_k], acc);
+    acc1 = fmaf(a[(size_t)(k + 1) * sa_k], b[(size_t)(k + 1) * sb_k], acc1);
+    acc2 = fmaf(a[(size_t)(k + 2) * sa_k], b[(size_t)(k + 2) * sb_k], acc2);
+    acc3 = fmaf(a[(size_t)(k + 3) * sa_k], b[(size_t)(k + 3) * sb_k], acc3);
   }
-  for (; k < p.K; ++k) acc = fmaf(a[k], b[(size_t)k * ldb], acc);
+  for (; k < p.K; ++k) acc = fmaf(a[(size_t)k * sa_k], b[(size_t)k * sb_k], acc);
   acc = (acc + acc1) + (acc2 + acc3);
   store_out(p.C + (size_t)row * p.ldc + col, acc, p.alpha, p.beta);
 }

@@ -24,7 +24,10 @@ namespace sg950 {
 constexpr int kSkinnyCols = 256;  // columns of B per workgroup
 constexpr int kSkinnyWaves = 4;
 
-template <int MR, bool VB>
+// TB: B is stored N x K (op(B) = its transpose); its elements are then read
+// one by one along the column (correct, not bandwidth-efficient: the table
+// never picks this kernel for a transposed B).
+template <int MR, bool VB, bool TB>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, int kchunk) {
   __shared__ float red[kSkinnyWaves][MR][kSkinnyCols];
   const int lane = threadIdx.x & 63;
@@ -40,8 +43,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
   int cc[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) cc[e] = min(c0 + e, p.N - 1);
-  const bool vec = VB && (c0 + 3 < p.N);
+  const bool vec = VB && !TB && (c0 + 3 < p.N);
   const size_t ldb = (size_t)p.ldb;
+  const size_t sa_r = p.ta ? 1 : (size_t)p.lda, sa_k = p.ta ? (size_t)p.lda : 1;
 
   float acc[MR][4];
 #pragma unroll
@@ -51,17 +55,22 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
 
 #pragma unroll 4
   for (int k = k0; k < k1; ++k) {
-    const float *brow = p.B + (size_t)k * ldb;
     floatx4 b;
-    if (vec) {
-      b = *reinterpret_cast<const floatx4 *>(brow + c0);
+    if (TB) {
+      b = floatx4{p.B[(size_t)cc[0] * ldb + k], p.B[(size_t)cc[1] * ldb + k],
+                  p.B[(size_t)cc[2] * ldb + k], p.B[(size_t)cc[3] * ldb + k]};
     } else {
-      b = floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
+      const float *brow = p.B + (size_t)k * ldb;
+      if (vec) {
+        b = *reinterpret_cast<const floatx4 *>(brow + c0);
+      } else {
+        b = floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
+      }
     }
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       if (r < p.M) {
-        const float a = p.A[(size_t)r * (size_t)p.lda + k];
+        const float a = p.A[(size_t)r * sa_r + (size_t)k * sa_k];
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a, b[e], acc[r][e]);
       }
@@ -110,12 +119,14 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
   const dim3 grid((unsigned)strips, (unsigned)chunks);
   const dim3 block(kSkinnyWaves * 64);
   const bool vb = b_vec_ok(p);
-#define SG950_SKINNY(MR_)                                                                    \
-  do {                                                                                       \
-    if (vb)                                                                                  \
-      hipLaunchKernelGGL((skinny_kernel<MR_, true>), grid, block, 0, stream, p, kc);  \
-    else                                                                                     \
-      hipLaunchKernelGGL((skinny_kernel<MR_, false>), grid, block, 0, stream, p, kc); \
+#define SG950_SKINNY(MR_)                                                                     \
+  do {                                                                                        \
+    if (p.tb)                                                                                 \
+      hipLaunchKernelGGL((skinny_kernel<MR_, false, true>), grid, block, 0, stream, p, kc); \
+    else if (vb)                                                                              \
+      hipLaunchKernelGGL((skinny_kernel<MR_, true, false>), grid, block, 0, stream, p, kc); \
+    else                                                                                      \
+      hipLaunchKernelGGL((skinny_kernel<MR_, false, false>), grid, block, 0, stream, p, kc); \
   } while (0)
   if (p.M <= 1) {
     SG950_SKINNY(1);

@@ -8,8 +8,9 @@
 //   * a 256-thread workgroup owns a 128 x 128 tile of C; each thread owns an
 //     8 x 8 block of it, kept in 64 accumulator registers and updated as an
 //     outer product: per k, 8 values of A and 8 of B feed 64 FMAs;
-//   * A is stored k-major in LDS (As[k][m]) so a thread's 8 A values are two
-//     16-byte reads, like its 8 B values;
+//   * both tiles are stored k-major in LDS (As[k][m], Bs[k][n]) so a thread's
+//     8 A values are two 16-byte reads, like its 8 B values (an operand whose
+//     memory rows run along K is transposed on its way into LDS);
 //   * a thread's 8 rows are {4*ty .. 4*ty+3} and {64+4*ty .. 64+4*ty+3} (and
 //     likewise its 8 columns), so the 16 lanes that read one LDS row at a time
 //     touch 16 consecutive 16-byte chunks: no bank conflicts on the reads;
@@ -21,6 +22,7 @@
 #include "sgemm_tiles.hpp"
 
 #include <climits>
+#include <type_traits>
 
 namespace sg950 {
 
@@ -30,7 +32,7 @@ constexpr int kAPitch = kBM + 4;  // k-major A row pitch (floats)
 constexpr int kBPitch = kBN + 4;  // B row pitch (floats)
 }  // namespace
 
-template <bool VA, bool VB, bool VC>
+template <bool TA, bool TB, bool VA, bool VB, bool VC>
 __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, int tiles_n,
                                                         int group_m) {
   __shared__ __attribute__((aligned(16))) float As[2 * kBK * kAPitch];
@@ -44,20 +46,30 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, 
   const int tx = tid & 15;
   const int ty = tid >> 4;
 
-  ATileLoader<kBM, kBK, kThreads, VA> la;
-  BTileLoader<kBK, kBN, kThreads, VB> lb;
-  using LA = decltype(la);
-  using LB = decltype(lb);
-  la.init(p, m0, tid);
-  lb.init(p, n0, tid);
+  // Both tiles live k-major in LDS (As[k][m], Bs[k][n]).  An operand whose
+  // memory rows run along K (A untransposed, B transposed) is transposed on
+  // the way in with four scalar stores per vector; the other kind is stored
+  // as is.
+  using LA = typename std::conditional<TA, KRowTileLoader<kBK, kBM, kThreads, VA>,
+                                       RowTileLoader<kBM, kBK, kThreads, VA>>::type;
+  using LB = typename std::conditional<TB, RowTileLoader<kBN, kBK, kThreads, VB>,
+                                       KRowTileLoader<kBK, kBN, kThreads, VB>>::type;
+  LA la;
+  LB lb;
+  la.init(p.A, p.lda, p.M, m0, tid);
+  lb.init(p.B, p.ldb, p.N, n0, tid);
 
-  // LDS store positions: A goes in transposed (four scalar stores per vector).
+  // LDS store positions (k-major).
   int a_st[LA::kVecs];
   int b_st[LB::kVecs];
 #pragma unroll
-  for (int i = 0; i < LA::kVecs; ++i) a_st[i] = LA::col_of(tid, i) * kAPitch + LA::row_of(tid, i);
+  for (int i = 0; i < LA::kVecs; ++i)
+    a_st[i] = TA ? LA::row_of(tid, i) * kAPitch + LA::col_of(tid, i)
+                 : LA::col_of(tid, i) * kAPitch + LA::row_of(tid, i);
 #pragma unroll
-  for (int i = 0; i < LB::kVecs; ++i) b_st[i] = LB::row_of(tid, i) * kBPitch + LB::col_of(tid, i);
+  for (int i = 0; i < LB::kVecs; ++i)
+    b_st[i] = TB ? LB::col_of(tid, i) * kBPitch + LB::row_of(tid, i)
+                 : LB::row_of(tid, i) * kBPitch + LB::col_of(tid, i);
 
   float acc[8][8];
 #pragma unroll
@@ -71,11 +83,23 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, 
 
   auto stage = [&](float *as, float *bs) {
 #pragma unroll
-    for (int i = 0; i < LA::kVecs; ++i)
+    for (int i = 0; i < LA::kVecs; ++i) {
+      if (TA) {
+        *reinterpret_cast<floatx4 *>(as + a_st[i]) = la.v[i];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) as[a_st[i] + e * kAPitch] = la.v[i][e];
+        for (int e = 0; e < 4; ++e) as[a_st[i] + e * kAPitch] = la.v[i][e];
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < LB::kVecs; ++i) *reinterpret_cast<floatx4 *>(bs + b_st[i]) = lb.v[i];
+    for (int i = 0; i < LB::kVecs; ++i) {
+      if (TB) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bs[b_st[i] + e * kBPitch] = lb.v[i][e];
+      } else {
+        *reinterpret_cast<floatx4 *>(bs + b_st[i]) = lb.v[i];
+      }
+    }
   };
 
   if (ragged && nk == 1) {
@@ -150,26 +174,39 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, 
   }
 }
 
+template <bool TA, bool TB>
+static void launch_valu_t(const Problem &p, dim3 grid, hipStream_t stream, int tm, int tn, int gm) {
+  const bool va = a_vec_ok(p), vb = b_vec_ok(p), vc = c_vec_ok(p);
+  const dim3 block(kThreads);
+  // The C alignment only changes the epilogue, so it is folded into the
+  // fully aligned case rather than doubling the instantiations.
+  if (va && vb && vc) {
+    hipLaunchKernelGGL((valu_kernel<TA, TB, true, true, true>), grid, block, 0, stream, p, tm, tn, gm);
+  } else if (va && vb) {
+    hipLaunchKernelGGL((valu_kernel<TA, TB, true, true, false>), grid, block, 0, stream, p, tm, tn, gm);
+  } else if (va) {
+    hipLaunchKernelGGL((valu_kernel<TA, TB, true, false, false>), grid, block, 0, stream, p, tm, tn, gm);
+  } else if (vb) {
+    hipLaunchKernelGGL((valu_kernel<TA, TB, false, true, false>), grid, block, 0, stream, p, tm, tn, gm);
+  } else {
+    hipLaunchKernelGGL((valu_kernel<TA, TB, false, false, false>), grid, block, 0, stream, p, tm, tn, gm);
+  }
+}
+
 int launch_valu_128x128(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + kBM - 1) / kBM;
   const long long tiles_n = ((long long)p.N + kBN - 1) / kBN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  const dim3 block(kThreads);
   const int tm = (int)tiles_m, tn = (int)tiles_n, gm = 8;
-  const bool va = a_vec_ok(p), vb = b_vec_ok(p), vc = c_vec_ok(p);
-  // Eight instantiations would triple the build for a secondary kernel; the
-  // C alignment only changes the epilogue, so it is folded into VB's case.
-  if (va && vb && vc) {
-    hipLaunchKernelGGL((valu_kernel<true, true, true>), grid, block, 0, stream, p, tm, tn, gm);
-  } else if (va && vb) {
-    hipLaunchKernelGGL((valu_kernel<true, true, false>), grid, block, 0, stream, p, tm, tn, gm);
-  } else if (va) {
-    hipLaunchKernelGGL((valu_kernel<true, false, false>), grid, block, 0, stream, p, tm, tn, gm);
-  } else if (vb) {
-    hipLaunchKernelGGL((valu_kernel<false, true, false>), grid, block, 0, stream, p, tm, tn, gm);
+  if (!p.ta && !p.tb) {
+    launch_valu_t<false, false>(p, grid, stream, tm, tn, gm);
+  } else if (!p.ta) {
+    launch_valu_t<false, true>(p, grid, stream, tm, tn, gm);
+  } else if (!p.tb) {
+    launch_valu_t<true, false>(p, grid, stream, tm, tn, gm);
   } else {
-    hipLaunchKernelGGL((valu_kernel<false, false, false>), grid, block, 0, stream, p, tm, tn, gm);
+    launch_valu_t<true, true>(p, grid, stream, tm, tn, gm);
   }
   return 0;
 }

@@ -50,11 +50,16 @@ extern "C" {
 
 #define SGEMM_OK 0
 #define SGEMM_ERR_DIM (-1)     /* M, N or K negative, or a grid too large */
-#define SGEMM_ERR_LD (-2)      /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define SGEMM_ERR_LD (-2)      /* a leading dimension shorter than the stored row */
 #define SGEMM_ERR_PTR (-3)     /* a matrix that must be read or written is NULL */
 #define SGEMM_ERR_LAUNCH (-4)  /* the HIP runtime rejected a kernel launch */
 #define SGEMM_ERR_DEVICE (-5)  /* the current device is not gfx950, or no device */
 #define SGEMM_ERR_VARIANT (-6) /* sgemm_ex: variant index out of range */
+#define SGEMM_ERR_OP (-7)      /* sgemm_op: opA or opB not SGEMM_OP_N / SGEMM_OP_T */
+
+/* Operand orientation for sgemm_op: use the matrix as stored, or its transpose. */
+#define SGEMM_OP_N 0
+#define SGEMM_OP_T 1
 
 /*
  * C = alpha * A * B + beta * C on `stream`, with the kernel variant and tile
@@ -76,12 +81,41 @@ int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
 /*
  * As sgemm(), but runs kernel variant `variant` (0 <= variant <
  * sgemm_num_variants()); -1 means the automatic choice.  Every variant accepts
- * every valid problem (any shape, leading dimension and alignment), so the
- * variants can be compared on the same inputs.
+ * every valid problem (any shape, leading dimension, alignment and operand
+ * orientation), so the variants can be compared on the same inputs.
  */
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
              void *stream, int variant);
+
+/*
+ * C = alpha * op(A) * op(B) + beta * C with op(X) = X (SGEMM_OP_N) or its
+ * transpose (SGEMM_OP_T); op(A) is M x K and op(B) is K x N.  The pages name
+ * "any transpose" as part of what a general SGEMM library covers (Tinyforge
+ * README, the comparison with the vendor library) and use the transposition
+ * identity to call a column-major library from row-major code ("Optimizing
+ * SGEMM in CUDA", "cuBLAS implementation"; "The road to a fast GEMM", the
+ * vendor call in "The complete code").
+ *
+ *   opA == SGEMM_OP_N: A is M x K, element (i,k) at A[i*lda + k], lda >= max(1,K)
+ *   opA == SGEMM_OP_T: A is K x M, op(A)(i,k) = A[k*lda + i],     lda >= max(1,M)
+ *   opB == SGEMM_OP_N: B is K x N, element (k,j) at B[k*ldb + j], ldb >= max(1,N)
+ *   opB == SGEMM_OP_T: B is N x K, op(B)(k,j) = B[j*ldb + k],     ldb >= max(1,K)
+ *   C is M x N as in sgemm(); everything else (ownership, asynchrony, special
+ *   cases, errors) is as for sgemm().  sgemm() is sgemm_op(N, N, ...).
+ *
+ * A column-major caller computing C = A*B (all column-major) calls
+ * sgemm_op(N, N, N_, M_, K_, alpha, B, ldb, A, lda, beta, C, ldc, stream):
+ * a column-major matrix is the row-major storage of its transpose, and
+ * (A*B)^T = B^T * A^T.
+ */
+int sgemm_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc, void *stream);
+
+/* As sgemm_op() with an explicit kernel variant (-1 = automatic). */
+int sgemm_op_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, void *stream,
+                int variant);
 
 /* Number of kernel variants, and a stable name for each ("" when out of range). */
 int sgemm_num_variants(void);
@@ -96,10 +130,15 @@ int sgemm_select_variant(int M, int N, int K, float alpha, const float *A,
                          int lda, const float *B, int ldb, float beta,
                          const float *C, int ldc);
 
+/* sgemm_select_variant for sgemm_op problems. */
+int sgemm_op_select_variant(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                            int lda, const float *B, int ldb, float beta, const float *C,
+                            int ldc);
+
 /* Short English description of a status code (never NULL). */
 const char *sgemm_status_string(int status);
 
-/* Interface version, currently 1. */
+/* Interface version, currently 2 (2 added the sgemm_op entry points). */
 int sgemm_version(void);
 
 #ifdef __cplusplus

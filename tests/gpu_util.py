@@ -43,18 +43,21 @@ class DevMatrix:
 
 
 def run(A, B, C=None, alpha=1.0, beta=0.0, *, variant=-1, lds=(None, None, None),
-        offsets=(0, 0, 0), check_outside=False):
+        offsets=(0, 0, 0), check_outside=False, trans_a=False, trans_b=False):
     """Runs the HIP SGEMM on device copies; returns C as numpy (float32).
 
-    C=None means a NaN-filled output buffer (only valid with beta == 0)."""
-    M, K = A.shape
-    N = B.shape[1]
+    A and B are the matrices as stored: with trans_a, A is K x M and op(A) is
+    its transpose (likewise B with trans_b).  C=None means a NaN-filled output
+    buffer (only valid with beta == 0)."""
+    M = A.shape[1] if trans_a else A.shape[0]
+    N = B.shape[0] if trans_b else B.shape[1]
     if C is None:
         C = np.full((M, N), np.nan, np.float32)
     dA = DevMatrix(A, lds[0], offsets[0])
     dB = DevMatrix(B, lds[1], offsets[1])
     dC = DevMatrix(C, lds[2], offsets[2])
-    sg.gemm(dA.view, dB.view, dC.view, alpha, beta, variant=variant)
+    sg.gemm(dA.view, dB.view, dC.view, alpha, beta, variant=variant, trans_a=trans_a,
+            trans_b=trans_b)
     torch.cuda.synchronize()
     out = dC.numpy()
     if check_outside:

@@ -56,7 +56,7 @@ def test_variant_registry(lib):
     assert names[0] == "simple"
     assert any(x.startswith("mfma32") for x in names) and any(x.startswith("valu") for x in names)
     assert sg.sgemm_variant_name(n) == "" and sg.sgemm_variant_name(-1) == ""
-    assert sg.sgemm_version() == 1
+    assert sg.sgemm_version() == 2
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails or returns before any HIP call
@@ -90,8 +90,36 @@ def test_variant_index_checked(lib):
     assert sg.sgemm_ex(*args, 0, -2) == sg.SGEMM_ERR_VARIANT
 
 
+@pytest.mark.parametrize("ops,args,status", [
+    ((2, 0), (4, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_OP),
+    ((0, -1), (4, 4, 8, 1.0, FAKE, 8, FAKE, 4, 0.0, FAKE, 4), sg.SGEMM_ERR_OP),
+    ((1, 0), (4, 6, 8, 1.0, FAKE, 3, FAKE, 6, 0.0, FAKE, 6), sg.SGEMM_ERR_LD),  # A^T: lda >= M
+    ((1, 0), (4, 6, 8, 1.0, FAKE, 4, FAKE, 6, 0.0, FAKE, 6), "valid"),
+    ((0, 1), (4, 6, 8, 1.0, FAKE, 8, FAKE, 7, 0.0, FAKE, 6), sg.SGEMM_ERR_LD),  # B^T: ldb >= K
+    ((1, 1), (0, 6, 8, 1.0, None, 1, None, 8, 0.0, None, 6), sg.SGEMM_OK),
+    ((1, 1), (4, 6, 8, 1.0, FAKE, 4, None, 8, 0.0, FAKE, 6), sg.SGEMM_ERR_PTR),
+])
+def test_op_argument_checks(lib, ops, args, status):
+    if status == "valid":   # a valid problem: the choice is a variant index
+        st = sg.sgemm_op_select_variant(*ops, *args)
+        assert 0 <= st < sg.sgemm_num_variants()
+        return
+    assert sg.sgemm_op(*ops, *args, 0) == status
+    assert sg.sgemm_op_ex(*ops, *args, 0, -1) == status
+
+
+def test_op_select_avoids_few_rows_kernel_for_transposed_b(lib):
+    n = sg.sgemm_variant_name
+    assert n(sg.sgemm_op_select_variant(0, 0, 1, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE,
+                                        4096)) == "skinny_m8"
+    assert n(sg.sgemm_op_select_variant(0, 1, 1, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0, FAKE,
+                                        4096)) != "skinny_m8"
+    assert n(sg.sgemm_op_select_variant(1, 1, 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0,
+                                        FAKE, 4096)).startswith("mfma32_256x256")
+
+
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         s = sg.sgemm_status_string(st)
         assert s and s != "unknown status"
     assert sg.sgemm_status_string(12345) == "unknown status"

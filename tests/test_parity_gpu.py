@@ -126,6 +126,58 @@ def test_leading_dims_alignment_and_canaries(variant):
         check_exact(C, A, B, Cin, 1.0, 1.0, "%s lds=%s offs=%s" % (VNAMES[variant], lds, offs))
 
 
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+@pytest.mark.parametrize("ops", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
+def test_transposed_operands_every_variant(variant, ops):
+    """op(A), op(B) in {N, T}: the stored matrices are the transposes; the
+    oracle gets op(A) and op(B) written out, the GPU the stored matrices."""
+    ta, tb = ops
+    for (M, N, K), pad in (((300, 200, 100), False), ((129, 257, 33), False), ((65, 63, 17), True),
+                           ((520, 130, 1000), False)):
+        A, B, Cin = draw(M, N, K, seed=M + N + K + 7, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        # padded case: leading dimensions longer than the stored rows
+        lds = (As.shape[1] + 6, Bs.shape[1] + 3, N + 7) if pad else (None, None, None)
+        say("transposed", ops, (M, N, K), VNAMES[variant])
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, lds=lds,
+                check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "%s %s %s" % (VNAMES[variant], ops, (M, N, K)))
+        Ai, Bi, Ci = draw(M, N, K, seed=M + N + K + 7, kind="int", with_c=True)
+        C = run(np.ascontiguousarray(Ai.T) if ta else Ai, np.ascontiguousarray(Bi.T) if tb else Bi,
+                Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb)
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s int" % (VNAMES[variant], ops, (M, N, K)))
+
+
+@pytest.mark.parametrize("ops", [(False, False), (False, True), (True, False), (True, True)],
+                         ids=["NN", "NT", "TN", "TT"])
+def test_transposed_operands_full_size(ops):
+    """4096^3 and 1x4096x4096 through the automatic choice for every transpose
+    combination; 4096^3 checked on 128 sampled whole rows and columns."""
+    ta, tb = ops
+    A, B, _ = draw(4096, 4096, 4096, seed=21)
+    say("transposed 4096^3", ops)
+    C = run(np.ascontiguousarray(A.T) if ta else A, np.ascontiguousarray(B.T) if tb else B,
+            trans_a=ta, trans_b=tb)
+    _sampled_check(A, B, C, 1.0, 0.0, None, 128, 128, 21, "4096^3 %s" % (ops,))
+    A, B, _ = draw(1, 4096, 4096, seed=22)
+    C = run(np.ascontiguousarray(A.T) if ta else A, np.ascontiguousarray(B.T) if tb else B,
+            trans_a=ta, trans_b=tb)
+    check_real(C, A, B, None, 1.0, 0.0, "1x4096x4096 %s" % (ops,))
+
+
+def test_column_major_via_transposition_identity():
+    """A column-major C = A*B is the row-major call with the operands swapped."""
+    M, N, K = 300, 200, 150
+    A, B, _ = draw(M, N, K, seed=23)
+    # column-major storage of A (M x K) is the row-major storage of A^T (K x M)
+    A_cm = np.ascontiguousarray(A.T)
+    B_cm = np.ascontiguousarray(B.T)
+    say("column-major")
+    Ct = run(B_cm, A_cm)            # (B^T) (A^T) = (AB)^T, N x M row-major = C column-major
+    check_real(np.ascontiguousarray(Ct.T), A, B, None, 1.0, 0.0, "column-major")
+
+
 # ---------------------------------------------------------------- special cases
 
 def test_beta_zero_ignores_nan_in_c():
