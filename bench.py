@@ -171,30 +171,36 @@ def time_steps(fn, steps: int, stream):
 class Problem:
     """Device buffers of one GEMM and a zero-overhead launcher."""
 
-    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real", ops="NN"):
+    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real", ops="NN", batch=1):
         torch = _torch()
         import numpy as np
         from workloads import draw
         self.M, self.N, self.K, self.alpha, self.beta = M, N, K, alpha, beta
         self.ta, self.tb = ops[0] == "T", ops[1] == "T"
+        self.batch = batch
         A, B, C = draw(M, N, K, seed=seed, kind=kind, with_c=(beta != 0.0))
         self.host = (A, B, C)
         # stored matrices: the transposes when the operation transposes them
         As = np.ascontiguousarray(A.T) if self.ta else A
         Bs = np.ascontiguousarray(B.T) if self.tb else B
         self.lda, self.ldb = max(1, As.shape[1]), max(1, Bs.shape[1])
-        self.A = torch.from_numpy(As).cuda()
-        self.B = torch.from_numpy(Bs).cuda()
-        self.C = (torch.from_numpy(C).cuda() if C is not None
-                  else torch.zeros((M, N), dtype=torch.float32, device="cuda"))
+        # a batch repeats the drawn slice (the timing does not depend on values)
+        self.A = torch.from_numpy(As).cuda().repeat(batch, 1, 1) if batch > 1 else torch.from_numpy(As).cuda()
+        self.B = torch.from_numpy(Bs).cuda().repeat(batch, 1, 1) if batch > 1 else torch.from_numpy(Bs).cuda()
+        Cd = (torch.from_numpy(C).cuda() if C is not None
+              else torch.zeros((M, N), dtype=torch.float32, device="cuda"))
+        self.C = Cd.repeat(batch, 1, 1) if batch > 1 else Cd
+        self.strides = ((self.A.stride(0), self.B.stride(0), self.C.stride(0)) if batch > 1
+                        else (0, 0, 0))
         self.stream = torch.cuda.current_stream()
 
     def launcher(self, variant=-1):
         import dense_fp32_gemm_sgemm_amd as sg
+        sa, sb, sc = self.strides
         args = (int(self.ta), int(self.tb), self.M, self.N, self.K, float(self.alpha),
-                self.A.data_ptr(), self.lda, self.B.data_ptr(), self.ldb, float(self.beta),
-                self.C.data_ptr(), max(1, self.N), self.stream.cuda_stream, variant)
-        fn_ex = sg.load().sgemm_op_ex
+                self.A.data_ptr(), self.lda, sa, self.B.data_ptr(), self.ldb, sb, float(self.beta),
+                self.C.data_ptr(), max(1, self.N), sc, self.batch, self.stream.cuda_stream, variant)
+        fn_ex = sg.load().sgemm_strided_batched_ex
 
         def fn():
             st = fn_ex(*args)
@@ -206,9 +212,11 @@ class Problem:
         import dense_fp32_gemm_sgemm_amd as sg
         if variant >= 0:
             return sg.sgemm_variant_name(variant)
-        v = sg.sgemm_op_select_variant(int(self.ta), int(self.tb), self.M, self.N, self.K,
-                                       self.alpha, self.A.data_ptr(), self.lda, self.B.data_ptr(),
-                                       self.ldb, self.beta, self.C.data_ptr(), max(1, self.N))
+        sa, sb, sc = self.strides
+        v = sg.sgemm_strided_batched_select_variant(
+            int(self.ta), int(self.tb), self.M, self.N, self.K, self.alpha, self.A.data_ptr(),
+            self.lda, sa, self.B.data_ptr(), self.ldb, sb, self.beta, self.C.data_ptr(),
+            max(1, self.N), sc, self.batch)
         return sg.sgemm_variant_name(v) if v >= 0 else "none"
 
 
@@ -324,6 +332,8 @@ def main(argv=None):
     ap.add_argument("--variant", type=int, default=-1)
     ap.add_argument("--shape", type=int, nargs=3, metavar=("M", "N", "K"))
     ap.add_argument("--beta", type=float, default=0.0)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="strided batch of this many slices (non-contract modes)")
     ap.add_argument("--ops", default="NN", choices=["NN", "NT", "TN", "TT"],
                     help="op(A) op(B) for the non-contract modes (T = transposed operand)")
     ap.add_argument("--alpha", type=float, default=1.0)
@@ -452,22 +462,23 @@ def run_modes(args):
         jobs = [(tuple(args.shape), args.variant)]
     for shape, v in jobs:
         M, N, K = shape
-        prob = Problem(M, N, K, args.alpha, args.beta, seed=0, ops=args.ops)
+        prob = Problem(M, N, K, args.alpha, args.beta, seed=0, ops=args.ops, batch=args.batch)
         name = prob.variant_name(v)
-        work = flops(M, N, K)
+        work = flops(M, N, K) * args.batch
         steps = max(5, min(args.steps, int(2e12 / max(work, 1.0))))
         if name == "simple" and work > 1e11:
             steps = 3
         total, per = bench_problem(prob, steps, min(args.warmup, steps), v)
         kern_ms = statistics.median(per)
         rec = {"mode": "sweep" if args.sweep else ("matrix" if args.matrix else "variant"),
-               "ops": args.ops, "M": M, "N": N, "K": K,
+               "ops": args.ops, "batch": args.batch, "M": M, "N": N, "K": K,
                "beta": args.beta, "variant": name, "steps": steps,
                "kernel_ms_median": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
                "gflops": round(work / (kern_ms * 1e-3) / 1e9, 1),
                "frac_fp32_peak": round(work / (kern_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
                "ai_flop_per_byte": round(arithmetic_intensity(M, N, K, args.beta), 2),
-               "hbm_gbs_at_min_bytes": round(min_bytes(M, N, K, args.beta) / (kern_ms * 1e-3) / 1e9, 1)}
+               "hbm_gbs_at_min_bytes": round(args.batch * min_bytes(M, N, K, args.beta) /
+                                             (kern_ms * 1e-3) / 1e9, 1)}
         print(json.dumps(rec), flush=True)
         del prob
         _torch().cuda.empty_cache()

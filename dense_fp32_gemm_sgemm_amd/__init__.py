@@ -17,14 +17,16 @@ from __future__ import annotations
 
 from ._lib import (EXPORTS, LIBRARY, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM,  # noqa: F401
                    SGEMM_ERR_LAUNCH, SGEMM_ERR_LD, SGEMM_ERR_OP, SGEMM_ERR_PTR,
-                   SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N, SGEMM_OP_T,
-                   LibraryMissing, load, sgemm, sgemm_ceiling_copy, sgemm_ceiling_fma,
-                   sgemm_ceiling_mfma, sgemm_ex, sgemm_num_variants, sgemm_op, sgemm_op_ex,
-                   sgemm_op_select_variant, sgemm_select_variant, sgemm_status_string,
-                   sgemm_variant_name, sgemm_version)
+                   SGEMM_ERR_STRIDE, SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N,
+                   SGEMM_OP_T, LibraryMissing, load, sgemm, sgemm_ceiling_copy,
+                   sgemm_ceiling_fma, sgemm_ceiling_mfma, sgemm_ex, sgemm_num_variants, sgemm_op,
+                   sgemm_op_ex, sgemm_op_select_variant, sgemm_select_variant,
+                   sgemm_status_string, sgemm_strided_batched, sgemm_strided_batched_ex,
+                   sgemm_strided_batched_select_variant, sgemm_variant_name, sgemm_version)
 
-__all__ = ["gemm", "variant_names", "sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex",
-           "sgemm_op_select_variant", "sgemm_num_variants",
+__all__ = ["gemm", "gemm_batched", "variant_names", "sgemm", "sgemm_ex", "sgemm_op",
+           "sgemm_op_ex", "sgemm_op_select_variant", "sgemm_strided_batched",
+           "sgemm_strided_batched_ex", "sgemm_strided_batched_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
            "sgemm_version", "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
            "LibraryMissing", "SgemmError"]
@@ -93,6 +95,50 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = Fals
         st = sgemm_op_ex(SGEMM_OP_T if trans_a else SGEMM_OP_N, SGEMM_OP_T if trans_b else SGEMM_OP_N,
                          M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
                          float(beta), C.data_ptr() or None, ldc, handle, variant)
+    if st != SGEMM_OK:
+        raise SgemmError(st)
+    return C
+
+
+def _batch_stride(t, name):
+    if t.dim() != 3:
+        raise ValueError("%s must be 3-D (batch, rows, cols)" % name)
+    return t.stride(0) if t.shape[0] > 1 else 0
+
+
+def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
+                 trans_b: bool = False, variant: int = -1, stream=None):
+    """C[z] = alpha * op(A[z]) @ op(B[z]) + beta * C[z] for every z, in place on
+    3-D float32 HIP tensors (batch, rows, cols), each slice row-major; returns
+    C.  A or B may be broadcast along the batch (stride 0, e.g. from
+    ``expand``).  One strided-batched call, enqueued on ``stream``."""
+    import torch
+    if not (A.dim() == B.dim() == C.dim() == 3):
+        raise ValueError("A, B and C must be 3-D")
+    batch = int(C.shape[0])
+    if A.shape[0] != batch or B.shape[0] != batch:
+        raise ValueError("batch sizes differ: %d, %d, %d" % (A.shape[0], B.shape[0], batch))
+    if batch == 0:
+        return C
+    a0, b0, c0 = A[0], B[0], C[0]
+    M = int(a0.shape[1] if trans_a else a0.shape[0])
+    K = int(a0.shape[0] if trans_a else a0.shape[1])
+    N = int(b0.shape[0] if trans_b else b0.shape[1])
+    kb = int(b0.shape[1] if trans_b else b0.shape[0])
+    if kb != K:
+        raise ValueError("inner dimensions differ: op(A) has K=%d, op(B) has K=%d" % (K, kb))
+    lda = _leading_dim(a0, K if trans_a else M, M if trans_a else K, "A")
+    ldb = _leading_dim(b0, N if trans_b else K, K if trans_b else N, "B")
+    ldc = _leading_dim(c0, M, N, "C")
+    sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(C.device):
+        st = sgemm_strided_batched_ex(
+            SGEMM_OP_T if trans_a else SGEMM_OP_N, SGEMM_OP_T if trans_b else SGEMM_OP_N, M, N, K,
+            float(alpha), A.data_ptr() or None, lda, sa, B.data_ptr() or None, ldb, sb, float(beta),
+            C.data_ptr() or None, ldc, sc, batch, handle, variant)
     if st != SGEMM_OK:
         raise SgemmError(st)
     return C

@@ -23,13 +23,15 @@ SGEMM_ERR_LAUNCH = -4
 SGEMM_ERR_DEVICE = -5
 SGEMM_ERR_VARIANT = -6
 SGEMM_ERR_OP = -7
+SGEMM_ERR_STRIDE = -8
 SGEMM_NO_KERNEL = -100
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
 
 # Every exported symbol, as declared in include/*.h.
-EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_num_variants",
-           "sgemm_variant_name", "sgemm_select_variant", "sgemm_op_select_variant",
+EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_strided_batched",
+           "sgemm_strided_batched_ex", "sgemm_num_variants", "sgemm_variant_name",
+           "sgemm_select_variant", "sgemm_op_select_variant", "sgemm_strided_batched_select_variant",
            "sgemm_status_string", "sgemm_version",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy")
 
@@ -55,6 +57,15 @@ def _declare(lib):
     lib.sgemm_op_select_variant.argtypes = [c_int, c_int, c_int, c_int, c_int, c_float, vp, c_int,
                                             vp, c_int, c_float, vp, c_int]
     lib.sgemm_op_select_variant.restype = c_int
+    i64 = ctypes.c_longlong
+    batched = [c_int, c_int, c_int, c_int, c_int, c_float, vp, c_int, i64, vp, c_int, i64, c_float,
+               vp, c_int, i64, c_int]
+    lib.sgemm_strided_batched.argtypes = batched + [vp]
+    lib.sgemm_strided_batched.restype = c_int
+    lib.sgemm_strided_batched_ex.argtypes = batched + [vp, c_int]
+    lib.sgemm_strided_batched_ex.restype = c_int
+    lib.sgemm_strided_batched_select_variant.argtypes = batched
+    lib.sgemm_strided_batched_select_variant.restype = c_int
     lib.sgemm_num_variants.argtypes = []
     lib.sgemm_num_variants.restype = c_int
     lib.sgemm_variant_name.argtypes = [c_int]
@@ -112,6 +123,26 @@ def sgemm_op_ex(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0
 
 def sgemm_op_select_variant(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) -> int:
     return load().sgemm_op_select_variant(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)
+
+
+def sgemm_strided_batched(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                          ldc, strideC, batch, stream=0) -> int:
+    """C_z = alpha*op(A_z)*op(B_z) + beta*C_z for z < batch (element strides)."""
+    return load().sgemm_strided_batched(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                                        beta, C, ldc, strideC, batch, stream)
+
+
+def sgemm_strided_batched_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                             ldc, strideC, batch, stream=0, variant=-1) -> int:
+    return load().sgemm_strided_batched_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                           strideB, beta, C, ldc, strideC, batch, stream, variant)
+
+
+def sgemm_strided_batched_select_variant(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                         strideB, beta, C, ldc, strideC, batch) -> int:
+    return load().sgemm_strided_batched_select_variant(opA, opB, M, N, K, alpha, A, lda, strideA,
+                                                       B, ldb, strideB, beta, C, ldc, strideC,
+                                                       batch)
 
 
 def sgemm_num_variants() -> int:

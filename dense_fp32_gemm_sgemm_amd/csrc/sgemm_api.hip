@@ -75,17 +75,22 @@ enum VariantId {
 constexpr int kNoKernel = -100;
 
 // Argument checks shared by every entry point (BLAS order: operations, sizes,
-// then leading dimensions, then pointers).
+// then leading dimensions and strides, then pointers).  For a batch, slice z
+// of A, B and C starts z*sa, z*sb, z*sc elements after the first; the slices
+// of C must not overlap (those of A and B may, e.g. a shared B with sb = 0).
 int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
-               const float *B, int ldb, float beta, const float *C, int ldc) {
+               long long sa, const float *B, int ldb, long long sb, float beta, const float *C,
+               int ldc, long long sc, int batch) {
   if ((opA != SGEMM_OP_N && opA != SGEMM_OP_T) || (opB != SGEMM_OP_N && opB != SGEMM_OP_T))
     return SGEMM_ERR_OP;
-  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_DIM;
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_ERR_DIM;
   const int a_row = opA == SGEMM_OP_T ? M : K;  // stored row length of A
   const int b_row = opB == SGEMM_OP_T ? K : N;  // stored row length of B
   if (lda < (a_row > 1 ? a_row : 1) || ldb < (b_row > 1 ? b_row : 1) || ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_LD;
-  if (M == 0 || N == 0) return SGEMM_OK;
+  if (sa < 0 || sb < 0 || sc < 0) return SGEMM_ERR_STRIDE;
+  if (batch > 1 && M > 0 && N > 0 && sc < (long long)(M - 1) * ldc + N) return SGEMM_ERR_STRIDE;
+  if (M == 0 || N == 0 || batch == 0) return SGEMM_OK;
   if (C == nullptr) return SGEMM_ERR_PTR;
   if (alpha != 0.0f && K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_PTR;
   (void)beta;
@@ -93,38 +98,51 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 }
 
 // The per-shape table.  Every entry names a variant that handles any shape,
-// so the table only trades speed; the thresholds come from a measured sweep
-// of every variant over the square sizes 128..8192 and the rectangular shapes
-// on an MI355X.
+// so the table only trades speed; the thresholds come from measured sweeps of
+// every variant over the square sizes 128..8192, the rectangular shapes and
+// strided batches of small and mid-sized slices on an MI355X.  Work and tile
+// counts are those of the whole batch.
 //   * tiny problems (little work and little data) are launch-latency bound:
 //     one lane per output wins;
 //   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
-//     fastest when the tile count fills the 256 CUs in whole rounds;
-//   * 128x128x32 tiles when there are at least as many tiles as CUs and both
-//     operands allow 16-byte loads, with the pinned software pipeline when the
-//     K loop is long;
+//     fastest when the tiles are mostly inside C and their count fills the
+//     256 CUs in whole rounds;
+//   * 128x128 tiles when there are at least as many tiles as CUs, they are
+//     mostly inside C and both operands allow 16-byte loads: 16-deep slabs for
+//     a short K loop, 32-deep ones otherwise, with the pinned software pipeline
+//     when the K loop is long;
 //   * otherwise 64x64 tiles on the 16x16x4 instruction, splitting K over
 //     workgroups when even those tiles cannot give every CU one workgroup.
+
+// Percentage of the T x T tiles' area that lies inside an M x N slice.
+long long tile_fill_pct(int M, int N, int T) {
+  const long long tm = ((long long)M + T - 1) / T, tn = ((long long)N + T - 1) / T;
+  return (long long)M * N * 100 / (tm * T * tn * T);
+}
+
 int choose_variant(const Problem &p) {
-  const long long work = (long long)p.M * p.N * p.K;
-  const long long nk = (long long)p.N * p.K;
+  const long long batch = p.batch;
+  const long long work = (long long)p.M * p.N * p.K * batch;
+  const long long nk = (long long)p.N * p.K * batch;
   if (p.M <= 2 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
   if (p.N < 16) return kSimple;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
   if (work <= 256LL * 256 * 256 && nk < (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
   if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
-  const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256);
-  const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128);
+  const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
+  const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
   const long long cus = 256;
-  if (t256 >= cus) {
+  if (t256 >= cus && tile_fill_pct(p.M, p.N, 256) >= 75) {
     const long long tail = t256 % cus;
     if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32;
   }
   // Operands that need scalar loads (unaligned base or leading dimension)
   // favour the smaller tiles, whose many workgroups hide the longer loads.
-  if (t128 >= cus && a_vec_ok(p) && b_vec_ok(p))
+  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128) >= 75 && a_vec_ok(p) && b_vec_ok(p)) {
+    if (p.K <= 256) return kMfma32_128x128x16_w4;
     return (p.K >= 4096) ? kMfma32_128x128x32_pipe : kMfma32_128x128x32;
+  }
   return kMfma16_64x64x16_splitk;
 }
 
@@ -144,36 +162,44 @@ int check_device() {
   return state == 1 ? SGEMM_OK : SGEMM_ERR_DEVICE;
 }
 
-int run(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
-        int ldb, float beta, float *C, int ldc, void *stream, int variant) {
-  int st = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+constexpr int kMaxGridZ = 65535;
+
+int run(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, long long sa,
+        const float *B, int ldb, long long sb, float beta, float *C, int ldc, long long sc,
+        int batch, void *stream, int variant) {
+  int st = check_args(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch);
   if (st != SGEMM_OK) return st;
   if (variant < -1 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
-  if (M == 0 || N == 0) return SGEMM_OK;
+  if (M == 0 || N == 0 || batch == 0) return SGEMM_OK;
   const bool no_product = (alpha == 0.0f || K == 0);
   if (no_product && beta == 1.0f) return SGEMM_OK;
   st = check_device();
   if (st != SGEMM_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  int rc;
-  if (no_product) {
-    rc = launch_scale(M, N, beta, C, ldc, s);
-  } else {
-    const Problem p{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T};
-    const int v = (variant >= 0) ? variant : choose_variant(p);
-    rc = kVariants[v].launch(p, s);
+  Problem p{M,  N,  K,  alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T,
+            sa, sb, sc, batch};
+  const int v = no_product ? -1 : ((variant >= 0) ? variant : choose_variant(p));
+  // Grids hold at most 65535 batch slices: larger batches go in chunks.
+  for (int z0 = 0; z0 < batch; z0 += kMaxGridZ) {
+    Problem q = p;
+    q.batch = (batch - z0 < kMaxGridZ) ? batch - z0 : kMaxGridZ;
+    q.A = p.A ? p.A + (size_t)z0 * (size_t)sa : nullptr;
+    q.B = p.B ? p.B + (size_t)z0 * (size_t)sb : nullptr;
+    q.C = p.C + (size_t)z0 * (size_t)sc;
+    const int rc = no_product ? launch_scale(q, s) : kVariants[v].launch(q, s);
+    if (rc != 0) return SGEMM_ERR_DIM;
   }
-  if (rc != 0) return SGEMM_ERR_DIM;
   return (hipGetLastError() == hipSuccess) ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
 int select(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
-           const float *B, int ldb, float beta, const float *C, int ldc) {
-  const int st = check_args(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+           long long sa, const float *B, int ldb, long long sb, float beta, const float *C, int ldc,
+           long long sc, int batch) {
+  const int st = check_args(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch);
   if (st != SGEMM_OK) return st;
-  if (M == 0 || N == 0 || alpha == 0.0f || K == 0) return kNoKernel;
+  if (M == 0 || N == 0 || batch == 0 || alpha == 0.0f || K == 0) return kNoKernel;
   const Problem p{M,   N,   K,   alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc,
-                  opA == SGEMM_OP_T, opB == SGEMM_OP_T};
+                  opA == SGEMM_OP_T, opB == SGEMM_OP_T, sa, sb, sc, batch};
   return choose_variant(p);
 }
 
@@ -184,23 +210,41 @@ extern "C" {
 
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, void *stream) {
-  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+                    stream, -1);
 }
 
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream, int variant) {
-  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
-                    variant);
+  return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
+                    stream, variant);
 }
 
 int sgemm_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
-  return sg950::run(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, -1);
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, stream, -1);
 }
 
 int sgemm_op_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
                 const float *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
-  return sg950::run(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, stream,
+                    variant);
+}
+
+int sgemm_strided_batched(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                          int lda, long long strideA, const float *B, int ldb, long long strideB,
+                          float beta, float *C, int ldc, long long strideC, int batch,
+                          void *stream) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                    strideC, batch, stream, -1);
+}
+
+int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                             int lda, long long strideA, const float *B, int ldb,
+                             long long strideB, float beta, float *C, int ldc, long long strideC,
+                             int batch, void *stream, int variant) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                    strideC, batch, stream, variant);
 }
 
 int sgemm_num_variants(void) { return sg950::kNumVariants; }
@@ -212,28 +256,38 @@ const char *sgemm_variant_name(int variant) {
 
 int sgemm_select_variant(int M, int N, int K, float alpha, const float *A, int lda,
                          const float *B, int ldb, float beta, const float *C, int ldc) {
-  return sg950::select(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  return sg950::select(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc,
+                       0, 1);
 }
 
 int sgemm_op_select_variant(int opA, int opB, int M, int N, int K, float alpha, const float *A,
                             int lda, const float *B, int ldb, float beta, const float *C, int ldc) {
-  return sg950::select(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  return sg950::select(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1);
+}
+
+int sgemm_strided_batched_select_variant(int opA, int opB, int M, int N, int K, float alpha,
+                                         const float *A, int lda, long long strideA,
+                                         const float *B, int ldb, long long strideB, float beta,
+                                         const float *C, int ldc, long long strideC, int batch) {
+  return sg950::select(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                       strideC, batch);
 }
 
 const char *sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
-    case SGEMM_ERR_DIM: return "invalid dimension (negative M, N or K, or grid too large)";
+    case SGEMM_ERR_DIM: return "invalid dimension (negative M, N, K or batch, or grid too large)";
     case SGEMM_ERR_LD: return "invalid leading dimension (shorter than the stored row it spans)";
     case SGEMM_ERR_PTR: return "NULL matrix pointer";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
     case SGEMM_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
     case SGEMM_ERR_VARIANT: return "variant index out of range";
     case SGEMM_ERR_OP: return "invalid operation (opA and opB must be SGEMM_OP_N or SGEMM_OP_T)";
+    case SGEMM_ERR_STRIDE: return "invalid batch stride (negative, or slices of C overlap)";
     default: return "unknown status";
   }
 }
 
-int sgemm_version(void) { return 2; }
+int sgemm_version(void) { return 3; }
 
 }  // extern "C"

@@ -15,6 +15,10 @@ namespace sg950 {
 // A[k*lda + i]) when ta == 1; likewise op(B) is K x N, from B (element (k,j)
 // at B[k*ldb + j]) or, when tb == 1, from the N x K matrix B (element (k,j)
 // at B[j*ldb + k]).
+//
+// Batches: `batch` independent problems of this shape, slice z using
+// A + z*sa, B + z*sb and C + z*sc (element strides); kernels take the slice
+// from blockIdx.z.  A single problem has batch = 1 and zero strides.
 struct Problem {
   int M, N, K;
   float alpha, beta;
@@ -25,7 +29,17 @@ struct Problem {
   float *C;
   int ldc;
   int ta, tb;
+  long long sa, sb, sc;
+  int batch;
 };
+
+// Moves the operand pointers to batch slice blockIdx.z.
+__device__ __forceinline__ void select_slice(Problem &p) {
+  const size_t z = blockIdx.z;
+  p.A += z * (size_t)p.sa;
+  p.B += z * (size_t)p.sb;
+  p.C += z * (size_t)p.sc;
+}
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

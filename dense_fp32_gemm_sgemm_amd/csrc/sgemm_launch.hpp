@@ -12,8 +12,11 @@
 
 namespace sg950 {
 
+// Every launcher covers all p.batch slices of the problem (grid z = batch,
+// at most 65535; the entry points split larger batches).
 int launch_simple(const Problem &p, hipStream_t stream);
-int launch_scale(int M, int N, float beta, float *C, int ldc, hipStream_t stream);
+// C = beta*C over every batch slice (zeros without reading C when beta == 0).
+int launch_scale(const Problem &p, hipStream_t stream);
 
 // Register-tiled VALU kernel: 128x128 tile, 8x8 outputs per thread.
 int launch_valu_128x128(const Problem &p, hipStream_t stream);

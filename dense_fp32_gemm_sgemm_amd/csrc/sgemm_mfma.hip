@@ -150,6 +150,7 @@ template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, in
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Problem p, int tiles_m,
                                                                               int tiles_n, int group_m,
                                                                               int k_per_split) {
+  select_slice(p);
   if constexpr (SPLITK) {
     const int kb = blockIdx.y * k_per_split;  // < K by construction of the grid
     p.A += TA ? (size_t)kb * (size_t)p.lda : (size_t)kb;
@@ -304,7 +305,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
     }
 }
 
-// Number of K splits for a grid of `tiles` output tiles: none when the tiles
+// Number of K splits for a grid of `tiles` output tiles (over all batch
+// slices): none when the tiles
 // alone give every CU a workgroup, otherwise enough for about two workgroups
 // per CU, each split at least four slabs deep.
 template <int BK>
@@ -370,13 +372,13 @@ static int launch_mfma(const Problem &p, hipStream_t stream) {
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
   int k_per_split = p.K;
-  const int splits = SPLITK ? choose_splits<BK>(tiles_m * tiles_n, p.K, k_per_split) : 1;
+  const int splits = SPLITK ? choose_splits<BK>(tiles_m * tiles_n * p.batch, p.K, k_per_split) : 1;
   if (SPLITK && splits > 1) {
     if (splits > 65535) return -1;
     // C = beta*C first; the split workgroups then add into it.
-    if (p.beta != 1.0f && launch_scale(p.M, p.N, p.beta, p.C, p.ldc, stream) != 0) return -1;
+    if (p.beta != 1.0f && launch_scale(p, stream) != 0) return -1;
   }
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits, (unsigned)p.batch);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
   if (SPLITK && splits > 1) {

@@ -19,6 +19,7 @@ constexpr int kSimpleCols = 64;  // one wave along N
 constexpr int kSimpleRows = 4;   // four waves per workgroup, one row each
 
 __global__ __launch_bounds__(kSimpleCols *kSimpleRows) void simple_kernel(Problem p) {
+  select_slice(p);
   const int col = blockIdx.y * kSimpleCols + (threadIdx.x & (kSimpleCols - 1));
   const int row = blockIdx.x * kSimpleRows + (threadIdx.x >> 6);
   if (row >= p.M || col >= p.N) return;  // no barrier in this kernel
@@ -44,12 +45,14 @@ __global__ __launch_bounds__(kSimpleCols *kSimpleRows) void simple_kernel(Proble
   store_out(p.C + (size_t)row * p.ldc + col, acc, p.alpha, p.beta);
 }
 
-// C = beta * C (beta == 0 writes zeros without reading C).
-__global__ __launch_bounds__(256) void scale_kernel(int M, int N, float beta, float *C, int ldc) {
+// C = beta * C (beta == 0 writes zeros without reading C), batch slice
+// blockIdx.z at C + z*sc.
+__global__ __launch_bounds__(256) void scale_kernel(int M, int N, float beta, float *C, int ldc,
+                                                   long long sc) {
   const int col = blockIdx.y * 64 + (threadIdx.x & 63);
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M || col >= N) return;
-  float *c = C + (size_t)row * ldc + col;
+  float *c = C + (size_t)blockIdx.z * (size_t)sc + (size_t)row * ldc + col;
   *c = (beta == 0.0f) ? 0.0f : beta * *c;
 }
 
@@ -57,17 +60,17 @@ int launch_simple(const Problem &p, hipStream_t stream) {
   const long long gx = ((long long)p.M + kSimpleRows - 1) / kSimpleRows;
   const long long gy = ((long long)p.N + kSimpleCols - 1) / kSimpleCols;
   if (gx > 0x7fffffffLL || gy > 65535) return -1;
-  hipLaunchKernelGGL(simple_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kSimpleCols * kSimpleRows),
-                     0, stream, p);
+  hipLaunchKernelGGL(simple_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)p.batch),
+                     dim3(kSimpleCols * kSimpleRows), 0, stream, p);
   return 0;
 }
 
-int launch_scale(int M, int N, float beta, float *C, int ldc, hipStream_t stream) {
-  const long long gx = ((long long)M + 3) / 4;
-  const long long gy = ((long long)N + 63) / 64;
+int launch_scale(const Problem &p, hipStream_t stream) {
+  const long long gx = ((long long)p.M + 3) / 4;
+  const long long gy = ((long long)p.N + 63) / 64;
   if (gx > 0x7fffffffLL || gy > 65535) return -1;
-  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, M, N,
-                     beta, C, ldc);
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)p.batch), dim3(256), 0,
+                     stream, p.M, p.N, p.beta, p.C, p.ldc, p.sc);
   return 0;
 }
 

@@ -29,6 +29,7 @@ constexpr int kSkinnyWaves = 4;
 // never picks this kernel for a transposed B).
 template <int MR, bool VB, bool TB>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, int kchunk) {
+  select_slice(p);
   __shared__ float red[kSkinnyWaves][MR][kSkinnyCols];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -96,11 +97,11 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
   }
 }
 
-// K rows per workgroup: enough workgroups for about four per CU, at least 64
-// rows (16 per wave) each, a multiple of 16.
+// K rows per workgroup: enough workgroups (over all batch slices) for about
+// four per CU, at least 64 rows (16 per wave) each, a multiple of 16.
 static int skinny_kchunk(const Problem &p, long long strips) {
   const long long target = 1024;
-  long long chunks = target / (strips > 0 ? strips : 1);
+  long long chunks = target / (strips * p.batch > 0 ? strips * p.batch : 1);
   if (chunks < 1) chunks = 1;
   long long kc = ((long long)p.K + chunks - 1) / chunks;
   if (kc < 64) kc = 64;
@@ -115,8 +116,8 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
   const long long chunks = ((long long)p.K + kc - 1) / kc;
   if (strips > INT_MAX || chunks > 65535) return -1;
   // C = beta*C first (zeros when beta == 0, nothing when beta == 1).
-  if (p.beta != 1.0f && launch_scale(p.M, p.N, p.beta, p.C, p.ldc, stream) != 0) return -1;
-  const dim3 grid((unsigned)strips, (unsigned)chunks);
+  if (p.beta != 1.0f && launch_scale(p, stream) != 0) return -1;
+  const dim3 grid((unsigned)strips, (unsigned)chunks, (unsigned)p.batch);
   const dim3 block(kSkinnyWaves * 64);
   const bool vb = b_vec_ok(p);
 #define SG950_SKINNY(MR_)                                                                     \

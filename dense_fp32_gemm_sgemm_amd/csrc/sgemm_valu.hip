@@ -35,6 +35,7 @@ constexpr int kBPitch = kBN + 4;  // B row pitch (floats)
 template <bool TA, bool TB, bool VA, bool VB, bool VC>
 __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, int tiles_n,
                                                         int group_m) {
+  select_slice(p);
   __shared__ __attribute__((aligned(16))) float As[2 * kBK * kAPitch];
   __shared__ __attribute__((aligned(16))) float Bs[2 * kBK * kBPitch];
 
@@ -197,7 +198,7 @@ int launch_valu_128x128(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + kBM - 1) / kBM;
   const long long tiles_n = ((long long)p.N + kBN - 1) / kBN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const dim3 grid((unsigned)(tiles_m * tiles_n), 1, (unsigned)p.batch);
   const int tm = (int)tiles_m, tn = (int)tiles_n, gm = 8;
   if (!p.ta && !p.tb) {
     launch_valu_t<false, false>(p, grid, stream, tm, tn, gm);

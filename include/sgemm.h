@@ -49,13 +49,14 @@ extern "C" {
 #endif
 
 #define SGEMM_OK 0
-#define SGEMM_ERR_DIM (-1)     /* M, N or K negative, or a grid too large */
+#define SGEMM_ERR_DIM (-1)     /* M, N, K or batch negative, or a grid too large */
 #define SGEMM_ERR_LD (-2)      /* a leading dimension shorter than the stored row */
 #define SGEMM_ERR_PTR (-3)     /* a matrix that must be read or written is NULL */
 #define SGEMM_ERR_LAUNCH (-4)  /* the HIP runtime rejected a kernel launch */
 #define SGEMM_ERR_DEVICE (-5)  /* the current device is not gfx950, or no device */
 #define SGEMM_ERR_VARIANT (-6) /* sgemm_ex: variant index out of range */
 #define SGEMM_ERR_OP (-7)      /* sgemm_op: opA or opB not SGEMM_OP_N / SGEMM_OP_T */
+#define SGEMM_ERR_STRIDE (-8)  /* batched: a negative stride, or slices of C overlap */
 
 /* Operand orientation for sgemm_op: use the matrix as stored, or its transpose. */
 #define SGEMM_OP_N 0
@@ -117,6 +118,32 @@ int sgemm_op_ex(int opA, int opB, int M, int N, int K, float alpha, const float 
                 const float *B, int ldb, float beta, float *C, int ldc, void *stream,
                 int variant);
 
+/*
+ * A batch of independent GEMMs of one shape (strided batched SGEMM, the
+ * "batching" the Tinyforge README lists among what a general library covers):
+ * for z in [0, batch),
+ *
+ *     C_z = alpha * op(A_z) * op(B_z) + beta * C_z
+ *
+ * with A_z = A + z*strideA, B_z = B + z*strideB, C_z = C + z*strideC (element
+ * strides, >= 0; a stride of 0 shares one matrix among all slices).  Each slice
+ * is laid out as in sgemm_op().  The slices of C must not overlap: with
+ * batch > 1, strideC >= (M-1)*ldc + N, else SGEMM_ERR_STRIDE.  batch == 0 is a
+ * no-op; everything else is as for sgemm_op().  All slices are computed by one
+ * set of launches (the kernels take the slice from the grid), so small
+ * matrices in large batches fill the GPU.
+ */
+int sgemm_strided_batched(int opA, int opB, int M, int N, int K, float alpha,
+                          const float *A, int lda, long long strideA, const float *B, int ldb,
+                          long long strideB, float beta, float *C, int ldc, long long strideC,
+                          int batch, void *stream);
+
+/* As sgemm_strided_batched() with an explicit kernel variant (-1 = automatic). */
+int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long strideA, const float *B,
+                             int ldb, long long strideB, float beta, float *C, int ldc,
+                             long long strideC, int batch, void *stream, int variant);
+
 /* Number of kernel variants, and a stable name for each ("" when out of range). */
 int sgemm_num_variants(void);
 const char *sgemm_variant_name(int variant);
@@ -135,10 +162,16 @@ int sgemm_op_select_variant(int opA, int opB, int M, int N, int K, float alpha, 
                             int lda, const float *B, int ldb, float beta, const float *C,
                             int ldc);
 
+/* sgemm_select_variant for sgemm_strided_batched problems. */
+int sgemm_strided_batched_select_variant(int opA, int opB, int M, int N, int K, float alpha,
+                                         const float *A, int lda, long long strideA,
+                                         const float *B, int ldb, long long strideB, float beta,
+                                         const float *C, int ldc, long long strideC, int batch);
+
 /* Short English description of a status code (never NULL). */
 const char *sgemm_status_string(int status);
 
-/* Interface version, currently 2 (2 added the sgemm_op entry points). */
+/* Interface version, currently 3 (2 added sgemm_op, 3 the strided batches). */
 int sgemm_version(void);
 
 #ifdef __cplusplus

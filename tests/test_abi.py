@@ -56,7 +56,7 @@ def test_variant_registry(lib):
     assert names[0] == "simple"
     assert any(x.startswith("mfma32") for x in names) and any(x.startswith("valu") for x in names)
     assert sg.sgemm_variant_name(n) == "" and sg.sgemm_variant_name(-1) == ""
-    assert sg.sgemm_version() == 2
+    assert sg.sgemm_version() == 3
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails or returns before any HIP call
@@ -118,8 +118,53 @@ def test_op_select_avoids_few_rows_kernel_for_transposed_b(lib):
                                         FAKE, 4096)).startswith("mfma32_256x256")
 
 
+@pytest.mark.parametrize("args,status", [
+    # opA opB M N K alpha A lda sA B ldb sB beta C ldc sC batch
+    ((0, 0, 4, 4, 8, 1.0, FAKE, 8, 32, FAKE, 4, 32, 0.0, FAKE, 4, 16, -1), sg.SGEMM_ERR_DIM),
+    ((0, 0, 4, 4, 8, 1.0, FAKE, 8, -1, FAKE, 4, 32, 0.0, FAKE, 4, 16, 2), sg.SGEMM_ERR_STRIDE),
+    ((0, 0, 4, 4, 8, 1.0, FAKE, 8, 32, FAKE, 4, 32, 0.0, FAKE, 4, 15, 2), sg.SGEMM_ERR_STRIDE),
+    ((0, 0, 4, 4, 8, 1.0, FAKE, 8, 32, FAKE, 4, 32, 0.0, FAKE, 4, 0, 1), "valid"),   # one slice
+    ((0, 0, 4, 4, 8, 1.0, FAKE, 8, 0, FAKE, 4, 0, 0.0, FAKE, 4, 16, 9), "valid"),    # shared A, B
+    ((0, 0, 4, 4, 8, 1.0, None, 8, 0, None, 4, 0, 0.0, None, 4, 16, 0), sg.SGEMM_OK),  # empty batch
+    ((1, 0, 4, 4, 8, 1.0, FAKE, 3, 32, FAKE, 4, 32, 0.0, FAKE, 4, 16, 2), sg.SGEMM_ERR_LD),
+    ((3, 0, 4, 4, 8, 1.0, FAKE, 8, 32, FAKE, 4, 32, 0.0, FAKE, 4, 16, 2), sg.SGEMM_ERR_OP),
+])
+def test_batched_argument_checks(lib, args, status):
+    if status == "valid":
+        st = sg.sgemm_strided_batched_select_variant(*args)
+        assert 0 <= st < sg.sgemm_num_variants()
+        return
+    assert sg.sgemm_strided_batched(*args, 0) == status
+    assert sg.sgemm_strided_batched_ex(*args, 0, -1) == status
+
+
+def test_batched_select_counts_every_slice(lib):
+    n = sg.sgemm_variant_name
+    one = sg.sgemm_strided_batched_select_variant(0, 0, 512, 512, 512, 1.0, FAKE, 512, 512 * 512, FAKE,
+                                                  512, 512 * 512, 0.0, FAKE, 512, 512 * 512, 1)
+    many = sg.sgemm_strided_batched_select_variant(0, 0, 512, 512, 512, 1.0, FAKE, 512, 512 * 512,
+                                                   FAKE, 512, 512 * 512, 0.0, FAKE, 512, 512 * 512, 64)
+    assert n(one).endswith("splitk") and n(many).startswith("mfma32_256x256")
+
+
+def _batched_choice(batch, M, N, K):
+    return sg.sgemm_variant_name(sg.sgemm_strided_batched_select_variant(
+        0, 0, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, batch))
+
+
+def test_batched_select_small_slices(lib):
+    """Many small slices leave the one-lane kernel for tiled ones; tiles that
+    would mostly lie outside a slice are not chosen."""
+    assert _batched_choice(1, 128, 128, 128) == "simple"
+    assert _batched_choice(1024, 128, 128, 128) == "mfma32_128x128x16_2x2_w4"
+    assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_4x2"
+    assert _batched_choice(4096, 32, 32, 32) == "mfma16_64x64x16_2x2_splitk"
+    assert _batched_choice(128, 200, 300, 100) == "mfma16_64x64x16_2x2_splitk"
+    assert _batched_choice(8, 1, 4096, 4096) == "skinny_m8"
+
+
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = sg.sgemm_status_string(st)
         assert s and s != "unknown status"
     assert sg.sgemm_status_string(12345) == "unknown status"

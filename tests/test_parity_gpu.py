@@ -178,6 +178,96 @@ def test_column_major_via_transposition_identity():
     check_real(np.ascontiguousarray(Ct.T), A, B, None, 1.0, 0.0, "column-major")
 
 
+def run_batched(A, B, C, alpha, beta, *, variant=-1, trans_a=False, trans_b=False, shared_b=False,
+                gap=0):
+    """Strided-batched call on stacked slices (numpy (batch, rows, cols));
+    `gap` extra NaN floats between consecutive slices, `shared_b` passes one
+    B with stride 0.  Returns C as numpy and checks the gaps stay NaN."""
+    batch = C.shape[0]
+
+    def dev(X, gap_):
+        b, r, c = X.shape
+        stride = r * c + gap_
+        buf = torch.full((b * stride + 16,), float("nan"), dtype=torch.float32, device="cuda")
+        view = torch.as_strided(buf, (b, r, c), (stride, c, 1), 8)
+        view.copy_(torch.from_numpy(np.ascontiguousarray(X)).cuda())
+        return buf, view
+
+    _, dA = dev(A, gap)
+    if shared_b:
+        _, dB1 = dev(B[:1], 0)
+        dB = dB1.expand(batch, -1, -1)
+    else:
+        _, dB = dev(B, gap)
+    bufC, dC = dev(C, gap)
+    sg.gemm_batched(dA, dB, dC, alpha, beta, variant=variant, trans_a=trans_a, trans_b=trans_b)
+    torch.cuda.synchronize()
+    mask = torch.ones_like(bufC, dtype=torch.bool)
+    idx = torch.as_strided(torch.arange(bufC.numel(), device="cuda"), dC.shape, dC.stride(), 8)
+    mask[idx.reshape(-1)] = False
+    assert bool(torch.isnan(bufC[mask]).all().item()), "memory outside the C slices was written"
+    return dC.cpu().numpy()
+
+
+def check_batched(C, A, B, Cin, alpha, beta, what, exact=False, ta=False, tb=False):
+    for z in range(C.shape[0]):
+        a = np.ascontiguousarray(A[z].T) if ta else A[z]
+        b = np.ascontiguousarray(B[z].T) if tb else B[z]
+        if exact:
+            check_exact(C[z], a, b, Cin[z], alpha, beta, "%s slice %d" % (what, z))
+        else:
+            check_real(C[z], a, b, Cin[z], alpha, beta, "%s slice %d" % (what, z))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_strided_batched_every_variant(variant):
+    """Three slices with gaps between them, every transpose combination, a
+    shared B (stride 0); real data to the tolerance, integer data exactly."""
+    rng = np.random.default_rng(41)
+    for ta, tb in ((False, False), (True, False), (False, True), (True, True)):
+        M, N, K, batch = 131, 70, 97, 3
+        A = rng.uniform(-1, 1, (batch, K, M) if ta else (batch, M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, (batch, N, K) if tb else (batch, K, N)).astype(np.float32)
+        C = rng.standard_normal((batch, M, N)).astype(np.float32)
+        say("batched", VNAMES[variant], ta, tb)
+        out = run_batched(A, B, C, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, gap=5)
+        check_batched(out, A, B, C, 1.5, 0.5, VNAMES[variant], ta=ta, tb=tb)
+    Ai = rng.integers(-4, 5, (4, 65, 40)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (4, 40, 33)).astype(np.float32)
+    Bi[:] = Bi[0]
+    Ci = rng.integers(-4, 5, (4, 65, 33)).astype(np.float32)
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, shared_b=True)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, VNAMES[variant] + " shared B", exact=True)
+
+
+@pytest.mark.parametrize("shape", [(64, 512, 512, 512), (256, 64, 64, 64), (8, 1024, 1024, 1024),
+                                   (2, 1, 4096, 4096), (1024, 128, 128, 128), (256, 256, 256, 256),
+                                   (4096, 32, 32, 32), (128, 200, 300, 100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_strided_batched_automatic(shape):
+    batch, M, N, K = shape
+    rng = np.random.default_rng(batch + M)
+    A = rng.uniform(-1, 1, (batch, M, K)).astype(np.float32)
+    B = rng.uniform(-1, 1, (batch, K, N)).astype(np.float32)
+    C = np.full((batch, M, N), np.nan, np.float32)
+    say("batched auto", shape)
+    out = run_batched(A, B, C, 1.0, 0.0)
+    check_batched(out, A, B, np.zeros_like(C), 1.0, 0.0, "auto %s" % (shape,))
+
+
+def test_strided_batched_more_slices_than_one_grid():
+    """65,543 slices: more than one grid's worth (65,535), so the entry point
+    splits the batch into launches."""
+    rng = np.random.default_rng(43)
+    batch, M, N, K = 65543, 2, 3, 4
+    A = rng.integers(-4, 5, (batch, M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (batch, K, N)).astype(np.float32)
+    C = rng.integers(-4, 5, (batch, M, N)).astype(np.float32)
+    say("batched 65543 slices")
+    out = run_batched(A, B, C, 1.0, 1.0)
+    check_batched(out, A, B, C, 1.0, 1.0, "65543 slices", exact=True)
+
+
 # ---------------------------------------------------------------- special cases
 
 def test_beta_zero_ignores_nan_in_c():
