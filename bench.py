@@ -79,7 +79,7 @@ def lds_reads_per_fma(TM: int, TN: int) -> float:
 
 
 # The sources that define the matrix-core kernel whose counters are stored.
-KERNEL_FILES = ("sgemm_mfma.hip", "sgemm_tiles.hpp", "sgemm_common.hpp")
+KERNEL_FILES = ("sgemm_mfma.hpp", "sgemm_mfma.hip", "sgemm_tiles.hpp", "sgemm_common.hpp")
 
 
 def kernel_source_hash(files=KERNEL_FILES) -> str:
@@ -220,7 +220,7 @@ class Problem:
         return sg.sgemm_variant_name(v) if v >= 0 else "none"
 
 
-def measure_ceilings(samples: int = 7):
+def measure_ceilings(samples: int = 15):
     """Measured FP32 matrix-core, FP32 vector and HBM copy rates."""
     torch = _torch()
     import dense_fp32_gemm_sgemm_amd as sg
@@ -247,7 +247,7 @@ def measure_ceilings(samples: int = 7):
             if ms >= target_ms * 0.5 or iters >= 1 << 22:
                 break
             iters = int(iters * max(2.0, target_ms / max(ms, 1e-3)))
-        wake(0.3, lambda: launch(iters))
+        wake(0.5, lambda: launch(iters))
         vals = []
         for _ in range(samples):
             t0 = torch.cuda.Event(enable_timing=True)
@@ -315,6 +315,29 @@ def stored_traffic(variant: str):
     return round(t.get("bytes_per_launch"))
 
 
+def vendor_context(prob: Problem, steps: int, warmup: int):
+    """torch.mm on the same device tensors with TF32 off: the vendor BLAS in
+    strict FP32, timed the same way.  A reported stopwatch, not part of the
+    library; beta = 0 problems only (torch.mm overwrites its output)."""
+    torch = _torch()
+    if prob.beta != 0.0 or prob.ta or prob.tb:
+        return {}
+    prev = torch.backends.cuda.matmul.allow_tf32
+    torch.backends.cuda.matmul.allow_tf32 = False
+    try:
+        A, B, C = prob.A, prob.B, prob.C
+        fn = lambda: torch.mm(A, B, out=C)
+        for _ in range(warmup):
+            fn()
+        wake(0.25, fn)
+        _, per = time_steps(fn, steps, torch.cuda.current_stream())
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = prev
+    ms = statistics.median(per)
+    return {"torch_mm_fp32_ms_median": round(ms, 5),
+            "torch_mm_fp32_gflops": round(flops(prob.M, prob.N, prob.K) / (ms * 1e-3) / 1e9, 1)}
+
+
 def bench_problem(prob: Problem, steps: int, warmup: int, variant=-1):
     fn = prob.launcher(variant)
     for _ in range(warmup):
@@ -346,6 +369,8 @@ def main(argv=None):
                     help="write the stored traffic figure from four counter_collection.csv files")
     ap.add_argument("--copy-calib", action="store_true",
                     help="one 256 MiB streaming copy (to scale HBM byte counters)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="with --sweep/--shape: also time torch.mm in strict FP32 (context only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     args = ap.parse_args(argv)
@@ -410,8 +435,10 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel_ms_mean": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
-                     "kernel_ms_max": round(max(per), 5)},
+                     "kernel_ms_mean": round(kern_ms, 5),
+                     "kernel_ms_median": round(statistics.median(per), 5),
+                     "kernel_ms_std": round(statistics.pstdev(per), 5),
+                     "kernel_ms_min": round(min(per), 5), "kernel_ms_max": round(max(per), 5)},
         "cpu_baseline": cpu,
     }
     if ceilings:
@@ -425,7 +452,7 @@ def main(argv=None):
 
 
 def run_modes(args):
-    from workloads import RAGGED_SHAPES, SWEEP_SIZES
+    from workloads import RAGGED_SHAPES, SHARD_SHAPES, SWEEP_SIZES
     import dense_fp32_gemm_sgemm_amd as sg
     jobs = []
     if args.copy_calib:
@@ -450,9 +477,10 @@ def run_modes(args):
                           "tflops": round(flops(*shape) / (kern_ms * 1e-3) / 1e12, 2)}), flush=True)
         return 0
     if args.sweep:
-        jobs = [((n, n, n), -1) for n in SWEEP_SIZES] + [(s, -1) for s in RAGGED_SHAPES]
+        jobs = ([((n, n, n), -1) for n in SWEEP_SIZES] + [(s, -1) for s in RAGGED_SHAPES] +
+                [(s, -1) for s in SHARD_SHAPES])
     elif args.matrix:
-        shapes = [(n, n, n) for n in SWEEP_SIZES] + list(RAGGED_SHAPES)
+        shapes = [(n, n, n) for n in SWEEP_SIZES] + list(RAGGED_SHAPES) + list(SHARD_SHAPES)
         jobs = [(sh, v) for sh in shapes for v in range(sg.sgemm_num_variants())
                 if not (sg.sgemm_variant_name(v) == "simple" and flops(*sh) > 2e10)]
     elif args.variants:
@@ -479,6 +507,8 @@ def run_modes(args):
                "ai_flop_per_byte": round(arithmetic_intensity(M, N, K, args.beta), 2),
                "hbm_gbs_at_min_bytes": round(args.batch * min_bytes(M, N, K, args.beta) /
                                              (kern_ms * 1e-3) / 1e9, 1)}
+        if args.vendor and args.ops == "NN" and args.batch == 1 and v == -1:
+            rec.update(vendor_context(prob, steps, min(args.warmup, steps)))
         print(json.dumps(rec), flush=True)
         del prob
         _torch().cuda.empty_cache()

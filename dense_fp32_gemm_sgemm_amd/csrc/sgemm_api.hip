@@ -52,6 +52,11 @@ const Variant kVariants[] = {
     {"mfma16_64x64x16_2x2_splitk", launch_mfma16_64x64x16_2x2_splitk},
     {"mfma32_64x64x16_1x1_splitk", launch_mfma32_64x64x16_1x1_splitk},
     {"skinny_m8", launch_skinny_any},
+    {"mfma32_128x128x32_4x2", launch_mfma32_128x128x32_4x2},
+    {"mfma32_128x128x64_4x2", launch_mfma32_128x128x64_4x2},
+    {"mfma16_64x64x64_4x2_pipe", launch_mfma16_64x64x64_4x2_pipe},
+    {"mfma32_128x128x32_4x2_splitk", launch_mfma32_128x128x32_4x2_splitk},
+    {"mfma16_64x64x64_4x2_pipe_splitk", launch_mfma16_64x64x64_4x2_pipe_splitk},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -70,6 +75,11 @@ enum VariantId {
   kMfma16_64x64x16_splitk = 11,
   kMfma32_64x64x16_splitk = 12,
   kSkinny = 13,
+  kMfma32_128x128x32_w8 = 14,
+  kMfma32_128x128x64_w8 = 15,
+  kMfma16_64x64x64_w8_pipe = 16,
+  kMfma32_128x128x32_w8_splitk = 17,
+  kMfma16_64x64x64_w8_pipe_splitk = 18,
 };
 
 constexpr int kNoKernel = -100;
@@ -99,21 +109,25 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 
 // The per-shape table.  Every entry names a variant that handles any shape,
 // so the table only trades speed; the thresholds come from measured sweeps of
-// every variant over the square sizes 128..8192, the rectangular shapes and
-// strided batches of small and mid-sized slices on an MI355X.  Work and tile
-// counts are those of the whole batch.
-//   * tiny problems (little work and little data) are launch-latency bound:
-//     one lane per output wins;
+// every variant over the square sizes 128..8192, the rectangular shapes, one
+// GPU's share of an eight-way split of 4096^3, and strided batches of small
+// and mid-sized slices on an MI355X.  Work and tile counts are those of the
+// whole batch.
+//   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
+//     output wins;
 //   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
 //     fastest when the tiles are mostly inside C and their count fills the
 //     256 CUs in whole rounds;
-//   * 128x128 tiles when there are at least as many tiles as CUs, they are
-//     mostly inside C and both operands allow 16-byte loads: 16-deep slabs for
-//     a short K loop, 32-deep ones otherwise, with the pinned software pipeline
-//     when the K loop is long;
-//   * otherwise 64x64 tiles on the 16x16x4 instruction, splitting K over
-//     workgroups when even those tiles cannot give every CU one workgroup.
+//   * 128x128 tiles with eight waves (two per SIMD) when there are at least as
+//     many tiles as CUs and they are mostly inside C: 64-deep slabs while a
+//     single round of tiles gives each CU one long K loop, 32-deep ones (two
+//     workgroups per CU fit) otherwise; for K < 256 four waves with 16-deep
+//     slabs;
+//   * otherwise 64x64 tiles with eight waves and 64-deep slabs (16-deep ones,
+//     four waves, for a short K that is not a multiple of 64), splitting K
+//     over workgroups when even those tiles cannot give every CU one
+//     workgroup.
 
 // Percentage of the T x T tiles' area that lies inside an M x N slice.
 long long tile_fill_pct(int M, int N, int T) {
@@ -128,7 +142,7 @@ int choose_variant(const Problem &p) {
   if (p.M <= 2 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
   if (p.N < 16) return kSimple;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
-  if (work <= 256LL * 256 * 256 && nk < (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
+  if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
   if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
@@ -137,13 +151,14 @@ int choose_variant(const Problem &p) {
     const long long tail = t256 % cus;
     if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32;
   }
-  // Operands that need scalar loads (unaligned base or leading dimension)
-  // favour the smaller tiles, whose many workgroups hide the longer loads.
-  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128) >= 75 && a_vec_ok(p) && b_vec_ok(p)) {
-    if (p.K <= 256) return kMfma32_128x128x16_w4;
-    return (p.K >= 4096) ? kMfma32_128x128x32_pipe : kMfma32_128x128x32;
+  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128) >= 75) {
+    if (p.K < 256) return kMfma32_128x128x16_w4;
+    return (t128 < 2 * cus) ? kMfma32_128x128x64_w8 : kMfma32_128x128x32_w8;
   }
-  return kMfma16_64x64x16_splitk;
+  // A short K that is not a multiple of 64 would leave most of a 64-deep
+  // slab empty: 16-deep slabs then.
+  if (p.K < 256 && p.K % 64 != 0) return kMfma16_64x64x16_splitk;
+  return kMfma16_64x64x64_w8_pipe_splitk;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other

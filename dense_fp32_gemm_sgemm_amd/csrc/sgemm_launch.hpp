@@ -38,6 +38,13 @@ int launch_mfma16_64x64x16_2x2(const Problem &p, hipStream_t stream);
 int launch_mfma32_128x128x32_2x2_splitk(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x16_2x2_splitk(const Problem &p, hipStream_t stream);
 int launch_mfma32_64x64x16_1x1_splitk(const Problem &p, hipStream_t stream);
+// Eight waves (4x2) on 128x128 and 64x64 tiles, two waves per SIMD
+// (sgemm_mfma8.hip).
+int launch_mfma32_128x128x32_4x2(const Problem &p, hipStream_t stream);
+int launch_mfma32_128x128x64_4x2(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x64_4x2_pipe(const Problem &p, hipStream_t stream);
+int launch_mfma32_128x128x32_4x2_splitk(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x64_4x2_pipe_splitk(const Problem &p, hipStream_t stream);
 
 // Few rows of C (M <= 8): streams B across every CU, K split over
 // workgroups, float atomics into C (scaled by beta first).  Returns -1 for

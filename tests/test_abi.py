@@ -155,7 +155,8 @@ def _batched_choice(batch, M, N, K):
 def test_batched_select_small_slices(lib):
     """Many small slices leave the one-lane kernel for tiled ones; tiles that
     would mostly lie outside a slice are not chosen."""
-    assert _batched_choice(1, 128, 128, 128) == "simple"
+    assert _batched_choice(1, 127, 129, 17) == "simple"
+    assert _batched_choice(1, 128, 128, 128) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1024, 128, 128, 128) == "mfma32_128x128x16_2x2_w4"
     assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_4x2"
     assert _batched_choice(4096, 32, 32, 32) == "mfma16_64x64x16_2x2_splitk"

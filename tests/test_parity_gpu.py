@@ -19,7 +19,7 @@ import oracle  # noqa: E402
 import dense_fp32_gemm_sgemm_amd as sg  # noqa: E402
 from tests.gpu_util import run  # noqa: E402
 from workloads import (ACCUM, ACCUM_INT, HEADLINE, SMALL, SMALL_INT, draw,  # noqa: E402
-                       draw_workload, ragged_workloads, sweep_workloads)
+                       draw_workload, ragged_workloads, shard_workloads, sweep_workloads)
 
 pytestmark = pytest.mark.gpu
 
@@ -456,7 +456,7 @@ def test_sweep_8192_sampled():
     _sampled_check(A, B, C, 1.0, 0.0, None, 256, 256, 8192, w.name)
 
 
-@pytest.mark.parametrize("w", ragged_workloads(), ids=lambda w: w.name)
+@pytest.mark.parametrize("w", ragged_workloads() + shard_workloads(), ids=lambda w: w.name)
 def test_rectangular_and_ragged(w):
     A, B, _ = draw_workload(w)
     say("shape", w.name)

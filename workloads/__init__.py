@@ -27,6 +27,9 @@ import numpy as np
 SWEEP_SIZES = (128, 256, 512, 1024, 2048, 4096, 8192)
 RAGGED_SHAPES = ((4095, 4097, 1023), (8192, 1024, 8192), (1024, 8192, 256),
                  (127, 129, 17), (1, 4096, 4096))
+# One GPU's share of the 4096^3 problem split over eight GPUs: by rows of C
+# (each GPU holds 512 rows of A and all of B) and on a 2 x 4 grid of C blocks.
+SHARD_SHAPES = ((512, 4096, 4096), (2048, 1024, 4096))
 
 
 @dataclass(frozen=True)
@@ -54,6 +57,11 @@ ACCUM_INT = Workload("square-4096-accumulate-int", 4096, 4096, 4096, 1.0, 1.0, "
 
 def sweep_workloads():
     return [Workload("square-%d" % n, n, n, n, 1.0, 0.0, "real", n) for n in SWEEP_SIZES]
+
+
+def shard_workloads():
+    return [Workload("shard-%dx%dx%d" % s, s[0], s[1], s[2], 1.0, 0.0, "real", 200 + i)
+            for i, s in enumerate(SHARD_SHAPES)]
 
 
 def ragged_workloads():
