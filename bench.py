@@ -79,7 +79,8 @@ def lds_reads_per_fma(TM: int, TN: int) -> float:
 
 
 # The sources that define the matrix-core kernel whose counters are stored.
-KERNEL_FILES = ("sgemm_mfma.hpp", "sgemm_mfma.hip", "sgemm_tiles.hpp", "sgemm_common.hpp")
+KERNEL_FILES = ("sgemm_sched.hpp", "sgemm_mfma_sched.hip", "sgemm_mfma.hpp", "sgemm_mfma.hip",
+                "sgemm_tiles.hpp", "sgemm_common.hpp")
 
 
 def kernel_source_hash(files=KERNEL_FILES) -> str:
@@ -93,9 +94,14 @@ def kernel_source_hash(files=KERNEL_FILES) -> str:
     return h.hexdigest()[:16]
 
 
+# Names of the matrix-core GEMM kernels as the profiler prints them.
+GEMM_KERNEL_PREFIXES = ("void sg950::mfma_kernel", "void sg950::sched_kernel")
+
+
 def _counter_means(path, kernel_prefix):
     """Mean counter value per counter name over the dispatches of kernels whose
-    name starts with kernel_prefix, from a rocprofv3 counter_collection.csv."""
+    name starts with kernel_prefix (a string or a tuple of strings), from a
+    rocprofv3 counter_collection.csv."""
     import csv
     vals = {}
     names = set()
@@ -112,7 +118,7 @@ def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     """HBM-side bytes per launch of the GEMM kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for a streaming copy that reads and writes copy_bytes."""
-    gemm_prefix = "void sg950::mfma_kernel"
+    gemm_prefix = GEMM_KERNEL_PREFIXES
     f, fnames, fn = _counter_means(fetch_csv, gemm_prefix)
     w, _, wn = _counter_means(write_csv, gemm_prefix)
     cf, _, _ = _counter_means(copy_fetch_csv, "sg950::copy_kernel")

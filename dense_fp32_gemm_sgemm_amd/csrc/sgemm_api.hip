@@ -57,6 +57,10 @@ const Variant kVariants[] = {
     {"mfma16_64x64x64_4x2_pipe", launch_mfma16_64x64x64_4x2_pipe},
     {"mfma32_128x128x32_4x2_splitk", launch_mfma32_128x128x32_4x2_splitk},
     {"mfma16_64x64x64_4x2_pipe_splitk", launch_mfma16_64x64x64_4x2_pipe_splitk},
+    {"mfma32_256x256x32_2x2_sched", launch_mfma32_256x256x32_2x2_sched},
+    {"mfma32_256x256x32_4x2_sched", launch_mfma32_256x256x32_4x2_sched},
+    {"mfma32_128x128x32_4x2_sched", launch_mfma32_128x128x32_4x2_sched},
+    {"mfma16_64x64x64_4x2_sched", launch_mfma16_64x64x64_4x2_sched},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -80,6 +84,10 @@ enum VariantId {
   kMfma16_64x64x64_w8_pipe = 16,
   kMfma32_128x128x32_w8_splitk = 17,
   kMfma16_64x64x64_w8_pipe_splitk = 18,
+  kMfma32_256x256x32_w4_sched = 19,
+  kMfma32_256x256x32_w8_sched = 20,
+  kMfma32_128x128x32_w8_sched = 21,
+  kMfma16_64x64x64_w8_sched = 22,
 };
 
 constexpr int kNoKernel = -100;
@@ -116,18 +124,19 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
 //   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
-//   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs) are
-//     fastest when the tiles are mostly inside C and their count fills the
-//     256 CUs in whole rounds;
-//   * 128x128 tiles with eight waves (two per SIMD) when there are at least as
-//     many tiles as CUs and they are mostly inside C: 64-deep slabs while a
-//     single round of tiles gives each CU one long K loop, 32-deep ones (two
-//     workgroups per CU fit) otherwise; for K < 256 four waves with 16-deep
-//     slabs;
-//   * otherwise 64x64 tiles with eight waves and 64-deep slabs (16-deep ones,
-//     four waves, for a short K that is not a multiple of 64), splitting K
-//     over workgroups when even those tiles cannot give every CU one
-//     workgroup.
+//   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs, the
+//     ordered slab loop) are fastest when the tiles are mostly inside C and
+//     their count fills the 256 CUs in whole rounds;
+//   * 128x128 tiles with eight waves (two per SIMD, the ordered loop) when
+//     there are at least as many tiles as CUs and they are mostly inside C;
+//     for K < 256 four waves with 16-deep slabs;
+//   * otherwise 64x64 tiles with eight waves and 64-deep slabs on the ordered
+//     loop (16-deep ones, four waves, for a short K that is not a multiple of
+//     64), splitting K over workgroups when the tiles cannot occupy half the
+//     CUs and K is long.
+// The ordered-loop variants fall back to their tile family's plain loop when
+// K is not a multiple of the slab depth, the tile is larger than C or an
+// operand does not allow 16-byte loads.
 
 // Percentage of the T x T tiles' area that lies inside an M x N slice.
 long long tile_fill_pct(int M, int N, int T) {
@@ -146,19 +155,22 @@ int choose_variant(const Problem &p) {
   if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
+  const long long t64 = ((long long)p.M + 63) / 64 * (((long long)p.N + 63) / 64) * batch;
   const long long cus = 256;
   if (t256 >= cus && tile_fill_pct(p.M, p.N, 256) >= 75) {
     const long long tail = t256 % cus;
-    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32;
+    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w8_sched;
   }
   if (t128 >= cus && tile_fill_pct(p.M, p.N, 128) >= 75) {
     if (p.K < 256) return kMfma32_128x128x16_w4;
-    return (t128 < 2 * cus) ? kMfma32_128x128x64_w8 : kMfma32_128x128x32_w8;
+    return kMfma32_128x128x32_w8_sched;
   }
   // A short K that is not a multiple of 64 would leave most of a 64-deep
   // slab empty: 16-deep slabs then.
   if (p.K < 256 && p.K % 64 != 0) return kMfma16_64x64x16_splitk;
-  return kMfma16_64x64x64_w8_pipe_splitk;
+  // Too few tiles for half the CUs and a long K: split K over workgroups.
+  if (t64 < cus / 2 && p.K >= 1024) return kMfma16_64x64x64_w8_pipe_splitk;
+  return kMfma16_64x64x64_w8_sched;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other

@@ -45,6 +45,13 @@ int launch_mfma32_128x128x64_4x2(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x64_4x2_pipe(const Problem &p, hipStream_t stream);
 int launch_mfma32_128x128x32_4x2_splitk(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x64_4x2_pipe_splitk(const Problem &p, hipStream_t stream);
+// _sched: the explicitly ordered slab loop (sgemm_mfma_sched.hip) when K is a
+// multiple of the slab depth, the tile fits in C and both operands allow
+// 16-byte loads; otherwise the same tile family on the plain loop.
+int launch_mfma32_256x256x32_2x2_sched(const Problem &p, hipStream_t stream);
+int launch_mfma32_256x256x32_4x2_sched(const Problem &p, hipStream_t stream);
+int launch_mfma32_128x128x32_4x2_sched(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x64_4x2_sched(const Problem &p, hipStream_t stream);
 
 // Few rows of C (M <= 8): streams B across every CU, K split over
 // workgroups, float atomics into C (scaled by beta first).  Returns -1 for
@@ -57,14 +64,15 @@ int launch_skinny(const Problem &p, hipStream_t stream);
 // row length must be one too, so a vector never crosses the end of a row.
 inline bool a_vec_ok(const Problem &p) {
   return ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && (p.lda % 4 == 0) &&
-         (!p.ta || p.M % 4 == 0);
+         (!p.ta || p.M % 4 == 0) && (p.batch <= 1 || p.sa % 4 == 0);
 }
 inline bool b_vec_ok(const Problem &p) {
   return ((reinterpret_cast<uintptr_t>(p.B) & 15) == 0) && (p.ldb % 4 == 0) &&
-         (p.tb || p.N % 4 == 0);
+         (p.tb || p.N % 4 == 0) && (p.batch <= 1 || p.sb % 4 == 0);
 }
 inline bool c_vec_ok(const Problem &p) {
-  return ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0) && (p.N % 4 == 0);
+  return ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0) && (p.N % 4 == 0) &&
+         (p.batch <= 1 || p.sc % 4 == 0);
 }
 
 }  // namespace sg950

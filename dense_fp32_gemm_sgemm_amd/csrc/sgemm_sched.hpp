@@ -1,0 +1,255 @@
+// sgemm_sched.hpp -- the matrix-core kernel with an explicitly ordered slab
+// loop, for problems whose shape lets every load be a whole 16-byte vector.
+//
+// It computes what mfma_kernel (sgemm_mfma.hpp) computes, with the same LDS
+// layout, operand reads and matrix-core blocks, and the same order of the
+// K-sum for every output.  The loop around them is different: the pages'
+// double buffering ("The road to a fast GEMM", section on prefetching the next
+// tile while computing the current one) is taken one step further, and the
+// instruction order inside a slab is pinned instead of left to the compiler:
+//
+//   * operand group q+1 of the slab is read from LDS while group q is
+//     multiplied, and those reads are issued first in the group, so they have
+//     landed long before their matrix instructions;
+//   * in the middle of slab t the registers holding slab t+1 are stored to the
+//     free LDS stage and the global loads of slab t+2 are issued at once, two
+//     matrix instructions apart: global loads get about a slab and a half to
+//     arrive, with one set of staging registers;
+//   * the last operand group of a slab is multiplied half before and half
+//     after the barrier, behind the first LDS reads of the next slab;
+//   * there are no branches in the slab loop: at the end the loads repeat the
+//     last slab (clamped index) and the stores go to the stage nobody reads.
+//
+// Addressing is stateless: one base pointer per operand and thread, plus
+// offsets that are uniform across the workgroup, which keeps the register
+// count low enough for four waves with 128x128 wave tiles.  A tile that would
+// stick out of C is shifted back inside (its first row becomes M - BM, or its
+// first column N - BN), so every load is in bounds without clamping; the
+// epilogue then stores only the rows and columns that belong to the tile.
+//
+// Preconditions (checked on the host; other problems go to mfma_kernel):
+// K a positive multiple of BK, M >= BM, N >= BN, both operands 16-byte
+// vector-aligned (base, leading dimension, batch stride; M or N a multiple of
+// 4 for a transposed A or an untransposed B), no split of K.
+#pragma once
+
+#include "sgemm_mfma.hpp"
+
+namespace sg950 {
+
+template <class T, class Acc, int E0, int E1>
+__device__ __forceinline__ void multiply_part(Acc (&acc)[T::FM][T::FN], const Operands<T> &o) {
+#pragma unroll
+  for (int e = E0; e < E1; ++e)
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma_step(o.a[i][e], o.b[j][e], acc[i][j]);
+}
+
+// Stateless loader of one operand's slab: ROWS x BK (k contiguous, KROWS =
+// false) or BK x ROWS (k-rows, KROWS = true) of a row-major matrix X with
+// leading dimension ld.  Thread t handles the 4-float vectors t, t+NT, ...;
+// with NT a multiple of the vectors per row, a thread's vectors sit at fixed
+// uniform row distances (DR) in one column.
+template <int ROWS, int BK, int NT, bool KROWS>
+struct SlabLoader {
+  static constexpr int COLS = KROWS ? ROWS : BK;  // floats per block row
+  static constexpr int VPR = COLS / 4;           // vectors per block row
+  static constexpr int NV = ROWS * BK / 4 / NT;  // vectors per thread
+  static constexpr int DR = NT / VPR;            // block rows between them
+  static_assert(NT % VPR == 0, "a thread's vectors must share one column");
+  static_assert(ROWS * BK / 4 % NT == 0, "slab must split evenly over the threads");
+
+  const float *base;  // this thread's first vector at k = 0
+  size_t ld;
+  floatx4 v[NV];
+
+  // r0: first row (or column, for k-rows) of the block inside X.
+  __device__ __forceinline__ void init(const float *X, int ld_, int r0, int tid) {
+    ld = (size_t)ld_;
+    const int br = tid / VPR, bc = (tid % VPR) * 4;
+    base = KROWS ? X + (size_t)br * ld + r0 + bc : X + (size_t)(r0 + br) * ld + bc;
+  }
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float *q = KROWS ? base + ((size_t)k0 + (size_t)i * DR) * ld
+                             : base + (size_t)i * DR * ld + k0;
+      v[i] = *reinterpret_cast<const floatx4 *>(q);
+    }
+  }
+  // LDS offset (floats) of vector 0 in a stage of row pitch `pitch`; vector i
+  // is i*DR rows further.
+  static __device__ __forceinline__ int lds_offset(int tid, int pitch) {
+    return (tid / VPR) * pitch + (tid % VPR) * 4;
+  }
+};
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
+          bool TB>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
+                                                                               int tiles_n, int group_m) {
+  select_slice(p);
+  using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD, TA, TB>;
+  using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
+  constexpr int kRegs = MI * MI / 64;
+  constexpr int NT = T::kThreads;
+  static_assert(T::NQ >= 2, "at least two operand groups per slab");
+  using LA = SlabLoader<BM, BK, NT, TA>;
+  using LB = SlabLoader<BN, BK, NT, !TB>;
+
+  __shared__ __attribute__((aligned(16))) float As[2 * T::A_STAGE];
+  __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_STAGE];
+
+  int tm, tn;
+  grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int ms = min(m0, p.M - BM), ns = min(n0, p.N - BN);  // shifted inside C
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int g = lane / MI, li = lane % MI;
+
+  LA la;
+  LB lb;
+  la.init(p.A, p.lda, ms, tid);
+  lb.init(p.B, p.ldb, ns, tid);
+  const int a_st = LA::lds_offset(tid, T::APITCH);
+  const int b_st = LB::lds_offset(tid, T::BPITCH);
+  auto store = [&](int stage) {
+    float *an = As + stage * T::A_STAGE + a_st;
+    float *bn = Bs + stage * T::B_STAGE + b_st;
+#pragma unroll
+    for (int i = 0; i < LA::NV; ++i) *reinterpret_cast<floatx4 *>(an + i * LA::DR * T::APITCH) = la.v[i];
+#pragma unroll
+    for (int i = 0; i < LB::NV; ++i) *reinterpret_cast<floatx4 *>(bn + i * LB::DR * T::BPITCH) = lb.v[i];
+  };
+  const int a_rd = TA ? (g * T::KPG) * T::APITCH + wm * T::WTM + li
+                      : (wm * T::WTM + li) * T::APITCH + g * T::KPG;
+  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::KPG
+                      : (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
+
+  Acc acc[T::FM][T::FN];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) acc[i][j][r] = 0.0f;
+
+  // Scheduling-group masks (LLVM AMDGPU): matrix instructions, LDS reads, LDS
+  // writes, global reads.
+  constexpr int kMfma = 0x008, kDsRead = 0x100, kDsWrite = 0x200, kVmemRead = 0x020;
+  constexpr int kReads = T::FM + 2 * T::FN;  // LDS read instructions per group
+  constexpr int kVecs = LA::NV + LB::NV;     // stores / loads per thread and slab
+
+  const int nk = p.K / BK;
+  la.load(0);
+  lb.load(0);
+  store(0);
+  __syncthreads();
+  la.load(min(1, nk - 1) * BK);
+  lb.load(min(1, nk - 1) * BK);
+  Operands<T> o;
+  read_operands<MI, TA, TB>(o, As + a_rd, Bs + b_rd, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const float *as = As + cur * T::A_STAGE + a_rd;
+    const float *bs = Bs + cur * T::B_STAGE + b_rd;
+#pragma unroll
+    for (int q = 0; q + 1 < T::NQ; ++q) {
+      Operands<T> nxt;
+      read_operands<MI, TA, TB>(nxt, as, bs, q + 1);
+      if (q == T::NQ / 2 - 1) {
+        store(cur ^ 1);                        // slab kt+1 (a repeat at the end)
+        la.load(min(kt + 2, nk - 1) * BK);     // slab kt+2, clamped
+        lb.load(min(kt + 2, nk - 1) * BK);
+      }
+      multiply_part<T, Acc, 0, 4>(acc, o);
+#pragma unroll
+      for (int s = 0; s < kReads; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      }
+      if (q == T::NQ / 2 - 1) {
+#pragma unroll
+        for (int s = 0; s < kVecs; ++s) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsWrite, 1, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < kVecs; ++s) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
+        }
+      }
+      o = nxt;
+    }
+    multiply_part<T, Acc, 0, 2>(acc, o);
+    __syncthreads();
+    Operands<T> nxt;
+    read_operands<MI, TA, TB>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd,
+                              Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
+    multiply_part<T, Acc, 2, 4>(acc, o);
+#pragma unroll
+    for (int s = 0; s < kReads; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+    o = nxt;
+  }
+
+  // Epilogue: C = alpha*acc + beta*C for the rows and columns of this tile
+  // (a shifted tile also computed some of its neighbour's).
+  const int row0 = ms + wm * T::WTM;
+  const int col0 = ns + wn * T::WTN + li;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int col = col0 + j * MI;
+      if (col < n0) continue;
+#pragma unroll
+      for (int r = 0; r < kRegs; ++r) {
+        const int row = row0 + i * MI + acc_row<MI>(g, r);
+        if (row < m0) continue;
+        store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
+      }
+    }
+}
+
+// True when sched_kernel<..., BM, BN, BK, ...> may run this problem.
+template <int BM, int BN, int BK>
+inline bool sched_ok(const Problem &p) {
+  return p.K >= BK && p.K % BK == 0 && p.M >= BM && p.N >= BN && a_vec_ok(p) && b_vec_ok(p);
+}
+
+// Launches sched_kernel when its preconditions hold, else `fallback` (a
+// variant of the same tile family that accepts every problem).
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD>
+static int launch_sched(const Problem &p, hipStream_t stream,
+                        int (*fallback)(const Problem &, hipStream_t)) {
+  if (!sched_ok<BM, BN, BK>(p)) return fallback(p, stream);
+  const long long tiles_m = ((long long)p.M + BM - 1) / BM;
+  const long long tiles_n = ((long long)p.N + BN - 1) / BN;
+  if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
+  const dim3 grid((unsigned)(tiles_m * tiles_n), 1u, (unsigned)p.batch);
+  const dim3 block(WAVES_M * WAVES_N * 64);
+  const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
+#define SG950_SCHED(TA_, TB_)                                                                         \
+  hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_>), grid, \
+                     block, 0, stream, p, tm, tn, group_m)
+  if (!p.ta && !p.tb) {
+    SG950_SCHED(false, false);
+  } else if (!p.ta) {
+    SG950_SCHED(false, true);
+  } else if (!p.tb) {
+    SG950_SCHED(true, false);
+  } else {
+    SG950_SCHED(true, true);
+  }
+#undef SG950_SCHED
+  return 0;
+}
+
+}  // namespace sg950

@@ -144,7 +144,7 @@ def test_batched_select_counts_every_slice(lib):
                                                   512, 512 * 512, 0.0, FAKE, 512, 512 * 512, 1)
     many = sg.sgemm_strided_batched_select_variant(0, 0, 512, 512, 512, 1.0, FAKE, 512, 512 * 512,
                                                    FAKE, 512, 512 * 512, 0.0, FAKE, 512, 512 * 512, 64)
-    assert n(one).endswith("splitk") and n(many).startswith("mfma32_256x256")
+    assert n(one) == "mfma16_64x64x64_4x2_sched" and n(many).startswith("mfma32_256x256")
 
 
 def _batched_choice(batch, M, N, K):
@@ -156,9 +156,10 @@ def test_batched_select_small_slices(lib):
     """Many small slices leave the one-lane kernel for tiled ones; tiles that
     would mostly lie outside a slice are not chosen."""
     assert _batched_choice(1, 127, 129, 17) == "simple"
-    assert _batched_choice(1, 128, 128, 128) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 128, 128, 128) == "mfma16_64x64x64_4x2_sched"
+    assert _batched_choice(1, 256, 256, 65536) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1024, 128, 128, 128) == "mfma32_128x128x16_2x2_w4"
-    assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_4x2"
+    assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_4x2_sched"
     assert _batched_choice(4096, 32, 32, 32) == "mfma16_64x64x16_2x2_splitk"
     assert _batched_choice(128, 200, 300, 100) == "mfma16_64x64x16_2x2_splitk"
     assert _batched_choice(8, 1, 4096, 4096) == "skinny_m8"

@@ -219,6 +219,60 @@ def check_batched(C, A, B, Cin, alpha, beta, what, exact=False, ta=False, tb=Fal
             check_real(C[z], a, b, Cin[z], alpha, beta, "%s slice %d" % (what, z))
 
 
+SCHED = [v for v in VARIANTS if VNAMES[v].endswith("_sched")]
+
+
+@pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
+@pytest.mark.parametrize("shape", [(300, 264, 64), (256, 256, 32), (520, 392, 96), (600, 500, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_sched_path_shapes_and_orientations(variant, shape):
+    """Shapes that meet the ordered-loop kernel's preconditions (K a multiple
+    of the slab depth, the tile inside C, 16-byte operands) for at least the
+    smaller tiles: tiles shifted back inside C on both edges, a single slab,
+    every operand orientation, the accumulate form; real to 1e-5 and integer
+    data exactly."""
+    M, N, K = shape
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        A, B, Cin = draw(M, N, K, seed=M + 7 * N + K, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        say("sched", VNAMES[variant], shape, ta, tb)
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "%s %s %s%s" % (VNAMES[variant], shape, ta, tb))
+        Ai, Bi, Ci = draw(M, N, K, seed=M + 7 * N + K, kind="int", with_c=True)
+        Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+        Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+        C = run(Ais, Bis, Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb)
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], shape, ta, tb))
+
+
+@pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
+def test_sched_path_permutation_and_batch(variant):
+    """Lane maps of the ordered loop pinned exactly (A = P with K = 256, N a
+    multiple of 4 past the tile), and a strided batch with 16-byte strides."""
+    rng = np.random.default_rng(41)
+    M = K = 256
+    N = 264
+    perm = rng.permutation(K)
+    P = np.zeros((M, K), np.float32)
+    P[np.arange(M), perm] = 1.0
+    B = rng.uniform(-1, 1, (K, N)).astype(np.float32)
+    say("sched perm", VNAMES[variant])
+    C = run(P, B, variant=variant)
+    assert np.array_equal(C, B[perm]), VNAMES[variant]
+    Ai = rng.integers(-4, 5, (3, 260, 128)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (3, 128, 256)).astype(np.float32)
+    Ci = rng.integers(-4, 5, (3, 260, 256)).astype(np.float32)
+    say("sched batch", VNAMES[variant])
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, gap=4)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, VNAMES[variant] + " batch", exact=True)
+    # slice strides that are not whole 16-byte vectors: aligned first slice and
+    # leading dimensions, misaligned later slices (the scalar-load path)
+    say("sched batch odd stride", VNAMES[variant])
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, gap=1)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, VNAMES[variant] + " batch odd stride", exact=True)
+
+
 @pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 def test_strided_batched_every_variant(variant):
     """Three slices with gaps between them, every transpose combination, a
