@@ -123,7 +123,9 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 // whole batch.
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
-//   * one or two rows of C: the B-streaming few-rows kernel (bandwidth bound);
+//   * up to four rows of C: the B-streaming few-rows kernel (bandwidth bound);
+//   * fewer than 16 rows or columns otherwise: 64x64 tiles with K split over
+//     workgroups, bound by streaming the large operand;
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs, the
 //     ordered slab loop) are fastest when the tiles are mostly inside C and
 //     their count fills the 256 CUs in whole rounds;
@@ -148,11 +150,13 @@ int choose_variant(const Problem &p) {
   const long long batch = p.batch;
   const long long work = (long long)p.M * p.N * p.K * batch;
   const long long nk = (long long)p.N * p.K * batch;
-  if (p.M <= 2 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
-  if (p.N < 16) return kSimple;
+  if (p.M <= 4 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
   if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
-  if (p.M < 16) return (nk >= (1LL << 20)) ? kMfma16_64x64x16_splitk : kSimple;
+  // Few rows or few columns: bound by streaming the large operand; 64x64
+  // tiles with K split over workgroups (16-deep slabs for a short ragged K).
+  if (p.M < 16 || p.N < 16)
+    return (p.K < 256 && p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_pipe_splitk;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
   const long long t64 = ((long long)p.M + 63) / 64 * (((long long)p.N + 63) / 64) * batch;

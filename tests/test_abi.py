@@ -165,6 +165,17 @@ def test_batched_select_small_slices(lib):
     assert _batched_choice(8, 1, 4096, 4096) == "skinny_m8"
 
 
+def test_select_narrow_problems(lib):
+    """Few columns or rows of C go to split-K tiles, never to the one-lane
+    kernel (which leaves most of a wave idle when N is small)."""
+    assert _batched_choice(1, 4096, 1, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 65536, 8, 1024) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 3000, 15, 100) == "mfma16_64x64x16_2x2_splitk"
+    assert _batched_choice(1, 3, 4096, 4096) == "skinny_m8"
+    assert _batched_choice(1, 8, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 5, 7, 9) == "simple"
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = sg.sgemm_status_string(st)

@@ -417,6 +417,23 @@ def test_few_rows_automatic(M):
     check_real(C, A, B, Cin, 2.0, -1.0, "M=%d padded" % M)
 
 
+@pytest.mark.parametrize("shape", [(4096, 1, 4096), (1000, 7, 3000), (3000, 15, 100), (65536, 8, 1024),
+                                   (12, 2500, 777)], ids=lambda s: "x".join(map(str, s)))
+def test_few_columns_or_rows_automatic(shape):
+    """Fewer than 16 columns (or rows) of C through the automatic choice:
+    real data to 1e-5, integer data exactly, and a padded / misaligned copy."""
+    M, N, K = shape
+    A, B, Cin = draw(M, N, K, seed=M + N, with_c=True)
+    say("narrow", shape)
+    C = run(A, B, Cin, 1.5, 0.5, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "narrow %s" % (shape,))
+    C = run(A, B, Cin, 1.5, 0.5, lds=(K + 1, N + 3, N + 2), offsets=(3, 1, 2), check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "narrow %s padded" % (shape,))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "narrow %s int" % (shape,))
+
+
 def test_runs_on_a_side_stream():
     A, B, _ = draw(512, 384, 256, seed=13)
     dA = torch.from_numpy(A).cuda()
