@@ -61,6 +61,8 @@ const Variant kVariants[] = {
     {"mfma32_256x256x32_4x2_sched", launch_mfma32_256x256x32_4x2_sched},
     {"mfma32_128x128x32_4x2_sched", launch_mfma32_128x128x32_4x2_sched},
     {"mfma16_64x64x64_4x2_sched", launch_mfma16_64x64x64_4x2_sched},
+    {"mfma16_128x128x64_4x2_sched", launch_mfma16_128x128x64_4x2_sched},
+    {"mfma16_128x64x64_4x2_sched", launch_mfma16_128x64x64_4x2_sched},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -88,6 +90,8 @@ enum VariantId {
   kMfma32_256x256x32_w8_sched = 20,
   kMfma32_128x128x32_w8_sched = 21,
   kMfma16_64x64x64_w8_sched = 22,
+  kMfma16_128x128x64_w8_sched = 23,
+  kMfma16_128x64x64_w8_sched = 24,
 };
 
 constexpr int kNoKernel = -100;
@@ -130,8 +134,10 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //     ordered slab loop) are fastest when the tiles are mostly inside C and
 //     their count fills the 256 CUs in whole rounds;
 //   * 128x128 tiles with eight waves (two per SIMD, the ordered loop) when
-//     there are at least as many tiles as CUs and they are mostly inside C;
-//     for K < 256 four waves with 16-deep slabs;
+//     there are at least as many tiles as CUs and they are mostly inside C:
+//     64-deep slabs for K >= 1024, 32-deep below, and for K < 256 four waves
+//     with 16-deep slabs;
+//   * 128x64 tiles (same loop) when those number at least as many as CUs;
 //   * otherwise 64x64 tiles with eight waves and 64-deep slabs on the ordered
 //     loop (16-deep ones, four waves, for a short K that is not a multiple of
 //     64), splitting K over workgroups when the tiles cannot occupy half the
@@ -140,10 +146,10 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 // K is not a multiple of the slab depth, the tile is larger than C or an
 // operand does not allow 16-byte loads.
 
-// Percentage of the T x T tiles' area that lies inside an M x N slice.
-long long tile_fill_pct(int M, int N, int T) {
-  const long long tm = ((long long)M + T - 1) / T, tn = ((long long)N + T - 1) / T;
-  return (long long)M * N * 100 / (tm * T * tn * T);
+// Percentage of the TM x TN tiles' area that lies inside an M x N slice.
+long long tile_fill_pct(int M, int N, int TM, int TN) {
+  const long long tm = ((long long)M + TM - 1) / TM, tn = ((long long)N + TN - 1) / TN;
+  return (long long)M * N * 100 / (tm * TM * tn * TN);
 }
 
 int choose_variant(const Problem &p) {
@@ -161,14 +167,17 @@ int choose_variant(const Problem &p) {
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
   const long long t64 = ((long long)p.M + 63) / 64 * (((long long)p.N + 63) / 64) * batch;
   const long long cus = 256;
-  if (t256 >= cus && tile_fill_pct(p.M, p.N, 256) >= 75) {
+  if (t256 >= cus && tile_fill_pct(p.M, p.N, 256, 256) >= 75) {
     const long long tail = t256 % cus;
     if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w8_sched;
   }
-  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128) >= 75) {
+  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 75) {
     if (p.K < 256) return kMfma32_128x128x16_w4;
-    return kMfma32_128x128x32_w8_sched;
+    return (p.K < 1024) ? kMfma32_128x128x32_w8_sched : kMfma16_128x128x64_w8_sched;
   }
+  const long long t12864 = ((long long)p.M + 127) / 128 * (((long long)p.N + 63) / 64) * batch;
+  if (t12864 >= cus && p.K >= 256 && tile_fill_pct(p.M, p.N, 128, 64) >= 75)
+    return kMfma16_128x64x64_w8_sched;
   // A short K that is not a multiple of 64 would leave most of a 64-deep
   // slab empty: 16-deep slabs then.
   if (p.K < 256 && p.K % 64 != 0) return kMfma16_64x64x16_splitk;

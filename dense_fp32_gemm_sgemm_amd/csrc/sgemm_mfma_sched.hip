@@ -18,6 +18,16 @@ int launch_mfma32_256x256x32_4x2_sched(const Problem &p, hipStream_t s) {
 int launch_mfma32_128x128x32_4x2_sched(const Problem &p, hipStream_t s) {
   return launch_sched<32, 128, 128, 32, 4, 2, 2, 4>(p, s, launch_mfma32_128x128x32_4x2);
 }
+// 128x128 tile, eight waves with 32x64 wave tiles of 16x16 blocks, 64-deep
+// slabs (half the barriers of the 32-deep form; one workgroup per CU).
+int launch_mfma16_128x128x64_4x2_sched(const Problem &p, hipStream_t s) {
+  return launch_sched<16, 128, 128, 64, 4, 2, 2, 4>(p, s, launch_mfma32_128x128x32_4x2_sched);
+}
+// 128x64 tile, eight waves with 32x32 wave tiles of 16x16 blocks, 64-deep
+// slabs: one tile per CU for problems with half as many 128x128 tiles.
+int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t s) {
+  return launch_sched<16, 128, 64, 64, 4, 2, 2, 4>(p, s, launch_mfma16_64x64x64_4x2_sched);
+}
 // 64x64 tile, eight waves with 16x32 wave tiles, 64-deep slabs.
 int launch_mfma16_64x64x64_4x2_sched(const Problem &p, hipStream_t s) {
   return launch_sched<16, 64, 64, 64, 4, 2, 2, 4>(p, s, launch_mfma16_64x64x64_4x2_pipe);
