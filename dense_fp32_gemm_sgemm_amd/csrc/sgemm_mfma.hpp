@@ -25,9 +25,13 @@
 // Operand layout.  For the 32x32x2 instruction lane l supplies A[l%32][k] and
 // B[k][l%32] with k = l/32 (the 16x16x4 one: A[l%16][l/16], B[l/16][l%16]).
 // Which k of the slab a lane group stands for is free, as long as A and B
-// agree, so lane group g takes the KPG = BK/(64/MI) consecutive k values
-// [g*KPG, (g+1)*KPG).  Each operand tile is kept in LDS in the orientation it
-// has in memory:
+// agree.  With the 32x32x2 instruction lane group g takes the KPG = BK/2
+// consecutive k values [g*KPG, (g+1)*KPG); with the 16x16x4 one, whose four
+// lane groups would otherwise read rows KPG apart -- a multiple of 64 banks
+// for the padded M/N-contiguous tiles, a four-way conflict -- group g takes
+// the runs of four k at 4g + 16q (q = 0, 1, ...), so the groups read rows four
+// apart, on disjoint banks.  Each operand tile is kept in LDS in the
+// orientation it has in memory:
 //   * k contiguous (A untransposed, B transposed): rows of BK+4 floats; a
 //     lane's four k values of an operand group are one 16-byte read, and the
 //     4-float pad puts the reads of 8 (or 16) consecutive rows on disjoint
@@ -59,8 +63,13 @@ struct MfmaTile {
   static constexpr int FM = WTM / MI;       // matrix-core blocks per wave, M
   static constexpr int FN = WTN / MI;       // matrix-core blocks per wave, N
   static constexpr int KG = 64 / MI;        // lane groups along k
-  static constexpr int KPG = BK / KG;       // consecutive k per lane group and slab
+  static constexpr int KPG = BK / KG;       // k values per lane group and slab
   static constexpr int NQ = KPG / 4;        // 4-deep operand groups per slab
+  // k of lane group g's first value (g * GK) and k distance between its
+  // operand groups (QK): consecutive runs for 32x32x2, interleaved runs of
+  // four for 16x16x4.
+  static constexpr int GK = (MI == 16) ? 4 : KPG;
+  static constexpr int QK = (MI == 16) ? 4 * KG : 4;
   // LDS row pitch (floats) and stage size of each operand tile.
   static constexpr int APITCH = TA ? BM + 4 : BK + 4;
   static constexpr int BPITCH = TB ? BK + 4 : BN + BPAD;
@@ -104,19 +113,19 @@ __device__ __forceinline__ void read_operands(Operands<T> &o, const float *as, c
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     if constexpr (!TA) {
-      o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + 4 * q);
+      o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + T::QK * q);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o.a[i][e] = as[(4 * q + e) * T::APITCH + i * MI];
+      for (int e = 0; e < 4; ++e) o.a[i][e] = as[(T::QK * q + e) * T::APITCH + i * MI];
     }
   }
 #pragma unroll
   for (int j = 0; j < T::FN; ++j) {
     if constexpr (!TB) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o.b[j][e] = bs[(4 * q + e) * T::BPITCH + j * MI];
+      for (int e = 0; e < 4; ++e) o.b[j][e] = bs[(T::QK * q + e) * T::BPITCH + j * MI];
     } else {
-      o.b[j] = *reinterpret_cast<const floatx4 *>(bs + j * MI * T::BPITCH + 4 * q);
+      o.b[j] = *reinterpret_cast<const floatx4 *>(bs + j * MI * T::BPITCH + T::QK * q);
     }
   }
 }
@@ -208,10 +217,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void mfma_kernel(Probl
   for (int i = 0; i < LA::kVecs; ++i) a_st[i] = LA::row_of(tid, i) * T::APITCH + LA::col_of(tid, i);
 #pragma unroll
   for (int i = 0; i < LB::kVecs; ++i) b_st[i] = LB::row_of(tid, i) * T::BPITCH + LB::col_of(tid, i);
-  const int a_rd = TA ? (g * T::KPG) * T::APITCH + wm * T::WTM + li
-                      : (wm * T::WTM + li) * T::APITCH + g * T::KPG;
-  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::KPG
-                      : (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
+  const int a_rd = TA ? (g * T::GK) * T::APITCH + wm * T::WTM + li
+                      : (wm * T::WTM + li) * T::APITCH + g * T::GK;
+  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::GK
+                      : (g * T::GK) * T::BPITCH + wn * T::WTN + li;
 
   // Loads slab `slab` into the loaders' registers (zero-filled K tail).
   auto load = [&](int slab) {

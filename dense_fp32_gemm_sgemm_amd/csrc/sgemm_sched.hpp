@@ -124,10 +124,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
     for (int i = 0; i < LB::NV; ++i) *reinterpret_cast<floatx4 *>(bn + i * LB::DR * T::BPITCH) = lb.v[i];
   };
-  const int a_rd = TA ? (g * T::KPG) * T::APITCH + wm * T::WTM + li
-                      : (wm * T::WTM + li) * T::APITCH + g * T::KPG;
-  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::KPG
-                      : (g * T::KPG) * T::BPITCH + wn * T::WTN + li;
+  const int a_rd = TA ? (g * T::GK) * T::APITCH + wm * T::WTM + li
+                      : (wm * T::WTM + li) * T::APITCH + g * T::GK;
+  const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::GK
+                      : (g * T::GK) * T::BPITCH + wn * T::WTN + li;
 
   Acc acc[T::FM][T::FN];
 #pragma unroll
