@@ -4,16 +4,29 @@
 // With M <= 8 a GEMM does 2*M FLOP per element of B it reads, below the
 // MI355X ridge point (about 20 FLOP/byte): the whole of B has to stream from
 // HBM once, and the kernel's job is to keep enough loads in flight on every
-// CU.  The work is split over columns of B (256 per workgroup: 64 lanes x a
-// 16-byte vector, so each wavefront load is 1 KiB of one row) and over K
-// (each workgroup takes a chunk of rows, its four waves a quarter of the chunk
-// each).  A lane keeps M x 4 partial sums; the four waves' sums are added
-// through LDS in a fixed order, and the workgroup adds alpha * sum into C with
-// one float atomic per element.  C is first scaled by beta in a separate
-// launch, so the result is beta*C + alpha*A*B with the K-chunks' partial sums
-// added in an unspecified order (exact on integer data; within fp32 rounding
-// otherwise).  A's values are the same for every lane and are read through
-// the scalar path.
+// CU.  Two kernels:
+//
+//   * full-K strips (moderate B): a workgroup owns 32 columns of C and runs
+//     the whole K for them -- lanes hold 4 columns x one row of B each, so a
+//     wavefront load covers 16 rows x 128 bytes; each lane keeps M x 4
+//     partial sums, reduced over the wave's 16 row slots by lane shuffles and
+//     over the waves through LDS in a fixed order, and C = alpha*sum + beta*C
+//     is written once.  One launch, no atomics, deterministic.
+//   * split-K (large B, or too few column strips): the work is split over
+//     columns of B (256 per workgroup: 64 lanes x a 16-byte vector, so each
+//     wavefront load is 1 KiB of one row) and over K (each workgroup takes a
+//     chunk of rows, its four waves a quarter of the chunk each).  A lane keeps
+//     M x 4 partial sums; the four waves' sums are added through LDS in a
+//     fixed order, and the workgroup adds alpha * sum into C with one float
+//     atomic per element.  C is first scaled by beta in a separate launch, so
+//     the result is beta*C + alpha*A*B with the K-chunks' partial sums added
+//     in an unspecified order (exact on integer data; within fp32 rounding
+//     otherwise).  A's values are the same for every lane and are read
+//     through the scalar path.
+//
+// The second launch of the split form costs about 4 us on an MI355X, a fifth
+// of a (1, 4096, 4096) product; the full-K form avoids it whenever the column
+// strips alone give enough workgroups.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
 
@@ -97,6 +110,117 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
   }
 }
 
+constexpr int kFullKCq = 8;                  // 16-byte column quads per workgroup
+constexpr int kFullKCols = 4 * kFullKCq;     // 32 columns
+constexpr int kFullKRpi = 64 / kFullKCq;     // rows of B per wavefront load
+constexpr int kFullKWaves = 4;
+constexpr int kFullKUnroll = 8;              // loads in flight per lane
+
+// Full-K strip kernel (op(B) untransposed).  Lane l takes column quad
+// cq = l % 8 and row slot rr = l / 8; wave w reads the rows k = 8w + rr +
+// 32i.  Columns past N read the last column (or quad) instead -- in bounds,
+// never stored -- so the loads carry no branch and the unrolled ones issue
+// together; rows past K in the last, partial sweep are skipped.
+template <int MR, bool VB>
+__global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem p) {
+  select_slice(p);
+  __shared__ float red[kFullKWaves][MR][kFullKCols];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cq = lane % kFullKCq, rr = lane / kFullKCq;
+  const int c0 = blockIdx.x * kFullKCols + 4 * cq;
+  // VB implies N % 4 == 0: quads past the edge read the last one instead.
+  const int cv = min(c0, p.N - 4);
+  int cc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cc[e] = min(c0 + e, p.N - 1);
+  const size_t ldb = (size_t)p.ldb;
+  const size_t sa_r = p.ta ? 1 : (size_t)p.lda, sa_k = p.ta ? (size_t)p.lda : 1;
+  constexpr int kstep = kFullKWaves * kFullKRpi;
+  const int kfirst = w * kFullKRpi + rr;
+
+  float acc[MR][4];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
+
+  auto load_b = [&](int k) -> floatx4 {
+    const float *brow = p.B + (size_t)k * ldb;
+    if constexpr (VB) {
+      return *reinterpret_cast<const floatx4 *>(brow + cv);
+    } else {
+      return floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
+    }
+  };
+  // A rows past M read row M-1 (in bounds; their sums are never stored).
+  auto load_a = [&](int r, int k) -> float {
+    return p.A[(size_t)min(r, p.M - 1) * sa_r + (size_t)k * sa_k];
+  };
+
+  const int nfull = p.K / kstep;  // sweeps in which every lane's row is < K
+  int i = 0;
+  for (; i + kFullKUnroll <= nfull; i += kFullKUnroll) {
+    floatx4 b[kFullKUnroll];
+    float a[kFullKUnroll][MR];
+#pragma unroll
+    for (int u = 0; u < kFullKUnroll; ++u) {
+      const int k = kfirst + (i + u) * kstep;
+      b[u] = load_b(k);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) a[u][r] = load_a(r, k);
+    }
+    // All loads of the batch are issued before the first use (the compiler
+    // would otherwise interleave them with the FMAs and wait on each).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kFullKUnroll; ++u)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a[u][r], b[u][e], acc[r][e]);
+  }
+  for (; i <= nfull; ++i) {
+    const int k = kfirst + i * kstep;
+    if (k < p.K) {
+      const floatx4 b = load_b(k);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const float a = load_a(r, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a, b[e], acc[r][e]);
+      }
+    }
+  }
+
+  // Sum over the wave's row slots (lanes cq, cq+8, ..., cq+56), then over the
+  // waves in a fixed order.
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int d = kFullKCq; d < 64; d *= 2) acc[r][e] += __shfl_xor(acc[r][e], d);
+  if (rr == 0) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][r][4 * cq + e] = acc[r][e];
+  }
+  __syncthreads();
+  if (threadIdx.x < kFullKCols) {
+    const int c = blockIdx.x * kFullKCols + threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      if (r >= p.M || c >= p.N) continue;
+      float s = red[0][r][threadIdx.x];
+#pragma unroll
+      for (int q = 1; q < kFullKWaves; ++q) s += red[q][r][threadIdx.x];
+      store_out(p.C + (size_t)r * (size_t)p.ldc + c, s, p.alpha, p.beta);
+    }
+  }
+}
+
 // K rows per workgroup: enough workgroups (over all batch slices) for about
 // four per CU, at least 64 rows (16 per wave) each, a multiple of 16.
 static int skinny_kchunk(const Problem &p, long long strips) {
@@ -111,6 +235,34 @@ static int skinny_kchunk(const Problem &p, long long strips) {
 
 int launch_skinny(const Problem &p, hipStream_t stream) {
   if (p.M > 8) return -1;
+  // Full-K strips when the 32-column strips give at least a quarter of the
+  // CUs a workgroup and B is moderate (measured: (1, 4096, 4096) 14 us
+  // against 21 us for the split form with its scaling launch).
+  const long long fstrips = ((long long)p.N + kFullKCols - 1) / kFullKCols;
+  if (!p.tb && fstrips * p.batch >= 64 && (long long)p.N * p.K <= (1LL << 26) &&
+      fstrips <= INT_MAX) {
+    const dim3 fgrid((unsigned)fstrips, 1u, (unsigned)p.batch);
+    const dim3 fblock(kFullKWaves * 64);
+    const bool fvb = b_vec_ok(p);
+#define SG950_FULLK(MR_)                                                                      \
+  do {                                                                                        \
+    if (fvb)                                                                                  \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true>), fgrid, fblock, 0, stream, p);      \
+    else                                                                                      \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false>), fgrid, fblock, 0, stream, p);     \
+  } while (0)
+    if (p.M <= 1) {
+      SG950_FULLK(1);
+    } else if (p.M <= 2) {
+      SG950_FULLK(2);
+    } else if (p.M <= 4) {
+      SG950_FULLK(4);
+    } else {
+      SG950_FULLK(8);
+    }
+#undef SG950_FULLK
+    return 0;
+  }
   const long long strips = ((long long)p.N + kSkinnyCols - 1) / kSkinnyCols;
   const int kc = skinny_kchunk(p, strips);
   const long long chunks = ((long long)p.K + kc - 1) / kc;

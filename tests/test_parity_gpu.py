@@ -417,6 +417,30 @@ def test_few_rows_automatic(M):
     check_real(C, A, B, Cin, 2.0, -1.0, "M=%d padded" % M)
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("NK", [(2053, 1), (2048, 33), (4096, 4097), (3000, 250)],
+                         ids=lambda t: "N%dK%d" % t)
+def test_few_rows_full_k_strips(M, NK):
+    """The few-rows kernel's full-K strip form (at least 64 strips of 32
+    columns, moderate B): K tails that leave the last sweep partial (K = 1
+    included), a ragged and misaligned column edge, a transposed A, the
+    accumulate form; real data to 1e-5, integer data exactly."""
+    N, K = NK
+    v = VNAMES.index("skinny_m8")
+    A, B, Cin = draw(M, N, K, seed=M * 31 + N + K, with_c=True)
+    say("full-K strips", M, N, K)
+    C = run(A, B, Cin, 1.5, 0.5, variant=v, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d" % (M, N, K))
+    C = run(A, B, Cin, 1.5, 0.5, variant=v, lds=(K + 3, N + 1, N + 2), offsets=(1, 3, 2),
+            check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d padded" % (M, N, K))
+    C = run(np.ascontiguousarray(A.T), B, Cin, 1.5, 0.5, variant=v, trans_a=True, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d TA" % (M, N, K))
+    Ai, Bi, Ci = draw(M, N, K, seed=M * 31 + N + K, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
+
+
 @pytest.mark.parametrize("shape", [(4096, 1, 4096), (1000, 7, 3000), (3000, 15, 100), (65536, 8, 1024),
                                    (12, 2500, 777)], ids=lambda s: "x".join(map(str, s)))
 def test_few_columns_or_rows_automatic(shape):
