@@ -31,6 +31,20 @@ int launch_skinny_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// The few-columns kernel covers N <= 16; as a forced variant on a wider
+// problem it runs on column blocks of 16.
+int launch_narrow_any(const Problem &p, hipStream_t s) {
+  for (int c = 0; c < p.N; c += 16) {
+    Problem q = p;
+    q.N = (p.N - c < 16) ? p.N - c : 16;
+    q.B = p.tb ? p.B + (size_t)c * (size_t)p.ldb : p.B + c;
+    q.C = p.C + c;
+    const int rc = launch_narrow(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 struct Variant {
   const char *name;
   Launcher launch;
@@ -63,6 +77,7 @@ const Variant kVariants[] = {
     {"mfma16_64x64x64_4x2_sched", launch_mfma16_64x64x64_4x2_sched},
     {"mfma16_128x128x64_4x2_sched", launch_mfma16_128x128x64_4x2_sched},
     {"mfma16_128x64x64_4x2_sched", launch_mfma16_128x64x64_4x2_sched},
+    {"narrow_n16", launch_narrow_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -92,6 +107,7 @@ enum VariantId {
   kMfma16_64x64x64_w8_sched = 22,
   kMfma16_128x128x64_w8_sched = 23,
   kMfma16_128x64x64_w8_sched = 24,
+  kNarrow = 25,
 };
 
 constexpr int kNoKernel = -100;
@@ -128,8 +144,9 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
 //   * up to four rows of C: the B-streaming few-rows kernel (bandwidth bound);
-//   * fewer than 16 rows or columns otherwise: 64x64 tiles with K split over
-//     workgroups, bound by streaming the large operand;
+//   * up to 16 columns of C: the A-streaming few-columns kernel;
+//   * fewer than 16 rows otherwise: 64x64 tiles with K split over
+//     workgroups, bound by streaming B;
 //   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs, the
 //     ordered slab loop) are fastest when the tiles are mostly inside C and
 //     their count fills the 256 CUs in whole rounds;
@@ -159,8 +176,10 @@ int choose_variant(const Problem &p) {
   if (p.M <= 4 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
   if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
-  // Few rows or few columns: bound by streaming the large operand; 64x64
-  // tiles with K split over workgroups (16-deep slabs for a short ragged K).
+  // Few columns: the A-streaming few-columns kernel.
+  if (p.N <= 16 && p.M >= 16) return kNarrow;
+  // Few rows: bound by streaming B; 64x64 tiles with K split over workgroups
+  // (16-deep slabs for a short ragged K).
   if (p.M < 16 || p.N < 16)
     return (p.K < 256 && p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_pipe_splitk;
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;

@@ -60,6 +60,11 @@ int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t stream);
 // M > 8.
 int launch_skinny(const Problem &p, hipStream_t stream);
 
+// Few columns of C (N <= 16): streams A, the matrix cores accumulate 16 x 16
+// blocks, K split over the waves of a workgroup, one launch.  Returns -1 for
+// N > 16.
+int launch_narrow(const Problem &p, hipStream_t stream);
+
 // Operand alignment classes: an operand may be read with 16-byte vector
 // loads when its base is 16-byte aligned and its leading dimension is a
 // multiple of four; when its rows run along M or N (A transposed, B not) the

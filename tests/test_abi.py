@@ -166,11 +166,13 @@ def test_batched_select_small_slices(lib):
 
 
 def test_select_narrow_problems(lib):
-    """Few columns or rows of C go to split-K tiles, never to the one-lane
-    kernel (which leaves most of a wave idle when N is small)."""
-    assert _batched_choice(1, 4096, 1, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
-    assert _batched_choice(1, 65536, 8, 1024) == "mfma16_64x64x64_4x2_pipe_splitk"
-    assert _batched_choice(1, 3000, 15, 100) == "mfma16_64x64x16_2x2_splitk"
+    """Few columns of C go to the few-columns kernel, few rows to the
+    few-rows kernel or split-K tiles, never to the one-lane kernel (which
+    leaves most of a wave idle when N is small)."""
+    assert _batched_choice(1, 4096, 1, 4096) == "narrow_n16"
+    assert _batched_choice(1, 65536, 8, 1024) == "narrow_n16"
+    assert _batched_choice(1, 3000, 16, 100) == "narrow_n16"
+    assert _batched_choice(1, 12, 15, 100000) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1, 3, 4096, 4096) == "skinny_m8"
     assert _batched_choice(1, 8, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1, 5, 7, 9) == "simple"

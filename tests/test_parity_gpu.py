@@ -441,6 +441,32 @@ def test_few_rows_full_k_strips(M, NK):
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
 
 
+@pytest.mark.parametrize("N", [1, 5, 16])
+@pytest.mark.parametrize("MK", [(16, 1), (100, 15), (1000, 33), (333, 4099), (64, 20000)],
+                         ids=lambda t: "M%dK%d" % t)
+def test_few_columns_kernel(N, MK):
+    """The few-columns kernel forced: K ranges that leave the last wave empty
+    or partial (K = 1 included), ragged rows, every operand orientation, a
+    padded / misaligned copy, the accumulate form; real data to 1e-5 and
+    integer data exactly."""
+    M, K = MK
+    v = VNAMES.index("narrow_n16")
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        A, B, Cin = draw(M, N, K, seed=M + 3 * N + K, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        say("few columns", M, N, K, ta, tb)
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb, check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d %s%s" % (M, N, K, ta, tb))
+    A, B, Cin = draw(M, N, K, seed=M + 3 * N + K, with_c=True)
+    C = run(A, B, Cin, 1.5, 0.5, variant=v, lds=(K + 1, N + 3, N + 2), offsets=(3, 1, 2),
+            check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d padded" % (M, N, K))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + 3 * N + K, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
+
+
 @pytest.mark.parametrize("shape", [(4096, 1, 4096), (1000, 7, 3000), (3000, 15, 100), (65536, 8, 1024),
                                    (12, 2500, 777)], ids=lambda s: "x".join(map(str, s)))
 def test_few_columns_or_rows_automatic(shape):
