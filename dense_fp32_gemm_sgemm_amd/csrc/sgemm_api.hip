@@ -143,7 +143,7 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 // whole batch.
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
-//   * up to four rows of C: the B-streaming few-rows kernel (bandwidth bound);
+//   * up to eight rows of C: the B-streaming few-rows kernel (bandwidth bound);
 //   * up to 16 columns of C: the A-streaming few-columns kernel;
 //   * fewer than 16 rows otherwise: 64x64 tiles with K split over
 //     workgroups, bound by streaming B;
@@ -173,7 +173,7 @@ int choose_variant(const Problem &p) {
   const long long batch = p.batch;
   const long long work = (long long)p.M * p.N * p.K * batch;
   const long long nk = (long long)p.N * p.K * batch;
-  if (p.M <= 4 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
+  if (p.M <= 8 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
   if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
   // Few columns: the A-streaming few-columns kernel.

@@ -7,8 +7,9 @@
 // CU.  Two kernels:
 //
 //   * full-K strips (moderate B): a workgroup owns 32 columns of C and runs
-//     the whole K for them -- lanes hold 4 columns x one row of B each, so a
-//     wavefront load covers 16 rows x 128 bytes; each lane keeps M x 4
+//     the whole K for them -- a lane loads 4 columns of 4 consecutive rows of
+//     B and the matching 4 values of each row of A as 16-byte vectors, so a
+//     wavefront load covers 8 rows x 128 bytes of B; each lane keeps M x 4
 //     partial sums, reduced over the wave's 16 row slots by lane shuffles and
 //     over the waves through LDS in a fixed order, and C = alpha*sum + beta*C
 //     is written once.  One launch, no atomics, deterministic.
@@ -112,16 +113,17 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
 
 constexpr int kFullKCq = 8;                  // 16-byte column quads per workgroup
 constexpr int kFullKCols = 4 * kFullKCq;     // 32 columns
-constexpr int kFullKRpi = 64 / kFullKCq;     // rows of B per wavefront load
 constexpr int kFullKWaves = 4;
-constexpr int kFullKUnroll = 8;              // loads in flight per lane
+constexpr int kFullKUnroll = 2;              // sweeps (4 rows each) in flight per lane
 
 // Full-K strip kernel (op(B) untransposed).  Lane l takes column quad
-// cq = l % 8 and row slot rr = l / 8; wave w reads the rows k = 8w + rr +
-// 32i.  Columns past N read the last column (or quad) instead -- in bounds,
-// never stored -- so the loads carry no branch and the unrolled ones issue
-// together; rows past K in the last, partial sweep are skipped.
-template <int MR, bool VB>
+// cq = l % 8 and row slot rr = l / 8.  In sweep i, wave w covers the 32 rows
+// of B from 32(4i + w), slot rr four consecutive ones: four 16-byte loads of
+// B and, per row of C, one 16-byte load of A (VA) for four k.  Columns past N
+// read the last column (or quad) instead -- in bounds, never stored -- so the
+// loads carry no branch and the unrolled ones issue together.  Rows of B left
+// after the last whole sweep are taken one per slot, rows past K skipped.
+template <int MR, bool VA, bool VB>
 __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem p) {
   select_slice(p);
   __shared__ float red[kFullKWaves][MR][kFullKCols];
@@ -136,8 +138,6 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
   for (int e = 0; e < 4; ++e) cc[e] = min(c0 + e, p.N - 1);
   const size_t ldb = (size_t)p.ldb;
   const size_t sa_r = p.ta ? 1 : (size_t)p.lda, sa_k = p.ta ? (size_t)p.lda : 1;
-  constexpr int kstep = kFullKWaves * kFullKRpi;
-  const int kfirst = w * kFullKRpi + rr;
 
   float acc[MR][4];
 #pragma unroll
@@ -157,18 +157,27 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
   auto load_a = [&](int r, int k) -> float {
     return p.A[(size_t)min(r, p.M - 1) * sa_r + (size_t)k * sa_k];
   };
+  auto load_a4 = [&](int r, int k) -> floatx4 {
+    if constexpr (VA) {
+      return *reinterpret_cast<const floatx4 *>(p.A + (size_t)min(r, p.M - 1) * sa_r + k);
+    } else {
+      return floatx4{load_a(r, k), load_a(r, k + 1), load_a(r, k + 2), load_a(r, k + 3)};
+    }
+  };
 
-  const int nfull = p.K / kstep;  // sweeps in which every lane's row is < K
+  constexpr int kSweep = kFullKWaves * 32;  // rows of B per sweep
+  const int nfull = p.K / kSweep;
   int i = 0;
   for (; i + kFullKUnroll <= nfull; i += kFullKUnroll) {
-    floatx4 b[kFullKUnroll];
-    float a[kFullKUnroll][MR];
+    floatx4 b[kFullKUnroll][4];
+    floatx4 a[kFullKUnroll][MR];
 #pragma unroll
     for (int u = 0; u < kFullKUnroll; ++u) {
-      const int k = kfirst + (i + u) * kstep;
-      b[u] = load_b(k);
+      const int k = (i + u) * kSweep + 32 * w + 4 * rr;
 #pragma unroll
-      for (int r = 0; r < MR; ++r) a[u][r] = load_a(r, k);
+      for (int e = 0; e < 4; ++e) b[u][e] = load_b(k + e);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) a[u][r] = load_a4(r, k);
     }
     // All loads of the batch are issued before the first use (the compiler
     // would otherwise interleave them with the FMAs and wait on each).
@@ -176,20 +185,33 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
 #pragma unroll
     for (int u = 0; u < kFullKUnroll; ++u)
 #pragma unroll
-      for (int r = 0; r < MR; ++r)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a[u][r], b[u][e], acc[r][e]);
+        for (int r = 0; r < MR; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[u][r][e], b[u][e][c], acc[r][c]);
   }
-  for (; i <= nfull; ++i) {
-    const int k = kfirst + i * kstep;
-    if (k < p.K) {
-      const floatx4 b = load_b(k);
+  for (; i < nfull; ++i) {
+    const int k = i * kSweep + 32 * w + 4 * rr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const floatx4 b = load_b(k + e);
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
-        const float a = load_a(r, k);
+        const float a = load_a(r, k + e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a, b[e], acc[r][e]);
+        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a, b[c], acc[r][c]);
       }
+    }
+  }
+  // Rows after the last whole sweep: one per slot.
+  for (int k = nfull * kSweep + 8 * w + rr; k < p.K; k += kFullKWaves * 8) {
+    const floatx4 b = load_b(k);
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const float a = load_a(r, k);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a, b[c], acc[r][c]);
     }
   }
 
@@ -243,13 +265,17 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
       fstrips <= INT_MAX) {
     const dim3 fgrid((unsigned)fstrips, 1u, (unsigned)p.batch);
     const dim3 fblock(kFullKWaves * 64);
-    const bool fvb = b_vec_ok(p);
-#define SG950_FULLK(MR_)                                                                      \
-  do {                                                                                        \
-    if (fvb)                                                                                  \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true>), fgrid, fblock, 0, stream, p);      \
-    else                                                                                      \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false>), fgrid, fblock, 0, stream, p);     \
+    const bool fvb = b_vec_ok(p), fva = !p.ta && a_vec_ok(p);
+#define SG950_FULLK(MR_)                                                                        \
+  do {                                                                                          \
+    if (fva && fvb)                                                                             \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true, true>), fgrid, fblock, 0, stream, p);  \
+    else if (fvb)                                                                               \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false, true>), fgrid, fblock, 0, stream, p); \
+    else if (fva)                                                                               \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true, false>), fgrid, fblock, 0, stream, p); \
+    else                                                                                        \
+      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false, false>), fgrid, fblock, 0, stream, p); \
   } while (0)
     if (p.M <= 1) {
       SG950_FULLK(1);

@@ -174,7 +174,8 @@ def test_select_narrow_problems(lib):
     assert _batched_choice(1, 3000, 16, 100) == "narrow_n16"
     assert _batched_choice(1, 12, 15, 100000) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1, 3, 4096, 4096) == "skinny_m8"
-    assert _batched_choice(1, 8, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 8, 4096, 4096) == "skinny_m8"
+    assert _batched_choice(1, 9, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1, 5, 7, 9) == "simple"
 
 
