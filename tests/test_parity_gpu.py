@@ -127,6 +127,22 @@ def test_leading_dims_alignment_and_canaries(variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
+def test_offsets_beyond_32_bits(variant):
+    """A leading dimension of 2^27 with 17 rows puts the last row 2^31
+    elements (8 GiB) past the first: any 32-bit element index on the path of
+    A, B or C would wrap.  Integer data, exact."""
+    big = 1 << 27
+    for which, (M, N, K) in (("A", (17, 192, 64)), ("B", (96, 128, 17)), ("C", (17, 160, 48))):
+        A, B, Cin = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+        lds = (big if which == "A" else None, big if which == "B" else None,
+               big if which == "C" else None)
+        say("64-bit offsets", VNAMES[variant], which)
+        C = run(A, B, Cin, 1.0, 1.0, variant=variant, lds=lds)
+        check_exact(C, A, B, Cin, 1.0, 1.0, "%s ld(%s)=2^27" % (VNAMES[variant], which))
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VNAMES)
 @pytest.mark.parametrize("ops", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
 def test_transposed_operands_every_variant(variant, ops):
     """op(A), op(B) in {N, T}: the stored matrices are the transposes; the
