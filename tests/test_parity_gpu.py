@@ -325,6 +325,56 @@ def test_strided_batched_automatic(shape):
     check_batched(out, A, B, np.zeros_like(C), 1.0, 0.0, "auto %s" % (shape,))
 
 
+def _random_problem(rng):
+    """A seeded random problem: dimensions near powers of two and tile edges
+    or anywhere up to ~700 (or, for a third of the problems, 1500..4200 with
+    K below 600, so that the large tiles run), random operand orientations, a
+    batch of one to three, random alpha and beta, packed or padded leading
+    dimensions."""
+    def dim():
+        if rng.random() < 0.5:
+            return int(max(1, rng.choice([16, 32, 64, 128, 256, 512]) + rng.integers(-2, 3)))
+        return int(rng.integers(1, 700))
+
+    def big():
+        if rng.random() < 0.5:
+            return int(256 * rng.integers(6, 17) + rng.choice([0, 0, 4, -4, 3]))
+        return int(rng.integers(1500, 4200))
+    if rng.random() < 0.35:  # enough tiles for the 128x128 and 256x256 families
+        M, N, K = big(), big(), int(rng.integers(1, 600))
+    else:
+        M, N, K = dim(), dim(), dim()
+    ta, tb = bool(rng.random() < 0.3), bool(rng.random() < 0.3)
+    batch = int(rng.choice([1, 1, 2, 3]))
+    alpha = float(rng.choice([1.0, 1.5, -0.5]))
+    beta = float(rng.choice([0.0, 1.0, 0.5]))
+    pad = int(rng.choice([0, 0, 1, 4]))
+    return M, N, K, ta, tb, batch, alpha, beta, pad
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_random_problems_automatic(seed):
+    """Random shapes, orientations, batches and scalars through the automatic
+    choice (every kernel family and its fallbacks get some), real data to
+    1e-5 against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    M, N, K, ta, tb, batch, alpha, beta, pad = _random_problem(rng)
+    say("random", seed, M, N, K, ta, tb, batch, alpha, beta, pad)
+    if batch == 1:
+        A, B, Cin = draw(M, N, K, seed=seed, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        lds = (As.shape[1] + pad, Bs.shape[1] + pad, N + pad)
+        C = run(As, Bs, Cin, alpha, beta, trans_a=ta, trans_b=tb, lds=lds, check_outside=True)
+        check_real(C, A, B, Cin, alpha, beta, "random %d" % seed)
+    else:
+        A = rng.uniform(-1, 1, (batch, K, M) if ta else (batch, M, K)).astype(np.float32)
+        B = rng.uniform(-1, 1, (batch, N, K) if tb else (batch, K, N)).astype(np.float32)
+        Cin = rng.standard_normal((batch, M, N)).astype(np.float32)
+        out = run_batched(A, B, Cin, alpha, beta, trans_a=ta, trans_b=tb, gap=pad)
+        check_batched(out, A, B, Cin, alpha, beta, "random %d" % seed, ta=ta, tb=tb)
+
+
 def test_strided_batched_more_slices_than_one_grid():
     """65,543 slices: more than one grid's worth (65,535), so the entry point
     splits the batch into launches."""
