@@ -116,6 +116,9 @@ def test_op_select_avoids_few_rows_kernel_for_transposed_b(lib):
                                         4096)) != "skinny_m8"
     assert n(sg.sgemm_op_select_variant(1, 1, 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0,
                                         FAKE, 4096)).startswith("mfma32_256x256")
+    # B transposed alone: the four-wave 256x256 form (the eight-wave one spills)
+    assert n(sg.sgemm_op_select_variant(0, 1, 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0,
+                                        FAKE, 4096)) == "mfma32_256x256x32_2x2_sched"
 
 
 @pytest.mark.parametrize("args,status", [
