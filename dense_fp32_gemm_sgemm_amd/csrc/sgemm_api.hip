@@ -147,9 +147,9 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //   * up to 16 columns of C: the A-streaming few-columns kernel;
 //   * fewer than 16 rows otherwise: 64x64 tiles with K split over
 //     workgroups, bound by streaming B;
-//   * 256x256 tiles (eight waves, one workgroup per CU, 32-deep K slabs, the
-//     ordered slab loop) are fastest when the tiles are mostly inside C and
-//     their count fills the 256 CUs in whole rounds;
+//   * 256x256 tiles (four waves with 128x128 wave tiles, one workgroup per
+//     CU, 32-deep K slabs, the ordered slab loop) are fastest when the tiles
+//     are mostly inside C and their count fills the 256 CUs in whole rounds;
 //   * 128x128 tiles with eight waves (two per SIMD, the ordered loop) when
 //     there are at least as many tiles as CUs and they are mostly inside C:
 //     64-deep slabs for K >= 1024, 32-deep below, and for K < 256 four waves
@@ -188,10 +188,7 @@ int choose_variant(const Problem &p) {
   const long long cus = 256;
   if (t256 >= cus && tile_fill_pct(p.M, p.N, 256, 256) >= 75) {
     const long long tail = t256 % cus;
-    // (with B transposed the eight-wave form runs out of registers: 134 vs
-    // 148 TFLOP/s at 4096^3 for the four-wave one)
-    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus)
-      return (p.tb && !p.ta) ? kMfma32_256x256x32_w4_sched : kMfma32_256x256x32_w8_sched;
+    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w4_sched;
   }
   if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 75) {
     if (p.K < 256) return kMfma32_128x128x16_w4;

@@ -41,6 +41,7 @@ __device__ __forceinline__ void select_slice(Problem &p) {
   p.C += z * (size_t)p.sc;
 }
 
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 

@@ -20,6 +20,13 @@
 //   * there are no branches in the slab loop: at the end the loads repeat the
 //     last slab (clamped index) and the stores go to the stage nobody reads.
 //
+// B operand reads.  With B untransposed (k-rows in LDS) and two or four
+// matrix-core blocks across a wave tile, lane li of block j takes column
+// FN*li + j of the wave tile instead of j*MI + li: its FN values of one k are
+// then one 8- or 16-byte LDS read instead of FN scalar reads, and in the
+// epilogue it holds FN consecutive columns of a row, written as one vector.
+// The K-sum of every output is unchanged.
+//
 // Addressing is stateless: one base pointer per operand and thread, plus
 // offsets that are uniform across the workgroup, which keeps the register
 // count low enough for four waves with 128x128 wave tiles.  A tile that would
@@ -86,6 +93,40 @@ struct SlabLoader {
   }
 };
 
+// Operand reads of the ordered loop: as read_operands, except that with
+// PERMB the B values of one k for the FN blocks are one vector read.
+template <int MI, bool TA, bool TB, bool PERMB, class T>
+__device__ __forceinline__ void read_sched_operands(Operands<T> &o, const float *as, const float *bs,
+                                                    int q) {
+  if constexpr (!PERMB) {
+    read_operands<MI, TA, TB>(o, as, bs, q);
+  } else {
+    static_assert(!TB && (T::FN == 2 || T::FN == 4), "permuted B needs k-rows and 2 or 4 blocks");
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      if constexpr (!TA) {
+        o.a[i] = *reinterpret_cast<const floatx4 *>(as + i * MI * T::APITCH + T::QK * q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.a[i][e] = as[(T::QK * q + e) * T::APITCH + i * MI];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float *row = bs + (T::QK * q + e) * T::BPITCH;
+      if constexpr (T::FN == 4) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(row);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o.b[j][e] = v[j];
+      } else {
+        const floatx2 v = *reinterpret_cast<const floatx2 *>(row);
+        o.b[0][e] = v[0];
+        o.b[1][e] = v[1];
+      }
+    }
+  }
+}
+
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
           bool TB>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
@@ -98,6 +139,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   static_assert(T::NQ >= 2, "at least two operand groups per slab");
   using LA = SlabLoader<BM, BK, NT, TA>;
   using LB = SlabLoader<BN, BK, NT, !TB>;
+  constexpr bool PERMB = !TB && (T::FN == 2 || T::FN == 4);
 
   __shared__ __attribute__((aligned(16))) float As[2 * T::A_STAGE];
   __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_STAGE];
@@ -127,7 +169,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   const int a_rd = TA ? (g * T::GK) * T::APITCH + wm * T::WTM + li
                       : (wm * T::WTM + li) * T::APITCH + g * T::GK;
   const int b_rd = TB ? (wn * T::WTN + li) * T::BPITCH + g * T::GK
-                      : (g * T::GK) * T::BPITCH + wn * T::WTN + li;
+                      : (g * T::GK) * T::BPITCH + wn * T::WTN + (PERMB ? T::FN * li : li);
 
   Acc acc[T::FM][T::FN];
 #pragma unroll
@@ -140,7 +182,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   // Scheduling-group masks (LLVM AMDGPU): matrix instructions, LDS reads, LDS
   // writes, global reads.
   constexpr int kMfma = 0x008, kDsRead = 0x100, kDsWrite = 0x200, kVmemRead = 0x020;
-  constexpr int kReads = T::FM + 2 * T::FN;  // LDS read instructions per group
+  // LDS read instructions per operand group: a 16-byte read per block for a
+  // k-contiguous operand, scalar pairs (two per block) for an M/N-contiguous
+  // one, four vector reads for the permuted B.
+  constexpr int kReads = (TA ? 2 * T::FM : T::FM) + (TB ? T::FN : (PERMB ? 4 : 2 * T::FN));
   constexpr int kVecs = LA::NV + LB::NV;     // stores / loads per thread and slab
 
   const int nk = p.K / BK;
@@ -151,7 +196,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   la.load(min(1, nk - 1) * BK);
   lb.load(min(1, nk - 1) * BK);
   Operands<T> o;
-  read_operands<MI, TA, TB>(o, As + a_rd, Bs + b_rd, 0);
+  read_sched_operands<MI, TA, TB, PERMB>(o, As + a_rd, Bs + b_rd, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const float *as = As + cur * T::A_STAGE + a_rd;
@@ -159,7 +204,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
     for (int q = 0; q + 1 < T::NQ; ++q) {
       Operands<T> nxt;
-      read_operands<MI, TA, TB>(nxt, as, bs, q + 1);
+      read_sched_operands<MI, TA, TB, PERMB>(nxt, as, bs, q + 1);
       if (q == T::NQ / 2 - 1) {
         store(cur ^ 1);                        // slab kt+1 (a repeat at the end)
         la.load(min(kt + 2, nk - 1) * BK);     // slab kt+2, clamped
@@ -188,8 +233,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
     multiply_part<T, Acc, 0, 2>(acc, o);
     __syncthreads();
     Operands<T> nxt;
-    read_operands<MI, TA, TB>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd,
-                              Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
+    read_sched_operands<MI, TA, TB, PERMB>(nxt, As + (cur ^ 1) * T::A_STAGE + a_rd,
+                                           Bs + (cur ^ 1) * T::B_STAGE + b_rd, 0);
     multiply_part<T, Acc, 2, 4>(acc, o);
 #pragma unroll
     for (int s = 0; s < kReads; ++s) {
@@ -202,20 +247,63 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   // Epilogue: C = alpha*acc + beta*C for the rows and columns of this tile
   // (a shifted tile also computed some of its neighbour's).
   const int row0 = ms + wm * T::WTM;
-  const int col0 = ns + wn * T::WTN + li;
+  if constexpr (PERMB) {
+    // FN consecutive columns per lane and row: one vector store when C's rows
+    // allow it (N is a multiple of 4 here, so groups never straddle n0).
+    const int colq = ns + wn * T::WTN + T::FN * li;
+    const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    if (colq >= n0) {
 #pragma unroll
-  for (int i = 0; i < T::FM; ++i)
+      for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      const int col = col0 + j * MI;
-      if (col < n0) continue;
+        for (int r = 0; r < kRegs; ++r) {
+          const int row = row0 + i * MI + acc_row<MI>(g, r);
+          if (row < m0) continue;
+          float *c = p.C + (size_t)row * (size_t)p.ldc + colq;
+          if (cvec) {
+            if constexpr (T::FN == 4) {
+              floatx4 v;
 #pragma unroll
-      for (int r = 0; r < kRegs; ++r) {
-        const int row = row0 + i * MI + acc_row<MI>(g, r);
-        if (row < m0) continue;
-        store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
-      }
+              for (int j = 0; j < 4; ++j) v[j] = p.alpha * acc[i][j][r];
+              if (p.beta != 0.0f) {
+                const floatx4 old = *reinterpret_cast<const floatx4 *>(c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = fmaf(p.beta, old[j], v[j]);
+              }
+              *reinterpret_cast<floatx4 *>(c) = v;
+            } else {
+              floatx2 v;
+#pragma unroll
+              for (int j = 0; j < 2; ++j) v[j] = p.alpha * acc[i][j][r];
+              if (p.beta != 0.0f) {
+                const floatx2 old = *reinterpret_cast<const floatx2 *>(c);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) v[j] = fmaf(p.beta, old[j], v[j]);
+              }
+              *reinterpret_cast<floatx2 *>(c) = v;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) store_out(c + j, acc[i][j][r], p.alpha, p.beta);
+          }
+        }
     }
+  } else {
+    const int col0 = ns + wn * T::WTN + li;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = col0 + j * MI;
+        if (col < n0) continue;
+#pragma unroll
+        for (int r = 0; r < kRegs; ++r) {
+          const int row = row0 + i * MI + acc_row<MI>(g, r);
+          if (row < m0) continue;
+          store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
+        }
+      }
+  }
 }
 
 // True when sched_kernel<..., BM, BN, BK, ...> may run this problem.

@@ -116,7 +116,6 @@ def test_op_select_avoids_few_rows_kernel_for_transposed_b(lib):
                                         4096)) != "skinny_m8"
     assert n(sg.sgemm_op_select_variant(1, 1, 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0,
                                         FAKE, 4096)).startswith("mfma32_256x256")
-    # B transposed alone: the four-wave 256x256 form (the eight-wave one spills)
     assert n(sg.sgemm_op_select_variant(0, 1, 4096, 4096, 4096, 1.0, FAKE, 4096, FAKE, 4096, 0.0,
                                         FAKE, 4096)) == "mfma32_256x256x32_2x2_sched"
 
@@ -162,7 +161,7 @@ def test_batched_select_small_slices(lib):
     assert _batched_choice(1, 128, 128, 128) == "mfma16_64x64x64_4x2_sched"
     assert _batched_choice(1, 256, 256, 65536) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1024, 128, 128, 128) == "mfma32_128x128x16_2x2_w4"
-    assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_4x2_sched"
+    assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_2x2_sched"
     assert _batched_choice(4096, 32, 32, 32) == "mfma16_64x64x16_2x2_splitk"
     assert _batched_choice(128, 200, 300, 100) == "mfma16_64x64x16_2x2_splitk"
     assert _batched_choice(8, 1, 4096, 4096) == "skinny_m8"
