@@ -78,6 +78,7 @@ const Variant kVariants[] = {
     {"mfma16_128x128x64_4x2_sched", launch_mfma16_128x128x64_4x2_sched},
     {"mfma16_128x64x64_4x2_sched", launch_mfma16_128x64x64_4x2_sched},
     {"narrow_n16", launch_narrow_any},
+    {"mfma16_128x128x32_2x2_sched", launch_mfma16_128x128x32_2x2_sched},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -108,6 +109,7 @@ enum VariantId {
   kMfma16_128x128x64_w8_sched = 23,
   kMfma16_128x64x64_w8_sched = 24,
   kNarrow = 25,
+  kMfma16_128x128x32_w4_sched = 26,
 };
 
 constexpr int kNoKernel = -100;
@@ -150,10 +152,11 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //   * 256x256 tiles (four waves with 128x128 wave tiles, one workgroup per
 //     CU, 32-deep K slabs, the ordered slab loop) are fastest when the tiles
 //     are mostly inside C and their count fills the 256 CUs in whole rounds;
-//   * 128x128 tiles with eight waves (two per SIMD, the ordered loop) when
-//     there are at least as many tiles as CUs and they are mostly inside C:
-//     64-deep slabs for K >= 1024, 32-deep below, and for K < 256 four waves
-//     with 16-deep slabs;
+//   * 128x128 tiles (the ordered loop) when there are at least as many tiles
+//     as CUs and they are mostly inside C: with two or more tiles per CU,
+//     four waves and 32-deep slabs (two workgroups per CU); with fewer, eight
+//     waves (two per SIMD), 64-deep slabs for K >= 1024 and 32-deep below;
+//     for K < 256 four waves with 16-deep slabs;
 //   * 128x64 tiles (same loop) when those number at least as many as CUs;
 //   * otherwise 64x64 tiles with eight waves and 64-deep slabs on the ordered
 //     loop (16-deep ones, four waves, for a short K that is not a multiple of
@@ -192,6 +195,7 @@ int choose_variant(const Problem &p) {
   }
   if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 75) {
     if (p.K < 256) return kMfma32_128x128x16_w4;
+    if (t128 >= 2 * cus) return kMfma16_128x128x32_w4_sched;
     return (p.K < 1024) ? kMfma32_128x128x32_w8_sched : kMfma16_128x128x64_w8_sched;
   }
   const long long t12864 = ((long long)p.M + 127) / 128 * (((long long)p.N + 63) / 64) * batch;

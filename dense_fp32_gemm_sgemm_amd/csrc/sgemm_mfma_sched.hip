@@ -23,6 +23,12 @@ int launch_mfma32_128x128x32_4x2_sched(const Problem &p, hipStream_t s) {
 int launch_mfma16_128x128x64_4x2_sched(const Problem &p, hipStream_t s) {
   return launch_sched<16, 128, 128, 64, 4, 2, 2, 4>(p, s, launch_mfma32_128x128x32_4x2_sched);
 }
+// 128x128 tile, four waves with 64x64 wave tiles of 16x16 blocks, 32-deep
+// slabs: 69 KiB of LDS, so two workgroups share a CU when there are at least
+// two tiles per CU.
+int launch_mfma16_128x128x32_2x2_sched(const Problem &p, hipStream_t s) {
+  return launch_sched<16, 128, 128, 32, 2, 2, 1, 4>(p, s, launch_mfma32_128x128x32_4x2);
+}
 // 128x64 tile, eight waves with 32x32 wave tiles of 16x16 blocks, 64-deep
 // slabs: one tile per CU for problems with half as many 128x128 tiles.
 int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t s) {

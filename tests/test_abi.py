@@ -167,6 +167,16 @@ def test_batched_select_small_slices(lib):
     assert _batched_choice(8, 1, 4096, 4096) == "skinny_m8"
 
 
+def test_select_128_tiles(lib):
+    """128x128 tiles: four waves (two workgroups per CU) once there are two
+    tiles per CU, eight waves when one round of tiles leaves each CU one."""
+    assert _batched_choice(1, 8192, 1024, 8192) == "mfma16_128x128x32_2x2_sched"
+    assert _batched_choice(1, 1024, 8192, 256) == "mfma16_128x128x32_2x2_sched"
+    assert _batched_choice(1, 2048, 2048, 2048) == "mfma16_128x128x64_4x2_sched"
+    assert _batched_choice(1, 2048, 2048, 512) == "mfma32_128x128x32_4x2_sched"
+    assert _batched_choice(2, 2048, 2048, 2048) == "mfma16_128x128x32_2x2_sched"
+
+
 def test_select_narrow_problems(lib):
     """Few columns of C go to the few-columns kernel, few rows to the
     few-rows kernel or split-K tiles, never to the one-lane kernel (which
