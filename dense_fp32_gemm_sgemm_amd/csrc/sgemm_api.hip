@@ -163,8 +163,7 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //     64), splitting K over workgroups when the tiles cannot occupy half the
 //     CUs and K is long.
 // The ordered-loop variants fall back to their tile family's plain loop when
-// K is not a multiple of the slab depth, the tile is larger than C or an
-// operand does not allow 16-byte loads.
+// the tile is larger than C or K is shorter than one slab.
 
 // Percentage of the TM x TN tiles' area that lies inside an M x N slice.
 long long tile_fill_pct(int M, int N, int TM, int TN) {

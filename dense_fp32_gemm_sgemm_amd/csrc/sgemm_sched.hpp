@@ -1,9 +1,9 @@
 // sgemm_sched.hpp -- the matrix-core kernel with an explicitly ordered slab
-// loop, for problems whose shape lets every load be a whole 16-byte vector.
+// loop, for problems that span at least one tile in each dimension.
 //
 // It computes what mfma_kernel (sgemm_mfma.hpp) computes, with the same LDS
-// layout, operand reads and matrix-core blocks, and the same order of the
-// K-sum for every output.  The loop around them is different: the pages'
+// layout, operand reads and matrix-core blocks, and (when BK divides K) the
+// same order of the K-sum for every output.  The loop around them is different: the pages'
 // double buffering ("The road to a fast GEMM", section on prefetching the next
 // tile while computing the current one) is taken one step further, and the
 // instruction order inside a slab is pinned instead of left to the compiler:
@@ -20,6 +20,12 @@
 //   * there are no branches in the slab loop: at the end the loads repeat the
 //     last slab (clamped index) and the stores go to the stage nobody reads.
 //
+// K need not be a multiple of BK: every slab after the first then starts ov =
+// nk*BK - K values of k early, so the last one ends at K and every load stays
+// inside the operands, and the first slab's last ov values are overwritten
+// with zeros in LDS, in both operands, so nothing is counted twice and no
+// 0 * Inf arises.
+//
 // B operand reads.  With B untransposed (k-rows in LDS) and two or four
 // matrix-core blocks across a wave tile, lane li of block j takes column
 // FN*li + j of the wave tile instead of j*MI + li: its FN values of one k are
@@ -34,10 +40,12 @@
 // first column N - BN), so every load is in bounds without clamping; the
 // epilogue then stores only the rows and columns that belong to the tile.
 //
+// Global loads are 16-byte vectors of four consecutive floats; the hardware
+// needs only 4-byte alignment for them, so leading dimensions, batch strides
+// and shifted tiles may put them anywhere.
+//
 // Preconditions (checked on the host; other problems go to mfma_kernel):
-// K a positive multiple of BK, M >= BM, N >= BN, both operands 16-byte
-// vector-aligned (base, leading dimension, batch stride; M or N a multiple of
-// 4 for a transposed A or an untransposed B), no split of K.
+// K >= BK, M >= BM, N >= BN, A and B 4-byte aligned, no split of K.
 #pragma once
 
 #include "sgemm_mfma.hpp"
@@ -70,6 +78,7 @@ struct SlabLoader {
 
   const float *base;  // this thread's first vector at k = 0
   size_t ld;
+  int kpos;           // k of this thread's first value inside a slab
   floatx4 v[NV];
 
   // r0: first row (or column, for k-rows) of the block inside X.
@@ -77,13 +86,32 @@ struct SlabLoader {
     ld = (size_t)ld_;
     const int br = tid / VPR, bc = (tid % VPR) * 4;
     base = KROWS ? X + (size_t)br * ld + r0 + bc : X + (size_t)(r0 + br) * ld + bc;
+    kpos = KROWS ? br : bc;
   }
+  // Writes zeros over this thread's values of a stored slab whose k inside
+  // the slab is kcut or more (lds: the thread's vector 0 in the stage, pitch:
+  // the stage's row pitch).
+  __device__ __forceinline__ void zero_from(float *lds, int pitch, int kcut) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = KROWS ? kpos + i * DR : kpos + e;
+        if (k >= kcut) lds[i * DR * pitch + e] = 0.0f;
+      }
+  }
+  // Moves every later load d values of k back.
+  __device__ __forceinline__ void shift_k(int d) { base -= KROWS ? (size_t)d * ld : (size_t)d; }
   __device__ __forceinline__ void load(int k0) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const float *q = KROWS ? base + ((size_t)k0 + (size_t)i * DR) * ld
                              : base + (size_t)i * DR * ld + k0;
-      v[i] = *reinterpret_cast<const floatx4 *>(q);
+      // Four consecutive floats at any 4-byte aligned address: the copy
+      // compiles to one global_load_dwordx4, which needs only dword alignment.
+      floatx4 t;
+      __builtin_memcpy(&t, q, sizeof(t));
+      v[i] = t;
     }
   }
   // LDS offset (floats) of vector 0 in a stage of row pitch `pitch`; vector i
@@ -128,7 +156,7 @@ __device__ __forceinline__ void read_sched_operands(Operands<T> &o, const float 
 }
 
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
-          bool TB>
+          bool TB, bool RAGGED>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
                                                                                int tiles_n, int group_m) {
   select_slice(p);
@@ -188,10 +216,27 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   constexpr int kReads = (TA ? 2 * T::FM : T::FM) + (TB ? T::FN : (PERMB ? 4 : 2 * T::FN));
   constexpr int kVecs = LA::NV + LB::NV;     // stores / loads per thread and slab
 
-  const int nk = p.K / BK;
-  la.load(0);
-  lb.load(0);
-  store(0);
+  // RAGGED (BK does not divide K): slab t >= 1 covers [t BK - ov, (t+1) BK -
+  // ov), so the last slab ends at K and every load stays inside the operands,
+  // and slab 0 covers [0, BK - ov): its last ov values are overwritten with
+  // zeros in LDS, in both operands, so nothing is counted twice and no 0 * Inf
+  // arises.  (A separate instantiation keeps the register allocation of the
+  // common case untouched.)
+  const int nk = RAGGED ? (p.K + BK - 1) / BK : p.K / BK;
+  if constexpr (RAGGED) {
+    const int ov = nk * BK - p.K;
+    la.shift_k(ov);
+    lb.shift_k(ov);
+    la.load(ov);
+    lb.load(ov);
+    store(0);
+    la.zero_from(As + a_st, T::APITCH, BK - ov);
+    lb.zero_from(Bs + b_st, T::BPITCH, BK - ov);
+  } else {
+    la.load(0);
+    lb.load(0);
+    store(0);
+  }
   __syncthreads();
   la.load(min(1, nk - 1) * BK);
   lb.load(min(1, nk - 1) * BK);
@@ -243,15 +288,17 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
     }
     o = nxt;
   }
-
   // Epilogue: C = alpha*acc + beta*C for the rows and columns of this tile
   // (a shifted tile also computed some of its neighbour's).
   const int row0 = ms + wm * T::WTM;
   if constexpr (PERMB) {
-    // FN consecutive columns per lane and row: one vector store when C's rows
-    // allow it (N is a multiple of 4 here, so groups never straddle n0).
+    // FN consecutive columns per lane and row: one vector store when they are
+    // FN-float aligned in memory (then a group lies wholly on one side of n0,
+    // since n0 - ns is a multiple of FN), else one store per column of the
+    // tile's own.
     const int colq = ns + wn * T::WTN + T::FN * li;
-    const bool cvec = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    const bool cvec = (reinterpret_cast<uintptr_t>(p.C) % (4 * T::FN) == 0) && (p.ldc % T::FN == 0) &&
+                      (ns % T::FN == 0);
     if (colq >= n0) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
@@ -287,6 +334,20 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
             for (int j = 0; j < T::FN; ++j) store_out(c + j, acc[i][j][r], p.alpha, p.beta);
           }
         }
+    } else if (colq + T::FN > n0) {
+      // A group that straddles the first column of a shifted tile (only when
+      // n0 - ns is not a multiple of FN): the tile's own columns only.
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < kRegs; ++r) {
+          const int row = row0 + i * MI + acc_row<MI>(g, r);
+          if (row < m0) continue;
+          float *c = p.C + (size_t)row * (size_t)p.ldc + colq;
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j)
+            if (colq + j >= n0) store_out(c + j, acc[i][j][r], p.alpha, p.beta);
+        }
     }
   } else {
     const int col0 = ns + wn * T::WTN + li;
@@ -309,7 +370,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 // True when sched_kernel<..., BM, BN, BK, ...> may run this problem.
 template <int BM, int BN, int BK>
 inline bool sched_ok(const Problem &p) {
-  return p.K >= BK && p.K % BK == 0 && p.M >= BM && p.N >= BN && a_vec_ok(p) && b_vec_ok(p);
+  return p.K >= BK && p.M >= BM && p.N >= BN &&
+         (reinterpret_cast<uintptr_t>(p.A) & 3) == 0 && (reinterpret_cast<uintptr_t>(p.B) & 3) == 0;
 }
 
 // Launches sched_kernel when its preconditions hold, else `fallback` (a
@@ -324,9 +386,15 @@ static int launch_sched(const Problem &p, hipStream_t stream,
   const dim3 grid((unsigned)(tiles_m * tiles_n), 1u, (unsigned)p.batch);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
-#define SG950_SCHED(TA_, TB_)                                                                         \
-  hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_>), grid, \
-                     block, 0, stream, p, tm, tn, group_m)
+#define SG950_SCHED(TA_, TB_)                                                                      \
+  do {                                                                                             \
+    if (p.K % BK == 0)                                                                             \
+      hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, false>), \
+                         grid, block, 0, stream, p, tm, tn, group_m);                              \
+    else                                                                                           \
+      hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, true>), \
+                         grid, block, 0, stream, p, tm, tn, group_m);                              \
+  } while (0)
   if (!p.ta && !p.tb) {
     SG950_SCHED(false, false);
   } else if (!p.ta) {

@@ -242,11 +242,10 @@ SCHED = [v for v in VARIANTS if VNAMES[v].endswith("_sched")]
 @pytest.mark.parametrize("shape", [(300, 264, 64), (256, 256, 32), (520, 392, 96), (600, 500, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_sched_path_shapes_and_orientations(variant, shape):
-    """Shapes that meet the ordered-loop kernel's preconditions (K a multiple
-    of the slab depth, the tile inside C, 16-byte operands) for at least the
-    smaller tiles: tiles shifted back inside C on both edges, a single slab,
-    every operand orientation, the accumulate form; real to 1e-5 and integer
-    data exactly."""
+    """Shapes that meet the ordered-loop kernel's preconditions (the tile
+    inside C, K at least one slab) for at least the smaller tiles: tiles
+    shifted back inside C on both edges, a single slab, every operand
+    orientation, the accumulate form; real to 1e-5 and integer data exactly."""
     M, N, K = shape
     for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
         A, B, Cin = draw(M, N, K, seed=M + 7 * N + K, with_c=True)
@@ -260,6 +259,55 @@ def test_sched_path_shapes_and_orientations(variant, shape):
         Bis = np.ascontiguousarray(Bi.T) if tb else Bi
         C = run(Ais, Bis, Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb)
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], shape, ta, tb))
+
+
+@pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
+@pytest.mark.parametrize("shape", [(300, 270, 70), (260, 301, 33), (520, 390, 161)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_sched_path_ragged_k_and_unaligned(variant, shape):
+    """K that is not a multiple of the slab depth (later slabs start early so
+    the last ends at K; the k two slabs share are zero in the first), operands and C at
+    4-byte but not 16-byte aligned addresses with odd leading dimensions, and N
+    not a multiple of 4 (column groups of the permuted B straddling a shifted
+    tile's edge); every orientation, the accumulate form; nothing outside C is
+    written."""
+    M, N, K = shape
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        A, B, Cin = draw(M, N, K, seed=M + 3 * N + K, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        lds = (As.shape[1] + 3, Bs.shape[1] + 1, N + 5)
+        say("sched ragged", VNAMES[variant], shape, ta, tb)
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, lds=lds,
+                offsets=(1, 3, 2), check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "%s %s %s%s" % (VNAMES[variant], shape, ta, tb))
+        Ai, Bi, Ci = draw(M, N, K, seed=M + 3 * N + K, kind="int", with_c=True)
+        Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+        Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+        C = run(Ais, Bis, Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb, lds=lds,
+                offsets=(2, 1, 3))
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], shape, ta, tb))
+
+
+@pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
+def test_sched_path_inf_in_repeated_k(variant):
+    """Infs at a k that two slabs cover when the slab depth does not divide K,
+    one in A (row 7) and one in B (column 5): one of the two copies must be
+    zero in both operands, so C is +-Inf exactly in row 7 and column 5, as
+    the definition gives, never NaN (a zero in one operand only would make
+    0 * Inf there)."""
+    M, N, K = 300, 264, 70
+    rng = np.random.default_rng(5)
+    A = (rng.integers(1, 5, (M, K)) * rng.choice([-1, 1], (M, K))).astype(np.float32)
+    B = rng.integers(1, 5, (K, N)).astype(np.float32)   # positive: no Inf - Inf
+    k = 20          # among the k that slab 0 zeroes for 32- and 64-deep slabs ([6, 32), [6, 64))
+    A[7, k] = np.inf
+    B[k, 5] = np.inf
+    say("sched inf", VNAMES[variant])
+    C = run(A, B, variant=variant)
+    ref, _ = oracle.gemm(A, B, None, 1.0, 0.0)
+    assert not np.isnan(ref).any()
+    assert np.array_equal(C.astype(np.float64), ref), VNAMES[variant]
 
 
 @pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
@@ -283,7 +331,7 @@ def test_sched_path_permutation_and_batch(variant):
     out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, gap=4)
     check_batched(out, Ai, Bi, Ci, 1.0, 1.0, VNAMES[variant] + " batch", exact=True)
     # slice strides that are not whole 16-byte vectors: aligned first slice and
-    # leading dimensions, misaligned later slices (the scalar-load path)
+    # leading dimensions, later slices only 4-byte aligned
     say("sched batch odd stride", VNAMES[variant])
     out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, gap=1)
     check_batched(out, Ai, Bi, Ci, 1.0, 1.0, VNAMES[variant] + " batch odd stride", exact=True)
