@@ -45,6 +45,20 @@ int launch_narrow_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// The matrix-core few-rows kernel covers M <= 32; as a forced variant on a
+// taller problem it runs on row blocks of 32.
+int launch_fewrows_any(const Problem &p, hipStream_t s) {
+  for (int r = 0; r < p.M; r += 32) {
+    Problem q = p;
+    q.M = (p.M - r < 32) ? p.M - r : 32;
+    q.A = p.ta ? p.A + r : p.A + (size_t)r * (size_t)p.lda;
+    q.C = p.C + (size_t)r * (size_t)p.ldc;
+    const int rc = launch_fewrows(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 struct Variant {
   const char *name;
   Launcher launch;
@@ -79,6 +93,7 @@ const Variant kVariants[] = {
     {"mfma16_128x64x64_4x2_sched", launch_mfma16_128x64x64_4x2_sched},
     {"narrow_n16", launch_narrow_any},
     {"mfma16_128x128x32_2x2_sched", launch_mfma16_128x128x32_2x2_sched},
+    {"fewrows_m32", launch_fewrows_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -110,6 +125,7 @@ enum VariantId {
   kMfma16_128x64x64_w8_sched = 24,
   kNarrow = 25,
   kMfma16_128x128x32_w4_sched = 26,
+  kFewRows = 27,
 };
 
 constexpr int kNoKernel = -100;
@@ -175,7 +191,19 @@ int choose_variant(const Problem &p) {
   const long long batch = p.batch;
   const long long work = (long long)p.M * p.N * p.K * batch;
   const long long nk = (long long)p.N * p.K * batch;
-  if (p.M <= 8 && !p.tb && p.N >= 64 && nk >= (1LL << 20)) return kSkinny;
+  // Few rows and enough of B: bound by streaming B.  The vector-unit kernel
+  // for up to four rows of a moderate B read in full-K strips, the matrix-core
+  // kernel for up to 32 rows when its column strips fill the CUs (with a
+  // transposed B, which it reads along k, up to 16 rows).
+  if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20)) {
+    const long long nb = (long long)p.N * batch;  // columns over the batch
+    const bool valu_ok = !p.tb && p.M <= 8;
+    if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&
+        (p.M <= 2 || p.N >= 4096))
+      return kSkinny;
+    if (p.tb ? (p.M <= 16 && nb >= 2048) : nb >= (p.M <= 16 ? 1024 : 2048)) return kFewRows;
+    if (valu_ok) return kSkinny;
+  }
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
   if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
   // Few columns: the A-streaming few-columns kernel.

@@ -1,0 +1,335 @@
+// sgemm_fewrows.hip -- SGEMM with few rows of C (M <= 32) on the matrix
+// cores: a product bound by the bandwidth of streaming B.
+//
+// With M <= 32 a GEMM does at most 64 FLOP per element of B it reads, near
+// the MI355X ridge point, so B has to stream from HBM once with many loads in
+// flight, and the arithmetic must keep up with it: the vector units cannot
+// (up to 32 rows of FMAs per loaded element), the matrix cores can.
+//
+// A workgroup owns a strip of columns of C and all of its rows (one or two
+// 16-row blocks, sharing every load of B); its eight waves take eight
+// contiguous K ranges.  Each wave accumulates 16 x 16 blocks
+// with v_mfma_f32_16x16x4f32, whose lane l supplies A[l%16][slot l/16] and
+// B[slot][l%16] for the four k slots of one instruction; the k behind a slot
+// is free to choose as long as A and B agree on it:
+//
+//   * B untransposed (k-rows): in step e of a group of 16 k the lanes of slot
+//     s read row k0 + 4s + e, lane j taking CPL adjacent columns as one 4-, 8-
+//     or 16-byte load (a wavefront load is four rows x 64 CPL bytes).  Value
+//     c of the load feeds block c, so block c holds the columns CPL*j + c of
+//     the strip (16 CPL columns); a lane's A values for the group (row l%16,
+//     k0 + 4s .. 4s + 3) are one 16-byte load and serve all CPL blocks;
+//   * B transposed (stored N x K): lane j of slot s reads four consecutive k
+//     of its column, k0 + 4s .. 4s + 3, as one 16-byte load, and value e
+//     feeds instruction e of four, with the matching four k of A.
+//
+// Loads of eight steps are issued before their first use.  Rows past M read
+// row M-1 and columns past N read column N-1 (in bounds, never stored); k
+// past the end of a wave's range is skipped by selection, so a NaN or Inf
+// outside the matrices cannot leak in.  The eight waves' blocks are added
+// through LDS in a fixed order and C = alpha*sum + beta*C is written once:
+// one launch, no atomics, deterministic.
+#include "sgemm_common.hpp"
+#include "sgemm_launch.hpp"
+
+#include <climits>
+
+namespace sg950 {
+
+namespace {
+constexpr int kFewWaves = 8;   // waves per workgroup, each a K range
+constexpr int kFewUnroll = 8;  // steps whose loads are in flight together
+}  // namespace
+
+// NR: 16-row blocks of C (M <= 16 NR).  CPL: columns per lane (untransposed
+// B; 1 for a transposed B).  VB: an untransposed B's rows hold whole
+// CPL-column groups (N % CPL == 0), so a lane's columns are one load.
+template <int NR, int CPL, bool TA, bool TB, bool VB>
+__global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange) {
+  select_slice(p);
+  constexpr int NB = TB ? 1 : CPL;        // 16 x 16 blocks per wave and row block
+  constexpr int NC = TB ? 16 : 16 * CPL;  // columns per workgroup
+  __shared__ floatx4 red[kFewWaves][NR * NB][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane % 16, sl = lane / 16;
+  // Neighbouring strips share cache lines of B: give each XCD (and its L2) a
+  // contiguous run of them.
+  const int n0 = xcd_remap((int)blockIdx.x, (int)gridDim.x) * NC;
+  int arow[NR];  // A rows of this lane, one per row block
+#pragma unroll
+  for (int r = 0; r < NR; ++r) arow[r] = min(16 * r + li, p.M - 1);
+  const int kb = w * krange;          // this wave's K range [kb, ke)
+  const int ke = min(p.K, kb + krange);
+  const size_t lda = (size_t)p.lda, ldb = (size_t)p.ldb;
+
+  floatx4 acc[NR][NB];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < NB; ++e) acc[r][e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if constexpr (!TB) {
+    const int c0 = n0 + CPL * li;  // this lane's first column
+    struct Cols {
+      float v[CPL];
+    };
+    auto load_b = [&](int k) -> Cols {
+      const float *row = p.B + (size_t)k * ldb;
+      Cols b;
+      if constexpr (VB) {
+        // Whole groups: a group past N repeats the last one (never stored).
+        __builtin_memcpy(b.v, row + min(c0, p.N - CPL), sizeof(b.v));
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) b.v[e] = row[min(c0 + e, p.N - 1)];
+      }
+      return b;
+    };
+    // Four consecutive k of one of this lane's rows of op(A), for one slot.
+    auto load_a4 = [&](int r, int k) -> floatx4 {
+      if constexpr (!TA) {
+        floatx4 v;
+        __builtin_memcpy(&v, p.A + (size_t)arow[r] * lda + k, sizeof(v));
+        return v;
+      } else {
+        const float *q = p.A + (size_t)k * lda + arow[r];
+        return floatx4{q[0], q[lda], q[2 * lda], q[3 * lda]};
+      }
+    };
+    // Groups of 16 k: slot sl takes k = k0 + 4 sl + e in step e, so a lane's
+    // A values for the group are one vector.
+    const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
+    int t = 0;
+    for (; t + kFewUnroll / 4 <= nfull; t += kFewUnroll / 4) {
+      Cols b[kFewUnroll / 4][4];
+      floatx4 a[kFewUnroll / 4][NR];
+#pragma unroll
+      for (int u = 0; u < kFewUnroll / 4; ++u) {
+        const int k = kb + 16 * (t + u) + 4 * sl;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[u][e] = load_b(k + e);
+      }
+      // All loads of the batch are issued before the first use.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kFewUnroll / 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][e].v[c], acc[r][c], 0, 0, 0);
+    }
+    for (; t < nfull; ++t) {
+      const int k = kb + 16 * t + 4 * sl;
+      floatx4 a[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) a[r] = load_a4(r, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const Cols b = load_b(k + e);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r][e], b.v[c], acc[r][c], 0, 0, 0);
+      }
+    }
+    // The rest of the range (fewer than 16 k): k past ke contribute 0.
+    const int kt = kb + 16 * nfull;
+    if (kt < ke) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = kt + 4 * sl + e;
+        const bool in = k < ke;
+        const int kk = in ? k : kb;  // any in-range k; the values are replaced
+        Cols b = load_b(kk);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) b.v[c] = in ? b.v[c] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float av = TA ? p.A[(size_t)kk * lda + arow[r]] : p.A[(size_t)arow[r] * lda + kk];
+          const float a = in ? av : 0.0f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b.v[c], acc[r][c], 0, 0, 0);
+        }
+      }
+    }
+  } else {
+    const int bcol = min(n0 + li, p.N - 1);  // column of op(B) (row of stored B)
+    const float *brow = p.B + (size_t)bcol * ldb;
+    auto load_b4 = [&](int k) -> floatx4 {
+      floatx4 v;
+      __builtin_memcpy(&v, brow + k, sizeof(v));
+      return v;
+    };
+    auto load_a4 = [&](int r, int k) -> floatx4 {
+      if constexpr (!TA) {
+        floatx4 v;
+        __builtin_memcpy(&v, p.A + (size_t)arow[r] * lda + k, sizeof(v));
+        return v;
+      } else {
+        const float *q = p.A + (size_t)k * lda + arow[r];
+        return floatx4{q[0], q[lda], q[2 * lda], q[3 * lda]};
+      }
+    };
+    // Groups of 16 k: slot sl takes k = kb + 16t + 4sl .. + 3.
+    const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
+    int t = 0;
+    for (; t + kFewUnroll / NR <= nfull; t += kFewUnroll / NR) {
+      floatx4 a[kFewUnroll / NR][NR], b[kFewUnroll / NR];
+#pragma unroll
+      for (int u = 0; u < kFewUnroll / NR; ++u) {
+        const int k = kb + 16 * (t + u) + 4 * sl;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
+        b[u] = load_b4(k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kFewUnroll / NR; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][e], acc[r][0], 0, 0, 0);
+    }
+    for (; t < nfull; ++t) {
+      const int k = kb + 16 * t + 4 * sl;
+      const floatx4 b = load_b4(k);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const floatx4 a = load_a4(r, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[r][0], 0, 0, 0);
+      }
+    }
+    // The rest of the range (fewer than 16 k): element by element, k < ke only.
+    const int kt = kb + 16 * nfull;
+    if (kt < ke) {
+      floatx4 b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = kt + 4 * sl + e;
+        const bool in = k < ke;
+        b[e] = in ? brow[in ? k : kb] : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        floatx4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = kt + 4 * sl + e;
+          const bool in = k < ke;
+          const int kk = in ? k : kb;
+          const float av = TA ? p.A[(size_t)kk * lda + arow[r]] : p.A[(size_t)arow[r] * lda + kk];
+          a[e] = in ? av : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[r][0], 0, 0, 0);
+      }
+    }
+  }
+
+  // Lane l holds rows 16 rb + 4*(l/16) + r of row block rb; block e's column
+  // j = l%16 is column CPL*j + e of the strip (B untransposed) or j
+  // (transposed).
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+    for (int e = 0; e < NB; ++e) red[w][rb * NB + e][lane] = acc[rb][e];
+  __syncthreads();
+  if (w != 0) return;  // no barrier after this point
+#pragma unroll
+  for (int rb = 0; rb < NR; ++rb)
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      floatx4 s = red[0][rb * NB + e][lane];
+#pragma unroll
+      for (int q = 1; q < kFewWaves; ++q) {
+        const floatx4 v = red[q][rb * NB + e][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] += v[r];
+      }
+      const int col = TB ? n0 + li : n0 + CPL * li + e;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rb + 4 * sl + r;
+        if (row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, s[r], p.alpha, p.beta);
+      }
+    }
+}
+
+namespace {
+template <int NR, int CPL, bool TA, bool TB, bool VB>
+void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange) {
+  hipLaunchKernelGGL((fewrows_kernel<NR, CPL, TA, TB, VB>), grid, dim3(kFewWaves * 64), 0, stream, p,
+                     krange);
+}
+
+template <int NR, int CPL, bool TB>
+void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int krange, bool vb) {
+  if (p.ta) {
+    if (vb)
+      launch_fewrows_t<NR, CPL, true, TB, true>(p, grid, stream, krange);
+    else
+      launch_fewrows_t<NR, CPL, true, TB, false>(p, grid, stream, krange);
+  } else {
+    if (vb)
+      launch_fewrows_t<NR, CPL, false, TB, true>(p, grid, stream, krange);
+    else
+      launch_fewrows_t<NR, CPL, false, TB, false>(p, grid, stream, krange);
+  }
+}
+
+template <int NR>
+void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl) {
+  if (p.tb) {
+    launch_fewrows_ta<NR, 1, true>(p, grid, stream, krange, false);
+    return;
+  }
+  const bool vb = p.N % cpl == 0;
+  if (cpl == 4)
+    launch_fewrows_ta<NR, 4, false>(p, grid, stream, krange, vb);
+  else if (cpl == 2)
+    launch_fewrows_ta<NR, 2, false>(p, grid, stream, krange, vb);
+  else
+    launch_fewrows_ta<NR, 1, false>(p, grid, stream, krange, vb);
+}
+}  // namespace
+
+int launch_fewrows(const Problem &p, hipStream_t stream) {
+  if (p.M < 1 || p.M > 32) return -1;
+  // Columns per lane (untransposed B): the widest that still gives the strips
+  // at least one workgroup per CU over the batch.
+  int cpl = 1;
+  if (!p.tb) {
+    for (int c = 4; c >= 2; c /= 2) {
+      const long long strips = ((long long)p.N + 16 * c - 1) / (16 * c);
+      if (strips * p.batch >= 256) {
+        cpl = c;
+        break;
+      }
+    }
+  }
+  const int nc = p.tb ? 16 : 16 * cpl;
+  const long long blocks = ((long long)p.N + nc - 1) / nc;
+  if (blocks > INT_MAX) return -1;
+  // Eight K ranges, each a multiple of 16 k (the groups of the four slots).
+  int krange = (p.K + kFewWaves - 1) / kFewWaves;
+  krange = (krange + 15) / 16 * 16;
+  const dim3 grid((unsigned)blocks, 1u, (unsigned)p.batch);
+  if (p.M > 16)
+    launch_fewrows_nr<2>(p, grid, stream, krange, cpl);
+  else
+    launch_fewrows_nr<1>(p, grid, stream, krange, cpl);
+  return 0;
+}
+
+}  // namespace sg950

@@ -66,6 +66,11 @@ int launch_skinny(const Problem &p, hipStream_t stream);
 // N > 16.
 int launch_narrow(const Problem &p, hipStream_t stream);
 
+// Few rows of C (M <= 32): streams B, the matrix cores accumulate 16 x 16
+// blocks, K split over the waves of a workgroup, one launch.  Returns -1 for
+// M outside 1..32.
+int launch_fewrows(const Problem &p, hipStream_t stream);
+
 // Operand alignment classes: an operand may be read with 16-byte vector
 // loads when its base is 16-byte aligned and its leading dimension is a
 // multiple of four; when its rows run along M or N (A transposed, B not) the

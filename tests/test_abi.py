@@ -186,9 +186,35 @@ def test_select_narrow_problems(lib):
     assert _batched_choice(1, 3000, 16, 100) == "narrow_n16"
     assert _batched_choice(1, 12, 15, 100000) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1, 3, 4096, 4096) == "skinny_m8"
-    assert _batched_choice(1, 8, 4096, 4096) == "skinny_m8"
-    assert _batched_choice(1, 9, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _batched_choice(1, 8, 4096, 4096) == "fewrows_m32"
+    assert _batched_choice(1, 9, 4096, 4096) == "fewrows_m32"
     assert _batched_choice(1, 5, 7, 9) == "simple"
+
+
+def _op_choice(ta, tb, M, N, K, batch=1):
+    lda = M if ta else K
+    ldb = K if tb else N
+    return sg.sgemm_variant_name(sg.sgemm_strided_batched_select_variant(
+        ta, tb, M, N, K, 1.0, FAKE, lda, M * K, FAKE, ldb, K * N, 0.0, FAKE, N, M * N, batch))
+
+
+def test_select_few_rows(lib):
+    """Up to four rows of a moderate untransposed B on the vector-unit kernel,
+    up to 32 rows (16 with B transposed) on the matrix-core kernel when its
+    column strips fill the CUs, split-K tiles otherwise."""
+    assert _op_choice(0, 0, 1, 4096, 4096) == "skinny_m8"
+    assert _op_choice(0, 0, 4, 8192, 8192) == "skinny_m8"
+    assert _op_choice(0, 0, 4, 16384, 16384) == "fewrows_m32"       # B too large for full-K strips
+    assert _op_choice(0, 0, 4, 2048, 2048) == "fewrows_m32"
+    assert _op_choice(0, 0, 1, 1024, 4096) == "fewrows_m32"
+    assert _op_choice(0, 0, 12, 4096, 4096) == "fewrows_m32"
+    assert _op_choice(1, 0, 32, 8192, 8192) == "fewrows_m32"
+    assert _op_choice(0, 0, 24, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 1, 16, 4096, 4096) == "fewrows_m32"
+    assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 1, 24, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 0, 8, 512, 4096) == "skinny_m8"                # too few strips
+    assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 
 
 def test_status_strings(lib):

@@ -581,8 +581,55 @@ def test_few_columns_kernel(N, MK):
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
 
 
+@pytest.mark.parametrize("shape", [(9, 100, 33), (16, 1000, 1000), (1, 4099, 5), (12, 4096, 1),
+                                   (16, 257, 4099), (24, 4099, 33), (32, 257, 1000), (37, 300, 70),
+                                   (12, 16384, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_matrix_core_kernel(shape):
+    """The matrix-core few-rows kernel forced: K ranges that leave the last
+    wave empty or partial (K = 1 included), N not a multiple of the columns a
+    lane loads, every operand orientation, a padded / misaligned copy, one
+    and two 16-row blocks, row blocks past 32 (M = 37), the accumulate form;
+    real data to 1e-5 and integer data exactly."""
+    M, N, K = shape
+    v = VNAMES.index("fewrows_m32")
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        A, B, Cin = draw(M, N, K, seed=M + 5 * N + K, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        say("few rows", shape, ta, tb)
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb, check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "few rows %s %s%s" % (shape, ta, tb))
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb,
+                lds=(As.shape[1] + 3, Bs.shape[1] + 1, N + 2), offsets=(1, 3, 2), check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "few rows %s %s%s padded" % (shape, ta, tb))
+        Ai, Bi, Ci = draw(M, N, K, seed=M + 5 * N + K, kind="int", with_c=True)
+        Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+        Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+        C = run(Ais, Bis, Ci, 1.0, 1.0, variant=v, trans_a=ta, trans_b=tb)
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "few rows %s %s%s int" % (shape, ta, tb))
+
+
+@pytest.mark.parametrize("batch,N", [(16, 1000), (8, 1000), (16, 1001), (3, 130)],
+                         ids=lambda x: str(x))
+def test_few_rows_matrix_core_kernel_batched(batch, N):
+    """Enough slices for the 4- and 2-column lane loads (16 and 8 slices of
+    1000 columns), a column count they do not divide (1001), and a small batch
+    with one-column loads; integer data exactly, slices with gaps."""
+    rng = np.random.default_rng(batch * 7 + N)
+    M, K = (12 if batch % 2 == 0 else 20), 300
+    v = VNAMES.index("fewrows_m32")
+    Ai = rng.integers(-4, 5, (batch, M, K)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (batch, K, N)).astype(np.float32)
+    Ci = rng.integers(-4, 5, (batch, M, N)).astype(np.float32)
+    say("few rows batched", batch, N)
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=v, gap=3)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, "few rows batch %d N %d" % (batch, N), exact=True)
+
+
 @pytest.mark.parametrize("shape", [(4096, 1, 4096), (1000, 7, 3000), (3000, 15, 100), (65536, 8, 1024),
-                                   (12, 2500, 777)], ids=lambda s: "x".join(map(str, s)))
+                                   (12, 2500, 777), (8, 4096, 1500), (20, 3000, 1000), (3, 2100, 2500)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_few_columns_or_rows_automatic(shape):
     """Fewer than 16 columns (or rows) of C through the automatic choice:
     real data to 1e-5, integer data exactly, and a padded / misaligned copy."""
