@@ -375,6 +375,9 @@ def main(argv=None):
                     help="write the stored traffic figure from four counter_collection.csv files")
     ap.add_argument("--copy-calib", action="store_true",
                     help="one 256 MiB streaming copy (to scale HBM byte counters)")
+    ap.add_argument("--few-rows", action="store_true",
+                    help="few-rows grid (M <= 32, both orientations of B): the automatic choice, "
+                         "the three candidate kernels and the vendor BLAS")
     ap.add_argument("--vendor", action="store_true",
                     help="with --sweep/--shape: also time torch.mm in strict FP32 (context only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -406,6 +409,8 @@ def main(argv=None):
     import dense_fp32_gemm_sgemm_amd as sg
     sg.load()
 
+    if args.few_rows:
+        return few_rows(args)
     if args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib:
         return run_modes(args)
 
@@ -454,6 +459,46 @@ def main(argv=None):
         line["pct_of_measured_valu_f32"] = round(100.0 * value / 1e3 / ceilings["valu_fma_f32_tflops"], 2)
         line["pct_of_datasheet_fp32"] = round(100.0 * value / 1e3 / PEAK_FP32_TFLOPS, 2)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+FEW_ROWS_M = (1, 4, 8, 12, 16, 20, 24, 32)
+FEW_ROWS_NK = ((4096, 4096), (8192, 8192), (16384, 16384), (1024, 4096), (2048, 2048),
+               (4096, 1024), (4096, 16384), (65536, 1024))
+
+
+def few_rows(args):
+    """Median kernel time (us) of the automatic choice, of each few-rows
+    candidate forced (vector-unit kernel, split-K 64x64 tiles, matrix-core
+    kernel) and of torch.mm in strict FP32, per shape and orientation of B."""
+    import dense_fp32_gemm_sgemm_amd as sg
+    torch = _torch()
+    names = sg.variant_names()
+    cands = [names.index(n) for n in ("skinny_m8", "mfma16_64x64x64_4x2_pipe_splitk", "fewrows_m32")]
+    for M in FEW_ROWS_M:
+        for N, K in FEW_ROWS_NK:
+            for ops in ("NN", "NT"):
+                prob = Problem(M, N, K, ops=ops)
+                rec = {"mode": "few-rows", "M": M, "N": N, "K": K, "ops": ops,
+                       "auto": prob.variant_name(-1)}
+                for v in [-1] + cands:
+                    _, per = bench_problem(prob, args.steps, min(args.warmup, args.steps), v)
+                    rec["us_" + ("auto" if v < 0 else names[v])] = round(statistics.median(per) * 1e3, 2)
+                prev = torch.backends.cuda.matmul.allow_tf32
+                torch.backends.cuda.matmul.allow_tf32 = False
+                try:
+                    Bm = prob.B.t() if prob.tb else prob.B
+                    fn = lambda: torch.mm(prob.A, Bm, out=prob.C)
+                    for _ in range(min(args.warmup, args.steps)):
+                        fn()
+                    wake(0.1, fn)
+                    _, per = time_steps(fn, args.steps, torch.cuda.current_stream())
+                finally:
+                    torch.backends.cuda.matmul.allow_tf32 = prev
+                rec["us_torch_mm_fp32"] = round(statistics.median(per) * 1e3, 2)
+                print(json.dumps(rec), flush=True)
+                del prob
+                torch.cuda.empty_cache()
     return 0
 
 
