@@ -94,6 +94,7 @@ const Variant kVariants[] = {
     {"narrow_n16", launch_narrow_any},
     {"mfma16_128x128x32_2x2_sched", launch_mfma16_128x128x32_2x2_sched},
     {"fewrows_m32", launch_fewrows_any},
+    {"mfma16_64x64x64_4x2_sched_splitk", launch_mfma16_64x64x64_4x2_sched_splitk},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -126,6 +127,7 @@ enum VariantId {
   kNarrow = 25,
   kMfma16_128x128x32_w4_sched = 26,
   kFewRows = 27,
+  kMfma16_64x64x64_w8_sched_splitk = 28,
 };
 
 constexpr int kNoKernel = -100;
@@ -161,7 +163,9 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 // whole batch.
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
-//   * up to eight rows of C: the B-streaming few-rows kernel (bandwidth bound);
+//   * up to 32 rows of C (16 with B transposed): the B-streaming few-rows
+//     kernels (bandwidth bound), on the vector units for up to four rows of
+//     a moderate B, on the matrix cores otherwise;
 //   * up to 16 columns of C: the A-streaming few-columns kernel;
 //   * fewer than 16 rows otherwise: 64x64 tiles with K split over
 //     workgroups, bound by streaming B;
@@ -169,15 +173,17 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //     CU, 32-deep K slabs, the ordered slab loop) are fastest when the tiles
 //     are mostly inside C and their count fills the 256 CUs in whole rounds;
 //   * 128x128 tiles (the ordered loop) when there are at least as many tiles
-//     as CUs and they are mostly inside C: with two or more tiles per CU,
-//     four waves and 32-deep slabs (two workgroups per CU); with fewer, eight
-//     waves (two per SIMD), 64-deep slabs for K >= 1024 and 32-deep below;
-//     for K < 256 four waves with 16-deep slabs;
-//   * 128x64 tiles (same loop) when those number at least as many as CUs;
+//     as CUs and at least 90% of their area is inside C: with two or more
+//     tiles per CU, four waves and 32-deep slabs (two workgroups per CU);
+//     with fewer, eight waves (two per SIMD), 64-deep slabs for K >= 1024
+//     and 32-deep below; for K < 256 four waves with 16-deep slabs;
+//   * 128x64 tiles (same loop) when those number at least as many as CUs
+//     and are at least 85% inside C;
 //   * otherwise 64x64 tiles with eight waves and 64-deep slabs on the ordered
 //     loop (16-deep ones, four waves, for a short K that is not a multiple of
-//     64), splitting K over workgroups when the tiles cannot occupy half the
-//     CUs and K is long.
+//     64), splitting K over workgroups when the tiles cannot occupy the CUs
+//     and K is long (half of them from K = 1024, all from K = 2048), and on
+//     the ordered loop between one and two tiles per CU from K = 2048.
 // The ordered-loop variants fall back to their tile family's plain loop when
 // the tile is larger than C or K is shorter than one slab.
 
@@ -220,19 +226,22 @@ int choose_variant(const Problem &p) {
     const long long tail = t256 % cus;
     if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w4_sched;
   }
-  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 75) {
+  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 90) {
     if (p.K < 256) return kMfma32_128x128x16_w4;
     if (t128 >= 2 * cus) return kMfma16_128x128x32_w4_sched;
     return (p.K < 1024) ? kMfma32_128x128x32_w8_sched : kMfma16_128x128x64_w8_sched;
   }
   const long long t12864 = ((long long)p.M + 127) / 128 * (((long long)p.N + 63) / 64) * batch;
-  if (t12864 >= cus && p.K >= 256 && tile_fill_pct(p.M, p.N, 128, 64) >= 75)
+  if (t12864 >= cus && p.K >= 256 && tile_fill_pct(p.M, p.N, 128, 64) >= 85)
     return kMfma16_128x64x64_w8_sched;
   // A short K that is not a multiple of 64 would leave most of a 64-deep
   // slab empty: 16-deep slabs then.
   if (p.K < 256 && p.K % 64 != 0) return kMfma16_64x64x16_splitk;
-  // Too few tiles for half the CUs and a long K: split K over workgroups.
-  if (t64 < cus / 2 && p.K >= 1024) return kMfma16_64x64x64_w8_pipe_splitk;
+  // Too few tiles for the CUs and a long K: split K over workgroups.
+  if ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)) return kMfma16_64x64x64_w8_pipe_splitk;
+  // Between one and two tiles per CU with a long K: split K on the ordered
+  // loop, so that the CUs get two workgroups each.
+  if (t64 > cus && t64 < 2 * cus && p.K >= 2048) return kMfma16_64x64x64_w8_sched_splitk;
   return kMfma16_64x64x64_w8_sched;
 }
 

@@ -53,6 +53,7 @@ int launch_mfma32_256x256x32_4x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma32_128x128x32_4x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x64_4x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x128x64_4x2_sched(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x64_4x2_sched_splitk(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x128x32_2x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t stream);
 

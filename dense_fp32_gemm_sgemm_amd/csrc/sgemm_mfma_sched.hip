@@ -34,6 +34,11 @@ int launch_mfma16_128x128x32_2x2_sched(const Problem &p, hipStream_t s) {
 int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t s) {
   return launch_sched<16, 128, 64, 64, 4, 2, 2, 4>(p, s, launch_mfma16_64x64x64_4x2_sched);
 }
+// The same tile with K split over workgroups when the tiles cannot give the
+// CUs two workgroups each.
+int launch_mfma16_64x64x64_4x2_sched_splitk(const Problem &p, hipStream_t s) {
+  return launch_sched<16, 64, 64, 64, 4, 2, 2, 4, true>(p, s, launch_mfma16_64x64x64_4x2_pipe_splitk);
+}
 // 64x64 tile, eight waves with 16x32 wave tiles, 64-deep slabs.
 int launch_mfma16_64x64x64_4x2_sched(const Problem &p, hipStream_t s) {
   return launch_sched<16, 64, 64, 64, 4, 2, 2, 4>(p, s, launch_mfma16_64x64x64_4x2_pipe);

@@ -155,11 +155,22 @@ __device__ __forceinline__ void read_sched_operands(Operands<T> &o, const float 
   }
 }
 
+// SPLITK: blockIdx.y selects a range of k_per_split values of K (the last
+// range takes the rest, at least BK); the workgroup multiplies only that
+// range and adds alpha times its partial product into C with float atomics
+// (C was scaled by beta before the launch).
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
-          bool TB, bool RAGGED>
+          bool TB, bool RAGGED, bool SPLITK>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
-                                                                               int tiles_n, int group_m) {
+                                                                               int tiles_n, int group_m,
+                                                                               int k_per_split) {
   select_slice(p);
+  if constexpr (SPLITK) {
+    const int kb = (int)blockIdx.y * k_per_split;
+    p.A += TA ? (size_t)kb * (size_t)p.lda : (size_t)kb;
+    p.B += TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb;
+    p.K = (blockIdx.y + 1 == gridDim.y) ? p.K - kb : k_per_split;
+  }
   using T = MfmaTile<MI, BM, BN, BK, WAVES_M, WAVES_N, BPAD, TA, TB>;
   using Acc = typename std::conditional<MI == 32, floatx16, floatx4>::type;
   constexpr int kRegs = MI * MI / 64;
@@ -291,7 +302,21 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   // Epilogue: C = alpha*acc + beta*C for the rows and columns of this tile
   // (a shifted tile also computed some of its neighbour's).
   const int row0 = ms + wm * T::WTM;
-  if constexpr (PERMB) {
+  if constexpr (SPLITK) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+        const int col = ns + wn * T::WTN + (PERMB ? T::FN * li + j : j * MI + li);
+        if (col < n0) continue;
+#pragma unroll
+        for (int r = 0; r < kRegs; ++r) {
+          const int row = row0 + i * MI + acc_row<MI>(g, r);
+          if (row < m0) continue;
+          atomicAdd(p.C + (size_t)row * (size_t)p.ldc + col, p.alpha * acc[i][j][r]);
+        }
+      }
+  } else if constexpr (PERMB) {
     // FN consecutive columns per lane and row: one vector store when they are
     // FN-float aligned in memory (then a group lies wholly on one side of n0,
     // since n0 - ns is a multiple of FN), else one store per column of the
@@ -374,26 +399,67 @@ inline bool sched_ok(const Problem &p) {
          (reinterpret_cast<uintptr_t>(p.A) & 3) == 0 && (reinterpret_cast<uintptr_t>(p.B) & 3) == 0;
 }
 
+// Number of K ranges for a grid of `tiles` output tiles (over all batch
+// slices) with two workgroups per CU: none when the tiles alone give every
+// slot one, otherwise enough to, each range at least four slabs deep and a
+// multiple of BK; the last range takes the rest, which is kept at least BK.
+template <int BK>
+static int sched_splits(long long tiles, int K, int &k_per_split) {
+  const long long slots = 512;
+  long long splits = (tiles >= slots) ? 1 : (slots + tiles - 1) / tiles;
+  const long long max_splits = K / (4 * BK);
+  if (splits > max_splits) splits = max_splits;
+  k_per_split = K;
+  if (splits < 2) return 1;
+  long long kps = ((long long)K + splits - 1) / splits;
+  kps = (kps + BK - 1) / BK * BK;
+  splits = ((long long)K + kps - 1) / kps;
+  if (K - (splits - 1) * kps < BK) --splits;  // fold a short rest into the range before
+  if (splits < 2) return 1;
+  k_per_split = (int)kps;
+  return (int)splits;
+}
+
 // Launches sched_kernel when its preconditions hold, else `fallback` (a
-// variant of the same tile family that accepts every problem).
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD>
+// variant of the same tile family that accepts every problem).  SPLIT: K may
+// be split over workgroups when the tiles leave CUs idle.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD,
+          bool SPLIT = false>
 static int launch_sched(const Problem &p, hipStream_t stream,
                         int (*fallback)(const Problem &, hipStream_t)) {
   if (!sched_ok<BM, BN, BK>(p)) return fallback(p, stream);
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), 1u, (unsigned)p.batch);
+  int k_per_split = p.K;
+  const int splits = SPLIT ? sched_splits<BK>(tiles_m * tiles_n * p.batch, p.K, k_per_split) : 1;
+  if (splits > 1) {
+    if (splits > 65535) return -1;
+    // C = beta*C first; the split workgroups then add into it.
+    if (p.beta != 1.0f && launch_scale(p, stream) != 0) return -1;
+  }
+  // Every range but the last is a multiple of BK; the last decides.
+  const bool ragged = (p.K - (splits - 1) * k_per_split) % BK != 0;
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits, (unsigned)p.batch);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
-#define SG950_SCHED(TA_, TB_)                                                                      \
-  do {                                                                                             \
-    if (p.K % BK == 0)                                                                             \
-      hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, false>), \
-                         grid, block, 0, stream, p, tm, tn, group_m);                              \
-    else                                                                                           \
-      hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, true>), \
-                         grid, block, 0, stream, p, tm, tn, group_m);                              \
+#define SG950_SCHED_K(TA_, TB_, RG_, SK_)                                                            \
+  hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_>), \
+                     grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
+#define SG950_SCHED(TA_, TB_)                       \
+  do {                                              \
+    if (splits > 1) {                               \
+      if constexpr (SPLIT) {                        \
+        if (ragged)                                 \
+          SG950_SCHED_K(TA_, TB_, true, true);      \
+        else                                        \
+          SG950_SCHED_K(TA_, TB_, false, true);     \
+      }                                             \
+    } else if (ragged) {                            \
+      SG950_SCHED_K(TA_, TB_, true, false);         \
+    } else {                                        \
+      SG950_SCHED_K(TA_, TB_, false, false);        \
+    }                                               \
   } while (0)
   if (!p.ta && !p.tb) {
     SG950_SCHED(false, false);
@@ -405,6 +471,7 @@ static int launch_sched(const Problem &p, hipStream_t stream,
     SG950_SCHED(true, true);
   }
 #undef SG950_SCHED
+#undef SG950_SCHED_K
   return 0;
 }
 

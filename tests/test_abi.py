@@ -217,6 +217,27 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 
 
+def test_select_split_k_below_one_round(lib):
+    """Fewer 64x64 tiles than CUs with a long K: K is split over workgroups
+    ((64, 8192, 8192): 84 us split against 139 us on 128 tiles)."""
+    assert _op_choice(0, 0, 64, 8192, 8192) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 0, 128, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 0, 128, 4096, 1024) != "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 0, 1024, 1024, 1024) == "mfma16_64x64x64_4x2_sched"
+
+
+def test_select_tile_fill_and_split_between_rounds(lib):
+    """128-row tiles only when little of them sticks out of C (90% for
+    128x128, 85% for 128x64), else 64x64 tiles; between one and two of those
+    per CU with a long K, K split on the ordered loop."""
+    assert _op_choice(0, 0, 192, 8192, 8192) == "mfma16_64x64x64_4x2_sched_splitk"
+    assert _op_choice(0, 0, 320, 4096, 4096) == "mfma16_64x64x64_4x2_sched_splitk"
+    assert _op_choice(0, 0, 192, 16384, 4096) == "mfma16_64x64x64_4x2_sched"
+    assert _op_choice(0, 0, 448, 4096, 8192) == "mfma16_128x64x64_4x2_sched"
+    assert _op_choice(0, 0, 256, 4096, 4096) == "mfma16_64x64x64_4x2_sched"
+    assert _op_choice(0, 0, 3000, 3000, 3000) == "mfma16_128x128x32_2x2_sched"
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = sg.sgemm_status_string(st)

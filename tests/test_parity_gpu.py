@@ -289,6 +289,33 @@ def test_sched_path_ragged_k_and_unaligned(variant, shape):
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], shape, ta, tb))
 
 
+@pytest.mark.parametrize("shape", [(64, 64, 4096), (100, 130, 3001), (70, 200, 1290), (128, 192, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_sched_split_k(shape):
+    """The ordered loop with K split over workgroups (few tiles, long K): 16
+    ranges of one tile, a ragged last range (3001), a short rest folded into
+    the range before (1290 = 4 x 320 + 10), every orientation, beta != 0 (C
+    scaled first), a padded / misaligned copy; real to 1e-5, integer data
+    exactly (atomic adds of integers are exact in any order)."""
+    M, N, K = shape
+    v = VNAMES.index("mfma16_64x64x64_4x2_sched_splitk")
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        A, B, Cin = draw(M, N, K, seed=M + N + K, with_c=True)
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        say("sched split", shape, ta, tb)
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb, check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "split %s %s%s" % (shape, ta, tb))
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb,
+                lds=(As.shape[1] + 1, Bs.shape[1] + 3, N + 2), offsets=(3, 1, 2), check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "split %s %s%s padded" % (shape, ta, tb))
+        Ai, Bi, Ci = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+        Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+        Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+        C = run(Ais, Bis, Ci, 1.0, 1.0, variant=v, trans_a=ta, trans_b=tb)
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "split %s %s%s int" % (shape, ta, tb))
+
+
 @pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
 def test_sched_path_inf_in_repeated_k(variant):
     """Infs at a k that two slabs cover when the slab depth does not divide K,
