@@ -282,6 +282,55 @@ def measure_ceilings(samples: int = 15):
     return out
 
 
+def clock_under_load(fn, settle_s: float = 1.0, limit_s: float = 20.0):
+    """GPU clocks while `fn` (one launch) runs back to back: `amd-smi metric
+    -c` is started after `settle_s` seconds of load and the launches go on
+    until it has answered.  Returns the gfx clocks (MHz) of the busiest GPU it
+    lists, or None when the tool is missing or fails (best effort only)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    torch = _torch()
+    proc = None
+    t0 = time.time()
+    try:
+        while time.time() - t0 < limit_s:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            if proc is None and time.time() - t0 > settle_s:
+                proc = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                        stderr=subprocess.DEVNULL)
+            if proc is not None and proc.poll() is not None:
+                break
+        if proc is None:
+            return None
+        if proc.poll() is None:
+            proc.kill()
+            proc.wait()
+            return None
+        data = json.loads(proc.stdout.read())
+        best = None
+        for gpu in data.get("gpu_data", []):
+            clk = gpu.get("clock", {})
+            gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")
+                   and isinstance(v.get("clk", {}).get("value"), (int, float))]
+            top = [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")
+                   and isinstance(v.get("max_clk", {}).get("value"), (int, float))]
+            if gfx and (best is None or statistics.mean(gfx) > best["gfx_mhz_mean"]):
+                best = {"gfx_mhz_mean": round(statistics.mean(gfx), 1), "gfx_mhz_min": min(gfx),
+                        "gfx_mhz_max": max(gfx), "gfx_mhz_limit": max(top) if top else None,
+                        "source": "amd-smi metric -c during back-to-back launches of the timed kernel"}
+        return best
+    except Exception:
+        if proc is not None and proc.poll() is None:
+            proc.kill()
+            proc.wait()
+        return None
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The oracle (as it stands) on a bounded row sample of the 4096^3
     workload, on the host cores."""
@@ -423,6 +472,7 @@ def main(argv=None):
     value = flops(M, N, K) / (ms_step * 1e-3) / 1e9
     achieved = flops(M, N, K) / (kern_ms * 1e-3) / 1e12
 
+    clocks = None if args.no_ceilings else clock_under_load(prob.launcher(args.variant))
     ceilings = None if args.no_ceilings else measure_ceilings()
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     traffic = stored_traffic(vname)
@@ -451,6 +501,7 @@ def main(argv=None):
                      "kernel_ms_std": round(statistics.pstdev(per), 5),
                      "kernel_ms_min": round(min(per), 5), "kernel_ms_max": round(max(per), 5)},
         "cpu_baseline": cpu,
+        "gpu_clocks": clocks,
     }
     if ceilings:
         mf = ceilings["mfma_f32_32x32x2_tflops"]
