@@ -3,10 +3,11 @@
 //
 // It computes what mfma_kernel (sgemm_mfma.hpp) computes, with the same LDS
 // layout, operand reads and matrix-core blocks, and (when BK divides K) the
-// same order of the K-sum for every output.  The loop around them is different: the pages'
-// double buffering ("The road to a fast GEMM", section on prefetching the next
-// tile while computing the current one) is taken one step further, and the
-// instruction order inside a slab is pinned instead of left to the compiler:
+// same order of the K-sum for every output.  The loop around them is
+// different: the pages' double buffering ("The road to a fast GEMM", section
+// on prefetching the next tile while computing the current one) is taken one
+// step further, and the instruction order inside a slab is pinned instead of
+// left to the compiler:
 //
 //   * operand group q+1 of the slab is read from LDS while group q is
 //     multiplied, and those reads are issued first in the group, so they have
@@ -44,8 +45,11 @@
 // needs only 4-byte alignment for them, so leading dimensions, batch strides
 // and shifted tiles may put them anywhere.
 //
+// K may also be split over workgroups (SPLITK, blockIdx.y): each range runs
+// the same loop and adds its partial tile into C with atomics.
+//
 // Preconditions (checked on the host; other problems go to mfma_kernel):
-// K >= BK, M >= BM, N >= BN, A and B 4-byte aligned, no split of K.
+// K >= BK, M >= BM, N >= BN, A and B 4-byte aligned.
 #pragma once
 
 #include "sgemm_mfma.hpp"

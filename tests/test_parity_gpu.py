@@ -672,6 +672,45 @@ def test_few_columns_or_rows_automatic(shape):
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "narrow %s int" % (shape,))
 
 
+@pytest.mark.parametrize("case", [("auto", (300, 260, 530)), ("mfma32_256x256x32_2x2_sched", (512, 512, 256)),
+                                  ("mfma16_64x64x64_4x2_sched_splitk", (64, 64, 4096)),
+                                  ("mfma16_64x64x64_4x2_pipe_splitk", (64, 64, 4096)),
+                                  ("fewrows_m32", (12, 2048, 1024))], ids=lambda c: c[0])
+def test_graph_capture_replays(case):
+    """Library calls captured in a HIP graph (through torch's graph capture)
+    replay correctly, several times, with eager work in between: every kernel
+    the library records is an ordinary launch (split K clears C with its own
+    kernel, no memset node).  Integer data, so every replay must equal the
+    oracle exactly whatever the order of the split sums."""
+    name, (M, N, K) = case
+    v = -1 if name == "auto" else VNAMES.index(name)
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+    ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0)
+    dA, dB, dC0 = (torch.from_numpy(x).cuda() for x in (Ai, Bi, Ci))
+    out = torch.empty_like(dC0)
+    say("graph", name)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager warm-up on the capture stream's side
+        torch.add(dC0, 0.0, out=out)
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=v)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        torch.add(dC0, 0.0, out=out)  # restore C with a kernel, not a copy node
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=v)
+    for i in range(3):
+        junk = torch.randn(4096, device="cuda")
+        float(junk.abs().sum())       # eager work and a synchronisation between replays
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), "%s replay %d" % (name, i)
+
+
 def test_runs_on_a_side_stream():
     A, B, _ = draw(512, 384, 256, seed=13)
     dA = torch.from_numpy(A).cuda()
