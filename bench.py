@@ -336,8 +336,9 @@ def cpu_baseline(target_s: float = 12.0):
     workload, on the host cores."""
     import numpy as np
     import oracle
-    from workloads import HEADLINE, draw_workload
+    from workloads import HEADLINE, draw_workload, sweep_workloads
     A, B, _ = draw_workload(HEADLINE)
+    squares = {w.M: w for w in sweep_workloads()}
     oracle.load()
     rows = 32
     t0 = time.perf_counter()
@@ -349,10 +350,20 @@ def cpu_baseline(target_s: float = 12.0):
     oracle.gemm(A, B, rows=sel)
     dt = time.perf_counter() - t0
     gfl = flops(nrows, HEADLINE.N, HEADLINE.K) / dt / 1e9
+    # The other sizes the oracle is quoted at: all of 256^3, and a row sample
+    # of 8192^3 (about a second of CPU time together).
+    by_size = {}
+    for n, r in ((256, 256), (8192, 128)):
+        An, Bn, _ = draw_workload(squares[n])
+        t0 = time.perf_counter()
+        oracle.gemm(An, Bn, rows=np.arange(r))
+        by_size["%d^3 (%d rows)" % (n, r)] = round(flops(r, n, n) / (time.perf_counter() - t0) / 1e9, 3)
+        del An, Bn
     return {"value": round(gfl, 3), "unit": "GFLOPS", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": "first %d of 4096 output rows of the 4096^3 workload (fp64 i-k-j "
-                      "oracle, OpenMP over rows), %.1f s" % (nrows, dt)}
+                      "oracle, OpenMP over rows), %.1f s" % (nrows, dt),
+            "by_size": by_size}
 
 
 def stored_traffic(variant: str):
