@@ -307,19 +307,35 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   // (a shifted tile also computed some of its neighbour's).
   const int row0 = ms + wm * T::WTM;
   if constexpr (SPLITK) {
+    // The partial tile goes through LDS (the operand stages are free now), a
+    // chunk of RC rows at a time, so that the atomic adds of one instruction
+    // cover consecutive columns of a row: each one then touches as few cache
+    // lines as possible on its way to memory.
+    constexpr int TP = BN + 1;                  // staged row pitch (floats)
+    constexpr int FIT = (2 * T::A_STAGE) / TP;  // rows that fit in the A stages
+    constexpr int RC = FIT >= BM ? BM : (FIT >= BM / 2 ? BM / 2 : BM / 4);
+    static_assert(RC * TP <= 2 * T::A_STAGE && BM % RC == 0, "a chunk of rows must fit in the A stages");
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
+    for (int c0 = 0; c0 < BM; c0 += RC) {
+      __syncthreads();  // the stage (operands, or the previous chunk) is no longer read
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int col = ns + wn * T::WTN + (PERMB ? T::FN * li + j : j * MI + li);
-        if (col < n0) continue;
+      for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-        for (int r = 0; r < kRegs; ++r) {
-          const int row = row0 + i * MI + acc_row<MI>(g, r);
-          if (row < m0) continue;
-          atomicAdd(p.C + (size_t)row * (size_t)p.ldc + col, p.alpha * acc[i][j][r]);
-        }
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < kRegs; ++r) {
+            const int tr = wm * T::WTM + i * MI + acc_row<MI>(g, r) - c0;
+            const int tc = wn * T::WTN + (PERMB ? T::FN * li + j : j * MI + li);
+            if (tr >= 0 && tr < RC) As[tr * TP + tc] = acc[i][j][r];
+          }
+      __syncthreads();
+      for (int e = tid; e < RC * BN; e += NT) {
+        const int tr = e / BN, tc = e % BN;
+        const int row = ms + c0 + tr, col = ns + tc;
+        if (row < m0 || col < n0) continue;
+        atomicAdd(p.C + (size_t)row * (size_t)p.ldc + col, p.alpha * As[tr * TP + tc]);
       }
+    }
   } else if constexpr (PERMB) {
     // FN consecutive columns per lane and row: one vector store when they are
     // FN-float aligned in memory (then a group lies wholly on one side of n0,
