@@ -316,6 +316,27 @@ def test_sched_split_k(shape):
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "split %s %s%s int" % (shape, ta, tb))
 
 
+@pytest.mark.parametrize("name", ["mfma16_64x64x64_4x2_sched_splitk", "mfma16_64x64x64_4x2_pipe_splitk"])
+def test_split_k_batched_and_nan_c(name):
+    """K split over workgroups together with a strided batch (blockIdx.y the
+    range, blockIdx.z the slice; slices with gaps), integer data exactly; and
+    beta = 0 over a NaN-filled C, which the scaling launch must overwrite with
+    zeros before the ranges add into it."""
+    v = VNAMES.index(name)
+    rng = np.random.default_rng(77)
+    batch, M, N, K = 3, 64, 96, 2048
+    Ai = rng.integers(-4, 5, (batch, M, K)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (batch, K, N)).astype(np.float32)
+    Ci = rng.integers(-4, 5, (batch, M, N)).astype(np.float32)
+    say("split batched", name)
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=v, gap=5)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, name + " batched", exact=True)
+    A, B, _ = draw(M, N, K, seed=78)
+    say("split nan C", name)
+    C = run(A, B, None, 1.0, 0.0, variant=v, check_outside=True)  # C starts NaN
+    check_real(C, A, B, None, 1.0, 0.0, name + " beta 0 over NaN")
+
+
 @pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
 def test_sched_path_inf_in_repeated_k(variant):
     """Infs at a k that two slabs cover when the slab depth does not divide K,
