@@ -23,14 +23,21 @@
  *
  * Asynchrony.  A call validates its arguments on the host, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the default stream) and
- * returns without synchronising.  C must not overlap A or B.
+ * returns without synchronising.  C must not overlap A or B.  Everything a
+ * call enqueues is a kernel launch (C is cleared or scaled by a kernel, never
+ * by a memset or copy), so calls may be captured into a HIP graph once one
+ * ordinary call on the device has checked it.
  *
  * Arithmetic.  Strict FP32: products and sums are IEEE single precision with
  * round-to-nearest-even (fused multiply-add where the hardware fuses); no input
  * is rounded to a narrower format.  The order of the K-sum is unspecified, so
  * results on real-valued data may differ from another correct implementation
  * by rounding; on integer-valued data whose partial sums stay below 2^24 they
- * are exact.
+ * are exact.  Repeating a call gives bitwise the same C, except on the
+ * variants that split K over workgroups (names ending in "_splitk", and the
+ * split form of the few-rows kernel for M <= 8 with a large B, chosen
+ * automatically when there are few output tiles and a long K): their partial
+ * sums are added into C with atomics in the order the hardware runs them.
  *
  * Special cases (BLAS conventions; the pages are silent on them):
  *   - M == 0 or N == 0: nothing is done.
