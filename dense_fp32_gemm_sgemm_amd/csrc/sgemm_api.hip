@@ -163,9 +163,9 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 // whole batch.
 //   * tiny problems (MNK <= 2^20) are launch-latency bound: one lane per
 //     output wins;
-//   * up to 32 rows of C (16 with B transposed): the B-streaming few-rows
-//     kernels (bandwidth bound), on the vector units for up to four rows of
-//     a moderate B, on the matrix cores otherwise;
+//   * up to 32 rows of C: the B-streaming few-rows kernels (bandwidth
+//     bound), on the vector units for up to four rows of a moderate B, on the
+//     matrix cores otherwise;
 //   * up to 16 columns of C: the A-streaming few-columns kernel;
 //   * fewer than 16 rows otherwise: 64x64 tiles with K split over
 //     workgroups, bound by streaming B;
@@ -200,14 +200,16 @@ int choose_variant(const Problem &p) {
   // Few rows and enough of B: bound by streaming B.  The vector-unit kernel
   // for up to four rows of a moderate B read in full-K strips, the matrix-core
   // kernel for up to 32 rows when its column strips fill the CUs (with a
-  // transposed B, which it reads along k, up to 16 rows).
+  // transposed B, above 16 rows only for wide strips or a K up to 4096).
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20)) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
     if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&
         (p.M <= 2 || p.N >= 4096))
       return kSkinny;
-    if (p.tb ? (p.M <= 16 && nb >= 2048) : nb >= (p.M <= 16 ? 1024 : 2048)) return kFewRows;
+    const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
+                              : nb >= (p.M <= 16 ? 1024 : 2048);
+    if (fewrows) return kFewRows;
     if (valu_ok) return kSkinny;
   }
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)

@@ -20,8 +20,9 @@
 //     the strip (16 CPL columns); a lane's A values for the group (row l%16,
 //     k0 + 4s .. 4s + 3) are one 16-byte load and serve all CPL blocks;
 //   * B transposed (stored N x K): lane j of slot s reads four consecutive k
-//     of its column, k0 + 4s .. 4s + 3, as one 16-byte load, and value e
-//     feeds instruction e of four, with the matching four k of A.
+//     of each of its columns j + 16c (c < CPL), k0 + 4s .. 4s + 3, as one
+//     16-byte load per column, and value e feeds instruction e of four, with
+//     the matching four k of A, one A load serving all CPL column blocks.
 //
 // Loads of eight steps are issued before their first use.  Rows past M read
 // row M-1 and columns past N read column N-1 (in bounds, never stored); k
@@ -41,14 +42,14 @@ constexpr int kFewWaves = 8;   // waves per workgroup, each a K range
 constexpr int kFewUnroll = 8;  // steps whose loads are in flight together
 }  // namespace
 
-// NR: 16-row blocks of C (M <= 16 NR).  CPL: columns per lane (untransposed
-// B; 1 for a transposed B).  VB: an untransposed B's rows hold whole
+// NR: 16-row blocks of C (M <= 16 NR).  CPL: column blocks per lane (the
+// strip is 16 CPL columns).  VB: an untransposed B's rows hold whole
 // CPL-column groups (N % CPL == 0), so a lane's columns are one load.
 template <int NR, int CPL, bool TA, bool TB, bool VB>
 __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange) {
   select_slice(p);
-  constexpr int NB = TB ? 1 : CPL;        // 16 x 16 blocks per wave and row block
-  constexpr int NC = TB ? 16 : 16 * CPL;  // columns per workgroup
+  constexpr int NB = CPL;       // 16 x 16 blocks per wave and row block
+  constexpr int NC = 16 * CPL;  // columns per workgroup
   __shared__ floatx4 red[kFewWaves][NR * NB][64];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,11 +162,14 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
       }
     }
   } else {
-    const int bcol = min(n0 + li, p.N - 1);  // column of op(B) (row of stored B)
-    const float *brow = p.B + (size_t)bcol * ldb;
-    auto load_b4 = [&](int k) -> floatx4 {
+    // Column block c of the strip: columns n0 + 16c + j; lane j reads row
+    // n0 + 16c + j of the stored B (clamped to N-1).
+    const float *brow[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) brow[c] = p.B + (size_t)min(n0 + 16 * c + li, p.N - 1) * ldb;
+    auto load_b4 = [&](int c, int k) -> floatx4 {
       floatx4 v;
-      __builtin_memcpy(&v, brow + k, sizeof(v));
+      __builtin_memcpy(&v, brow[c] + k, sizeof(v));
       return v;
     };
     auto load_a4 = [&](int r, int k) -> floatx4 {
@@ -178,47 +182,59 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
         return floatx4{q[0], q[lda], q[2 * lda], q[3 * lda]};
       }
     };
-    // Groups of 16 k: slot sl takes k = kb + 16t + 4sl .. + 3.
+    // Groups of 16 k: slot sl takes k = kb + 16t + 4sl .. + 3.  A lane's A
+    // vector serves all CPL column blocks, its B vector all NR row blocks.
+    constexpr int UN = (kFewUnroll / (NR * CPL)) > 1 ? kFewUnroll / (NR * CPL) : 2;
     const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
     int t = 0;
-    for (; t + kFewUnroll / NR <= nfull; t += kFewUnroll / NR) {
-      floatx4 a[kFewUnroll / NR][NR], b[kFewUnroll / NR];
+    for (; t + UN <= nfull; t += UN) {
+      floatx4 a[UN][NR], b[UN][CPL];
 #pragma unroll
-      for (int u = 0; u < kFewUnroll / NR; ++u) {
+      for (int u = 0; u < UN; ++u) {
         const int k = kb + 16 * (t + u) + 4 * sl;
 #pragma unroll
         for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
-        b[u] = load_b4(k);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) b[u][c] = load_b4(c, k);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kFewUnroll / NR; ++u)
+      for (int u = 0; u < UN; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int r = 0; r < NR; ++r)
-            acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][e], acc[r][0], 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][c][e], acc[r][c], 0, 0, 0);
     }
     for (; t < nfull; ++t) {
       const int k = kb + 16 * t + 4 * sl;
-      const floatx4 b = load_b4(k);
+      floatx4 b[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) b[c] = load_b4(c, k);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const floatx4 a = load_a4(r, k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[r][0], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[c][e], acc[r][c], 0, 0, 0);
       }
     }
     // The rest of the range (fewer than 16 k): element by element, k < ke only.
     const int kt = kb + 16 * nfull;
     if (kt < ke) {
-      floatx4 b;
+      floatx4 b[CPL];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = kt + 4 * sl + e;
-        const bool in = k < ke;
-        b[e] = in ? brow[in ? k : kb] : 0.0f;
-      }
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = kt + 4 * sl + e;
+          const bool in = k < ke;
+          b[c][e] = in ? brow[c][in ? k : kb] : 0.0f;
+        }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         floatx4 a;
@@ -231,13 +247,16 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
           a[e] = in ? av : 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc[r][0], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[c][e], acc[r][c], 0, 0, 0);
       }
     }
   }
 
   // Lane l holds rows 16 rb + 4*(l/16) + r of row block rb; block e's column
-  // j = l%16 is column CPL*j + e of the strip (B untransposed) or j
+  // j = l%16 is column CPL*j + e of the strip (B untransposed) or 16e + j
   // (transposed).
 #pragma unroll
   for (int rb = 0; rb < NR; ++rb)
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] += v[r];
       }
-      const int col = TB ? n0 + li : n0 + CPL * li + e;
+      const int col = TB ? n0 + 16 * e + li : n0 + CPL * li + e;
       if (col >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -291,7 +310,12 @@ void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int kran
 template <int NR>
 void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl) {
   if (p.tb) {
-    launch_fewrows_ta<NR, 1, true>(p, grid, stream, krange, false);
+    if (cpl == 4)
+      launch_fewrows_ta<NR, 4, true>(p, grid, stream, krange, false);
+    else if (cpl == 2)
+      launch_fewrows_ta<NR, 2, true>(p, grid, stream, krange, false);
+    else
+      launch_fewrows_ta<NR, 1, true>(p, grid, stream, krange, false);
     return;
   }
   const bool vb = p.N % cpl == 0;
@@ -306,19 +330,17 @@ void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int kran
 
 int launch_fewrows(const Problem &p, hipStream_t stream) {
   if (p.M < 1 || p.M > 32) return -1;
-  // Columns per lane (untransposed B): the widest that still gives the strips
-  // at least one workgroup per CU over the batch.
+  // Column blocks per lane: the most that still give the strips at least one
+  // workgroup per CU over the batch.
   int cpl = 1;
-  if (!p.tb) {
-    for (int c = 4; c >= 2; c /= 2) {
-      const long long strips = ((long long)p.N + 16 * c - 1) / (16 * c);
-      if (strips * p.batch >= 256) {
-        cpl = c;
-        break;
-      }
+  for (int c = 4; c >= 2; c /= 2) {
+    const long long strips = ((long long)p.N + 16 * c - 1) / (16 * c);
+    if (strips * p.batch >= 256) {
+      cpl = c;
+      break;
     }
   }
-  const int nc = p.tb ? 16 : 16 * cpl;
+  const int nc = 16 * cpl;
   const long long blocks = ((long long)p.N + nc - 1) / nc;
   if (blocks > INT_MAX) return -1;
   // Eight K ranges, each a multiple of 16 k (the groups of the four slots).

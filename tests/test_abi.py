@@ -200,8 +200,9 @@ def _op_choice(ta, tb, M, N, K, batch=1):
 
 def test_select_few_rows(lib):
     """Up to four rows of a moderate untransposed B on the vector-unit kernel,
-    up to 32 rows (16 with B transposed) on the matrix-core kernel when its
-    column strips fill the CUs, split-K tiles otherwise."""
+    up to 32 rows on the matrix-core kernel when its column strips fill the
+    CUs (with B transposed, above 16 rows only for wide strips or K <= 4096),
+    split-K tiles otherwise."""
     assert _op_choice(0, 0, 1, 4096, 4096) == "skinny_m8"
     assert _op_choice(0, 0, 4, 8192, 8192) == "skinny_m8"
     assert _op_choice(0, 0, 4, 16384, 16384) == "fewrows_m32"       # B too large for full-K strips
@@ -212,7 +213,9 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 0, 24, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 1, 16, 4096, 4096) == "fewrows_m32"
     assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
-    assert _op_choice(0, 1, 24, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 1, 24, 4096, 4096) == "fewrows_m32"
+    assert _op_choice(0, 1, 24, 8192, 8192) == "fewrows_m32"
+    assert _op_choice(0, 1, 24, 4096, 16384) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 8, 512, 4096) == "skinny_m8"                # too few strips
     assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 

@@ -663,7 +663,8 @@ def test_few_rows_matrix_core_kernel(shape):
 def test_few_rows_matrix_core_kernel_batched(batch, N):
     """Enough slices for the 4- and 2-column lane loads (16 and 8 slices of
     1000 columns), a column count they do not divide (1001), and a small batch
-    with one-column loads; integer data exactly, slices with gaps."""
+    with one-column loads; B as stored and transposed (4, 2 and 1 column
+    blocks per lane); integer data exactly, slices with gaps."""
     rng = np.random.default_rng(batch * 7 + N)
     M, K = (12 if batch % 2 == 0 else 20), 300
     v = VNAMES.index("fewrows_m32")
@@ -673,6 +674,12 @@ def test_few_rows_matrix_core_kernel_batched(batch, N):
     say("few rows batched", batch, N)
     out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=v, gap=3)
     check_batched(out, Ai, Bi, Ci, 1.0, 1.0, "few rows batch %d N %d" % (batch, N), exact=True)
+    # B transposed (stored N x K per slice): the same column-block choice
+    Bt = np.ascontiguousarray(np.transpose(Bi, (0, 2, 1)))
+    say("few rows batched B^T", batch, N)
+    out = run_batched(Ai, Bt, Ci, 1.0, 1.0, variant=v, gap=3, trans_b=True)
+    check_batched(out, Ai, Bt, Ci, 1.0, 1.0, "few rows batch %d N %d B^T" % (batch, N), exact=True,
+                  tb=True)
 
 
 @pytest.mark.parametrize("shape", [(4096, 1, 4096), (1000, 7, 3000), (3000, 15, 100), (65536, 8, 1024),
