@@ -169,21 +169,23 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //   * up to 16 columns of C: the A-streaming few-columns kernel;
 //   * fewer than 16 rows otherwise: 64x64 tiles with K split over
 //     workgroups, bound by streaming B;
-//   * 256x256 tiles (four waves with 128x128 wave tiles, one workgroup per
-//     CU, 32-deep K slabs, the ordered slab loop) are fastest when the tiles
-//     are mostly inside C and their count fills the 256 CUs in whole rounds;
-//   * 128x128 tiles (the ordered loop) when there are at least as many tiles
-//     as CUs and at least 90% of their area is inside C: with two or more
-//     tiles per CU, four waves and 32-deep slabs (two workgroups per CU);
-//     with fewer, eight waves (two per SIMD), 64-deep slabs for K >= 1024
-//     and 32-deep below; for K < 256 four waves with 16-deep slabs;
-//   * 128x64 tiles (same loop) when those number at least as many as CUs
-//     and are at least 85% inside C;
-//   * otherwise 64x64 tiles with eight waves and 64-deep slabs on the ordered
-//     loop (16-deep ones, four waves, for a short K that is not a multiple of
-//     64), splitting K over workgroups when the tiles cannot occupy the CUs
-//     and K is long (half of them from K = 1024, all from K = 2048), and on
-//     the ordered loop between one and two tiles per CU from K = 2048.
+//   * a short K (< 256): 256x256 tiles when they are mostly inside C and
+//     fill the 256 CUs in whole rounds, then 128x128 tiles with 16-deep slabs
+//     when there are as many as CUs and 90% of their area is inside C, else
+//     64x64 tiles (16-deep slabs when K is not a multiple of 64);
+//   * K split over workgroups on 64x64 tiles when those cannot occupy the
+//     CUs and K is long (half of them from K = 1024, all from K = 2048);
+//   * otherwise the ordered slab loop on the tile family with the best
+//     predicted rate -- 256x256 (four waves, 128x128 wave tiles, one
+//     workgroup per CU), 128x128 (four waves, 32-deep slabs, two workgroups
+//     per CU), 128x128 (eight waves, 64-deep slabs), 128x64, or 64x64 (eight
+//     waves, two workgroups per CU): each family's measured steady rate times
+//     the share of its tiles' area inside C times the share of its CU-rounds
+//     the tiles keep busy.  A tile count just past a whole number of rounds
+//     (an odd M or N adding a row or column of tiles) leaves the last round
+//     nearly empty, and smaller tiles then win; K split over workgroups
+//     on the ordered loop is taken between one and two 64x64 tiles per CU
+//     from K = 2048 when its rate beats the best family.
 // The ordered-loop variants fall back to their tile family's plain loop when
 // the tile is larger than C or K is shorter than one slab.
 
@@ -191,6 +193,50 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 long long tile_fill_pct(int M, int N, int TM, int TN) {
   const long long tm = ((long long)M + TM - 1) / TM, tn = ((long long)N + TN - 1) / TN;
   return (long long)M * N * 100 / (tm * TM * tn * TN);
+}
+
+constexpr long long kCus = 256;  // compute units of an MI355X
+
+// Tile families of the ordered slab loop, for the choice among them.  Rates
+// are the steady TFLOP/s of each family measured on MI355X over the shape
+// sweeps with whole rounds of tiles (at K >= 2048 and at K = 1024); a shape
+// gets rate x (share of the tiles' area inside C) x (share of the CU-rounds
+// the tiles keep busy).  Rounds count tiles per CU: 256 tiles make a round
+// whether one or two workgroups share a CU.  For the families that fit two
+// workgroups on a CU, an odd last round runs one workgroup alone on a CU at
+// `lone` of the paired rate per workgroup.
+struct TileFamily {
+  int variant, bm, bn;
+  double rate_long, rate_short, lone;  // lone = 0: one workgroup per CU
+};
+constexpr TileFamily kTileFamilies[] = {
+    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 0.0},
+    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 0.95},
+    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 0.0},
+    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 0.0},
+    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 0.92},  // last: the split-K base
+};
+constexpr int kNumTileFamilies = sizeof(kTileFamilies) / sizeof(kTileFamilies[0]);
+// Split K on 64x64 tiles against the same tiles unsplit, with every CU busy.
+constexpr double kSplitKEfficiency = 0.85;
+
+// Steady rate of a family at this K (linear between K = 1024 and 2048).
+double family_rate_full(const TileFamily &f, const Problem &p) {
+  if (p.K >= 2048) return f.rate_long;
+  if (p.K <= 1024) return f.rate_short;
+  return f.rate_short + (f.rate_long - f.rate_short) * (p.K - 1024) / 1024.0;
+}
+
+// Predicted rate of a family on this problem: steady rate x area fill x
+// round fill.
+double family_rate(const TileFamily &f, const Problem &p) {
+  const long long tm = ((long long)p.M + f.bm - 1) / f.bm, tn = ((long long)p.N + f.bn - 1) / f.bn;
+  const long long tiles = tm * tn * (long long)p.batch;
+  const double fill = (double)p.M * (double)p.N / ((double)(tm * f.bm) * (double)(tn * f.bn));
+  const long long rounds = (tiles + kCus - 1) / kCus;
+  const double span = f.lone > 0.0 ? (double)(rounds / 2 * 2) + (double)(rounds % 2) / f.lone
+                                   : (double)rounds;
+  return family_rate_full(f, p) * fill * (double)tiles / ((double)kCus * span);
 }
 
 int choose_variant(const Problem &p) {
@@ -223,28 +269,36 @@ int choose_variant(const Problem &p) {
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
   const long long t64 = ((long long)p.M + 63) / 64 * (((long long)p.N + 63) / 64) * batch;
-  const long long cus = 256;
-  if (t256 >= cus && tile_fill_pct(p.M, p.N, 256, 256) >= 75) {
-    const long long tail = t256 % cus;
-    if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w4_sched;
+  const long long cus = kCus;
+  // A short K: wide tiles with 16-deep slabs when they fill the CUs, else
+  // 64x64 tiles (16-deep slabs when K is not a multiple of 64, since a
+  // 64-deep slab would be mostly padding).
+  if (p.K < 256) {
+    if (t256 >= cus && tile_fill_pct(p.M, p.N, 256, 256) >= 75) {
+      const long long tail = t256 % cus;
+      if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w4_sched;
+    }
+    if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 90) return kMfma32_128x128x16_w4;
+    return (p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_sched;
   }
-  if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 90) {
-    if (p.K < 256) return kMfma32_128x128x16_w4;
-    if (t128 >= 2 * cus) return kMfma16_128x128x32_w4_sched;
-    return (p.K < 1024) ? kMfma32_128x128x32_w8_sched : kMfma16_128x128x64_w8_sched;
-  }
-  const long long t12864 = ((long long)p.M + 127) / 128 * (((long long)p.N + 63) / 64) * batch;
-  if (t12864 >= cus && p.K >= 256 && tile_fill_pct(p.M, p.N, 128, 64) >= 85)
-    return kMfma16_128x64x64_w8_sched;
-  // A short K that is not a multiple of 64 would leave most of a 64-deep
-  // slab empty: 16-deep slabs then.
-  if (p.K < 256 && p.K % 64 != 0) return kMfma16_64x64x16_splitk;
   // Too few tiles for the CUs and a long K: split K over workgroups.
   if ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)) return kMfma16_64x64x64_w8_pipe_splitk;
-  // Between one and two tiles per CU with a long K: split K on the ordered
-  // loop, so that the CUs get two workgroups each.
-  if (t64 > cus && t64 < 2 * cus && p.K >= 2048) return kMfma16_64x64x64_w8_sched_splitk;
-  return kMfma16_64x64x64_w8_sched;
+  // Otherwise the ordered-loop tile family with the best predicted rate.
+  int best = kMfma16_64x64x64_w8_sched;
+  double best_rate = -1.0;
+  for (const TileFamily &f : kTileFamilies) {
+    const double r = family_rate(f, p);
+    if (r > best_rate) best_rate = r, best = f.variant;
+  }
+  // Between one and two 64x64 tiles per CU with a long K: K split over
+  // workgroups on the ordered loop gives every CU two workgroups, at the cost
+  // of the atomics and the beta-scaling launch.
+  if (t64 > cus && t64 < 2 * cus && p.K >= 2048) {
+    const double split_rate = kSplitKEfficiency * family_rate_full(kTileFamilies[kNumTileFamilies - 1], p) *
+                              (double)tile_fill_pct(p.M, p.N, 64, 64) / 100.0;
+    if (split_rate > best_rate) return kMfma16_64x64x64_w8_sched_splitk;
+  }
+  return best;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other

@@ -169,12 +169,35 @@ def test_batched_select_small_slices(lib):
 
 def test_select_128_tiles(lib):
     """128x128 tiles: four waves (two workgroups per CU) once there are two
-    tiles per CU, eight waves when one round of tiles leaves each CU one."""
+    tiles per CU, eight waves with 64-deep slabs when one round leaves each CU
+    one tile; 128x128 over 256x256 tiles when the 256x256 tiles leave their
+    last round mostly empty ((10000, 10000, 1000): 134 vs 120 TFLOP/s)."""
     assert _batched_choice(1, 8192, 1024, 8192) == "mfma16_128x128x32_2x2_sched"
     assert _batched_choice(1, 1024, 8192, 256) == "mfma16_128x128x32_2x2_sched"
     assert _batched_choice(1, 2048, 2048, 2048) == "mfma16_128x128x64_4x2_sched"
-    assert _batched_choice(1, 2048, 2048, 512) == "mfma32_128x128x32_4x2_sched"
     assert _batched_choice(2, 2048, 2048, 2048) == "mfma16_128x128x32_2x2_sched"
+    assert _batched_choice(1, 256, 16384, 4096) == "mfma16_128x128x64_4x2_sched"
+    assert _batched_choice(1, 10000, 10000, 1000) == "mfma16_128x128x32_2x2_sched"
+
+
+def test_select_last_round_tail(lib):
+    """A tile count just past whole rounds of the 256 CUs (an odd M or N adds
+    a row or column of tiles) leaves the last round nearly empty: smaller
+    tiles then win (measured, TFLOP/s: (2047, 2049, 2047) 102 vs 68 on
+    128x128 tiles, (4095, 4097, 4095) 124 vs 117, (8191, 1025, 8191) 119 vs
+    105 on 128x64, 3000^3 126 vs 104, (6144, 1024, 4096) 135 vs 108 on
+    128x128), in every orientation."""
+    f64 = "mfma16_64x64x64_4x2_sched"
+    for shape in ((2047, 2049, 2047), (4095, 4097, 4095), (8191, 1025, 8191), (2047, 4097, 4095),
+                  (4096, 4097, 1024), (3000, 3000, 3000), (3072, 3072, 3072), (1536, 1536, 1536)):
+        assert _batched_choice(1, *shape) == f64, shape
+    for ta in (0, 1):
+        for tb in (0, 1):
+            assert _op_choice(ta, tb, 4095, 4097, 1023) == f64
+    assert _batched_choice(1, 6144, 1024, 4096) == "mfma16_128x64x64_4x2_sched"
+    # whole rounds keep the large tiles
+    assert _batched_choice(1, 4096, 4096, 1023) == "mfma32_256x256x32_2x2_sched"
+    assert _batched_choice(1, 8192, 8192, 8192) == "mfma32_256x256x32_2x2_sched"
 
 
 def test_select_narrow_problems(lib):
@@ -230,15 +253,14 @@ def test_select_split_k_below_one_round(lib):
 
 
 def test_select_tile_fill_and_split_between_rounds(lib):
-    """128-row tiles only when little of them sticks out of C (90% for
-    128x128, 85% for 128x64), else 64x64 tiles; between one and two of those
-    per CU with a long K, K split on the ordered loop."""
+    """128-row tiles lose to 64x64 ones when much of them sticks out of C;
+    between one and two 64x64 tiles per CU with a long K, K split on the
+    ordered loop ((192, 8192, 8192): 121 vs 102 TFLOP/s on 128x64 tiles)."""
     assert _op_choice(0, 0, 192, 8192, 8192) == "mfma16_64x64x64_4x2_sched_splitk"
     assert _op_choice(0, 0, 320, 4096, 4096) == "mfma16_64x64x64_4x2_sched_splitk"
     assert _op_choice(0, 0, 192, 16384, 4096) == "mfma16_64x64x64_4x2_sched"
     assert _op_choice(0, 0, 448, 4096, 8192) == "mfma16_128x64x64_4x2_sched"
     assert _op_choice(0, 0, 256, 4096, 4096) == "mfma16_64x64x64_4x2_sched"
-    assert _op_choice(0, 0, 3000, 3000, 3000) == "mfma16_128x128x32_2x2_sched"
 
 
 def test_status_strings(lib):
