@@ -849,3 +849,32 @@ def test_rectangular_and_ragged(w):
         assert oracle.exact_match(C[rows], ref), w.name + " int"
     else:
         check_exact(C, Ai, Bi, None, 1.0, 0.0, w.name + " int")
+
+
+# Shapes whose tile count sits just past whole rounds of the CUs, where the
+# automatic choice takes 64x64 (or 128x64) tiles; the automatic path, with
+# the selection pinned so the intended kernel is the one checked.
+TAIL_SHAPES = [((2047, 2049, 2047), "mfma16_64x64x64_4x2_sched"),
+               ((3000, 3000, 3000), "mfma16_64x64x64_4x2_sched"),
+               ((8191, 1025, 8191), "mfma16_64x64x64_4x2_sched"),
+               ((6144, 1024, 4096), "mfma16_128x64x64_4x2_sched")]
+
+
+@pytest.mark.parametrize("shape,expect", TAIL_SHAPES, ids=lambda v: "x".join(map(str, v))
+                         if isinstance(v, tuple) else v)
+def test_last_round_tail_shapes(shape, expect):
+    M, N, K = shape
+    v = sg.sgemm_select_variant(M, N, K, 1.0, 1, K, 1, N, 0.0, 1, N)
+    assert sg.sgemm_variant_name(v) == expect
+    A, B, _ = draw(M, N, K, seed=M + N + K)
+    say("tail shape", shape, expect)
+    C = run(A, B)
+    _sampled_check(A, B, C, 1.0, 0.0, None, 192, 192, M, "tail %s" % (shape,))
+    Ai, Bi, _ = draw(M, N, K, seed=M + N + K, kind="int")
+    C = run(Ai, Bi)
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 96)), [M - 1]]))
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 96)), [N - 1]]))
+    ref, _ = oracle.gemm(Ai, Bi, rows=rows)
+    assert oracle.exact_match(C[rows], ref), "tail %s int rows" % (shape,)
+    ref, _ = oracle.gemm(Ai, Bi, cols=cols)
+    assert oracle.exact_match(C[:, cols], ref), "tail %s int cols" % (shape,)
