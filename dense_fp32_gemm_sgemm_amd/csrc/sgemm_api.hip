@@ -7,6 +7,7 @@
 #include "../../include/sgemm.h"
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
+#include "sgemm_sched.hpp"
 
 #include <atomic>
 #include <climits>
@@ -95,6 +96,8 @@ const Variant kVariants[] = {
     {"mfma16_128x128x32_2x2_sched", launch_mfma16_128x128x32_2x2_sched},
     {"fewrows_m32", launch_fewrows_any},
     {"mfma16_64x64x64_4x2_sched_splitk", launch_mfma16_64x64x64_4x2_sched_splitk},
+    {"mfma16_32x64x64_2x2_sched", launch_mfma16_32x64x64_2x2_sched},
+    {"mfma16_32x64x64_2x2_sched_splitk", launch_mfma16_32x64x64_2x2_sched_splitk},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -128,6 +131,8 @@ enum VariantId {
   kMfma16_128x128x32_w4_sched = 26,
   kFewRows = 27,
   kMfma16_64x64x64_w8_sched_splitk = 28,
+  kMfma16_32x64x64_w4_sched = 29,
+  kMfma16_32x64x64_w4_sched_splitk = 30,
 };
 
 constexpr int kNoKernel = -100;
@@ -174,18 +179,20 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //     when there are as many as CUs and 90% of their area is inside C, else
 //     64x64 tiles (16-deep slabs when K is not a multiple of 64);
 //   * K split over workgroups on 64x64 tiles when those cannot occupy the
-//     CUs and K is long (half of them from K = 1024, all from K = 2048);
-//   * otherwise the ordered slab loop on the tile family with the best
-//     predicted rate -- 256x256 (four waves, 128x128 wave tiles, one
-//     workgroup per CU), 128x128 (four waves, 32-deep slabs, two workgroups
-//     per CU), 128x128 (eight waves, 64-deep slabs), 128x64, or 64x64 (eight
-//     waves, two workgroups per CU): each family's measured steady rate times
-//     the share of its tiles' area inside C times the share of its CU-rounds
-//     the tiles keep busy.  A tile count just past a whole number of rounds
-//     (an odd M or N adding a row or column of tiles) leaves the last round
-//     nearly empty, and smaller tiles then win; K split over workgroups
-//     on the ordered loop is taken between one and two 64x64 tiles per CU
-//     from K = 2048 when its rate beats the best family.
+//     CUs and K is long (half of them from K = 1024, all from K = 2048),
+//     unless 32-row tiles would leave fewer rows of their tiles empty;
+//   * otherwise the ordered slab loop on the tile family, with K split over
+//     workgroups or not, with the best predicted rate -- 256x256 (four
+//     waves, 128x128 wave tiles, one workgroup per CU), 128x128 (four waves,
+//     32-deep slabs, two workgroups per CU), 128x128 (eight waves, 64-deep
+//     slabs), 128x64, 64x64 (eight waves, two workgroups per CU) or 32x64
+//     (four waves, three workgroups per CU), the last two also split: each
+//     family's measured steady rate times the share of its tiles' area
+//     inside C times the share of the CU time its tiles keep busy, and for a
+//     split grid times the share of the rate a split of that depth keeps.  A
+//     tile count just past a whole number of rounds (an odd M or N adding a
+//     row or column of tiles) leaves the last round nearly empty, and smaller
+//     tiles then win; so do 32-row tiles for M just past a multiple of 64.
 // The ordered-loop variants fall back to their tile family's plain loop when
 // the tile is larger than C or K is shorter than one slab.
 
@@ -200,43 +207,91 @@ constexpr long long kCus = 256;  // compute units of an MI355X
 // Tile families of the ordered slab loop, for the choice among them.  Rates
 // are the steady TFLOP/s of each family measured on MI355X over the shape
 // sweeps with whole rounds of tiles (at K >= 2048 and at K = 1024); a shape
-// gets rate x (share of the tiles' area inside C) x (share of the CU-rounds
-// the tiles keep busy).  Rounds count tiles per CU: 256 tiles make a round
-// whether one or two workgroups share a CU.  For the families that fit two
-// workgroups on a CU, an odd last round runs one workgroup alone on a CU at
-// `lone` of the paired rate per workgroup.
+// gets rate x (share of the tiles' area inside C) x (share of the CU time
+// the tiles keep busy).  The busiest CU holds n = ceil(tiles / 256) tiles;
+// a family that fits s workgroups on a CU runs them s at a time at the
+// steady rate, and a last group of j < s at `partial[j]` of it, so the CU
+// takes s floor(n/s) + (n mod s) / partial[n mod s] steady tile-times.
 struct TileFamily {
   int variant, bm, bn;
-  double rate_long, rate_short, lone;  // lone = 0: one workgroup per CU
+  double rate_long, rate_short;
+  int slots;
+  double partial[3];  // [j]: rate with j < slots workgroups on the CU
 };
 constexpr TileFamily kTileFamilies[] = {
-    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 0.0},
-    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 0.95},
-    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 0.0},
-    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 0.0},
-    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 0.92},  // last: the split-K base
+    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 1, {0.0, 0.0, 0.0}},
+    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 2, {0.0, 0.95, 0.0}},
+    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 1, {0.0, 0.0, 0.0}},
+    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 1, {0.0, 0.0, 0.0}},
+    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 2, {0.0, 0.92, 0.0}},
+    {kMfma16_32x64x64_w4_sched, 32, 64, 120.0, 112.0, 3, {0.0, 0.75, 0.93}},
 };
-constexpr int kNumTileFamilies = sizeof(kTileFamilies) / sizeof(kTileFamilies[0]);
-// Split K on 64x64 tiles against the same tiles unsplit, with every CU busy.
-constexpr double kSplitKEfficiency = 0.85;
-
-// Steady rate of a family at this K (linear between K = 1024 and 2048).
-double family_rate_full(const TileFamily &f, const Problem &p) {
-  if (p.K >= 2048) return f.rate_long;
-  if (p.K <= 1024) return f.rate_short;
-  return f.rate_short + (f.rate_long - f.rate_short) * (p.K - 1024) / 1024.0;
+// The same loops with K split over workgroups (atomics after a beta-scaling
+// launch), priced by the unsplit family's rate at the range depth.
+struct SplitFamily {
+  int variant;
+  TileFamily base;
+};
+constexpr SplitFamily kSplitFamilies[] = {
+    {kMfma16_64x64x64_w8_sched_splitk, kTileFamilies[4]},
+    {kMfma16_32x64x64_w4_sched_splitk, kTileFamilies[5]},
+};
+// Share of the unsplit rate kept by a split grid whose ranges are k deep
+// (fitted to split-K runs on MI355X: 0.94-0.98 at k = 4096, 0.92-0.93 at
+// 2048, 0.76 at 1024; the atomic adds of the tile and the shorter pipeline
+// both weigh more as the range shrinks).
+double split_efficiency(double k) {
+  const double r = 4096.0 / k;
+  return 1.0 / (1.0 + 0.02 * r * r);
 }
+
+// Steady rate of a family for k-deep work per tile (linear between k = 1024
+// and 2048).
+double family_rate_full(const TileFamily &f, double k) {
+  if (k >= 2048.0) return f.rate_long;
+  if (k <= 1024.0) return f.rate_short;
+  return f.rate_short + (f.rate_long - f.rate_short) * (k - 1024.0) / 1024.0;
+}
+
+long long family_tiles(const TileFamily &f, const Problem &p) {
+  return ((long long)p.M + f.bm - 1) / f.bm * (((long long)p.N + f.bn - 1) / f.bn) * (long long)p.batch;
+}
+
+// Share of the family's tile area that lies inside C.
+double family_fill(const TileFamily &f, const Problem &p) {
+  const long long tm = ((long long)p.M + f.bm - 1) / f.bm, tn = ((long long)p.N + f.bn - 1) / f.bn;
+  return (double)p.M * (double)p.N / ((double)(tm * f.bm) * (double)(tn * f.bn));
+}
+
+// Share of the CU time that `units` workgroups of a family keep busy.
+double round_fill(const TileFamily &f, long long units) {
+  const long long n = (units + kCus - 1) / kCus;  // on the busiest CU
+  const long long rest = n % f.slots;
+  const double span = (double)(n - rest) + (rest ? (double)rest / f.partial[rest] : 0.0);
+  return (double)units / ((double)kCus * span);
+}
+
+// The ordered loop's own preconditions on the shape (else it runs the plain
+// fallback loop, which the rates do not describe).
+bool family_fits(const TileFamily &f, const Problem &p) { return p.M >= f.bm && p.N >= f.bn; }
 
 // Predicted rate of a family on this problem: steady rate x area fill x
 // round fill.
 double family_rate(const TileFamily &f, const Problem &p) {
-  const long long tm = ((long long)p.M + f.bm - 1) / f.bm, tn = ((long long)p.N + f.bn - 1) / f.bn;
-  const long long tiles = tm * tn * (long long)p.batch;
-  const double fill = (double)p.M * (double)p.N / ((double)(tm * f.bm) * (double)(tn * f.bn));
-  const long long rounds = (tiles + kCus - 1) / kCus;
-  const double span = f.lone > 0.0 ? (double)(rounds / 2 * 2) + (double)(rounds % 2) / f.lone
-                                   : (double)rounds;
-  return family_rate_full(f, p) * fill * (double)tiles / ((double)kCus * span);
+  return family_rate_full(f, (double)p.K) * family_fill(f, p) * round_fill(f, family_tiles(f, p));
+}
+
+// Predicted rate of a split family (0 when it would not split): the unsplit
+// rate at the range depth x the split efficiency x area fill x round fill of
+// tiles x ranges.
+double split_rate(const SplitFamily &sf, const Problem &p) {
+  const long long tiles = family_tiles(sf.base, p);
+  int kps = p.K;
+  const int splits = sched_splits<64>(tiles, p.K, kps);
+  if (splits < 2) return 0.0;
+  const double k = (double)p.K / splits;
+  return family_rate_full(sf.base, k) * split_efficiency(k) * family_fill(sf.base, p) *
+         round_fill(sf.base, tiles * splits);
 }
 
 int choose_variant(const Problem &p) {
@@ -281,22 +336,26 @@ int choose_variant(const Problem &p) {
     if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 90) return kMfma32_128x128x16_w4;
     return (p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_sched;
   }
-  // Too few tiles for the CUs and a long K: split K over workgroups.
-  if ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)) return kMfma16_64x64x64_w8_pipe_splitk;
-  // Otherwise the ordered-loop tile family with the best predicted rate.
+  // Too few tiles for the CUs and a long K: split K over workgroups on 64x64
+  // tiles, unless 32-row tiles leave fewer rows empty (then the scores below
+  // weigh both).
+  const bool rows32_fill_better =
+      p.M >= 32 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
+  if (!rows32_fill_better && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
+    return kMfma16_64x64x64_w8_pipe_splitk;
+  // Otherwise the ordered-loop tile family, split or not, with the best
+  // predicted rate.
   int best = kMfma16_64x64x64_w8_sched;
   double best_rate = -1.0;
   for (const TileFamily &f : kTileFamilies) {
+    if (!family_fits(f, p)) continue;
     const double r = family_rate(f, p);
     if (r > best_rate) best_rate = r, best = f.variant;
   }
-  // Between one and two 64x64 tiles per CU with a long K: K split over
-  // workgroups on the ordered loop gives every CU two workgroups, at the cost
-  // of the atomics and the beta-scaling launch.
-  if (t64 > cus && t64 < 2 * cus && p.K >= 2048) {
-    const double split_rate = kSplitKEfficiency * family_rate_full(kTileFamilies[kNumTileFamilies - 1], p) *
-                              (double)tile_fill_pct(p.M, p.N, 64, 64) / 100.0;
-    if (split_rate > best_rate) return kMfma16_64x64x64_w8_sched_splitk;
+  for (const SplitFamily &sf : kSplitFamilies) {
+    if (!family_fits(sf.base, p)) continue;
+    const double r = split_rate(sf, p);
+    if (r > best_rate) best_rate = r, best = sf.variant;
   }
   return best;
 }

@@ -56,6 +56,10 @@ int launch_mfma16_128x128x64_4x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_64x64x64_4x2_sched_splitk(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x128x32_2x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t stream);
+// 32x64 tiles (four waves, three workgroups per CU) for row counts just past
+// a multiple of 64, unsplit and with K split over workgroups.
+int launch_mfma16_32x64x64_2x2_sched(const Problem &p, hipStream_t stream);
+int launch_mfma16_32x64x64_2x2_sched_splitk(const Problem &p, hipStream_t stream);
 
 // Few rows of C (M <= 8): streams B across every CU, K split over
 // workgroups, float atomics into C (scaled by beta first).  Returns -1 for

@@ -851,13 +851,17 @@ def test_rectangular_and_ragged(w):
         check_exact(C, Ai, Bi, None, 1.0, 0.0, w.name + " int")
 
 
-# Shapes whose tile count sits just past whole rounds of the CUs, where the
-# automatic choice takes 64x64 (or 128x64) tiles; the automatic path, with
-# the selection pinned so the intended kernel is the one checked.
-TAIL_SHAPES = [((2047, 2049, 2047), "mfma16_64x64x64_4x2_sched"),
+# Shapes whose tile count sits just past whole rounds of the CUs, or whose
+# row count sits just past a multiple of 64, where the automatic choice takes
+# smaller tiles (32x64, 64x64, 128x64, K split or not); the automatic path,
+# with the selection pinned so the intended kernel is the one checked.
+TAIL_SHAPES = [((2047, 2049, 2047), "mfma16_32x64x64_2x2_sched"),
                ((3000, 3000, 3000), "mfma16_64x64x64_4x2_sched"),
                ((8191, 1025, 8191), "mfma16_64x64x64_4x2_sched"),
-               ((6144, 1024, 4096), "mfma16_128x64x64_4x2_sched")]
+               ((6144, 1024, 4096), "mfma16_128x64x64_4x2_sched"),
+               ((96, 8192, 8192), "mfma16_32x64x64_2x2_sched_splitk"),
+               ((160, 4096, 4096), "mfma16_32x64x64_2x2_sched_splitk"),
+               ((320, 8192, 8192), "mfma16_32x64x64_2x2_sched")]
 
 
 @pytest.mark.parametrize("shape,expect", TAIL_SHAPES, ids=lambda v: "x".join(map(str, v))
