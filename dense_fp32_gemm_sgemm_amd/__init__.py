@@ -15,20 +15,23 @@ and the functions raise ``LibraryMissing`` when the library is not built.
 """
 from __future__ import annotations
 
-from ._lib import (EXPORTS, LIBRARY, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM,  # noqa: F401
-                   SGEMM_ERR_LAUNCH, SGEMM_ERR_LD, SGEMM_ERR_OP, SGEMM_ERR_PTR,
-                   SGEMM_ERR_STRIDE, SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N,
-                   SGEMM_OP_T, LibraryMissing, load, sgemm, sgemm_ceiling_copy,
-                   sgemm_ceiling_fma, sgemm_ceiling_mfma, sgemm_ex, sgemm_num_variants, sgemm_op,
-                   sgemm_op_ex, sgemm_op_select_variant, sgemm_select_variant,
-                   sgemm_status_string, sgemm_strided_batched, sgemm_strided_batched_ex,
-                   sgemm_strided_batched_select_variant, sgemm_variant_name, sgemm_version)
+from ._lib import (EXPORTS, LIBRARY, SGEMM_ATOMICS_ALLOWED,  # noqa: F401
+                   SGEMM_ATOMICS_NOT_ALLOWED, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM, SGEMM_ERR_LAUNCH,
+                   SGEMM_ERR_LD, SGEMM_ERR_OP, SGEMM_ERR_PTR, SGEMM_ERR_STRIDE,
+                   SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N, SGEMM_OP_T,
+                   LibraryMissing, load, sgemm, sgemm_ceiling_copy, sgemm_ceiling_fma,
+                   sgemm_ceiling_mfma, sgemm_ex, sgemm_get_atomics_mode, sgemm_num_variants,
+                   sgemm_op, sgemm_op_ex, sgemm_op_select_variant, sgemm_select_variant,
+                   sgemm_set_atomics_mode, sgemm_status_string, sgemm_strided_batched,
+                   sgemm_strided_batched_ex, sgemm_strided_batched_select_variant,
+                   sgemm_variant_name, sgemm_version)
 
 __all__ = ["gemm", "gemm_batched", "variant_names", "sgemm", "sgemm_ex", "sgemm_op",
            "sgemm_op_ex", "sgemm_op_select_variant", "sgemm_strided_batched",
            "sgemm_strided_batched_ex", "sgemm_strided_batched_select_variant", "sgemm_num_variants",
            "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
-           "sgemm_version", "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
+           "sgemm_version", "sgemm_set_atomics_mode", "sgemm_get_atomics_mode",
+           "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
            "LibraryMissing", "SgemmError"]
 
 

@@ -27,12 +27,15 @@ SGEMM_ERR_STRIDE = -8
 SGEMM_NO_KERNEL = -100
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
+SGEMM_ATOMICS_NOT_ALLOWED = 0
+SGEMM_ATOMICS_ALLOWED = 1
 
 # Every exported symbol, as declared in include/*.h.
 EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_strided_batched",
            "sgemm_strided_batched_ex", "sgemm_num_variants", "sgemm_variant_name",
            "sgemm_select_variant", "sgemm_op_select_variant", "sgemm_strided_batched_select_variant",
-           "sgemm_status_string", "sgemm_version",
+           "sgemm_status_string", "sgemm_version", "sgemm_set_atomics_mode",
+           "sgemm_get_atomics_mode",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy")
 
 _lock = threading.Lock()
@@ -77,6 +80,10 @@ def _declare(lib):
     lib.sgemm_status_string.restype = ctypes.c_char_p
     lib.sgemm_version.argtypes = []
     lib.sgemm_version.restype = c_int
+    lib.sgemm_set_atomics_mode.argtypes = [c_int]
+    lib.sgemm_set_atomics_mode.restype = c_int
+    lib.sgemm_get_atomics_mode.argtypes = []
+    lib.sgemm_get_atomics_mode.restype = c_int
     dp = ctypes.POINTER(ctypes.c_double)
     lib.sgemm_ceiling_mfma.argtypes = [c_int, c_int, c_int, vp, vp, dp]
     lib.sgemm_ceiling_mfma.restype = c_int
@@ -163,6 +170,15 @@ def sgemm_status_string(status: int) -> str:
 
 def sgemm_version() -> int:
     return load().sgemm_version()
+
+
+def sgemm_set_atomics_mode(mode) -> int:
+    """SGEMM_ATOMICS_ALLOWED or SGEMM_ATOMICS_NOT_ALLOWED (process-wide)."""
+    return load().sgemm_set_atomics_mode(mode)
+
+
+def sgemm_get_atomics_mode() -> int:
+    return load().sgemm_get_atomics_mode()
 
 
 def sgemm_ceiling_mfma(shape, blocks, iters, sink, stream=0):

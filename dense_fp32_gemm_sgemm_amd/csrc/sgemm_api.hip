@@ -294,7 +294,18 @@ double split_rate(const SplitFamily &sf, const Problem &p) {
          round_fill(sf.base, tiles * splits);
 }
 
-int choose_variant(const Problem &p) {
+// Process-wide atomics mode (sgemm_set_atomics_mode).
+std::atomic<int> g_atomics_mode{SGEMM_ATOMICS_ALLOWED};
+
+// True when the vector-unit few-rows kernel takes its full-K form (one pass,
+// fixed-order sums) rather than its split form (atomics).
+bool skinny_full_k(const Problem &p) {
+  return !p.tb && ((long long)p.N + 31) / 32 * p.batch >= 64 && (long long)p.N * p.K <= (1LL << 26);
+}
+
+// The automatic choice.  atomics: whether variants that add partial sums into
+// C with atomics (an order the hardware decides) may be taken.
+int choose_variant(const Problem &p, bool atomics) {
   const long long batch = p.batch;
   const long long work = (long long)p.M * p.N * p.K * batch;
   const long long nk = (long long)p.N * p.K * batch;
@@ -311,16 +322,20 @@ int choose_variant(const Problem &p) {
     const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
                               : nb >= (p.M <= 16 ? 1024 : 2048);
     if (fewrows) return kFewRows;
-    if (valu_ok) return kSkinny;
+    if (valu_ok && (atomics || skinny_full_k(p))) return kSkinny;
   }
+  // 64x64 tiles with 16-deep slabs, split over K when atomics are allowed.
+  const int m16 = atomics ? kMfma16_64x64x16_splitk : kMfma16_64x64x16;
   // (the one-lane kernel reads a transposed B with a stride: small tiles then)
-  if (work <= (1LL << 20)) return p.tb ? kMfma16_64x64x16_splitk : kSimple;
+  if (work <= (1LL << 20)) return p.tb ? m16 : kSimple;
   // Few columns: the A-streaming few-columns kernel.
   if (p.N <= 16 && p.M >= 16) return kNarrow;
   // Few rows: bound by streaming B; 64x64 tiles with K split over workgroups
   // (16-deep slabs for a short ragged K).
   if (p.M < 16 || p.N < 16)
-    return (p.K < 256 && p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_pipe_splitk;
+    return (p.K < 256 && p.K % 64 != 0)
+               ? m16
+               : (atomics ? kMfma16_64x64x64_w8_pipe_splitk : kMfma16_64x64x64_w8_pipe);
   const long long t256 = ((long long)p.M + 255) / 256 * (((long long)p.N + 255) / 256) * batch;
   const long long t128 = ((long long)p.M + 127) / 128 * (((long long)p.N + 127) / 128) * batch;
   const long long t64 = ((long long)p.M + 63) / 64 * (((long long)p.N + 63) / 64) * batch;
@@ -334,14 +349,14 @@ int choose_variant(const Problem &p) {
       if (tail == 0 || tail * 100 >= cus * 85 || t256 >= 4 * cus) return kMfma32_256x256x32_w4_sched;
     }
     if (t128 >= cus && tile_fill_pct(p.M, p.N, 128, 128) >= 90) return kMfma32_128x128x16_w4;
-    return (p.K % 64 != 0) ? kMfma16_64x64x16_splitk : kMfma16_64x64x64_w8_sched;
+    return (p.K % 64 != 0) ? m16 : kMfma16_64x64x64_w8_sched;
   }
   // Too few tiles for the CUs and a long K: split K over workgroups on 64x64
   // tiles, unless 32-row tiles leave fewer rows empty (then the scores below
   // weigh both).
   const bool rows32_fill_better =
       p.M >= 32 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
-  if (!rows32_fill_better && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
+  if (atomics && !rows32_fill_better && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
     return kMfma16_64x64x64_w8_pipe_splitk;
   // Otherwise the ordered-loop tile family, split or not, with the best
   // predicted rate.
@@ -353,7 +368,7 @@ int choose_variant(const Problem &p) {
     if (r > best_rate) best_rate = r, best = f.variant;
   }
   for (const SplitFamily &sf : kSplitFamilies) {
-    if (!family_fits(sf.base, p)) continue;
+    if (!atomics || !family_fits(sf.base, p)) continue;
     const double r = split_rate(sf, p);
     if (r > best_rate) best_rate = r, best = sf.variant;
   }
@@ -392,7 +407,9 @@ int run(int opA, int opB, int M, int N, int K, float alpha, const float *A, int 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Problem p{M,  N,  K,  alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T,
             sa, sb, sc, batch};
-  const int v = no_product ? -1 : ((variant >= 0) ? variant : choose_variant(p));
+  const int v = no_product ? -1
+                           : ((variant >= 0) ? variant
+                                             : choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED));
   // Grids hold at most 65535 batch slices: larger batches go in chunks.
   for (int z0 = 0; z0 < batch; z0 += kMaxGridZ) {
     Problem q = p;
@@ -414,7 +431,7 @@ int select(int opA, int opB, int M, int N, int K, float alpha, const float *A, i
   if (M == 0 || N == 0 || batch == 0 || alpha == 0.0f || K == 0) return kNoKernel;
   const Problem p{M,   N,   K,   alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc,
                   opA == SGEMM_OP_T, opB == SGEMM_OP_T, sa, sb, sc, batch};
-  return choose_variant(p);
+  return choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
 }
 
 }  // namespace
@@ -502,6 +519,14 @@ const char *sgemm_status_string(int status) {
   }
 }
 
-int sgemm_version(void) { return 3; }
+int sgemm_version(void) { return 4; }
+
+int sgemm_set_atomics_mode(int mode) {
+  if (mode != SGEMM_ATOMICS_ALLOWED && mode != SGEMM_ATOMICS_NOT_ALLOWED) return SGEMM_ERR_OP;
+  sg950::g_atomics_mode.store(mode);
+  return SGEMM_OK;
+}
+
+int sgemm_get_atomics_mode(void) { return sg950::g_atomics_mode.load(); }
 
 }  // extern "C"

@@ -19,7 +19,8 @@
  *
  * Ownership.  Every matrix pointer is a device pointer on the calling thread's
  * current HIP device, owned by the caller.  The library allocates no device
- * memory, keeps no per-call state and may be called from several threads.
+ * memory, keeps no per-call state (its one setting is the process-wide
+ * atomics mode below) and may be called from several threads.
  *
  * Asynchrony.  A call validates its arguments on the host, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the default stream) and
@@ -38,6 +39,8 @@
  * split form of the few-rows kernel for M <= 8 with a large B, chosen
  * automatically when there are few output tiles and a long K): their partial
  * sums are added into C with atomics in the order the hardware runs them.
+ * sgemm_set_atomics_mode(SGEMM_ATOMICS_NOT_ALLOWED) keeps the automatic
+ * choice off those forms, so that every repeated call is bitwise the same.
  *
  * Special cases (BLAS conventions; the pages are silent on them):
  *   - M == 0 or N == 0: nothing is done.
@@ -178,8 +181,29 @@ int sgemm_strided_batched_select_variant(int opA, int opB, int M, int N, int K, 
 /* Short English description of a status code (never NULL). */
 const char *sgemm_status_string(int status);
 
-/* Interface version, currently 3 (2 added sgemm_op, 3 the strided batches). */
+/* Interface version, currently 4 (2 added sgemm_op, 3 the strided batches, 4
+ * the atomics mode). */
 int sgemm_version(void);
+
+/*
+ * Atomics mode, process-wide (default SGEMM_ATOMICS_ALLOWED).  The operation
+ * fixes C = alpha*A*B + beta*C but not the order of the K-sum ("The road to a
+ * fast GEMM", section "The problem and the ceiling"), so variants that split
+ * K over workgroups and add their partial sums into C with atomics are
+ * correct, but their last bits depend on the order the hardware runs the
+ * adds.  With SGEMM_ATOMICS_NOT_ALLOWED the automatic choice (variant -1 and
+ * the *_select_variant functions) takes only variants that write every
+ * element of C once from sums formed in a fixed order, at some cost in speed
+ * on problems with few output tiles and a long K; variants requested by
+ * index run as asked.  sgemm_set_atomics_mode returns SGEMM_OK, or
+ * SGEMM_ERR_OP for any other mode value (the mode is then unchanged).  The
+ * mode is read once per call; a change made while another thread is inside
+ * a call applies from that thread's next call.
+ */
+#define SGEMM_ATOMICS_NOT_ALLOWED 0
+#define SGEMM_ATOMICS_ALLOWED 1
+int sgemm_set_atomics_mode(int mode);
+int sgemm_get_atomics_mode(void);
 
 #ifdef __cplusplus
 }

@@ -56,7 +56,7 @@ def test_variant_registry(lib):
     assert names[0] == "simple"
     assert any(x.startswith("mfma32") for x in names) and any(x.startswith("valu") for x in names)
     assert sg.sgemm_variant_name(n) == "" and sg.sgemm_variant_name(-1) == ""
-    assert sg.sgemm_version() == 3
+    assert sg.sgemm_version() == 4
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails or returns before any HIP call
@@ -336,3 +336,55 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.load()
+
+
+def _skinny_full_k(tb, N, K, batch):
+    """The vector-unit few-rows kernel's one-pass form (no atomics): B not
+    transposed, at least 64 strips of 32 columns over the batch, N*K <= 2^26."""
+    return not tb and -(-N // 32) * batch >= 64 and N * K <= (1 << 26)
+
+
+def test_atomics_mode_setting(lib):
+    assert sg.sgemm_get_atomics_mode() == sg.SGEMM_ATOMICS_ALLOWED
+    try:
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_NOT_ALLOWED) == sg.SGEMM_OK
+        assert sg.sgemm_get_atomics_mode() == sg.SGEMM_ATOMICS_NOT_ALLOWED
+        assert sg.sgemm_set_atomics_mode(7) == sg.SGEMM_ERR_OP
+        assert sg.sgemm_get_atomics_mode() == sg.SGEMM_ATOMICS_NOT_ALLOWED
+    finally:
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED) == sg.SGEMM_OK
+    assert sg.sgemm_get_atomics_mode() == sg.SGEMM_ATOMICS_ALLOWED
+
+
+def test_atomics_not_allowed_selection(lib):
+    """With atomics not allowed the automatic choice takes no K-split variant
+    and the vector-unit few-rows kernel only in its one-pass form, over a grid
+    of shapes, orientations and batches that includes every case where the
+    default choice splits; with atomics allowed again the choice is the
+    default one."""
+    dims = (1, 3, 8, 15, 24, 48, 64, 96, 127, 192, 320, 512, 1024, 4097)
+    ks = (17, 100, 256, 1024, 4096, 16384, 100000)
+    default, split_seen = {}, 0
+    for ta in (0, 1):
+        for tb in (0, 1):
+            for batch in (1, 7):
+                for M in dims:
+                    for N in dims:
+                        for K in ks:
+                            if M * N * K * batch > 2 ** 37:
+                                continue
+                            name = _op_choice(ta, tb, M, N, K, batch)
+                            default[(ta, tb, batch, M, N, K)] = name
+                            split_seen += name.endswith("_splitk")
+    assert split_seen > 100
+    try:
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_NOT_ALLOWED) == sg.SGEMM_OK
+        for (ta, tb, batch, M, N, K) in default:
+            name = _op_choice(ta, tb, M, N, K, batch)
+            assert not name.endswith("_splitk"), (ta, tb, batch, M, N, K, name)
+            if name == "skinny_m8":
+                assert _skinny_full_k(tb, N, K, batch), (ta, tb, batch, M, N, K)
+    finally:
+        sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
+    for key, name in list(default.items())[::37]:
+        assert _op_choice(key[0], key[1], key[3], key[4], key[5], key[2]) == name

@@ -882,3 +882,39 @@ def test_last_round_tail_shapes(shape, expect):
     assert oracle.exact_match(C[rows], ref), "tail %s int rows" % (shape,)
     ref, _ = oracle.gemm(Ai, Bi, cols=cols)
     assert oracle.exact_match(C[:, cols], ref), "tail %s int cols" % (shape,)
+
+
+# Shapes whose default choice adds partial sums with atomics: K-split tiles
+# (few tiles, long K) and the split form of the vector-unit few-rows kernel.
+ATOMIC_SHAPES = [(64, 8192, 8192), (96, 8192, 8192), (8, 512, 4096), (300, 40, 100000)]
+
+
+@pytest.mark.parametrize("shape", ATOMIC_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_atomics_not_allowed_repeatable(shape):
+    """With atomics not allowed, the automatic choice leaves the atomic forms
+    and two calls on the same inputs give bitwise the same C, within the
+    tolerance of the oracle."""
+    M, N, K = shape
+    default = sg.sgemm_variant_name(sg.sgemm_select_variant(M, N, K, 1.0, 1, K, 1, N, 0.0, 1, N))
+    assert default.endswith("_splitk") or default == "skinny_m8", default
+    A, B, _ = draw(M, N, K, seed=7 + M)
+    try:
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_NOT_ALLOWED) == sg.SGEMM_OK
+        name = sg.sgemm_variant_name(sg.sgemm_select_variant(M, N, K, 1.0, 1, K, 1, N, 0.0, 1, N))
+        assert not name.endswith("_splitk") and name != "skinny_m8", name
+        say("no atomics", shape, name)
+        C1 = run(A, B)
+        C2 = run(A, B)
+    finally:
+        sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32)), "%s: repeated calls differ" % (shape,)
+    if M * N * K > 2 ** 32:
+        _sampled_check(A, B, C1, 1.0, 0.0, None, 128, 128, M, "no atomics %s" % (shape,))
+    else:
+        check_real(C1, A, B, None, 1.0, 0.0, "no atomics %s" % (shape,))
+    say("atomics", shape, default)
+    C3 = run(A, B)
+    if M * N * K > 2 ** 32:
+        _sampled_check(A, B, C3, 1.0, 0.0, None, 128, 128, M, "atomics %s" % (shape,))
+    else:
+        check_real(C3, A, B, None, 1.0, 0.0, "atomics %s" % (shape,))
