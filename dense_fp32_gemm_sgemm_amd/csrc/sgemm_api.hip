@@ -313,7 +313,12 @@ int choose_variant(const Problem &p, bool atomics) {
   // for up to four rows of a moderate B read in full-K strips, the matrix-core
   // kernel for up to 32 rows when its column strips fill the CUs (with a
   // transposed B, above 16 rows only for wide strips or a K up to 4096).
-  if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20)) {
+  // Exactly 32 rows with a large B go to 32-row tiles instead (split over K
+  // when they are few), which stream B as well with better matrix-core use
+  // ((32, 8192, 8192): 48.6 against 60.7 us, (32, 4096, 16384) 55.8 against
+  // 82.3); below N*K = 2^25 the few-rows kernel stays ahead.
+  const bool rows32_tiles = atomics && p.M == 32 && nk >= (1LL << 25);
+  if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
     if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&

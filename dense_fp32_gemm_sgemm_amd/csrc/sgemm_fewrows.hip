@@ -24,12 +24,15 @@
 //     16-byte load per column, and value e feeds instruction e of four, with
 //     the matching four k of A, one A load serving all CPL column blocks.
 //
-// Loads of eight steps are issued before their first use.  Rows past M read
+// Loads of eight steps are issued before their first use (with B
+// untransposed and four or more blocks per wave, one group's loads are
+// issued before the previous group's matrix instructions).  Rows past M read
 // row M-1 and columns past N read column N-1 (in bounds, never stored); k
 // past the end of a wave's range is skipped by selection, so a NaN or Inf
 // outside the matrices cannot leak in.  The eight waves' blocks are added
-// through LDS in a fixed order and C = alpha*sum + beta*C is written once:
-// one launch, no atomics, deterministic.
+// through LDS in a fixed order, each block by its own wave, and
+// C = alpha*sum + beta*C is written once: one launch, no atomics,
+// deterministic.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
 
@@ -102,28 +105,69 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
     // A values for the group are one vector.
     const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
     int t = 0;
-    for (; t + kFewUnroll / 4 <= nfull; t += kFewUnroll / 4) {
-      Cols b[kFewUnroll / 4][4];
-      floatx4 a[kFewUnroll / 4][NR];
+    if constexpr (NR * CPL >= 4) {
+      // Four or more blocks per wave: a group's matrix instructions take long
+      // enough that the next group's loads are issued before them (two sets
+      // of operand registers, the loop unrolled by two so that each set has
+      // fixed registers).
+      struct Group {
+        Cols b[4];
+        floatx4 a[NR];
+      };
+      auto issue = [&](Group &x, int g) {
+        const int k = kb + 16 * g + 4 * sl;
 #pragma unroll
-      for (int u = 0; u < kFewUnroll / 4; ++u) {
-        const int k = kb + 16 * (t + u) + 4 * sl;
+        for (int r = 0; r < NR; ++r) x.a[r] = load_a4(r, k);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[u][e] = load_b(k + e);
-      }
-      // All loads of the batch are issued before the first use.
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kFewUnroll / 4; ++u)
+        for (int e = 0; e < 4; ++e) x.b[e] = load_b(k + e);
+      };
+      auto multiply = [&](const Group &x) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-              acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][e].v[c], acc[r][c], 0, 0, 0);
+              acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a[r][e], x.b[e].v[c], acc[r][c], 0, 0, 0);
+      };
+      if (nfull > 0) {
+        Group x0, x1;
+        issue(x0, 0);
+        for (; t + 2 <= nfull; t += 2) {
+          issue(x1, t + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          multiply(x0);
+          if (t + 2 < nfull) issue(x0, t + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          multiply(x1);
+        }
+        if (t < nfull) multiply(x0);  // x0 holds group nfull - 1
+        t = nfull;
+      }
+    } else {
+      for (; t + kFewUnroll / 4 <= nfull; t += kFewUnroll / 4) {
+        Cols b[kFewUnroll / 4][4];
+        floatx4 a[kFewUnroll / 4][NR];
+#pragma unroll
+        for (int u = 0; u < kFewUnroll / 4; ++u) {
+          const int k = kb + 16 * (t + u) + 4 * sl;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[u][e] = load_b(k + e);
+        }
+        // All loads of the batch are issued before the first use.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kFewUnroll / 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+              for (int c = 0; c < CPL; ++c)
+                acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][e].v[c], acc[r][c], 0, 0, 0);
+      }
     }
     for (; t < nfull; ++t) {
       const int k = kb + 16 * t + 4 * sl;
@@ -263,26 +307,25 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
     for (int e = 0; e < NB; ++e) red[w][rb * NB + e][lane] = acc[rb][e];
   __syncthreads();
-  if (w != 0) return;  // no barrier after this point
+  // Block b of the NR x NB is summed by wave b mod 8, over the waves in
+  // order; no barrier after this point.
+  for (int blk = w; blk < NR * NB; blk += kFewWaves) {
+    const int rb = blk / NB, e = blk % NB;
+    floatx4 s = red[0][blk][lane];
 #pragma unroll
-  for (int rb = 0; rb < NR; ++rb)
+    for (int q = 1; q < kFewWaves; ++q) {
+      const floatx4 v = red[q][blk][lane];
 #pragma unroll
-    for (int e = 0; e < NB; ++e) {
-      floatx4 s = red[0][rb * NB + e][lane];
-#pragma unroll
-      for (int q = 1; q < kFewWaves; ++q) {
-        const floatx4 v = red[q][rb * NB + e][lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] += v[r];
-      }
-      const int col = TB ? n0 + 16 * e + li : n0 + CPL * li + e;
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rb + 4 * sl + r;
-        if (row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, s[r], p.alpha, p.beta);
-      }
+      for (int r = 0; r < 4; ++r) s[r] += v[r];
     }
+    const int col = TB ? n0 + 16 * e + li : n0 + CPL * li + e;
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * rb + 4 * sl + r;
+      if (row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, s[r], p.alpha, p.beta);
+    }
+  }
 }
 
 namespace {

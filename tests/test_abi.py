@@ -246,14 +246,25 @@ def test_select_few_rows(lib):
     """Up to four rows of a moderate untransposed B on the vector-unit kernel,
     up to 32 rows on the matrix-core kernel when its column strips fill the
     CUs (with B transposed, above 16 rows only for wide strips or K <= 4096),
-    split-K tiles otherwise."""
+    split-K tiles otherwise; exactly 32 rows with N*K >= 2^25 on 32-row
+    tiles."""
     assert _op_choice(0, 0, 1, 4096, 4096) == "skinny_m8"
     assert _op_choice(0, 0, 4, 8192, 8192) == "skinny_m8"
     assert _op_choice(0, 0, 4, 16384, 16384) == "fewrows_m32"       # B too large for full-K strips
     assert _op_choice(0, 0, 4, 2048, 2048) == "fewrows_m32"
     assert _op_choice(0, 0, 1, 1024, 4096) == "fewrows_m32"
     assert _op_choice(0, 0, 12, 4096, 4096) == "fewrows_m32"
-    assert _op_choice(1, 0, 32, 8192, 8192) == "fewrows_m32"
+    assert _op_choice(1, 0, 32, 4096, 4096) == "fewrows_m32"
+    # exactly 32 rows of a large B: 32-row tiles, split over K when few
+    # ((32, 8192, 8192): 48.6 against 60.7 us on the few-rows kernel)
+    assert _op_choice(0, 0, 32, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 1, 32, 4096, 16384) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 0, 32, 65536, 1024) == "mfma16_32x64x64_2x2_sched"
+    try:
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_NOT_ALLOWED) == sg.SGEMM_OK
+        assert _op_choice(0, 0, 32, 8192, 8192) == "fewrows_m32"
+    finally:
+        sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
     assert _op_choice(0, 0, 24, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 1, 16, 4096, 4096) == "fewrows_m32"
     assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"

@@ -861,7 +861,9 @@ TAIL_SHAPES = [((2047, 2049, 2047), "mfma16_32x64x64_2x2_sched"),
                ((6144, 1024, 4096), "mfma16_128x64x64_4x2_sched"),
                ((96, 8192, 8192), "mfma16_32x64x64_2x2_sched_splitk"),
                ((160, 4096, 4096), "mfma16_32x64x64_2x2_sched_splitk"),
-               ((320, 8192, 8192), "mfma16_32x64x64_2x2_sched")]
+               ((320, 8192, 8192), "mfma16_32x64x64_2x2_sched"),
+               ((32, 8192, 8192), "mfma16_32x64x64_2x2_sched_splitk"),
+               ((32, 65536, 1024), "mfma16_32x64x64_2x2_sched")]
 
 
 @pytest.mark.parametrize("shape,expect", TAIL_SHAPES, ids=lambda v: "x".join(map(str, v))
