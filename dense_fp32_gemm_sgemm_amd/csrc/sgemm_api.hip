@@ -217,14 +217,15 @@ struct TileFamily {
   double rate_long, rate_short;
   int slots;
   double partial[3];  // [j]: rate with j < slots workgroups on the CU
+  bool short_m;       // also runs M < bm (A untransposed)
 };
 constexpr TileFamily kTileFamilies[] = {
-    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 1, {0.0, 0.0, 0.0}},
-    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 2, {0.0, 0.95, 0.0}},
-    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 1, {0.0, 0.0, 0.0}},
-    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 1, {0.0, 0.0, 0.0}},
-    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 2, {0.0, 0.92, 0.0}},
-    {kMfma16_32x64x64_w4_sched, 32, 64, 120.0, 112.0, 3, {0.0, 0.75, 0.93}},
+    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 2, {0.0, 0.95, 0.0}, false},
+    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 2, {0.0, 0.92, 0.0}, false},
+    {kMfma16_32x64x64_w4_sched, 32, 64, 120.0, 112.0, 3, {0.0, 0.75, 0.93}, true},
 };
 // The same loops with K split over workgroups (atomics after a beta-scaling
 // launch), priced by the unsplit family's rate at the range depth.
@@ -273,7 +274,9 @@ double round_fill(const TileFamily &f, long long units) {
 
 // The ordered loop's own preconditions on the shape (else it runs the plain
 // fallback loop, which the rates do not describe).
-bool family_fits(const TileFamily &f, const Problem &p) { return p.M >= f.bm && p.N >= f.bn; }
+bool family_fits(const TileFamily &f, const Problem &p) {
+  return (p.M >= f.bm || (f.short_m && !p.ta)) && p.N >= f.bn;
+}
 
 // Predicted rate of a family on this problem: steady rate x area fill x
 // round fill.
@@ -313,11 +316,14 @@ int choose_variant(const Problem &p, bool atomics) {
   // for up to four rows of a moderate B read in full-K strips, the matrix-core
   // kernel for up to 32 rows when its column strips fill the CUs (with a
   // transposed B, above 16 rows only for wide strips or a K up to 4096).
-  // Exactly 32 rows with a large B go to 32-row tiles instead (split over K
-  // when they are few), which stream B as well with better matrix-core use
-  // ((32, 8192, 8192): 48.6 against 60.7 us, (32, 4096, 16384) 55.8 against
-  // 82.3); below N*K = 2^25 the few-rows kernel stays ahead.
-  const bool rows32_tiles = atomics && p.M == 32 && nk >= (1LL << 25);
+  // 17 to 32 rows with a large B go to 32-row tiles instead (split over K
+  // when they are few; below 32 rows only with A untransposed, the tile then
+  // reading row M - 1 for the rows past M), which stream B as well with better
+  // matrix-core use ((32, 8192, 8192): 48.6 against 60.7 us, (32, 4096,
+  // 16384) 55.8 against 82.3); below N*K = 2^25 the few-rows kernel stays
+  // ahead.
+  const bool rows32_tiles =
+      atomics && nk >= (1LL << 25) && (p.M == 32 || (p.M > 16 && p.M < 32 && !p.ta));
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
@@ -357,11 +363,12 @@ int choose_variant(const Problem &p, bool atomics) {
     return (p.K % 64 != 0) ? m16 : kMfma16_64x64x64_w8_sched;
   }
   // Too few tiles for the CUs and a long K: split K over workgroups on 64x64
-  // tiles, unless 32-row tiles leave fewer rows empty (then the scores below
-  // weigh both).
+  // tiles, unless 32-row tiles leave fewer rows empty or took over from the
+  // few-rows kernel above (then the scores below weigh both).
   const bool rows32_fill_better =
       p.M >= 32 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
-  if (atomics && !rows32_fill_better && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
+  if (atomics && !rows32_fill_better && !rows32_tiles &&
+      ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
     return kMfma16_64x64x64_w8_pipe_splitk;
   // Otherwise the ordered-loop tile family, split or not, with the best
   // predicted rate.

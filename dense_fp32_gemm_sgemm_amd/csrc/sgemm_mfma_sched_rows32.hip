@@ -10,19 +10,21 @@
 // choice takes it only where the better row fill pays.  The split form runs
 // K ranges on separate workgroups and adds them with atomics after a
 // beta-scaling launch, for shapes with too few tiles to give every CU work.
-// When the ordered loop's preconditions fail (C smaller than one tile, K
-// shorter than one slab) both fall back to the 64x64 variants, which accept
-// every problem.
+// With A not transposed the tile also serves M below 32 (rows past M read
+// row M - 1 of A and are not stored), so that 17 to 31 rows of a large B run
+// on it as well.  When the ordered loop's preconditions fail (K shorter than
+// one slab, N below 64, or M below 32 with A transposed) both fall back to
+// the 64x64 variants, which accept every problem.
 #include "sgemm_sched.hpp"
 
 namespace sg950 {
 
 int launch_mfma16_32x64x64_2x2_sched(const Problem &p, hipStream_t s) {
-  return launch_sched<16, 32, 64, 64, 2, 2, 2, 4>(p, s, launch_mfma16_64x64x64_4x2_sched);
+  return launch_sched<16, 32, 64, 64, 2, 2, 2, 4, false, true>(p, s, launch_mfma16_64x64x64_4x2_sched);
 }
 
 int launch_mfma16_32x64x64_2x2_sched_splitk(const Problem &p, hipStream_t s) {
-  return launch_sched<16, 32, 64, 64, 2, 2, 2, 4, true>(p, s, launch_mfma16_64x64x64_4x2_pipe_splitk);
+  return launch_sched<16, 32, 64, 64, 2, 2, 2, 4, true, true>(p, s, launch_mfma16_64x64x64_4x2_pipe_splitk);
 }
 
 }  // namespace sg950

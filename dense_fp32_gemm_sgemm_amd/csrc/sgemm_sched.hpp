@@ -49,7 +49,8 @@
 // the same loop and adds its partial tile into C with atomics.
 //
 // Preconditions (checked on the host; other problems go to mfma_kernel):
-// K >= BK, M >= BM, N >= BN, A and B 4-byte aligned.
+// K >= BK, M >= BM (or, with SHORTM and A not transposed, M >= 1), N >= BN,
+// A and B 4-byte aligned.
 #pragma once
 
 #include "sgemm_mfma.hpp"
@@ -92,6 +93,7 @@ struct SlabLoader {
     base = KROWS ? X + (size_t)br * ld + r0 + bc : X + (size_t)(r0 + br) * ld + bc;
     kpos = KROWS ? br : bc;
   }
+
   // Writes zeros over this thread's values of a stored slab whose k inside
   // the slab is kcut or more (lds: the thread's vector 0 in the stage, pitch:
   // the stage's row pitch).
@@ -122,6 +124,38 @@ struct SlabLoader {
   // is i*DR rows further.
   static __device__ __forceinline__ int lds_offset(int tid, int pitch) {
     return (tid / VPR) * pitch + (tid % VPR) * 4;
+  }
+};
+
+// SlabLoader for a row slab (k contiguous) that may extend past the last row
+// of X: rows from `maxrow` on read row `maxrow` (never stored).  Each vector
+// keeps its own row pointer.
+template <int ROWS, int BK, int NT>
+struct ClampedRowLoader : SlabLoader<ROWS, BK, NT, false> {
+  using Base = SlabLoader<ROWS, BK, NT, false>;
+  using Base::DR;
+  using Base::NV;
+  using Base::VPR;
+  const float *rowp[NV];  // each vector's row at k = 0
+
+  __device__ __forceinline__ void init(const float *X, int ld_, int r0, int tid, int maxrow) {
+    this->ld = (size_t)ld_;
+    const int br = tid / VPR, bc = (tid % VPR) * 4;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rowp[i] = X + (size_t)min(r0 + br + i * DR, maxrow) * this->ld + bc;
+    this->kpos = bc;
+  }
+  __device__ __forceinline__ void shift_k(int d) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rowp[i] -= d;
+  }
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      floatx4 t;
+      __builtin_memcpy(&t, rowp[i] + k0, sizeof(t));
+      this->v[i] = t;
+    }
   }
 };
 
@@ -163,8 +197,11 @@ __device__ __forceinline__ void read_sched_operands(Operands<T> &o, const float 
 // range takes the rest, at least BK); the workgroup multiplies only that
 // range and adds alpha times its partial product into C with float atomics
 // (C was scaled by beta before the launch).
+//
+// SHORTM (A not transposed): M may be below BM; the tile then starts at row 0,
+// rows from M on read row M - 1 of A and are not stored.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
-          bool TB, bool RAGGED, bool SPLITK>
+          bool TB, bool RAGGED, bool SPLITK, bool SHORTM = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
                                                                                int tiles_n, int group_m,
                                                                                int k_per_split) {
@@ -180,7 +217,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   constexpr int kRegs = MI * MI / 64;
   constexpr int NT = T::kThreads;
   static_assert(T::NQ >= 2, "at least two operand groups per slab");
-  using LA = SlabLoader<BM, BK, NT, TA>;
+  constexpr bool CLAMPM = SHORTM && !TA;  // rows of A clamped (M < BM allowed)
+  using LA = typename std::conditional<CLAMPM, ClampedRowLoader<BM, BK, NT>, SlabLoader<BM, BK, NT, TA>>::type;
   using LB = SlabLoader<BN, BK, NT, !TB>;
   constexpr bool PERMB = !TB && (T::FN == 2 || T::FN == 4);
 
@@ -190,14 +228,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   int tm, tn;
   grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int ms = min(m0, p.M - BM), ns = min(n0, p.N - BN);  // shifted inside C
+  // shifted inside C (with CLAMPM and M < BM: from row 0)
+  const int ms = CLAMPM ? max(0, min(m0, p.M - BM)) : min(m0, p.M - BM), ns = min(n0, p.N - BN);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int g = lane / MI, li = lane % MI;
 
   LA la;
   LB lb;
-  la.init(p.A, p.lda, ms, tid);
+  if constexpr (CLAMPM)
+    la.init(p.A, p.lda, ms, tid, p.M - 1);
+  else
+    la.init(p.A, p.lda, ms, tid);
   lb.init(p.B, p.ldb, ns, tid);
   const int a_st = LA::lds_offset(tid, T::APITCH);
   const int b_st = LB::lds_offset(tid, T::BPITCH);
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
       for (int e = tid; e < RC * BN; e += NT) {
         const int tr = e / BN, tc = e % BN;
         const int row = ms + c0 + tr, col = ns + tc;
-        if (row < m0 || col < n0) continue;
+        if (row < m0 || col < n0 || (CLAMPM && row >= p.M)) continue;
         atomicAdd(p.C + (size_t)row * (size_t)p.ldc + col, p.alpha * As[tr * TP + tc]);
       }
     }
@@ -350,7 +392,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
           const int row = row0 + i * MI + acc_row<MI>(g, r);
-          if (row < m0) continue;
+          if (row < m0 || (CLAMPM && row >= p.M)) continue;
           float *c = p.C + (size_t)row * (size_t)p.ldc + colq;
           if (cvec) {
             if constexpr (T::FN == 4) {
@@ -387,7 +429,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
           const int row = row0 + i * MI + acc_row<MI>(g, r);
-          if (row < m0) continue;
+          if (row < m0 || (CLAMPM && row >= p.M)) continue;
           float *c = p.C + (size_t)row * (size_t)p.ldc + colq;
 #pragma unroll
           for (int j = 0; j < T::FN; ++j)
@@ -405,17 +447,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
         for (int r = 0; r < kRegs; ++r) {
           const int row = row0 + i * MI + acc_row<MI>(g, r);
-          if (row < m0) continue;
+          if (row < m0 || (CLAMPM && row >= p.M)) continue;
           store_out(p.C + (size_t)row * (size_t)p.ldc + col, acc[i][j][r], p.alpha, p.beta);
         }
       }
   }
 }
 
-// True when sched_kernel<..., BM, BN, BK, ...> may run this problem.
-template <int BM, int BN, int BK>
+// True when sched_kernel<..., BM, BN, BK, ...> may run this problem
+// (SHORTM: also with M below BM when A is not transposed).
+template <int BM, int BN, int BK, bool SHORTM = false>
 inline bool sched_ok(const Problem &p) {
-  return p.K >= BK && p.M >= BM && p.N >= BN &&
+  return p.K >= BK && (p.M >= BM || (SHORTM && !p.ta && p.M >= 1)) && p.N >= BN &&
          (reinterpret_cast<uintptr_t>(p.A) & 3) == 0 && (reinterpret_cast<uintptr_t>(p.B) & 3) == 0;
 }
 
@@ -442,12 +485,13 @@ static int sched_splits(long long tiles, int K, int &k_per_split) {
 
 // Launches sched_kernel when its preconditions hold, else `fallback` (a
 // variant of the same tile family that accepts every problem).  SPLIT: K may
-// be split over workgroups when the tiles leave CUs idle.
+// be split over workgroups when the tiles leave CUs idle.  SHORTM: M may be
+// below BM when A is not transposed.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD,
-          bool SPLIT = false>
+          bool SPLIT = false, bool SHORTM = false>
 static int launch_sched(const Problem &p, hipStream_t stream,
                         int (*fallback)(const Problem &, hipStream_t)) {
-  if (!sched_ok<BM, BN, BK>(p)) return fallback(p, stream);
+  if (!sched_ok<BM, BN, BK, SHORTM>(p)) return fallback(p, stream);
   const long long tiles_m = ((long long)p.M + BM - 1) / BM;
   const long long tiles_n = ((long long)p.N + BN - 1) / BN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
@@ -463,9 +507,20 @@ static int launch_sched(const Problem &p, hipStream_t stream,
   const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits, (unsigned)p.batch);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
-#define SG950_SCHED_K(TA_, TB_, RG_, SK_)                                                            \
-  hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_>), \
-                     grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
+  // The row-clamping form only where M is below the tile (A untransposed).
+  const bool short_m = SHORTM && p.M < BM;
+#define SG950_SCHED_K(TA_, TB_, RG_, SK_)                                                                       \
+  do {                                                                                                        \
+    if constexpr (SHORTM && !(TA_)) {                                                                         \
+      if (short_m) {                                                                                          \
+        hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_, true>), \
+                           grid, block, 0, stream, p, tm, tn, group_m, k_per_split);                          \
+        break;                                                                                                \
+      }                                                                                                       \
+    }                                                                                                         \
+    hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_>), grid,  \
+                       block, 0, stream, p, tm, tn, group_m, k_per_split);                                     \
+  } while (0)
 #define SG950_SCHED(TA_, TB_)                       \
   do {                                              \
     if (splits > 1) {                               \

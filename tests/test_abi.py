@@ -246,8 +246,8 @@ def test_select_few_rows(lib):
     """Up to four rows of a moderate untransposed B on the vector-unit kernel,
     up to 32 rows on the matrix-core kernel when its column strips fill the
     CUs (with B transposed, above 16 rows only for wide strips or K <= 4096),
-    split-K tiles otherwise; exactly 32 rows with N*K >= 2^25 on 32-row
-    tiles."""
+    split-K tiles otherwise; 17 to 32 rows with N*K >= 2^25 on 32-row tiles
+    (below 32 rows only with A untransposed)."""
     assert _op_choice(0, 0, 1, 4096, 4096) == "skinny_m8"
     assert _op_choice(0, 0, 4, 8192, 8192) == "skinny_m8"
     assert _op_choice(0, 0, 4, 16384, 16384) == "fewrows_m32"       # B too large for full-K strips
@@ -269,8 +269,11 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 1, 16, 4096, 4096) == "fewrows_m32"
     assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 1, 24, 4096, 4096) == "fewrows_m32"
-    assert _op_choice(0, 1, 24, 8192, 8192) == "fewrows_m32"
-    assert _op_choice(0, 1, 24, 4096, 16384) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(1, 1, 24, 8192, 8192) == "fewrows_m32"  # A transposed: no short 32-row tile
+    assert _op_choice(0, 1, 24, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 0, 20, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 1, 24, 4096, 16384) == "mfma16_32x64x64_2x2_sched_splitk"  # 49 vs 80 us
+    assert _op_choice(1, 1, 24, 4096, 16384) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 8, 512, 4096) == "skinny_m8"                # too few strips
     assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 

@@ -920,3 +920,31 @@ def test_atomics_not_allowed_repeatable(shape):
         _sampled_check(A, B, C3, 1.0, 0.0, None, 128, 128, M, "atomics %s" % (shape,))
     else:
         check_real(C3, A, B, None, 1.0, 0.0, "atomics %s" % (shape,))
+
+
+R32 = [v for v in VARIANTS if VNAMES[v].startswith("mfma16_32x64x64")]
+
+
+@pytest.mark.parametrize("variant", R32, ids=[VNAMES[v] for v in R32])
+@pytest.mark.parametrize("ops", [(False, False), (False, True), (True, False)], ids=["NN", "NT", "TN"])
+def test_rows32_fewer_rows_than_the_tile(variant, ops):
+    """The 32-row tiles with M below 32 (A untransposed: rows past M read row
+    M - 1 and are never stored; A transposed: the fallback), with padded and
+    misaligned operands, K split or not: exact on integer data, nothing
+    outside C written, and the accumulate form on real data."""
+    ta, tb = ops
+    for (M, N, K) in [(1, 64, 64), (2, 65, 300), (15, 130, 64), (17, 333, 1000), (24, 256, 8192),
+                      (31, 200, 129), (31, 64, 4096)]:
+        Ai, Bi, Ci = draw(M, N, K, seed=5 * M + N + K, kind="int", with_c=True)
+        A = np.ascontiguousarray(Ai.T) if ta else Ai
+        B = np.ascontiguousarray(Bi.T) if tb else Bi
+        lds = (A.shape[1] + 3, B.shape[1] + 5, N + 7)
+        say("rows32", VNAMES[variant], ops, (M, N, K))
+        C = run(A, B, Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb, lds=lds,
+                offsets=(1, 2, 3), check_outside=True)
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s (%d,%d,%d)" % (VNAMES[variant], ops, M, N, K))
+        Ar, Br, Cr = draw(M, N, K, seed=7 * M + N + K, with_c=True)
+        A = np.ascontiguousarray(Ar.T) if ta else Ar
+        B = np.ascontiguousarray(Br.T) if tb else Br
+        C = run(A, B, Cr, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, check_outside=True)
+        check_real(C, Ar, Br, Cr, 1.5, 0.5, "%s %s (%d,%d,%d) real" % (VNAMES[variant], ops, M, N, K))
