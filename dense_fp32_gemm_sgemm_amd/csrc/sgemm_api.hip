@@ -320,10 +320,13 @@ int choose_variant(const Problem &p, bool atomics) {
   // when they are few; below 32 rows only with A untransposed, the tile then
   // reading row M - 1 for the rows past M), which stream B as well with better
   // matrix-core use ((32, 8192, 8192): 48.6 against 60.7 us, (32, 4096,
-  // 16384) 55.8 against 82.3); below N*K = 2^25 the few-rows kernel stays
-  // ahead.
+  // 16384) 55.8 against 82.3); so do 9 to 16 rows of a transposed B with a K
+  // of at least twice N ((16, 4096, 16384): 48.4 against 63.9 us; with N
+  // above K/2 the few-rows kernel wins).  Below N*K = 2^25 the few-rows
+  // kernel stays ahead.
   const bool rows32_tiles =
-      atomics && nk >= (1LL << 25) && (p.M == 32 || (p.M > 16 && p.M < 32 && !p.ta));
+      atomics && nk >= (1LL << 25) &&
+      (p.M == 32 || (!p.ta && ((p.M > 16 && p.M < 32) || (p.tb && p.M > 8 && p.M <= 16 && p.K >= 2LL * p.N))));
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
@@ -343,7 +346,7 @@ int choose_variant(const Problem &p, bool atomics) {
   if (p.N <= 16 && p.M >= 16) return kNarrow;
   // Few rows: bound by streaming B; 64x64 tiles with K split over workgroups
   // (16-deep slabs for a short ragged K).
-  if (p.M < 16 || p.N < 16)
+  if (!rows32_tiles && (p.M < 16 || p.N < 16))
     return (p.K < 256 && p.K % 64 != 0)
                ? m16
                : (atomics ? kMfma16_64x64x64_w8_pipe_splitk : kMfma16_64x64x64_w8_pipe);

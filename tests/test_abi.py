@@ -274,6 +274,12 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 0, 20, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
     assert _op_choice(0, 1, 24, 4096, 16384) == "mfma16_32x64x64_2x2_sched_splitk"  # 49 vs 80 us
     assert _op_choice(1, 1, 24, 4096, 16384) == "mfma16_64x64x64_4x2_pipe_splitk"
+    # 9 to 16 rows of a transposed B with K >= 2N: 32-row split tiles
+    # ((16, 4096, 16384): 48.4 against 63.9 us); N above K/2 stays
+    assert _op_choice(0, 1, 16, 4096, 16384) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 1, 12, 4096, 16384) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 1, 16, 16384, 16384) == "fewrows_m32"
+    assert _op_choice(0, 1, 8, 4096, 16384) == "fewrows_m32"
     assert _op_choice(0, 0, 8, 512, 4096) == "skinny_m8"                # too few strips
     assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 
