@@ -948,3 +948,25 @@ def test_rows32_fewer_rows_than_the_tile(variant, ops):
         B = np.ascontiguousarray(Br.T) if tb else Br
         C = run(A, B, Cr, 1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, check_outside=True)
         check_real(C, Ar, Br, Cr, 1.5, 0.5, "%s %s (%d,%d,%d) real" % (VNAMES[variant], ops, M, N, K))
+
+
+@pytest.mark.parametrize("variant", R32 + [-1], ids=[VNAMES[v] for v in R32] + ["automatic"])
+def test_rows32_fewer_rows_batched(variant):
+    """Strided batches with M below the 32-row tile, B untransposed and
+    transposed, slices with gaps: real data to the tolerance and integer data
+    exactly (the automatic choice takes the 32-row split tiles for the large
+    case: 20 rows, N*K*batch >= 2^25)."""
+    rng = np.random.default_rng(43)
+    for tb in (False, True):
+        for (batch, M, N, K) in ((3, 20, 130, 300), (4, 20, 1024, 8192)):
+            A = rng.uniform(-1, 1, (batch, M, K)).astype(np.float32)
+            B = rng.uniform(-1, 1, (batch, N, K) if tb else (batch, K, N)).astype(np.float32)
+            C = rng.standard_normal((batch, M, N)).astype(np.float32)
+            say("rows32 batched", variant, tb, (batch, M, N, K))
+            out = run_batched(A, B, C, 1.5, 0.5, variant=variant, trans_b=tb, gap=5)
+            check_batched(out, A, B, C, 1.5, 0.5, "rows32 batched %s" % variant, tb=tb)
+            Ai = rng.integers(-4, 5, A.shape).astype(np.float32)
+            Bi = rng.integers(-4, 5, B.shape).astype(np.float32)
+            Ci = rng.integers(-4, 5, C.shape).astype(np.float32)
+            out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=variant, trans_b=tb)
+            check_batched(out, Ai, Bi, Ci, 1.0, 1.0, "rows32 batched int %s" % variant, exact=True, tb=tb)
