@@ -408,3 +408,33 @@ def test_atomics_not_allowed_selection(lib):
         sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
     for key, name in list(default.items())[::37]:
         assert _op_choice(key[0], key[1], key[3], key[4], key[5], key[2]) == name
+
+
+def test_tile_choice_against_measured_rates(lib):
+    """Every shape of the committed tile-family measurements
+    (profiles/tile_choice_mi355x.md, every family timed on an MI355X): the
+    automatic choice is a measured family within 5% of the fastest family.
+    (The split form does not split once the tiles fill 512 slots, so a 5%
+    spread between it and its unsplit twin there is run-to-run noise.)"""
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
+                        "tile_choice_mi355x.md")
+    lines = open(path).read().splitlines()
+    head = [h.strip() for h in next(l for l in lines if l.startswith("| M x N")).split("|")[1:-1]]
+    fam = {"256x256": "mfma32_256x256x32_2x2_sched", "128x128 w4": "mfma16_128x128x32_2x2_sched",
+           "128x128 w8": "mfma16_128x128x64_4x2_sched", "128x64": "mfma16_128x64x64_4x2_sched",
+           "64x64": "mfma16_64x64x64_4x2_sched", "64x64 split-K": "mfma16_64x64x64_4x2_sched_splitk",
+           "32x64": "mfma16_32x64x64_2x2_sched", "32x64 split-K": "mfma16_32x64x64_2x2_sched_splitk"}
+    checked = 0
+    for line in lines:
+        cells = [c.strip() for c in line.split("|")[1:-1]]
+        if not cells or not cells[0][:1].isdigit():
+            continue
+        M, N, K = (int(x) for x in cells[0].split("x"))
+        ta, tb = (1 if cells[1][0] == "T" else 0), (1 if cells[1][1] == "T" else 0)
+        rates = {fam[h]: float(v.replace("*", "")) for h, v in zip(head, cells) if h in fam and v != "-"}
+        name = _op_choice(ta, tb, M, N, K)
+        assert name in rates, (cells[0], cells[1], name)
+        assert rates[name] >= 0.95 * max(rates.values()), (cells[0], cells[1], name, rates)
+        checked += 1
+    assert checked >= 40
