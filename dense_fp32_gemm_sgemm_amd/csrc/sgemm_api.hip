@@ -370,7 +370,11 @@ int choose_variant(const Problem &p, bool atomics) {
   // few-rows kernel above (then the scores below weigh both).
   const bool rows32_fill_better =
       p.M >= 32 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
-  if (atomics && !rows32_fill_better && !rows32_tiles &&
+  // (32 to 64 rows: the ordered loop's split tiles, scored below, beat it by
+  // 3-8%: (48, 8192, 8192) 80.7 against 78.5, (64, 8192, 8192) 111.5 against
+  // 102.9 TFLOP/s.)
+  const bool split_tiles_fit = p.M >= 32 && p.M <= 64 && p.N >= 64;
+  if (atomics && !rows32_fill_better && !rows32_tiles && !split_tiles_fit &&
       ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
     return kMfma16_64x64x64_w8_pipe_splitk;
   // Otherwise the ordered-loop tile family, split or not, with the best

@@ -216,7 +216,6 @@ def test_select_rows_just_past_64(lib):
     assert _op_choice(0, 0, 320, 8192, 8192) == r32
     assert _op_choice(0, 0, 320, 4096, 4096) == r32
     assert _op_choice(0, 0, 48, 16384, 4096) == r32
-    assert _op_choice(0, 0, 64, 8192, 8192) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 24, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 352, 8192, 8192) == "mfma16_64x64x64_4x2_sched"
 
@@ -286,8 +285,13 @@ def test_select_few_rows(lib):
 
 def test_select_split_k_below_one_round(lib):
     """Fewer 64x64 tiles than CUs with a long K: K is split over workgroups
-    ((64, 8192, 8192): 84 us split against 139 us on 128 tiles)."""
-    assert _op_choice(0, 0, 64, 8192, 8192) == "mfma16_64x64x64_4x2_pipe_splitk"
+    ((64, 8192, 8192): 84 us split against 139 us on 128 tiles); from 32 to
+    64 rows on the ordered loop's split tiles ((64, 8192, 8192) 111.5 against
+    102.9 TFLOP/s, (48, 8192, 8192) 80.7 against 78.5, (64, 2048, 8192) 29.1
+    against 31.9 us), above that the split 64x64 pipeline."""
+    assert _op_choice(0, 0, 64, 8192, 8192) == "mfma16_64x64x64_4x2_sched_splitk"
+    assert _op_choice(0, 0, 48, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 0, 64, 2048, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
     assert _op_choice(0, 0, 128, 4096, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 128, 4096, 1024) != "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 0, 1024, 1024, 1024) == "mfma16_64x64x64_4x2_sched"
