@@ -320,13 +320,16 @@ int choose_variant(const Problem &p, bool atomics) {
   // when they are few; below 32 rows only with A untransposed, the tile then
   // reading row M - 1 for the rows past M), which stream B as well with better
   // matrix-core use ((32, 8192, 8192): 48.6 against 60.7 us, (32, 4096,
-  // 16384) 55.8 against 82.3); so do 9 to 16 rows of a transposed B with a K
-  // of at least twice N ((16, 4096, 16384): 48.4 against 63.9 us; with N
-  // above K/2 the few-rows kernel wins).  Below N*K = 2^25 the few-rows
-  // kernel stays ahead.
+  // 16384) 55.8 against 82.3); below N*K = 2^25 the few-rows kernel stays
+  // ahead.  With B transposed the tiles win from N*K = 2^22 when K is at
+  // least N (above 16 rows) or twice N (9 to 16 rows): (24, 4096, 4096) 20.9
+  // against 23.5 us, (16, 4096, 16384) 48.4 against 63.9; with N above K
+  // (above K/2) the few-rows kernel wins.
+  const bool tb_long_k = p.tb && (p.M > 16 ? p.K >= p.N : (p.M > 8 && p.K >= 2LL * p.N));
+  const bool rows32_fits = p.M == 32 || (!p.ta && p.M > 8 && p.M < 32);
   const bool rows32_tiles =
-      atomics && nk >= (1LL << 25) &&
-      (p.M == 32 || (!p.ta && ((p.M > 16 && p.M < 32) || (p.tb && p.M > 8 && p.M <= 16 && p.K >= 2LL * p.N))));
+      atomics && rows32_fits &&
+      ((nk >= (1LL << 25) && p.M > 16) || (nk >= (1LL << 22) && tb_long_k));
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;

@@ -246,7 +246,8 @@ def test_select_few_rows(lib):
     up to 32 rows on the matrix-core kernel when its column strips fill the
     CUs (with B transposed, above 16 rows only for wide strips or K <= 4096),
     split-K tiles otherwise; 17 to 32 rows with N*K >= 2^25 on 32-row tiles
-    (below 32 rows only with A untransposed)."""
+    (below 32 rows only with A untransposed), and with B transposed from
+    N*K >= 2^22 when K >= N (17 to 32 rows) or K >= 2N (9 to 16 rows)."""
     assert _op_choice(0, 0, 1, 4096, 4096) == "skinny_m8"
     assert _op_choice(0, 0, 4, 8192, 8192) == "skinny_m8"
     assert _op_choice(0, 0, 4, 16384, 16384) == "fewrows_m32"       # B too large for full-K strips
@@ -266,8 +267,11 @@ def test_select_few_rows(lib):
         sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
     assert _op_choice(0, 0, 24, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 1, 16, 4096, 4096) == "fewrows_m32"
-    assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
-    assert _op_choice(0, 1, 24, 4096, 4096) == "fewrows_m32"
+    assert _op_choice(0, 1, 16, 1024, 4096) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _op_choice(0, 1, 24, 4096, 4096) == "mfma16_32x64x64_2x2_sched_splitk"  # 20.9 vs 23.5 us
+    assert _op_choice(0, 1, 32, 4096, 2048) == "fewrows_m32"  # N above K: 15.4 vs 16.4 us
+    assert _op_choice(0, 0, 24, 4096, 4096) == "fewrows_m32"  # B untransposed below 2^25
+    assert _op_choice(0, 1, 24, 4096, 1024) == "fewrows_m32"
     assert _op_choice(1, 1, 24, 8192, 8192) == "fewrows_m32"  # A transposed: no short 32-row tile
     assert _op_choice(0, 1, 24, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
     assert _op_choice(0, 0, 20, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
