@@ -326,7 +326,7 @@ int choose_variant(const Problem &p, bool atomics) {
   // against 23.5 us, (16, 4096, 16384) 48.4 against 63.9; with N above K
   // (above K/2) the few-rows kernel wins.
   const bool tb_long_k = p.tb && (p.M > 16 ? p.K >= p.N : (p.M > 8 && p.K >= 2LL * p.N));
-  const bool rows32_fits = p.M == 32 || (!p.ta && p.M > 8 && p.M < 32);
+  const bool rows32_fits = p.N >= 64 && (p.M == 32 || (!p.ta && p.M > 8 && p.M < 32));
   const bool rows32_tiles =
       atomics && rows32_fits &&
       ((nk >= (1LL << 25) && p.M > 16) || (nk >= (1LL << 22) && tb_long_k));

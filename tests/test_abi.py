@@ -271,6 +271,9 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 1, 24, 4096, 4096) == "mfma16_32x64x64_2x2_sched_splitk"  # 20.9 vs 23.5 us
     assert _op_choice(0, 1, 32, 4096, 2048) == "fewrows_m32"  # N above K: 15.4 vs 16.4 us
     assert _op_choice(0, 0, 24, 4096, 4096) == "fewrows_m32"  # B untransposed below 2^25
+    # fewer than 64 columns never go to the 32x64 tiles (they would not fit)
+    assert _op_choice(0, 1, 24, 48, 100000) == "mfma16_64x64x64_4x2_pipe_splitk"
+    assert _op_choice(0, 1, 12, 60, 200000) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _op_choice(0, 1, 24, 4096, 1024) == "fewrows_m32"
     assert _op_choice(1, 1, 24, 8192, 8192) == "fewrows_m32"  # A transposed: no short 32-row tile
     assert _op_choice(0, 1, 24, 8192, 8192) == "mfma16_32x64x64_2x2_sched_splitk"
