@@ -372,7 +372,7 @@ int choose_variant(const Problem &p, bool atomics) {
   // tiles, unless 32-row tiles leave fewer rows empty or took over from the
   // few-rows kernel above (then the scores below weigh both).
   const bool rows32_fill_better =
-      p.M >= 32 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
+      p.M >= 32 && p.N >= 64 && tile_fill_pct(p.M, p.N, 32, 64) > tile_fill_pct(p.M, p.N, 64, 64);
   // (32 to 64 rows: the ordered loop's split tiles, scored below, beat it by
   // 3-8%: (48, 8192, 8192) 80.7 against 78.5, (64, 8192, 8192) 111.5 against
   // 102.9 TFLOP/s.)

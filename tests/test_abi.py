@@ -449,3 +449,23 @@ def test_tile_choice_against_measured_rates(lib):
         assert rates[name] >= 0.95 * max(rates.values()), (cells[0], cells[1], name, rates)
         checked += 1
     assert checked >= 40
+
+
+def test_few_tiles_with_long_k_always_split(lib):
+    """With few output tiles and a long K the automatic choice always spreads
+    K over many workgroups: a K-split variant, or a streaming kernel whose
+    waves split K (few rows, few columns, the vector-unit few-rows kernel),
+    never a single-pass tile kernel with a handful of workgroups (tiny
+    problems, at most 2^20 multiply-adds, excepted)."""
+    streaming = {"fewrows_m32", "skinny_m8", "narrow_n16"}
+    dims_m = (1, 8, 16, 17, 24, 31, 32, 33, 48, 64, 65, 96, 128, 200)
+    dims_n = (1, 15, 16, 17, 48, 63, 64, 65, 100, 128, 200, 300)
+    for ta in (0, 1):
+        for tb in (0, 1):
+            for M in dims_m:
+                for N in dims_n:
+                    for K in (8192, 65536):
+                        if M * N * K <= (1 << 20):
+                            continue  # launch-latency bound: one lane per output
+                        name = _op_choice(ta, tb, M, N, K)
+                        assert name.endswith("_splitk") or name in streaming, (ta, tb, M, N, K, name)
