@@ -239,11 +239,13 @@ constexpr SplitFamily kSplitFamilies[] = {
 };
 // Share of the unsplit rate kept by a split grid whose ranges are k deep
 // (fitted to split-K runs on MI355X: 0.94-0.98 at k = 4096, 0.92-0.93 at
-// 2048, 0.76 at 1024; the atomic adds of the tile and the shorter pipeline
-// both weigh more as the range shrinks).
+// 2048, 0.76 at 1024, 0.59 at 512; the atomic adds of the tile and the
+// shorter pipeline both weigh more as the range shrinks).
 double split_efficiency(double k) {
   const double r = 4096.0 / k;
-  return 1.0 / (1.0 + 0.02 * r * r);
+  // Floored at one half below the measured depths (0.59 at k = 512): a grid
+  // of a few dozen workgroups is slower than any split of it.
+  return fmax(0.5, 1.0 / (1.0 + 0.02 * r * r));
 }
 
 // Steady rate of a family for k-deep work per tile (linear between k = 1024
@@ -377,8 +379,10 @@ int choose_variant(const Problem &p, bool atomics) {
   // 3-8%: (48, 8192, 8192) 80.7 against 78.5, (64, 8192, 8192) 111.5 against
   // 102.9 TFLOP/s.)
   const bool split_tiles_fit = p.M >= 32 && p.M <= 64 && p.N >= 64;
-  if (atomics && !rows32_fill_better && !rows32_tiles && !split_tiles_fit &&
-      ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
+  // (A K below 2048 is left to the scores as well: (300, 1000, 1024) 21.3 us
+  // here against 15.4 on unsplit 32x64 tiles, (128, 1024, 1024) 15.0 against
+  // 12.9 on split ones.)
+  if (atomics && !rows32_fill_better && !rows32_tiles && !split_tiles_fit && t64 < cus && p.K >= 2048)
     return kMfma16_64x64x64_w8_pipe_splitk;
   // Otherwise the ordered-loop tile family, split or not, with the best
   // predicted rate.
@@ -394,6 +398,10 @@ int choose_variant(const Problem &p, bool atomics) {
     const double r = split_rate(sf, p);
     if (r > best_rate) best_rate = r, best = sf.variant;
   }
+  // No family's tile fits C (fewer than 32 rows with A transposed, or fewer
+  // than 64 columns): few tiles with a long K still split K over workgroups.
+  if (best_rate < 0.0 && atomics && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
+    return kMfma16_64x64x64_w8_pipe_splitk;
   return best;
 }
 

@@ -458,14 +458,17 @@ def test_few_tiles_with_long_k_always_split(lib):
     never a single-pass tile kernel with a handful of workgroups (tiny
     problems, at most 2^20 multiply-adds, excepted)."""
     streaming = {"fewrows_m32", "skinny_m8", "narrow_n16"}
-    dims_m = (1, 8, 16, 17, 24, 31, 32, 33, 48, 64, 65, 96, 128, 200)
-    dims_n = (1, 15, 16, 17, 48, 63, 64, 65, 100, 128, 200, 300)
+    dims_m = (1, 8, 16, 17, 24, 31, 32, 33, 48, 64, 65, 96, 128, 200, 300)
+    dims_n = (1, 15, 16, 17, 48, 63, 64, 65, 100, 128, 200, 300, 700, 1000)
     for ta in (0, 1):
         for tb in (0, 1):
             for M in dims_m:
                 for N in dims_n:
-                    for K in (8192, 65536):
-                        if M * N * K <= (1 << 20):
-                            continue  # launch-latency bound: one lane per output
-                        name = _op_choice(ta, tb, M, N, K)
-                        assert name.endswith("_splitk") or name in streaming, (ta, tb, M, N, K, name)
+                    for K in (1024, 2048, 8192, 65536):
+                        for batch in (1, 3):
+                            if M * N * K * batch <= (1 << 20):
+                                continue  # launch-latency bound: one lane per output
+                            if -(-M // 64) * -(-N // 64) * batch >= 64:
+                                continue  # enough 64x64 tiles
+                            name = _op_choice(ta, tb, M, N, K, batch)
+                            assert name.endswith("_splitk") or name in streaming, (ta, tb, M, N, K, batch, name)
