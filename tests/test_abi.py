@@ -472,3 +472,42 @@ def test_few_tiles_with_long_k_always_split(lib):
                                 continue  # enough 64x64 tiles
                             name = _op_choice(ta, tb, M, N, K, batch)
                             assert name.endswith("_splitk") or name in streaming, (ta, tb, M, N, K, batch, name)
+
+
+def test_select_fuzz_valid_and_stable(lib):
+    """Random problems (every size class, orientation, batch and both atomics
+    modes): the automatic choice is a valid variant, the same on a repeated
+    call, and free of K-split variants when atomics are not allowed."""
+    import random
+    rnd = random.Random(1234)
+    nv = sg.sgemm_num_variants()
+
+    def dim():
+        r = rnd.random()
+        if r < 0.3:
+            return rnd.choice((1, 2, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 255, 256, 257))
+        if r < 0.8:
+            return rnd.randint(1, 3000)
+        return rnd.randint(3000, 70000)
+
+    try:
+        for i in range(6000):
+            M, N, K = dim(), dim(), dim()
+            batch = rnd.choice((1, 1, 1, 2, 7, 100))
+            if M * N * K * batch > 2 ** 44:
+                continue
+            ta, tb = rnd.randint(0, 1), rnd.randint(0, 1)
+            mode = sg.SGEMM_ATOMICS_ALLOWED if i % 3 else sg.SGEMM_ATOMICS_NOT_ALLOWED
+            assert sg.sgemm_set_atomics_mode(mode) == sg.SGEMM_OK
+            v = sg.sgemm_strided_batched_select_variant(
+                ta, tb, M, N, K, 1.0, FAKE, M if ta else K, M * K, FAKE, K if tb else N, K * N, 0.0,
+                FAKE, N, M * N, batch)
+            assert 0 <= v < nv, (ta, tb, M, N, K, batch, v)
+            again = sg.sgemm_strided_batched_select_variant(
+                ta, tb, M, N, K, 1.0, FAKE, M if ta else K, M * K, FAKE, K if tb else N, K * N, 0.0,
+                FAKE, N, M * N, batch)
+            assert again == v
+            if mode == sg.SGEMM_ATOMICS_NOT_ALLOWED:
+                assert not sg.sgemm_variant_name(v).endswith("_splitk"), (ta, tb, M, N, K, batch)
+    finally:
+        sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
