@@ -46,13 +46,12 @@ _lock = threading.Lock()
 _lib = None
 
 
-def build(output: str = LIBRARY, mutant: int = 0, quiet: bool = True) -> str:
-    """Compile ``sgemm_oracle.c`` with gcc into a shared library.
-
-    ``mutant`` > 0 builds a planted-mistake variant (tests only)."""
+def build(output: str = LIBRARY, source: str = SOURCE, quiet: bool = True) -> str:
+    """Compile ``sgemm_oracle.c`` (or, for the planted-mistake tests, an
+    altered copy given as ``source``) with gcc into a shared library."""
     tmp = output + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           "-DORACLE_MUTANT=%d" % int(mutant), SOURCE, "-o", tmp, "-lm"]
+           source, "-o", tmp, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + res.stderr)
@@ -71,7 +70,6 @@ def _declare(lib):
         fn.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64,
                        vp, i64, vp, vp]
     lib.oracle_max_threads.restype = ctypes.c_int
-    lib.oracle_mutant_id.restype = ctypes.c_int
     return lib
 
 

@@ -34,9 +34,9 @@
  *     and C; elements in the gaps between K (or N) and the leading dimension
  *     are never read.
  *
- * Planted-mistake builds: compiling with -DORACLE_MUTANT=n (n >= 1) switches
- * on exactly one deliberate error, used only by the test that proves the
- * oracle's pins catch such errors.  The default build has ORACLE_MUTANT == 0.
+ * The test-suite also builds altered copies of this file, each with one
+ * deliberate mistake patched into a temporary copy, to prove that the pins
+ * catch such mistakes; this file itself holds only the definition.
  */
 #include <math.h>
 #include <stdint.h>
@@ -45,12 +45,6 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
-
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-
-int oracle_mutant_id(void) { return ORACLE_MUTANT; }
 
 int oracle_max_threads(void) {
 #ifdef _OPENMP
@@ -67,24 +61,11 @@ static void row_sums(int64_t i, int64_t N, int64_t K, const float *A,
                      double *d) {
     memset(s, 0, (size_t)N * sizeof(double));
     memset(d, 0, (size_t)N * sizeof(double));
-#if ORACLE_MUTANT == 3
-    K = K - 1; /* planted: last term of every dot product dropped */
-#endif
-#if ORACLE_MUTANT == 5
-    lda = K; /* planted: A's leading dimension ignored */
-#endif
     for (int64_t k = 0; k < K; ++k) {
         const double a = (double)A[i * lda + k];
         const float *brow = B + k * ldb;
         for (int64_t j = 0; j < N; ++j) {
-#if ORACLE_MUTANT == 2
-            /* planted: B read transposed (kept in bounds) */
-            const double p = (j < K && k < N) ? a * (double)B[j * ldb + k] : 0.0;
-#elif ORACLE_MUTANT == 4
-            const double p = -a * (double)brow[j]; /* planted: wrong sign */
-#else
             const double p = a * (double)brow[j];
-#endif
             s[j] += p;
             d[j] += fabs(p);
         }
@@ -96,24 +77,9 @@ static void finish(double alpha, double beta, int use_ab, double s, double d,
                    const float *cin, double *cref, double *den) {
     double ab = use_ab ? alpha * s : 0.0;
     double bc = 0.0;
-    if (beta != 0.0) {
-#if ORACLE_MUTANT == 1
-        bc = 0.0; /* planted: beta term dropped */
-#else
-        bc = beta * (double)(*cin);
-#endif
-    }
-#if ORACLE_MUTANT == 7
-    *cref = use_ab ? alpha * (s + (beta != 0.0 ? (double)(*cin) * beta : 0.0))
-                   : bc; /* planted: alpha applied to the beta term too */
-#else
+    if (beta != 0.0) bc = beta * (double)(*cin);
     *cref = ab + bc;
-#endif
-#if ORACLE_MUTANT == 6
-    *den = use_ab ? d : 0.0; /* planted: |beta C| left out of the denominator */
-#else
     *den = (use_ab ? d : 0.0) + fabs(bc);
-#endif
 }
 
 /*
@@ -149,11 +115,7 @@ int oracle_sgemm_rows(int64_t M, int64_t N, int64_t K, double alpha,
                     memset(d, 0, (size_t)N * sizeof(double));
                 }
                 for (int64_t j = 0; j < N; ++j) {
-#if ORACLE_MUTANT == 8
-                    const float *cin = Cin ? Cin + i * ldb + j : NULL; /* planted: wrong ld for C */
-#else
                     const float *cin = Cin ? Cin + i * ldc + j : NULL;
-#endif
                     finish(alpha, beta, use_ab, s[j], d[j], cin, cref + r * N + j,
                            den + r * N + j);
                 }

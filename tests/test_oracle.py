@@ -18,34 +18,61 @@ def test_oracle_pin(pin):
     pin(oracle.load())
 
 
-# One planted mistake per build; each must fail at least one pin.  Run in a
-# child process so that a mistake which reads wild memory cannot take the test
-# session down with it.
+# One planted mistake per build, each applied as a text patch (old -> new,
+# the old text occurring exactly once) to a temporary copy of the oracle's C
+# file; the committed file holds only the definition.  Each altered build
+# must fail at least one pin.  The pins run in a child process so that a
+# mistake which reads wild memory cannot take the test session down with it.
+_ROW_LOOP = """    for (int64_t k = 0; k < K; ++k) {
+        const double a = (double)A[i * lda + k];
+        const float *brow = B + k * ldb;
+        for (int64_t j = 0; j < N; ++j) {"""
 MUTANTS = {
-    1: "beta term dropped",
-    2: "B read transposed",
-    3: "last k term dropped",
-    4: "product sign flipped",
-    5: "A's leading dimension ignored",
-    6: "|beta C| left out of the denominator",
-    7: "alpha applied to the beta term",
-    8: "C read with B's leading dimension",
+    "beta term dropped": (
+        "if (beta != 0.0) bc = beta * (double)(*cin);", "if (beta != 0.0) bc = 0.0;"),
+    "B read transposed": (
+        "const double p = a * (double)brow[j];",
+        "const double p = (j < K && k < N) ? a * (double)B[j * ldb + k] : 0.0;"),
+    "last k term dropped": (_ROW_LOOP, _ROW_LOOP.replace("k < K;", "k < K - 1;")),
+    "product sign flipped": (
+        "const double p = a * (double)brow[j];", "const double p = -a * (double)brow[j];"),
+    "A's leading dimension ignored": (_ROW_LOOP, _ROW_LOOP.replace("A[i * lda + k]", "A[i * K + k]")),
+    "|beta C| left out of the denominator": (
+        "*den = (use_ab ? d : 0.0) + fabs(bc);", "*den = use_ab ? d : 0.0;"),
+    "alpha applied to the beta term": (
+        "*cref = ab + bc;",
+        "*cref = use_ab ? alpha * (s + (beta != 0.0 ? beta * (double)(*cin) : 0.0)) : bc;"),
+    "C read with B's leading dimension": (
+        "const float *cin = Cin ? Cin + i * ldc + j : NULL;",
+        "const float *cin = Cin ? Cin + i * ldb + j : NULL;"),
 }
 
 
-@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m])
-def test_planted_mistake_is_caught(mutant, tmp_path):
-    lib = str(tmp_path / ("liboracle_mutant%d.so" % mutant))
-    oracle.build(output=lib, mutant=mutant)
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SOURCE) as f:
+        text = f.read()
+    assert text.count(old) == 1, "patch for %r does not apply once" % name
+    src = tmp_path / "sgemm_oracle_altered.c"
+    src.write_text(text.replace(old, new))
+    lib = str(tmp_path / "liboracle_altered.so")
+    oracle.build(output=lib, source=str(src))
     env = dict(os.environ, OMP_NUM_THREADS="2")
     res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pins.py"), lib],
                          capture_output=True, text=True, env=env, cwd=ROOT, timeout=300)
-    assert res.returncode != 0, ("planted mistake %d (%s) passed every pin:\n%s"
-                                 % (mutant, MUTANTS[mutant], res.stdout + res.stderr))
+    assert res.returncode != 0, ("planted mistake (%s) passed every pin:\n%s"
+                                 % (name, res.stdout + res.stderr))
 
 
-def test_unmutated_build_reports_zero():
-    assert oracle.load().oracle_mutant_id() == 0
+def test_committed_oracle_holds_no_planted_mistakes():
+    """The committed C file is the plain definition: no build switch, and
+    none of the altered texts above."""
+    with open(oracle.SOURCE) as f:
+        text = f.read()
+    assert "#if" not in text.replace("#ifdef _OPENMP", "").replace("#ifndef", "")
+    for name, (old, new) in MUTANTS.items():
+        assert new not in text, name
 
 
 def test_exact_match_and_normalized_error_rules():
