@@ -810,26 +810,52 @@ def test_sweep_full_check(w):
     check_exact(C, Ai, Bi, None, 1.0, 0.0, w.name + " int")
 
 
-def _sampled_check(A, B, C, alpha, beta, Cin, nrows, ncols, seed, what):
+def _sample(M, N, nrows, ncols, seed):
     rng = np.random.default_rng(seed)
-    M, N = C.shape
     rows = np.sort(rng.choice(M, size=min(nrows, M), replace=False))
     cols = np.sort(rng.choice(N, size=min(ncols, N), replace=False))
+    return rows, cols
+
+
+def _sampled_check(A, B, C, alpha, beta, Cin, nrows, ncols, seed, what):
+    """Whole rows and whole columns of C (each crosses every tile boundary
+    along its length) against the oracle, to the normalized-error bar."""
+    M, N = C.shape
+    rows, cols = _sample(M, N, nrows, ncols, seed)
     ref, den = oracle.gemm(A, B, Cin, alpha, beta, rows=rows)
     err_r = oracle.normalized_error(C[rows], ref, den)
     ref, den = oracle.gemm(A, B, Cin, alpha, beta, cols=cols)
     err_c = oracle.normalized_error(C[:, cols], ref, den)
     assert max(err_r, err_c) <= TOL, "%s: sampled normalized error %.3g" % (what, max(err_r, err_c))
+    return max(err_r, err_c)
+
+
+def _sampled_exact(A, B, C, alpha, beta, Cin, nrows, ncols, seed, what):
+    """Integer data: sampled whole rows and columns equal the oracle exactly."""
+    M, N = C.shape
+    rows, cols = _sample(M, N, nrows, ncols, seed)
+    ref, _ = oracle.gemm(A, B, Cin, alpha, beta, rows=rows)
+    assert oracle.exact_match(C[rows], ref), "%s: sampled rows differ from the oracle" % what
+    ref, _ = oracle.gemm(A, B, Cin, alpha, beta, cols=cols)
+    assert oracle.exact_match(C[:, cols], ref), "%s: sampled columns differ from the oracle" % what
 
 
 def test_sweep_8192_sampled():
-    """8192^3: 256 whole rows and 256 whole columns (each crosses every tile
-    boundary along its length) against the oracle."""
+    """8192^3 through the automatic choice: 512 seeded whole rows and 512
+    whole columns against the oracle on real data, and the same sample of
+    the integer copy exactly (every partial sum is an integer of magnitude
+    at most 16 * 8192 < 2^24, so any summation order is exact)."""
     w = [w for w in sweep_workloads() if w.M == 8192][0]
     A, B, _ = draw_workload(w)
-    say("sweep 8192^3")
+    say("sweep 8192^3 real")
     C = run(A, B)
-    _sampled_check(A, B, C, 1.0, 0.0, None, 256, 256, 8192, w.name)
+    err = _sampled_check(A, B, C, 1.0, 0.0, None, 512, 512, 8192, w.name)
+    say("8192^3 sampled normalized error %.3g" % err)
+    del A, B, C
+    Ai, Bi, _ = draw(w.M, w.N, w.K, seed=w.seed, kind="int")
+    say("sweep 8192^3 int")
+    C = run(Ai, Bi)
+    _sampled_exact(Ai, Bi, C, 1.0, 0.0, None, 512, 512, 8193, w.name + " int")
 
 
 @pytest.mark.parametrize("w", ragged_workloads() + shard_workloads(), ids=lambda w: w.name)
