@@ -10,12 +10,29 @@ clock-waking burst, see ``wake``), exactly K steps are timed between two device
 synchronisations; each launch is also bracketed by HIP events on the stream it
 is launched on, which gives the average kernel duration for the roofline.
 
+After timing, the CPU-baseline leg runs the oracle on the host over a row
+sample of the same workload and checks the C the timed calls left behind
+against it (normalized error, reported as ``max_norm_err``; the run fails
+when it exceeds 1e-5).
+
 Other modes (one JSON line per result, not the contract line):
   --sweep            every square size and rectangular shape, auto choice
   --variants         every kernel variant on the 4096^3 problem
   --shape M N K      a single shape (with --variant V to force a variant)
   --profile          only the timed steps, no ceilings or CPU baseline: the
                      command to run under rocprofv3
+  --trace-summary    tables from a rocprofv3 kernel trace of the above
+
+Timing in the non-contract modes.  Each record carries two times per call:
+``us_launch``, from HIP events around each Python->C launch (what a caller
+issuing one call at a time sees, host launch gap included), and
+``us_device``, from events around back-to-back replays of a HIP graph that
+holds many calls (the device time per call, launch gaps between dependent
+kernels included, host overhead excluded).  With ``--cold`` a third,
+``us_cold``: the graph cycles through enough copies of the operands (more
+than 1 GiB) that each call misses the 256 MB last-level cache.  Below about
+50 us only the device figure describes the kernel (Tinyforge README, its
+note on benchmark harness errors at small sizes).
 
 Accounting (as on the pages): FLOPs = 2*M*N*K, the epilogue is not counted
 ("Optimizing SGEMM in CUDA" and "The road to a fast GEMM", section "The
@@ -43,6 +60,8 @@ PEAK_HBM_GBS = 8000.0
 NUM_CUS = 256
 
 METRIC = "SGEMM GFLOPS at M=N=K=4096 on 1 MI355X; % of measured FP32 peak"
+# The largest workspace the workspace entry points can use for any problem.
+WS_BYTES = 4096 + (32 << 20)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_4096.json")
 
 
@@ -174,10 +193,71 @@ def time_steps(fn, steps: int, stream):
     return total, per
 
 
+def device_ms_per_call(fn_on, est_ms: float, target_ms: float = 2.0, replays: int = 20,
+                       copies: int = 1, mark=None):
+    """Device time (ms) per call with the host out of the way.
+
+    fn_on(handle, i) enqueues call i on the stream with that hipStream_t
+    handle.  reps calls (about target_ms of device work, at least `copies`)
+    are captured into one HIP graph, which is replayed `replays` times back to
+    back between two events after a short clock-waking burst; returns (ms per
+    call, reps).  mark(handle), if given, is called on the timing stream
+    right before the timed replays (a separator for kernel traces)."""
+    torch = _torch()
+    reps = int(min(4000, max(10, copies, target_ms / max(est_ms, 1e-4))))
+    reps = -(-reps // copies) * copies
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(copies, 4)):
+            fn_on(side.cuda_stream, i)
+    side.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(reps):
+            fn_on(side.cuda_stream, i)
+    cur = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        g.replay()
+        torch.cuda.synchronize()
+    if mark is not None:
+        mark(cur.cuda_stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(replays):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * replays)
+    del g
+    return ms, reps
+
+
+# Separator launches for kernel traces: an empty kernel of `code` workgroups
+# is enqueued before each timed phase of job j (code = 16 + 4j + phase; phase
+# 0: per-launch event timing, 1: graph replays, 2: end of the job), so a
+# rocprofv3 kernel trace of a sweep splits into jobs by these dispatches.
+def mark_code(job: int, phase: int) -> int:
+    return 16 + 4 * job + phase
+
+
+def _mark(job, phase):
+    import dense_fp32_gemm_sgemm_amd as sg
+
+    def fn(handle):
+        assert sg.sgemm_ceiling_empty(mark_code(job, phase), handle) == 0
+    return fn
+
+
 class Problem:
     """Device buffers of one GEMM and a zero-overhead launcher."""
 
-    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real", ops="NN", batch=1):
+    def __init__(self, M, N, K, alpha=1.0, beta=0.0, seed=0, kind="real", ops="NN", batch=1,
+                 copies=1, ws=False):
         torch = _torch()
         import numpy as np
         from workloads import draw
@@ -199,35 +279,60 @@ class Problem:
         self.strides = ((self.A.stride(0), self.B.stride(0), self.C.stride(0)) if batch > 1
                         else (0, 0, 0))
         self.stream = torch.cuda.current_stream()
+        # With ws: calls go through the workspace entry point, with the
+        # largest workspace any problem can use (zero-filled once).
+        self.ws = torch.zeros(WS_BYTES, dtype=torch.uint8, device="cuda") if ws else None
+        # Further copies of every operand (same values) for cold-cache timing.
+        self.sets = [(self.A, self.B, self.C)]
+        for _ in range(copies - 1):
+            self.sets.append((self.A.clone(), self.B.clone(), self.C.clone()))
 
-    def launcher(self, variant=-1):
+    def launcher_on(self, variant=-1):
+        """fn(handle, i): one call on stream `handle` with operand copy
+        i % copies; raises on a non-zero status."""
         import dense_fp32_gemm_sgemm_amd as sg
         sa, sb, sc = self.strides
-        args = (int(self.ta), int(self.tb), self.M, self.N, self.K, float(self.alpha),
-                self.A.data_ptr(), self.lda, sa, self.B.data_ptr(), self.ldb, sb, float(self.beta),
-                self.C.data_ptr(), max(1, self.N), sc, self.batch, self.stream.cuda_stream, variant)
-        fn_ex = sg.load().sgemm_strided_batched_ex
+        ptrs = [(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in self.sets]
+        head = (int(self.ta), int(self.tb), self.M, self.N, self.K, float(self.alpha))
+        if self.ws is None:
+            fn_ex = sg.load().sgemm_strided_batched_ex
+            tail = ()
+        else:
+            fn_ex = sg.load().sgemm_strided_batched_ws_ex
+            tail = (self.ws.data_ptr(), WS_BYTES)
 
-        def fn():
-            st = fn_ex(*args)
+        def fn(handle, i=0):
+            pa, pb, pc = ptrs[i % len(ptrs)]
+            st = fn_ex(*head, pa, self.lda, sa, pb, self.ldb, sb, float(self.beta), pc,
+                       max(1, self.N), sc, self.batch, *tail, handle, variant)
             if st != 0:
                 raise RuntimeError("sgemm status %d: %s" % (st, sg.sgemm_status_string(st)))
         return fn
+
+    def launcher(self, variant=-1):
+        """fn(): one call on the problem's stream."""
+        on = self.launcher_on(variant)
+        h = self.stream.cuda_stream
+        return lambda: on(h)
 
     def variant_name(self, variant=-1):
         import dense_fp32_gemm_sgemm_amd as sg
         if variant >= 0:
             return sg.sgemm_variant_name(variant)
         sa, sb, sc = self.strides
-        v = sg.sgemm_strided_batched_select_variant(
-            int(self.ta), int(self.tb), self.M, self.N, self.K, self.alpha, self.A.data_ptr(),
-            self.lda, sa, self.B.data_ptr(), self.ldb, sb, self.beta, self.C.data_ptr(),
-            max(1, self.N), sc, self.batch)
+        args = (int(self.ta), int(self.tb), self.M, self.N, self.K, self.alpha, self.A.data_ptr(),
+                self.lda, sa, self.B.data_ptr(), self.ldb, sb, self.beta, self.C.data_ptr(),
+                max(1, self.N), sc, self.batch)
+        if self.ws is None:
+            v = sg.sgemm_strided_batched_select_variant(*args)
+        else:
+            v = sg.sgemm_strided_batched_ws_select_variant(*args, WS_BYTES)
         return sg.sgemm_variant_name(v) if v >= 0 else "none"
 
 
 def measure_ceilings(samples: int = 15):
-    """Measured FP32 matrix-core, FP32 vector and HBM copy rates."""
+    """Measured FP32 matrix-core and vector rates, HBM copy and read-only
+    stream rates, and the dispatch floor."""
     torch = _torch()
     import dense_fp32_gemm_sgemm_amd as sg
     stream = torch.cuda.current_stream()
@@ -278,7 +383,29 @@ def measure_ceilings(samples: int = 15):
         total, _ = time_steps(cp, 1, stream)
         vals.append(2 * 4 * n / (total * 1e-3) / 1e9)
     out["hbm_copy_gbs"] = statistics.median(vals)
-    del src, dst
+    del dst
+    # Read-only stream over 2 GiB (eight times the last-level cache), so every
+    # launch reads HBM; the grid is swept and the best median kept.
+    n2 = 2 * n
+    big = torch.ones(n2, dtype=torch.float32, device="cuda")
+    del src
+    rsink = torch.empty(NUM_CUS * 32 * 256, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for per_cu in (4, 8, 16, 32):
+        rd = lambda: sg.sgemm_ceiling_read(big.data_ptr(), n2, NUM_CUS * per_cu, rsink.data_ptr(), h)
+        wake(0.1, rd)
+        vals = []
+        for _ in range(samples):
+            total, _ = time_steps(rd, 1, stream)
+            vals.append(4 * n2 / (total * 1e-3) / 1e9)
+        med = statistics.median(vals)
+        if med > best:
+            best, out["hbm_read_grid_per_cu"] = med, per_cu
+    out["hbm_read_gbs"] = best
+    del big, rsink
+    # Dispatch floor: an empty one-workgroup kernel, back to back in a graph.
+    out["dispatch_floor_us"] = device_ms_per_call(lambda hh, i: sg.sgemm_ceiling_empty(1, hh), 0.002,
+                                                  target_ms=1.0)[0] * 1e3
     return out
 
 
@@ -331,9 +458,15 @@ def clock_under_load(fn, settle_s: float = 1.0, limit_s: float = 20.0):
         return None
 
 
-def cpu_baseline(target_s: float = 12.0):
+def cpu_baseline(target_s: float = 12.0, check=None):
     """The oracle (as it stands) on a bounded row sample of the 4096^3
-    workload, on the host cores."""
+    workload, on the host cores.
+
+    check: optional (C, ncols) -- the GPU's 4096^3 result (numpy float32) and
+    a number of whole columns; the rows the oracle timing produced, plus
+    `ncols` seeded columns (each crosses every tile row), are compared with C
+    and the normalized error max |C - C_ref| / (sum_k |A_ik||B_kj|) is added
+    to the record ("check")."""
     import numpy as np
     import oracle
     from workloads import HEADLINE, draw_workload, sweep_workloads
@@ -347,9 +480,23 @@ def cpu_baseline(target_s: float = 12.0):
     nrows = int(min(HEADLINE.M, max(rows, rows * target_s / max(dt, 1e-6))))
     sel = np.arange(nrows)
     t0 = time.perf_counter()
-    oracle.gemm(A, B, rows=sel)
+    ref, den = oracle.gemm(A, B, rows=sel)
     dt = time.perf_counter() - t0
     gfl = flops(nrows, HEADLINE.N, HEADLINE.K) / dt / 1e9
+    rec = {"value": round(gfl, 3), "unit": "GFLOPS", "cores": oracle.max_threads(),
+           "kind": "oracle",
+           "sample": "first %d of 4096 output rows of the 4096^3 workload (fp64 i-k-j "
+                     "oracle, OpenMP over rows), %.1f s" % (nrows, dt)}
+    if check is not None:
+        C, ncols = check
+        err_r = oracle.normalized_error(C[sel], ref, den)
+        cols = np.sort(np.random.default_rng(4096).choice(HEADLINE.N, size=ncols, replace=False))
+        cref, cden = oracle.gemm(A, B, cols=cols)
+        err_c = oracle.normalized_error(C[:, cols], cref, cden)
+        rec["check"] = {"max_norm_err": max(err_r, err_c), "rows": int(nrows), "cols": int(ncols),
+                        "what": "the C left by the timed calls against the oracle: the first %d "
+                                "whole rows and %d seeded whole columns" % (nrows, ncols)}
+    del ref, den
     # The other sizes the oracle is quoted at: all of 256^3, and a row sample
     # of 8192^3 (about a second of CPU time together).
     by_size = {}
@@ -359,11 +506,8 @@ def cpu_baseline(target_s: float = 12.0):
         oracle.gemm(An, Bn, rows=np.arange(r))
         by_size["%d^3 (%d rows)" % (n, r)] = round(flops(r, n, n) / (time.perf_counter() - t0) / 1e9, 3)
         del An, Bn
-    return {"value": round(gfl, 3), "unit": "GFLOPS", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": "first %d of 4096 output rows of the 4096^3 workload (fp64 i-k-j "
-                      "oracle, OpenMP over rows), %.1f s" % (nrows, dt),
-            "by_size": by_size}
+    rec["by_size"] = by_size
+    return rec
 
 
 def stored_traffic(variant: str):
@@ -383,25 +527,87 @@ def stored_traffic(variant: str):
 
 def vendor_context(prob: Problem, steps: int, warmup: int):
     """torch.mm on the same device tensors with TF32 off: the vendor BLAS in
-    strict FP32, timed the same way.  A reported stopwatch, not part of the
-    library; beta = 0 problems only (torch.mm overwrites its output)."""
+    strict FP32, timed the same two ways as the library.  A reported
+    stopwatch, not part of the library; beta = 0 problems only (torch.mm
+    overwrites its output)."""
     torch = _torch()
-    if prob.beta != 0.0 or prob.ta or prob.tb:
+    if prob.beta != 0.0 or prob.ta or prob.batch != 1:
         return {}
     prev = torch.backends.cuda.matmul.allow_tf32
     torch.backends.cuda.matmul.allow_tf32 = False
+    out = {}
     try:
-        A, B, C = prob.A, prob.B, prob.C
+        A, C = prob.A, prob.C
+        B = prob.B.t() if prob.tb else prob.B
         fn = lambda: torch.mm(A, B, out=C)
         for _ in range(warmup):
             fn()
-        wake(0.25, fn)
+        wake(0.1, fn)
         _, per = time_steps(fn, steps, torch.cuda.current_stream())
+        ms = statistics.median(per)
+        out["torch_mm_us_launch"] = round(ms * 1e3, 2)
+        try:
+            dev, _ = device_ms_per_call(lambda h, i: fn(), ms)
+            out["torch_mm_us_device"] = round(dev * 1e3, 2)
+        except Exception as e:  # capture refused: keep the launch figure only
+            out["torch_mm_graph_error"] = type(e).__name__
     finally:
         torch.backends.cuda.matmul.allow_tf32 = prev
-    ms = statistics.median(per)
-    return {"torch_mm_fp32_ms_median": round(ms, 5),
-            "torch_mm_fp32_gflops": round(flops(prob.M, prob.N, prob.K) / (ms * 1e-3) / 1e9, 1)}
+    best = out.get("torch_mm_us_device", out["torch_mm_us_launch"])
+    out["torch_mm_tflops"] = round(flops(prob.M, prob.N, prob.K) / (best * 1e-6) / 1e12, 2)
+    return out
+
+
+def binding_roof(work: float, nbytes: float, us: float, ceil) -> dict:
+    """The roof that binds one call: the largest of its floors -- the matrix-
+    core time (work at the measured 32x32x2 FP32 rate), the HBM time (the
+    algorithmic bytes at the measured read-only stream rate; writes priced as
+    reads, which only lowers this floor) and the dispatch floor (an empty
+    kernel) -- and the call's fraction of it."""
+    t = {"mfma": work / (ceil["mfma_f32_32x32x2_tflops"] * 1e12) * 1e6,
+         "hbm": nbytes / (ceil["hbm_read_gbs"] * 1e9) * 1e6}
+    if ceil.get("dispatch_floor_us"):
+        t["latency"] = ceil["dispatch_floor_us"]
+    bound = max(t, key=t.get)
+    return {"bound": bound, "frac_of_bound": round(t[bound] / us, 4),
+            "floor_us": {k: round(v, 3) for k, v in t.items()},
+            "frac_measured_mfma": round(t["mfma"] / us, 4),
+            "frac_datasheet": round(work / (us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+
+
+DATASHEET_CEILINGS = {"mfma_f32_32x32x2_tflops": PEAK_FP32_TFLOPS, "hbm_read_gbs": PEAK_HBM_GBS,
+                      "dispatch_floor_us": None, "source": "datasheet"}
+
+
+def time_call(prob: Problem, variant: int, steps: int, warmup: int, job: int, cold=False):
+    """Times one problem both ways (see the module docstring); with cold,
+    also on rotated operand copies (a second Problem with enough copies to
+    exceed 1 GiB).  Trace separators mark the phases of `job`."""
+    torch = _torch()
+    fn = prob.launcher(variant)
+    for _ in range(warmup):
+        fn()
+    wake(0.1, fn)
+    h = prob.stream.cuda_stream
+    _mark(job, 0)(h)
+    _, per = time_steps(fn, steps, prob.stream)
+    launch_ms = statistics.median(per)
+    dev_ms, reps = device_ms_per_call(prob.launcher_on(variant), launch_ms, mark=_mark(job, 1))
+    _mark(job, 2)(h)
+    rec = {"job": job, "us_launch": round(launch_ms * 1e3, 3), "us_launch_min": round(min(per) * 1e3, 3),
+           "us_device": round(dev_ms * 1e3, 3), "graph_reps": reps, "graph_replays": 20}
+    if cold:
+        nb = prob.batch * min_bytes(prob.M, prob.N, prob.K, prob.beta)
+        copies = int(min(256, -(-1.5 * 2 ** 30 // nb)))
+        cp = Problem(prob.M, prob.N, prob.K, prob.alpha, prob.beta, seed=0,
+                     ops=("T" if prob.ta else "N") + ("T" if prob.tb else "N"), batch=prob.batch,
+                     copies=copies, ws=prob.ws is not None)
+        cold_ms, _ = device_ms_per_call(cp.launcher_on(variant), dev_ms, copies=copies)
+        rec["us_cold"] = round(cold_ms * 1e3, 3)
+        rec["cold_copies"] = copies
+        del cp
+        torch.cuda.empty_cache()
+    return rec
 
 
 def bench_problem(prob: Problem, steps: int, warmup: int, variant=-1):
@@ -442,7 +648,29 @@ def main(argv=None):
                     help="with --sweep/--shape: also time torch.mm in strict FP32 (context only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--ws", action="store_true",
+                    help="non-contract modes: call the workspace entry point (4 KiB + 32 MiB workspace)")
+    ap.add_argument("--cold", action="store_true",
+                    help="non-contract modes: also time on rotated operand copies past the 256 MB cache")
+    ap.add_argument("--shapes-from", metavar="FILE",
+                    help="extra shapes, one 'M N K' per line (with --sweep: added to it)")
+    ap.add_argument("--job0", type=int, default=0,
+                    help="first job number of the trace separators (to merge several runs)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "RUN_LOG"),
+                    help="print a markdown table of kernel-only times from a rocprofv3 kernel "
+                         "trace and the JSON lines of the run it traced (no GPU needed)")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("COUNTER_CSV", "RUN_LOG"),
+                    help="per-job mean counters from a rocprofv3 counter_collection.csv and the "
+                         "JSON lines of the run it profiled (no GPU needed)")
     args = ap.parse_args(argv)
+
+    if args.trace_summary:
+        sys.stdout.write(trace_summary(*args.trace_summary))
+        return 0
+    if args.counter_summary:
+        for rec in counter_summary(*args.counter_summary):
+            print(json.dumps(rec))
+        return 0
 
     if args.traffic_from:
         from_ = args.traffic_from
@@ -471,7 +699,8 @@ def main(argv=None):
 
     if args.few_rows:
         return few_rows(args)
-    if args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib:
+    if (args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib
+            or args.shapes_from):
         return run_modes(args)
 
     M = N = K = 4096
@@ -482,11 +711,15 @@ def main(argv=None):
     kern_ms = statistics.mean(per)
     value = flops(M, N, K) / (ms_step * 1e-3) / 1e9
     achieved = flops(M, N, K) / (kern_ms * 1e-3) / 1e12
+    # The C the timed calls left behind (beta = 0: every call rewrites it).
+    torch.cuda.synchronize()
+    timed_c = prob.C.cpu().numpy()
 
     clocks = None if args.no_ceilings else clock_under_load(prob.launcher(args.variant))
     ceilings = None if args.no_ceilings else measure_ceilings()
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(check=(timed_c, 256))
     traffic = stored_traffic(vname)
+    check = cpu.pop("check") if cpu else None
 
     line = {
         "metric": METRIC,
@@ -512,15 +745,23 @@ def main(argv=None):
                      "kernel_ms_std": round(statistics.pstdev(per), 5),
                      "kernel_ms_min": round(min(per), 5), "kernel_ms_max": round(max(per), 5)},
         "cpu_baseline": cpu,
+        "max_norm_err": None if check is None else float("%.4g" % check["max_norm_err"]),
+        "check": check,
         "gpu_clocks": clocks,
     }
     if ceilings:
         mf = ceilings["mfma_f32_32x32x2_tflops"]
         line["measured_ceilings"] = {k: round(v, 2) for k, v in ceilings.items()}
         line["pct_of_measured_mfma_f32"] = round(100.0 * value / 1e3 / mf, 2)
+        # above 100: the matrix cores outrun unpacked v_fma_f32 (packed FP32
+        # vector instructions are switched off in this build)
         line["pct_of_measured_valu_f32"] = round(100.0 * value / 1e3 / ceilings["valu_fma_f32_tflops"], 2)
         line["pct_of_datasheet_fp32"] = round(100.0 * value / 1e3 / PEAK_FP32_TFLOPS, 2)
     print(json.dumps(line), flush=True)
+    if check is not None and not check["max_norm_err"] <= 1e-5:
+        print("bench: timed 4096^3 result fails the oracle check (normalized error %.3g > 1e-5)"
+              % check["max_norm_err"], file=sys.stderr)
+        return 3
     return 0
 
 
@@ -530,38 +771,54 @@ FEW_ROWS_NK = ((4096, 4096), (8192, 8192), (16384, 16384), (1024, 4096), (2048, 
 
 
 def few_rows(args):
-    """Median kernel time (us) of the automatic choice, of each few-rows
+    """Per shape and orientation of B: the automatic choice, each few-rows
     candidate forced (vector-unit kernel, split-K 64x64 tiles, matrix-core
-    kernel) and of torch.mm in strict FP32, per shape and orientation of B."""
+    kernel) and torch.mm in strict FP32, each timed per launch and on the
+    device (graph replays); the automatic choice also cold."""
     import dense_fp32_gemm_sgemm_amd as sg
     torch = _torch()
     names = sg.variant_names()
     cands = [names.index(n) for n in ("skinny_m8", "mfma16_64x64x64_4x2_pipe_splitk", "fewrows_m32")]
+    ceil = _sweep_ceilings(args)
+    job = args.job0
     for M in FEW_ROWS_M:
         for N, K in FEW_ROWS_NK:
             for ops in ("NN", "NT"):
                 prob = Problem(M, N, K, ops=ops)
                 rec = {"mode": "few-rows", "M": M, "N": N, "K": K, "ops": ops,
-                       "auto": prob.variant_name(-1)}
+                       "auto": prob.variant_name(-1), "jobs": {}}
                 for v in [-1] + cands:
-                    _, per = bench_problem(prob, args.steps, min(args.warmup, args.steps), v)
-                    rec["us_" + ("auto" if v < 0 else names[v])] = round(statistics.median(per) * 1e3, 2)
-                prev = torch.backends.cuda.matmul.allow_tf32
-                torch.backends.cuda.matmul.allow_tf32 = False
-                try:
-                    Bm = prob.B.t() if prob.tb else prob.B
-                    fn = lambda: torch.mm(prob.A, Bm, out=prob.C)
-                    for _ in range(min(args.warmup, args.steps)):
-                        fn()
-                    wake(0.1, fn)
-                    _, per = time_steps(fn, args.steps, torch.cuda.current_stream())
-                finally:
-                    torch.backends.cuda.matmul.allow_tf32 = prev
-                rec["us_torch_mm_fp32"] = round(statistics.median(per) * 1e3, 2)
+                    key = "auto" if v < 0 else names[v]
+                    t = time_call(prob, v, args.steps, min(args.warmup, args.steps), job,
+                                  cold=(v < 0 and args.cold))
+                    rec["jobs"][key] = job
+                    job += 1
+                    rec["us_launch_" + key] = t["us_launch"]
+                    rec["us_device_" + key] = t["us_device"]
+                    rec["reps_" + key] = t["graph_reps"]
+                    if "us_cold" in t:
+                        rec["us_cold_auto"] = t["us_cold"]
+                nb = min_bytes(M, N, K)
+                rec["auto_gbs_device"] = round(nb / (rec["us_device_auto"] * 1e-6) / 1e9, 1)
+                if "us_cold_auto" in rec:
+                    rec["auto_gbs_cold"] = round(nb / (rec["us_cold_auto"] * 1e-6) / 1e9, 1)
+                rec.update(binding_roof(flops(M, N, K), nb, rec.get("us_cold_auto", rec["us_device_auto"]),
+                                        ceil))
+                rec.update(vendor_context(prob, args.steps, min(args.warmup, args.steps)))
                 print(json.dumps(rec), flush=True)
                 del prob
                 torch.cuda.empty_cache()
     return 0
+
+
+def _sweep_ceilings(args):
+    if args.no_ceilings:
+        return DATASHEET_CEILINGS
+    c = measure_ceilings(samples=7)
+    c["source"] = "measured"
+    print(json.dumps({"mode": "ceilings", **{k: (round(v, 3) if isinstance(v, float) else v)
+                                              for k, v in c.items()}}), flush=True)
+    return c
 
 
 def run_modes(args):
@@ -581,13 +838,36 @@ def run_modes(args):
                           "dispatches": 3}), flush=True)
         return 0
     if args.profile:
-        shape = tuple(args.shape) if args.shape else (4096, 4096, 4096)
-        prob = Problem(*shape, args.alpha, args.beta, seed=0, ops=args.ops)
-        total, per = bench_problem(prob, args.steps, args.warmup, args.variant)
-        kern_ms = statistics.mean(per)
-        print(json.dumps({"mode": "profile", "shape": shape, "variant": prob.variant_name(args.variant),
-                          "steps": args.steps, "kernel_ms_mean": round(kern_ms, 5),
-                          "tflops": round(flops(*shape) / (kern_ms * 1e-3) / 1e12, 2)}), flush=True)
+        # only timed calls (no graph, no ceilings): the command to run under
+        # rocprofv3; several shapes (--shapes-from) are split by separators
+        if args.shapes_from:
+            with open(args.shapes_from) as f:
+                shapes = [tuple(int(x) for x in line.split()[:3]) for line in f
+                          if line.strip() and not line.startswith("#")]
+        else:
+            shapes = [tuple(args.shape) if args.shape else (4096, 4096, 4096)]
+        for j, shape in enumerate(shapes):
+            prob = Problem(*shape, args.alpha, args.beta, seed=0, ops=args.ops, batch=args.batch,
+                           ws=args.ws)
+            fn = prob.launcher(args.variant)
+            for _ in range(args.warmup):
+                fn()
+            torch_ = _torch()
+            torch_.cuda.synchronize()
+            _mark(args.job0 + j, 1)(prob.stream.cuda_stream)
+            _, per = time_steps(fn, args.steps, prob.stream)
+            _mark(args.job0 + j, 2)(prob.stream.cuda_stream)
+            kern_ms = statistics.mean(per)
+            print(json.dumps({"mode": "profile", "job": args.job0 + j, "M": shape[0], "N": shape[1],
+                              "K": shape[2], "ops": args.ops, "batch": args.batch,
+                              "variant": prob.variant_name(args.variant), "steps": args.steps,
+                              "graph_reps": args.steps, "graph_replays": 1,
+                              "us_device": round(kern_ms * 1e3, 3), "us_launch": round(kern_ms * 1e3, 3),
+                              "kernel_ms_mean": round(kern_ms, 5),
+                              "tflops": round(args.batch * flops(*shape) / (kern_ms * 1e-3) / 1e12, 2)}),
+                  flush=True)
+            del prob
+            torch_.cuda.empty_cache()
         return 0
     if args.sweep:
         jobs = ([((n, n, n), -1) for n in SWEEP_SIZES] + [(s, -1) for s in RAGGED_SHAPES] +
@@ -601,31 +881,154 @@ def run_modes(args):
         jobs = [(shape, v) for v in range(sg.sgemm_num_variants())]
     elif args.shape:
         jobs = [(tuple(args.shape), args.variant)]
-    for shape, v in jobs:
+    if args.shapes_from:
+        with open(args.shapes_from) as f:
+            extra = [tuple(int(x) for x in line.split()[:3]) for line in f
+                     if line.strip() and not line.startswith("#")]
+        jobs = [(sh, args.variant) for sh in extra] if not (args.sweep or args.matrix) else jobs + [
+            (sh, -1) for sh in extra]
+    ceil = _sweep_ceilings(args)
+    mode = "sweep" if args.sweep else ("matrix" if args.matrix else "variant")
+    for j, (shape, v) in enumerate(jobs):
         M, N, K = shape
-        prob = Problem(M, N, K, args.alpha, args.beta, seed=0, ops=args.ops, batch=args.batch)
+        prob = Problem(M, N, K, args.alpha, args.beta, seed=0, ops=args.ops, batch=args.batch,
+                       ws=args.ws)
         name = prob.variant_name(v)
         work = flops(M, N, K) * args.batch
+        nb = args.batch * min_bytes(M, N, K, args.beta)
         steps = max(5, min(args.steps, int(2e12 / max(work, 1.0))))
         if name == "simple" and work > 1e11:
             steps = 3
-        total, per = bench_problem(prob, steps, min(args.warmup, steps), v)
-        kern_ms = statistics.median(per)
-        rec = {"mode": "sweep" if args.sweep else ("matrix" if args.matrix else "variant"),
-               "ops": args.ops, "batch": args.batch, "M": M, "N": N, "K": K,
-               "beta": args.beta, "variant": name, "steps": steps,
-               "kernel_ms_median": round(kern_ms, 5), "kernel_ms_min": round(min(per), 5),
-               "gflops": round(work / (kern_ms * 1e-3) / 1e9, 1),
-               "frac_fp32_peak": round(work / (kern_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
-               "ai_flop_per_byte": round(arithmetic_intensity(M, N, K, args.beta), 2),
-               "hbm_gbs_at_min_bytes": round(args.batch * min_bytes(M, N, K, args.beta) /
-                                             (kern_ms * 1e-3) / 1e9, 1)}
-        if args.vendor and args.ops == "NN" and args.batch == 1 and v == -1:
+        cold = args.cold and nb >= 4e6
+        t = time_call(prob, v, steps, min(args.warmup, steps), args.job0 + j, cold=cold)
+        us = t["us_device"]
+        rec = {"mode": mode, "ops": args.ops, "batch": args.batch, "M": M, "N": N, "K": K,
+               "beta": args.beta, "variant": name, "workspace": bool(args.ws), "steps": steps, **t,
+               "tflops_device": round(work / (us * 1e-6) / 1e12, 3),
+               "tflops_launch": round(work / (t["us_launch"] * 1e-6) / 1e12, 3),
+               "ai_flop_per_byte": round(work / nb, 2),
+               "hbm_gbs_device": round(nb / (us * 1e-6) / 1e9, 1)}
+        if "us_cold" in t:
+            rec["hbm_gbs_cold"] = round(nb / (t["us_cold"] * 1e-6) / 1e9, 1)
+        # judged on the cold time where the bytes bind, else the warm one
+        roof = binding_roof(work, nb, us, ceil)
+        if roof["bound"] == "hbm" and "us_cold" in t:
+            roof = binding_roof(work, nb, t["us_cold"], ceil)
+            roof["judged_on"] = "us_cold"
+        rec.update(roof)
+        if args.vendor and args.batch == 1 and v == -1:
             rec.update(vendor_context(prob, steps, min(args.warmup, steps)))
         print(json.dumps(rec), flush=True)
         del prob
         _torch().cuda.empty_cache()
     return 0
+
+
+def trace_summary(trace_csv: str, log_path: str, title: str = "") -> str:
+    """Markdown table of kernel-only time per call, from a rocprofv3 kernel
+    trace (csv) of a --sweep / --shape / --few-rows run and the JSON lines
+    that run printed: the dispatches between a job's graph-phase separators
+    are that job's graph replays (graph_reps x graph_replays calls)."""
+    import csv
+    with open(trace_csv) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    recs = {}
+    with open(log_path) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            r = json.loads(line)
+            if "job" in r:
+                recs[r["job"]] = r
+            for key, j in r.get("jobs", {}).items():
+                recs[j] = dict(r, variant=(r["auto"] if key == "auto" else key), job=j,
+                               us_device=r["us_device_" + key], us_launch=r["us_launch_" + key],
+                               graph_reps=r["reps_" + key], graph_replays=20)
+    per_job = {}
+    cur = None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "empty_kernel" in name:
+            wg = max(1, int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 64))
+            code = int(r.get("Grid_Size_X") or r.get("Grid_Size")) // wg
+            job, phase = divmod(code - 16, 4)
+            cur = job if phase == 1 else None
+            continue
+        if cur is None:
+            continue
+        d = per_job.setdefault(cur, {"ns": 0, "n": 0, "kernels": {}})
+        d["ns"] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        d["n"] += 1
+        short = name.split("(")[0].replace("void ", "")
+        d["kernels"][short] = d["kernels"].get(short, 0) + 1
+    out = []
+    if title:
+        out.append(title)
+        out.append("")
+    out.append("| job | M x N x K | ops | variant | dispatches / call | kernel-only us | "
+               "graph us | launch us | TFLOP/s (kernel-only) |")
+    out.append("|---|---|---|---|---|---|---|---|---|")
+    for job in sorted(per_job):
+        r = recs.get(job)
+        if r is None:
+            continue
+        calls = r["graph_reps"] * r["graph_replays"]
+        d = per_job[job]
+        if not calls:
+            continue
+        us = d["ns"] / calls / 1e3
+        work = flops(r["M"], r["N"], r["K"]) * r.get("batch", 1)
+        out.append("| %d | %dx%dx%d | %s | %s | %.2f | %.2f | %.2f | %.2f | %.1f |" % (
+            job, r["M"], r["N"], r["K"], r.get("ops", "NN"), r["variant"], d["n"] / calls, us,
+            r["us_device"], r["us_launch"], work / (us * 1e-6) / 1e12))
+    return "\n".join(out) + "\n"
+
+
+def counter_summary(counter_csv: str, log_path: str) -> list:
+    """Per job of a traced run (--profile / --sweep): the mean of each
+    counter over the job's GEMM dispatches (separators and C-scaling
+    launches left out), from a rocprofv3 counter_collection.csv."""
+    import csv
+    with open(counter_csv) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    recs = {}
+    with open(log_path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                r = json.loads(line)
+                if "job" in r:
+                    recs[r["job"]] = r
+    cur, per = None, {}
+    seen = set()
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "empty_kernel" in name:
+            if r["Dispatch_Id"] in seen:
+                continue
+            seen.add(r["Dispatch_Id"])
+            wg = max(1, int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 64))
+            code = int(r.get("Grid_Size_X") or r.get("Grid_Size")) // wg
+            job, phase = divmod(code - 16, 4)
+            cur = job if phase == 1 else None
+            continue
+        if cur is None or "scale_kernel" in name:
+            continue
+        d = per.setdefault(cur, {"kernel": name, "vals": {}, "dispatches": set()})
+        d["dispatches"].add(r["Dispatch_Id"])
+        d["vals"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = []
+    for job in sorted(per):
+        r = recs.get(job, {})
+        d = per[job]
+        out.append({"job": job, "M": r.get("M"), "N": r.get("N"), "K": r.get("K"),
+                    "variant": r.get("variant"), "kernel": d["kernel"],
+                    "dispatches": len(d["dispatches"]),
+                    "counters": {k: sum(v) / len(v) for k, v in d["vals"].items()}})
+    return out
 
 
 if __name__ == "__main__":

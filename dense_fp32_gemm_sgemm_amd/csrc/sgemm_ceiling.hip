@@ -9,7 +9,11 @@
 //     v_mfma_f32_16x16x4f32 on 8 independent accumulators per wave;
 //   * the FP32 vector rate: 16 independent v_fma_f32 chains per lane;
 //   * the HBM rate: a 16-byte-per-lane streaming copy, which is also the
-//     "plain copy of known size" used to calibrate the HBM byte counters.
+//     "plain copy of known size" used to calibrate the HBM byte counters,
+//     and a read-only stream with eight 16-byte loads in flight per lane,
+//     the roof for kernels that mostly read (a GEMM with few rows or
+//     columns streams one operand and writes little);
+//   * the dispatch floor: an empty kernel, the least time any launch takes.
 // Every launch fills every SIMD of every CU: `blocks` workgroups of 256
 // threads (four waves); callers pass a multiple of the CU count.
 #include "../../include/sgemm_ceiling.h"
@@ -85,6 +89,33 @@ __global__ __launch_bounds__(kCeilThreads) void copy_kernel(const floatx4 *__res
     dst[i] = src[i];
 }
 
+// Read-only stream: each lane keeps kReadDepth 16-byte loads in flight per
+// step and folds them into one sum (written per thread, so the loads stay
+// live).  A grid-stride loop over whole steps; the rest (fewer than one
+// step of the grid) is read one vector at a time.
+constexpr int kReadDepth = 8;
+
+__global__ __launch_bounds__(kCeilThreads) void read_kernel(const floatx4 *__restrict__ src, long long n4,
+                                                            float *__restrict__ sink) {
+  const long long nthreads = (long long)gridDim.x * kCeilThreads;
+  const long long tid = (long long)blockIdx.x * kCeilThreads + threadIdx.x;
+  const long long step = nthreads * kReadDepth;
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  long long base = 0;
+  for (; base + step <= n4; base += step) {
+    floatx4 v[kReadDepth];
+#pragma unroll
+    for (int u = 0; u < kReadDepth; ++u) v[u] = __builtin_nontemporal_load(src + base + u * nthreads + tid);
+#pragma unroll
+    for (int u = 0; u < kReadDepth; ++u) acc += v[u];
+  }
+  for (long long i = base + tid; i < n4; i += nthreads) acc += src[i];
+  sink[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Does nothing: its duration is the dispatch floor of a launch.
+__global__ void empty_kernel() {}
+
 }  // namespace sg950
 
 extern "C" {
@@ -121,6 +152,22 @@ int sgemm_ceiling_copy(const float *src, float *dst, long long n, int blocks, vo
   hipLaunchKernelGGL(sg950::copy_kernel, dim3(blocks), dim3(sg950::kCeilThreads), 0, s,
                      reinterpret_cast<const sg950::floatx4 *>(src),
                      reinterpret_cast<sg950::floatx4 *>(dst), n / 4);
+  return hipGetLastError() == hipSuccess ? 0 : SGEMM_CEIL_ERR_LAUNCH;
+}
+
+int sgemm_ceiling_read(const float *src, long long n, int blocks, float *sink, void *stream) {
+  if (src == nullptr || sink == nullptr || n < 0 || (n % 4) != 0 || blocks <= 0) return SGEMM_CEIL_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(src) & 15) return SGEMM_CEIL_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(sg950::read_kernel, dim3(blocks), dim3(sg950::kCeilThreads), 0, s,
+                     reinterpret_cast<const sg950::floatx4 *>(src), n / 4, sink);
+  return hipGetLastError() == hipSuccess ? 0 : SGEMM_CEIL_ERR_LAUNCH;
+}
+
+int sgemm_ceiling_empty(int blocks, void *stream) {
+  if (blocks <= 0) return SGEMM_CEIL_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(sg950::empty_kernel, dim3(blocks), dim3(64), 0, s);
   return hipGetLastError() == hipSuccess ? 0 : SGEMM_CEIL_ERR_LAUNCH;
 }
 

@@ -45,6 +45,25 @@ int sgemm_ceiling_fma(int blocks, int iters, float *sink, void *stream, double *
  */
 int sgemm_ceiling_copy(const float *src, float *dst, long long n, int blocks, void *stream);
 
+/*
+ * HBM read ceiling: streams n floats (n a multiple of 4, src 16-byte aligned)
+ * with `blocks` workgroups of 256 threads, eight 16-byte loads in flight per
+ * lane, and writes one partial sum per thread to `sink` (blocks*256 floats).
+ * Reads 4n bytes; a buffer well past the 256 MB last-level cache makes
+ * repeated launches read HBM.  maxxfuu ("Placing The Naive Kernel On The
+ * Roofline") places kernels under a bandwidth roof, and the Tinyforge README
+ * measures its roof rather than quoting it.
+ */
+int sgemm_ceiling_read(const float *src, long long n, int blocks, float *sink, void *stream);
+
+/*
+ * Dispatch floor: `blocks` workgroups of one wave that do nothing.  Its
+ * duration is the least time any kernel launch occupies the GPU, the floor
+ * under the smallest GEMMs of the sweep (the Tinyforge README warns that
+ * small-size timings mostly measure such overheads).
+ */
+int sgemm_ceiling_empty(int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

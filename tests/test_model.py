@@ -64,3 +64,84 @@ def test_bench_refuses_multi_gpu(capsys):
 def test_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def _write_trace(path, rows, counters=False):
+    import csv
+    keys = ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X",
+            "Grid_Size_X"] + (["Counter_Name", "Counter_Value"] if counters else [])
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=keys)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_trace_summary_splits_jobs_by_separators(tmp_path):
+    """Kernel-only time per call: the dispatches between a job's graph-phase
+    separator and its end separator, divided by the calls the log names."""
+    rows, t, d = [], 0, 0
+
+    def disp(name, dur, grid=256, wg=256):
+        nonlocal t, d
+        rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Start_Timestamp": t,
+                     "End_Timestamp": t + dur, "Workgroup_Size_X": wg, "Grid_Size_X": grid})
+        t += dur + 100
+        d += 1
+
+    sep = "sg950::empty_kernel()"
+    for job, dur, n_calls in ((0, 1000, 6), (1, 3000, 4)):
+        disp(sep, 10, grid=64 * bench.mark_code(job, 0), wg=64)
+        disp("void sg950::sched_kernel<...>(sg950::Problem)", 99999)   # eager phase: not counted
+        disp(sep, 10, grid=64 * bench.mark_code(job, 1), wg=64)
+        for _ in range(n_calls):
+            disp("void sg950::scale_kernel(int)", 200)
+            disp("void sg950::sched_kernel<...>(sg950::Problem)", dur)
+        disp(sep, 10, grid=64 * bench.mark_code(job, 2), wg=64)
+    tr = tmp_path / "kt.csv"
+    _write_trace(tr, rows)
+    log = tmp_path / "run.log"
+    with open(log, "w") as f:
+        f.write("not json\n")
+        f.write(json.dumps({"job": 0, "M": 64, "N": 64, "K": 64, "variant": "a", "graph_reps": 3,
+                            "graph_replays": 2, "us_device": 1.5, "us_launch": 7.0}) + "\n")
+        f.write(json.dumps({"job": 1, "M": 128, "N": 64, "K": 64, "variant": "b", "graph_reps": 2,
+                            "graph_replays": 2, "us_device": 3.5, "us_launch": 9.0}) + "\n")
+    table = bench.trace_summary(str(tr), str(log)).strip().splitlines()
+    assert len(table) == 4
+    r0 = [c.strip() for c in table[2].split("|")[1:-1]]
+    r1 = [c.strip() for c in table[3].split("|")[1:-1]]
+    assert r0[:4] == ["0", "64x64x64", "NN", "a"] and r0[4] == "2.00" and r0[5] == "1.20"
+    assert r1[4] == "2.00" and r1[5] == "3.20"
+
+
+def test_counter_summary_means_per_job(tmp_path):
+    rows = []
+    sep = "sg950::empty_kernel()"
+    did = 0
+    for job, vals in ((0, (10.0, 30.0)), (1, (5.0,))):
+        rows.append({"Dispatch_Id": did, "Kernel_Name": sep, "Start_Timestamp": 0, "End_Timestamp": 1,
+                     "Workgroup_Size_X": 64, "Grid_Size_X": 64 * bench.mark_code(job, 1),
+                     "Counter_Name": "X", "Counter_Value": 0})
+        did += 1
+        for v in vals:
+            rows.append({"Dispatch_Id": did, "Kernel_Name": "void sg950::scale_kernel(int)",
+                         "Start_Timestamp": 0, "End_Timestamp": 1, "Workgroup_Size_X": 256,
+                         "Grid_Size_X": 256, "Counter_Name": "X", "Counter_Value": 1e9})
+            did += 1
+            rows.append({"Dispatch_Id": did, "Kernel_Name": "void sg950::sched_kernel<1>()",
+                         "Start_Timestamp": 0, "End_Timestamp": 1, "Workgroup_Size_X": 256,
+                         "Grid_Size_X": 256, "Counter_Name": "X", "Counter_Value": v})
+            did += 1
+        rows.append({"Dispatch_Id": did, "Kernel_Name": sep, "Start_Timestamp": 0, "End_Timestamp": 1,
+                     "Workgroup_Size_X": 64, "Grid_Size_X": 64 * bench.mark_code(job, 2),
+                     "Counter_Name": "X", "Counter_Value": 0})
+        did += 1
+    p = tmp_path / "cc.csv"
+    _write_trace(p, rows, counters=True)
+    log = tmp_path / "run.log"
+    log.write_text(json.dumps({"job": 0, "M": 1, "N": 2, "K": 3, "variant": "v"}) + "\n")
+    out = bench.counter_summary(str(p), str(log))
+    assert [o["job"] for o in out] == [0, 1]
+    assert out[0]["counters"]["X"] == 20.0 and out[0]["dispatches"] == 2 and out[0]["M"] == 1
+    assert out[1]["counters"]["X"] == 5.0
