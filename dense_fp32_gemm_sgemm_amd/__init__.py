@@ -16,22 +16,28 @@ and the functions raise ``LibraryMissing`` when the library is not built.
 from __future__ import annotations
 
 from ._lib import (EXPORTS, LIBRARY, SGEMM_ATOMICS_ALLOWED,  # noqa: F401
-                   SGEMM_ATOMICS_NOT_ALLOWED, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM, SGEMM_ERR_LAUNCH,
+                   SGEMM_ATOMICS_NOT_ALLOWED, SGEMM_ERR_DEVICE, SGEMM_ERR_DIM, SGEMM_ERR_GRID,
+                   SGEMM_ERR_LAUNCH,
                    SGEMM_ERR_LD, SGEMM_ERR_OP, SGEMM_ERR_PTR, SGEMM_ERR_STRIDE,
                    SGEMM_ERR_VARIANT, SGEMM_NO_KERNEL, SGEMM_OK, SGEMM_OP_N, SGEMM_OP_T,
-                   LibraryMissing, load, sgemm, sgemm_ceiling_copy, sgemm_ceiling_fma,
-                   sgemm_ceiling_mfma, sgemm_ex, sgemm_get_atomics_mode, sgemm_num_variants,
-                   sgemm_op, sgemm_op_ex, sgemm_op_select_variant, sgemm_select_variant,
-                   sgemm_set_atomics_mode, sgemm_status_string, sgemm_strided_batched,
-                   sgemm_strided_batched_ex, sgemm_strided_batched_select_variant,
-                   sgemm_variant_name, sgemm_version)
+                   LibraryMissing, load, sgemm, sgemm_ceiling_copy, sgemm_ceiling_empty,
+                   sgemm_ceiling_fma, sgemm_ceiling_mfma, sgemm_ceiling_read, sgemm_ex,
+                   sgemm_get_atomics_mode, sgemm_num_variants, sgemm_op, sgemm_op_ex,
+                   sgemm_op_select_variant, sgemm_select_variant, sgemm_set_atomics_mode,
+                   sgemm_status_string, sgemm_strided_batched, sgemm_strided_batched_ex,
+                   sgemm_strided_batched_select_variant, sgemm_strided_batched_ws,
+                   sgemm_strided_batched_ws_ex, sgemm_strided_batched_ws_select_variant,
+                   sgemm_variant_name, sgemm_version, sgemm_workspace_size, SGEMM_ERR_WORKSPACE)
 
 __all__ = ["gemm", "gemm_batched", "variant_names", "sgemm", "sgemm_ex", "sgemm_op",
            "sgemm_op_ex", "sgemm_op_select_variant", "sgemm_strided_batched",
            "sgemm_strided_batched_ex", "sgemm_strided_batched_select_variant", "sgemm_num_variants",
+           "sgemm_strided_batched_ws", "sgemm_strided_batched_ws_ex",
+           "sgemm_strided_batched_ws_select_variant", "sgemm_workspace_size", "workspace",
            "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
            "sgemm_version", "sgemm_set_atomics_mode", "sgemm_get_atomics_mode",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",
+           "sgemm_ceiling_read", "sgemm_ceiling_empty",
            "LibraryMissing", "SgemmError"]
 
 
@@ -48,6 +54,11 @@ def variant_names():
 
 
 def _leading_dim(t, rows, cols, name):
+    """Leading dimension of a 2-D float32 tensor used as a row-major matrix.
+
+    Every row must be contiguous (unit column stride) whenever a row holds
+    more than one element, whatever the number of rows: a one-row view with a
+    column stride would otherwise be read or written as if it were packed."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -55,21 +66,40 @@ def _leading_dim(t, rows, cols, name):
         raise TypeError("%s must be float32, got %s" % (name, t.dtype))
     if t.dim() != 2:
         raise ValueError("%s must be 2-D" % name)
-    if not t.is_cuda:
-        raise ValueError("%s must be on a HIP device" % name)
     if tuple(t.shape) != (rows, cols):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (rows, cols)))
-    if rows > 1 and cols > 1 and t.stride(1) != 1:
+    if cols > 1 and t.stride(1) != 1:
         raise ValueError("%s must be row-major (stride(1) == 1)" % name)
     if rows <= 1:
         return max(1, cols)
-    if cols == 1 and t.stride(1) != 1:
-        return max(1, t.stride(0))
     return t.stride(0)
 
 
+def _same_hip_device(A, B, C):
+    for name, t in (("A", A), ("B", B), ("C", C)):
+        if not t.is_cuda:
+            raise ValueError("%s must be on a HIP device" % name)
+    if len({t.device for t in (A, B, C)}) != 1:
+        raise ValueError("A, B and C must be on the same device")
+
+
+def workspace(M: int, N: int, K: int, *, trans_a: bool = False, trans_b: bool = False,
+              device=None):
+    """A zero-filled device buffer of the size ``sgemm_workspace_size``
+    gives for this problem (a uint8 tensor), or None when the problem has
+    no use for one.  Allocated by torch; reusable for later calls."""
+    import torch
+    n = sgemm_workspace_size(SGEMM_OP_T if trans_a else SGEMM_OP_N,
+                             SGEMM_OP_T if trans_b else SGEMM_OP_N, M, N, K, 1)
+    if n < 0:
+        raise SgemmError(n)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = False,
-         trans_b: bool = False, variant: int = -1, stream=None):
+         trans_b: bool = False, variant: int = -1, stream=None, workspace=None):
     """C = alpha * op(A) @ op(B) + beta * C in place on float32 HIP tensors;
     returns C.
 
@@ -77,7 +107,9 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = Fals
     op(B) is B (K x N) or, with trans_b, the transpose of the N x K tensor B.
     Every tensor is row-major (unit column stride; the row stride is the
     leading dimension).  The call is enqueued on ``stream`` (default: the
-    current torch stream) and does not synchronise."""
+    current torch stream) and does not synchronise.  ``workspace``: an
+    optional zero-filled device tensor (see ``workspace()``) that lets the
+    call split its last partial round of tiles (sgemm_strided_batched_ws)."""
     import torch
     M = int(A.shape[1] if trans_a else A.shape[0])
     K = int(A.shape[0] if trans_a else A.shape[1])
@@ -88,16 +120,25 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: bool = Fals
     lda = _leading_dim(A, K if trans_a else M, M if trans_a else K, "A")
     ldb = _leading_dim(B, N if trans_b else K, K if trans_b else N, "B")
     ldc = _leading_dim(C, M, N, "C")
-    devs = {t.device for t in (A, B, C)}
-    if len(devs) != 1:
-        raise ValueError("A, B and C must be on the same device")
+    _same_hip_device(A, B, C)
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    opa = SGEMM_OP_T if trans_a else SGEMM_OP_N
+    opb = SGEMM_OP_T if trans_b else SGEMM_OP_N
     with torch.cuda.device(C.device):
-        st = sgemm_op_ex(SGEMM_OP_T if trans_a else SGEMM_OP_N, SGEMM_OP_T if trans_b else SGEMM_OP_N,
-                         M, N, K, float(alpha), A.data_ptr() or None, lda, B.data_ptr() or None, ldb,
-                         float(beta), C.data_ptr() or None, ldc, handle, variant)
+        if workspace is None:
+            st = sgemm_op_ex(opa, opb, M, N, K, float(alpha), A.data_ptr() or None, lda,
+                             B.data_ptr() or None, ldb, float(beta), C.data_ptr() or None, ldc,
+                             handle, variant)
+        else:
+            if not workspace.is_cuda or workspace.device != C.device:
+                raise ValueError("workspace must be on C's device")
+            nbytes = workspace.numel() * workspace.element_size()
+            st = sgemm_strided_batched_ws_ex(opa, opb, M, N, K, float(alpha), A.data_ptr() or None,
+                                             lda, 0, B.data_ptr() or None, ldb, 0, float(beta),
+                                             C.data_ptr() or None, ldc, 0, 1, workspace.data_ptr(),
+                                             nbytes, handle, variant)
     if st != SGEMM_OK:
         raise SgemmError(st)
     return C
@@ -133,6 +174,7 @@ def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, *, trans_a: boo
     lda = _leading_dim(a0, K if trans_a else M, M if trans_a else K, "A")
     ldb = _leading_dim(b0, N if trans_b else K, K if trans_b else N, "B")
     ldc = _leading_dim(c0, M, N, "C")
+    _same_hip_device(A, B, C)
     sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
     if stream is None:
         stream = torch.cuda.current_stream(C.device)

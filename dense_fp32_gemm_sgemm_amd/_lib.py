@@ -24,6 +24,8 @@ SGEMM_ERR_DEVICE = -5
 SGEMM_ERR_VARIANT = -6
 SGEMM_ERR_OP = -7
 SGEMM_ERR_STRIDE = -8
+SGEMM_ERR_GRID = -9
+SGEMM_ERR_WORKSPACE = -10
 SGEMM_NO_KERNEL = -100
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
@@ -35,8 +37,10 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_strided_batche
            "sgemm_strided_batched_ex", "sgemm_num_variants", "sgemm_variant_name",
            "sgemm_select_variant", "sgemm_op_select_variant", "sgemm_strided_batched_select_variant",
            "sgemm_status_string", "sgemm_version", "sgemm_set_atomics_mode",
-           "sgemm_get_atomics_mode",
-           "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy")
+           "sgemm_get_atomics_mode", "sgemm_strided_batched_ws", "sgemm_strided_batched_ws_ex",
+           "sgemm_strided_batched_ws_select_variant", "sgemm_workspace_size",
+           "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy", "sgemm_ceiling_read",
+           "sgemm_ceiling_empty")
 
 _lock = threading.Lock()
 _lib = None
@@ -69,6 +73,15 @@ def _declare(lib):
     lib.sgemm_strided_batched_ex.restype = c_int
     lib.sgemm_strided_batched_select_variant.argtypes = batched
     lib.sgemm_strided_batched_select_variant.restype = c_int
+    u64 = ctypes.c_ulonglong
+    lib.sgemm_strided_batched_ws.argtypes = batched + [vp, u64, vp]
+    lib.sgemm_strided_batched_ws.restype = c_int
+    lib.sgemm_strided_batched_ws_ex.argtypes = batched + [vp, u64, vp, c_int]
+    lib.sgemm_strided_batched_ws_ex.restype = c_int
+    lib.sgemm_strided_batched_ws_select_variant.argtypes = batched + [u64]
+    lib.sgemm_strided_batched_ws_select_variant.restype = c_int
+    lib.sgemm_workspace_size.argtypes = [c_int] * 6
+    lib.sgemm_workspace_size.restype = ctypes.c_longlong
     lib.sgemm_num_variants.argtypes = []
     lib.sgemm_num_variants.restype = c_int
     lib.sgemm_variant_name.argtypes = [c_int]
@@ -91,6 +104,10 @@ def _declare(lib):
     lib.sgemm_ceiling_fma.restype = c_int
     lib.sgemm_ceiling_copy.argtypes = [vp, vp, ctypes.c_longlong, c_int, vp]
     lib.sgemm_ceiling_copy.restype = c_int
+    lib.sgemm_ceiling_read.argtypes = [vp, ctypes.c_longlong, c_int, vp, vp]
+    lib.sgemm_ceiling_read.restype = c_int
+    lib.sgemm_ceiling_empty.argtypes = [c_int, vp]
+    lib.sgemm_ceiling_empty.restype = c_int
     return lib
 
 
@@ -152,6 +169,34 @@ def sgemm_strided_batched_select_variant(opA, opB, M, N, K, alpha, A, lda, strid
                                                        batch)
 
 
+def sgemm_strided_batched_ws(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                             ldc, strideC, batch, workspace, workspace_bytes, stream=0) -> int:
+    """sgemm_strided_batched with a caller workspace (device pointer, bytes)."""
+    return load().sgemm_strided_batched_ws(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                           strideB, beta, C, ldc, strideC, batch, workspace,
+                                           workspace_bytes, stream)
+
+
+def sgemm_strided_batched_ws_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta,
+                                C, ldc, strideC, batch, workspace, workspace_bytes, stream=0,
+                                variant=-1) -> int:
+    return load().sgemm_strided_batched_ws_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                              strideB, beta, C, ldc, strideC, batch, workspace,
+                                              workspace_bytes, stream, variant)
+
+
+def sgemm_strided_batched_ws_select_variant(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                            strideB, beta, C, ldc, strideC, batch,
+                                            workspace_bytes) -> int:
+    return load().sgemm_strided_batched_ws_select_variant(opA, opB, M, N, K, alpha, A, lda,
+                                                          strideA, B, ldb, strideB, beta, C, ldc,
+                                                          strideC, batch, workspace_bytes)
+
+
+def sgemm_workspace_size(opA, opB, M, N, K, batch=1) -> int:
+    return load().sgemm_workspace_size(opA, opB, M, N, K, batch)
+
+
 def sgemm_num_variants() -> int:
     return load().sgemm_num_variants()
 
@@ -197,3 +242,11 @@ def sgemm_ceiling_fma(blocks, iters, sink, stream=0):
 
 def sgemm_ceiling_copy(src, dst, n, blocks, stream=0) -> int:
     return load().sgemm_ceiling_copy(src, dst, n, blocks, stream)
+
+
+def sgemm_ceiling_read(src, n, blocks, sink, stream=0) -> int:
+    return load().sgemm_ceiling_read(src, n, blocks, sink, stream)
+
+
+def sgemm_ceiling_empty(blocks, stream=0) -> int:
+    return load().sgemm_ceiling_empty(blocks, stream)

@@ -98,6 +98,10 @@ const Variant kVariants[] = {
     {"mfma16_64x64x64_4x2_sched_splitk", launch_mfma16_64x64x64_4x2_sched_splitk},
     {"mfma16_32x64x64_2x2_sched", launch_mfma16_32x64x64_2x2_sched},
     {"mfma16_32x64x64_2x2_sched_splitk", launch_mfma16_32x64x64_2x2_sched_splitk},
+    {"mfma16_128x128x32_2x2_sched_tail", launch_mfma16_128x128x32_2x2_sched_tail},
+    {"mfma16_128x128x64_4x2_sched_tail", launch_mfma16_128x128x64_4x2_sched_tail},
+    {"mfma16_128x64x64_4x2_sched_tail", launch_mfma16_128x64x64_4x2_sched_tail},
+    {"mfma16_64x64x64_4x2_sched_tail", launch_mfma16_64x64x64_4x2_sched_tail},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -133,6 +137,10 @@ enum VariantId {
   kMfma16_64x64x64_w8_sched_splitk = 28,
   kMfma16_32x64x64_w4_sched = 29,
   kMfma16_32x64x64_w4_sched_splitk = 30,
+  kMfma16_128x128x32_w4_sched_tail = 31,
+  kMfma16_128x128x64_w8_sched_tail = 32,
+  kMfma16_128x64x64_w8_sched_tail = 33,
+  kMfma16_64x64x64_w8_sched_tail = 34,
 };
 
 constexpr int kNoKernel = -100;
@@ -178,9 +186,12 @@ int check_args(int opA, int opB, int M, int N, int K, float alpha, const float *
 //     fill the 256 CUs in whole rounds, then 128x128 tiles with 16-deep slabs
 //     when there are as many as CUs and 90% of their area is inside C, else
 //     64x64 tiles (16-deep slabs when K is not a multiple of 64);
-//   * K split over workgroups on 64x64 tiles when those cannot occupy the
-//     CUs and K is long (half of them from K = 1024, all from K = 2048),
-//     unless 32-row tiles would leave fewer rows of their tiles empty;
+//   * K split over workgroups on 64x64 tiles when there are fewer of them
+//     than CUs and K >= 2048, unless 32-row tiles would leave fewer rows of
+//     their tiles empty, M is 32 to 64 (the scored split tiles below win
+//     there) or 32-row tiles took over from the few-rows kernel; when no
+//     scored family's tile fits C, also with fewer 64x64 tiles than half the
+//     CUs from K = 1024;
 //   * otherwise the ordered slab loop on the tile family, with K split over
 //     workgroups or not, with the best predicted rate -- 256x256 (four
 //     waves, 128x128 wave tiles, one workgroup per CU), 128x128 (four waves,
@@ -299,6 +310,57 @@ double split_rate(const SplitFamily &sf, const Problem &p) {
          round_fill(sf.base, tiles * splits);
 }
 
+// The same loops with the fixed-order split of the last partial round of
+// tiles (workspace entry points only): whole rounds at the family's steady
+// rate, and the last round's tiles split into K ranges that fill the slots,
+// each range at the rate a split of that depth keeps.
+struct TailFamily {
+  int variant;
+  TileFamily base;
+  int bk;
+};
+constexpr TailFamily kTailFamilies[] = {
+    {kMfma16_128x128x32_w4_sched_tail, kTileFamilies[1], 32},
+    {kMfma16_128x128x64_w8_sched_tail, kTileFamilies[2], 64},
+    {kMfma16_128x64x64_w8_sched_tail, kTileFamilies[3], 64},
+    {kMfma16_64x64x64_w8_sched_tail, kTileFamilies[4], 64},
+};
+
+// Share of the rate a tail range of depth k (K values) keeps when its tile
+// was split `splits` ways: the range's own slabs against those plus a fixed
+// cost (its pipeline's start, about 140 values of k) and the partial tiles
+// written and read back (about 19 per split).  Fitted to the tail forms on
+// MI355X: 0.74 for 512-deep ranges of 64x64 tiles in two (1024^3), 0.78 for
+// 768-deep ranges of 128x128 tiles in four (3000^3), 0.43 for 191-deep
+// ranges of 128x128 tiles in seven ((4095, 4097, 1023)).
+double tail_efficiency(double k, int splits) { return k / (k + 143.0 + 18.5 * splits); }
+
+TailPlan family_tail_plan(const TailFamily &tf, const Problem &p) {
+  return tail_plan(family_tiles(tf.base, p), p.K, tf.base.slots, (long long)tf.base.bm * tf.base.bn, tf.bk);
+}
+
+// Predicted rate of a tail family (0 when it would not take the tail form:
+// a batch, no room in the workspace, whole rounds, too short a K).  In
+// steady tile-times on the busiest CU: the whole rounds' tiles, then the
+// last round's ranges there (each k_per_split/K of a tile, at the split
+// efficiency of its depth, and at the lone-workgroup rate when fewer than
+// the family's slots share the CU).
+double tail_rate(const TailFamily &tf, const Problem &p) {
+  if (p.batch != 1 || p.ws == nullptr) return 0.0;
+  const TailPlan tp = family_tail_plan(tf, p);
+  if (tp.splits < 2 || (unsigned long long)tp.bytes > p.ws_bytes) return 0.0;
+  const TileFamily &f = tf.base;
+  const long long tiles = family_tiles(f, p);
+  const double whole = (double)tp.dp_tiles / (double)kCus;  // tiles per CU in whole rounds
+  const long long wgs = (long long)tp.tail_tiles * tp.splits;
+  const long long per_cu = (wgs + kCus - 1) / kCus;
+  const double frac = (double)tp.max_range / (double)p.K;
+  double last = (double)per_cu * frac / tail_efficiency((double)tp.max_range, tp.splits);
+  if (per_cu < f.slots) last /= f.partial[per_cu];
+  const double span = whole + last;
+  return family_rate_full(f, (double)p.K) * family_fill(f, p) * (double)tiles / ((double)kCus * span);
+}
+
 // Process-wide atomics mode (sgemm_set_atomics_mode).
 std::atomic<int> g_atomics_mode{SGEMM_ATOMICS_ALLOWED};
 
@@ -398,6 +460,12 @@ int choose_variant(const Problem &p, bool atomics) {
     const double r = split_rate(sf, p);
     if (r > best_rate) best_rate = r, best = sf.variant;
   }
+  // With a workspace: the fixed-order tail forms (no atomics on C).
+  for (const TailFamily &tf : kTailFamilies) {
+    if (!family_fits(tf.base, p)) continue;
+    const double r = tail_rate(tf, p);
+    if (r > best_rate) best_rate = r, best = tf.variant;
+  }
   // No family's tile fits C (fewer than 32 rows with A transposed, or fewer
   // than 64 columns): few tiles with a long K still split K over workgroups.
   if (best_rate < 0.0 && atomics && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
@@ -423,45 +491,95 @@ int check_device() {
 
 constexpr int kMaxGridZ = 65535;
 
+// Enqueues (or, with the launch plan set dry, only checks) every launch of
+// one call: grids hold at most 65535 batch slices, so larger batches go in
+// chunks.  Returns 0, or -1 when some launch cannot be made.
+int launch_all(const Problem &p, int v, bool no_product, hipStream_t s) {
+  for (int z0 = 0; z0 < p.batch; z0 += kMaxGridZ) {
+    Problem q = p;
+    q.batch = (p.batch - z0 < kMaxGridZ) ? p.batch - z0 : kMaxGridZ;
+    q.A = p.A ? p.A + (size_t)z0 * (size_t)p.sa : nullptr;
+    q.B = p.B ? p.B + (size_t)z0 * (size_t)p.sb : nullptr;
+    q.C = p.C + (size_t)z0 * (size_t)p.sc;
+    const int rc = no_product ? launch_scale(q, s) : kVariants[v].launch(q, s);
+    if (rc != 0) return -1;
+  }
+  return 0;
+}
+
+// The launch plan of a call: every launch of every chunk checked against the
+// grid limits with nothing enqueued.  True when all of them fit.
+bool plan_fits(const Problem &p, int v, bool no_product) {
+  LaunchPlan &lp = launch_plan();
+  lp.dry = true;
+  lp.failed = false;
+  const int rc = launch_all(p, v, no_product, nullptr);
+  const bool ok = rc == 0 && !lp.failed;
+  lp.dry = false;
+  lp.failed = false;
+  return ok;
+}
+
+// Workspaces must be 16-byte aligned.
+bool ws_aligned(const void *ws) { return (reinterpret_cast<uintptr_t>(ws) & 15) == 0; }
+
 int run(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda, long long sa,
         const float *B, int ldb, long long sb, float beta, float *C, int ldc, long long sc,
-        int batch, void *stream, int variant) {
+        int batch, void *ws, unsigned long long ws_bytes, void *stream, int variant) {
   int st = check_args(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch);
   if (st != SGEMM_OK) return st;
   if (variant < -1 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+  if (ws != nullptr && !ws_aligned(ws)) return SGEMM_ERR_WORKSPACE;
   if (M == 0 || N == 0 || batch == 0) return SGEMM_OK;
   const bool no_product = (alpha == 0.0f || K == 0);
   if (no_product && beta == 1.0f) return SGEMM_OK;
-  st = check_device();
-  if (st != SGEMM_OK) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Problem p{M,  N,  K,  alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T,
-            sa, sb, sc, batch};
+            sa, sb, sc, batch, ws, ws != nullptr ? ws_bytes : 0ULL};
   const int v = no_product ? -1
                            : ((variant >= 0) ? variant
                                              : choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED));
-  // Grids hold at most 65535 batch slices: larger batches go in chunks.
-  for (int z0 = 0; z0 < batch; z0 += kMaxGridZ) {
-    Problem q = p;
-    q.batch = (batch - z0 < kMaxGridZ) ? batch - z0 : kMaxGridZ;
-    q.A = p.A ? p.A + (size_t)z0 * (size_t)sa : nullptr;
-    q.B = p.B ? p.B + (size_t)z0 * (size_t)sb : nullptr;
-    q.C = p.C + (size_t)z0 * (size_t)sc;
-    const int rc = no_product ? launch_scale(q, s) : kVariants[v].launch(q, s);
-    if (rc != 0) return SGEMM_ERR_DIM;
+  // Every launch is checked before the first is enqueued (host only).
+  if (!plan_fits(p, v, no_product)) return SGEMM_ERR_GRID;
+  st = check_device();
+  if (st != SGEMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (launch_all(p, v, no_product, s) != 0 || launch_plan().failed) {
+    launch_plan().failed = false;
+    return SGEMM_ERR_LAUNCH;  // not reached: the plan above fitted
   }
   return (hipGetLastError() == hipSuccess) ? SGEMM_OK : SGEMM_ERR_LAUNCH;
 }
 
 int select(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
            long long sa, const float *B, int ldb, long long sb, float beta, const float *C, int ldc,
-           long long sc, int batch) {
+           long long sc, int batch, unsigned long long ws_bytes = 0) {
   const int st = check_args(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch);
   if (st != SGEMM_OK) return st;
   if (M == 0 || N == 0 || batch == 0 || alpha == 0.0f || K == 0) return kNoKernel;
+  // (a stand-in workspace address: only its presence and size matter here)
   const Problem p{M,   N,   K,   alpha, beta, A, lda, B, ldb, const_cast<float *>(C), ldc,
-                  opA == SGEMM_OP_T, opB == SGEMM_OP_T, sa, sb, sc, batch};
-  return choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
+                  opA == SGEMM_OP_T, opB == SGEMM_OP_T, sa, sb, sc, batch,
+                  ws_bytes ? reinterpret_cast<void *>(256) : nullptr, ws_bytes};
+  const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
+  return plan_fits(p, v, false) ? v : SGEMM_ERR_GRID;
+}
+
+// Workspace the automatic choice of the workspace entry points would use for
+// this problem (0: none), or a negative status for invalid sizes.
+long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
+  if ((opA != SGEMM_OP_N && opA != SGEMM_OP_T) || (opB != SGEMM_OP_N && opB != SGEMM_OP_T))
+    return SGEMM_ERR_OP;
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_ERR_DIM;
+  if (M == 0 || N == 0 || K == 0 || batch != 1) return 0;
+  const float *fake = reinterpret_cast<const float *>(256);
+  const int lda = opA == SGEMM_OP_T ? M : K, ldb = opB == SGEMM_OP_T ? K : N;
+  const Problem p{M,    N,   K,   1.0f, 0.0f, fake, lda, fake, ldb, const_cast<float *>(fake), N,
+                  opA == SGEMM_OP_T, opB == SGEMM_OP_T, 0, 0, 0, 1,
+                  reinterpret_cast<void *>(256), (unsigned long long)kTailWorkspaceBytes};
+  const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
+  for (const TailFamily &tf : kTailFamilies)
+    if (tf.variant == v) return family_tail_plan(tf, p).bytes;
+  return 0;
 }
 
 }  // namespace
@@ -472,24 +590,25 @@ extern "C" {
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
           float beta, float *C, int ldc, void *stream) {
   return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-                    stream, -1);
+                    nullptr, 0, stream, -1);
 }
 
 int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
              float beta, float *C, int ldc, void *stream, int variant) {
   return sg950::run(SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1,
-                    stream, variant);
+                    nullptr, 0, stream, variant);
 }
 
 int sgemm_op(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc, void *stream) {
-  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, stream, -1);
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr, 0,
+                    stream, -1);
 }
 
 int sgemm_op_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
                 const float *B, int ldb, float beta, float *C, int ldc, void *stream, int variant) {
-  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, stream,
-                    variant);
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1, nullptr, 0,
+                    stream, variant);
 }
 
 int sgemm_strided_batched(int opA, int opB, int M, int N, int K, float alpha, const float *A,
@@ -497,7 +616,7 @@ int sgemm_strided_batched(int opA, int opB, int M, int N, int K, float alpha, co
                           float beta, float *C, int ldc, long long strideC, int batch,
                           void *stream) {
   return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
-                    strideC, batch, stream, -1);
+                    strideC, batch, nullptr, 0, stream, -1);
 }
 
 int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A,
@@ -505,7 +624,37 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
                              long long strideB, float beta, float *C, int ldc, long long strideC,
                              int batch, void *stream, int variant) {
   return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
-                    strideC, batch, stream, variant);
+                    strideC, batch, nullptr, 0, stream, variant);
+}
+
+int sgemm_strided_batched_ws(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                             int lda, long long strideA, const float *B, int ldb, long long strideB,
+                             float beta, float *C, int ldc, long long strideC, int batch,
+                             void *workspace, unsigned long long workspace_bytes, void *stream) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                    strideC, batch, workspace, workspace_bytes, stream, -1);
+}
+
+int sgemm_strided_batched_ws_ex(int opA, int opB, int M, int N, int K, float alpha, const float *A,
+                                int lda, long long strideA, const float *B, int ldb,
+                                long long strideB, float beta, float *C, int ldc, long long strideC,
+                                int batch, void *workspace, unsigned long long workspace_bytes,
+                                void *stream, int variant) {
+  return sg950::run(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                    strideC, batch, workspace, workspace_bytes, stream, variant);
+}
+
+int sgemm_strided_batched_ws_select_variant(int opA, int opB, int M, int N, int K, float alpha,
+                                            const float *A, int lda, long long strideA,
+                                            const float *B, int ldb, long long strideB, float beta,
+                                            const float *C, int ldc, long long strideC, int batch,
+                                            unsigned long long workspace_bytes) {
+  return sg950::select(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                       strideC, batch, workspace_bytes);
+}
+
+long long sgemm_workspace_size(int opA, int opB, int M, int N, int K, int batch) {
+  return sg950::workspace_size(opA, opB, M, N, K, batch);
 }
 
 int sgemm_num_variants(void) { return sg950::kNumVariants; }
@@ -537,7 +686,7 @@ int sgemm_strided_batched_select_variant(int opA, int opB, int M, int N, int K, 
 const char *sgemm_status_string(int status) {
   switch (status) {
     case SGEMM_OK: return "success";
-    case SGEMM_ERR_DIM: return "invalid dimension (negative M, N, K or batch, or grid too large)";
+    case SGEMM_ERR_DIM: return "invalid dimension (negative M, N, K or batch)";
     case SGEMM_ERR_LD: return "invalid leading dimension (shorter than the stored row it spans)";
     case SGEMM_ERR_PTR: return "NULL matrix pointer";
     case SGEMM_ERR_LAUNCH: return "kernel launch failed";
@@ -545,11 +694,13 @@ const char *sgemm_status_string(int status) {
     case SGEMM_ERR_VARIANT: return "variant index out of range";
     case SGEMM_ERR_OP: return "invalid operation (opA and opB must be SGEMM_OP_N or SGEMM_OP_T)";
     case SGEMM_ERR_STRIDE: return "invalid batch stride (negative, or slices of C overlap)";
+    case SGEMM_ERR_GRID: return "problem too large for the launch grid of its kernel (nothing was enqueued)";
+    case SGEMM_ERR_WORKSPACE: return "workspace not 16-byte aligned";
     default: return "unknown status";
   }
 }
 
-int sgemm_version(void) { return 4; }
+int sgemm_version(void) { return 5; }
 
 int sgemm_set_atomics_mode(int mode) {
   if (mode != SGEMM_ATOMICS_ALLOWED && mode != SGEMM_ATOMICS_NOT_ALLOWED) return SGEMM_ERR_OP;

@@ -19,6 +19,10 @@ namespace sg950 {
 // Batches: `batch` independent problems of this shape, slice z using
 // A + z*sa, B + z*sb and C + z*sc (element strides); kernels take the slice
 // from blockIdx.z.  A single problem has batch = 1 and zero strides.
+//
+// Workspace: `ws` (ws_bytes bytes of device memory, or NULL) is scratch a
+// call may use for the fixed-order split of its last round of tiles; only
+// kernels that take that form read it.
 struct Problem {
   int M, N, K;
   float alpha, beta;
@@ -31,6 +35,22 @@ struct Problem {
   int ta, tb;
   long long sa, sb, sc;
   int batch;
+  void *ws = nullptr;
+  unsigned long long ws_bytes = 0;
+};
+
+// The fixed-order split of the last round of output tiles ("tail"): the
+// first dp_tiles tiles run whole, one workgroup each; every other tile is
+// split into `splits` K ranges, one workgroup each: with nkf = K / BK whole
+// slabs, range s covers slabs [s*nkf/splits, (s+1)*nkf/splits) and the last
+// range also the ragged rest of K.  Each of those writes its partial tile to
+// `part`, then counts itself in flags[tile]; the one that counts last adds
+// the partials in range order and writes the tile of C.
+struct TailArgs {
+  int dp_tiles = 0;
+  int splits = 1;
+  unsigned *flags = nullptr;
+  float *part = nullptr;
 };
 
 // Moves the operand pointers to batch slice blockIdx.z.
@@ -73,6 +93,37 @@ __device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, i
   tm = first_m + in_group % rows;
   tn = in_group / rows;
 }
+
+// Launch planning (host side).  An entry point first runs every launcher of
+// a call with `dry` set: each launch then only checks its grid against the
+// HIP limits and records a failure, and nothing is enqueued.  Only when every
+// launch of every batch chunk fits does it run the launchers again for real,
+// so a call never leaves C partly updated behind a grid error.
+struct LaunchPlan {
+  bool dry = false;
+  bool failed = false;
+};
+inline LaunchPlan &launch_plan() {
+  static thread_local LaunchPlan plan;
+  return plan;
+}
+// HIP grid limits: each dimension's work-items (blocks x threads) below 2^32,
+// and at most 65535 blocks along y and z.
+inline bool grid_fits(dim3 grid, dim3 block) {
+  const unsigned long long lim = 0xffffffffULL;
+  return grid.x >= 1 && grid.y >= 1 && grid.z >= 1 && grid.y <= 65535 && grid.z <= 65535 &&
+         (unsigned long long)grid.x * block.x <= lim && (unsigned long long)grid.y * block.y <= lim &&
+         (unsigned long long)grid.z * block.z <= lim;
+}
+// Every GEMM-path kernel launch goes through this macro.
+#define SG950_LAUNCH(kernel, grid, block, shmem, stream, ...)                       \
+  do {                                                                              \
+    if (!::sg950::grid_fits((grid), (block))) {                                     \
+      ::sg950::launch_plan().failed = true;                                         \
+    } else if (!::sg950::launch_plan().dry) {                                       \
+      hipLaunchKernelGGL(kernel, (grid), (block), (shmem), (stream), __VA_ARGS__); \
+    }                                                                               \
+  } while (0)
 
 // Epilogue for one element: alpha*acc (+ beta*C when beta != 0; C is not read
 // otherwise).

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 namespace {
 template <int NR, int CPL, bool TA, bool TB, bool VB>
 void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange) {
-  hipLaunchKernelGGL((fewrows_kernel<NR, CPL, TA, TB, VB>), grid, dim3(kFewWaves * 64), 0, stream, p,
+  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB>), grid, dim3(kFewWaves * 64), 0, stream, p,
                      krange);
 }
 

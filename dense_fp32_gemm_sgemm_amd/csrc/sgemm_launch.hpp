@@ -61,6 +61,13 @@ int launch_mfma16_128x64x64_4x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_32x64x64_2x2_sched(const Problem &p, hipStream_t stream);
 int launch_mfma16_32x64x64_2x2_sched_splitk(const Problem &p, hipStream_t stream);
 
+// The same families with the fixed-order split of their last, partial round
+// of tiles (needs a workspace in the Problem; otherwise the plain loop).
+int launch_mfma16_128x128x32_2x2_sched_tail(const Problem &p, hipStream_t stream);
+int launch_mfma16_128x128x64_4x2_sched_tail(const Problem &p, hipStream_t stream);
+int launch_mfma16_128x64x64_4x2_sched_tail(const Problem &p, hipStream_t stream);
+int launch_mfma16_64x64x64_4x2_sched_tail(const Problem &p, hipStream_t stream);
+
 // Few rows of C (M <= 8): streams B across every CU, K split over
 // workgroups, float atomics into C (scaled by beta first).  Returns -1 for
 // M > 8.

@@ -343,20 +343,20 @@ template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, in
 static void launch_mfma_aligned(const Problem &p, dim3 grid, dim3 block, hipStream_t stream, int tm,
                                 int tn, int group_m, int k_per_split) {
   const bool va = a_vec_ok(p), vb = b_vec_ok(p);
-#define SG950_LAUNCH(VA_, VB_)                                                                        \
-  hipLaunchKernelGGL(                                                                                \
+#define SG950_LAUNCH_VA(VA_, VB_)                                                                     \
+  SG950_LAUNCH(                                                                                \
       (mfma_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, PIPE, SPLITK, TA, TB, VA_, VB_>), \
       grid, block, 0, stream, p, tm, tn, group_m, k_per_split)
   if (va && vb) {
-    SG950_LAUNCH(true, true);
+    SG950_LAUNCH_VA(true, true);
   } else if (va) {
-    SG950_LAUNCH(true, false);
+    SG950_LAUNCH_VA(true, false);
   } else if (vb) {
-    SG950_LAUNCH(false, true);
+    SG950_LAUNCH_VA(false, true);
   } else {
-    SG950_LAUNCH(false, false);
+    SG950_LAUNCH_VA(false, false);
   }
-#undef SG950_LAUNCH
+#undef SG950_LAUNCH_VA
 }
 
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool PIPE,

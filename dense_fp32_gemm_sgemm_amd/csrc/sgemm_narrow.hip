@@ -146,13 +146,13 @@ void launch_narrow_t(const Problem &p, dim3 grid, hipStream_t stream, int krange
   const bool vb = TB && (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 4 == 0 &&
                   (p.batch <= 1 || p.sb % 4 == 0);
   if (va && vb) {
-    hipLaunchKernelGGL((narrow_kernel<TA, TB, true, true>), grid, block, 0, stream, p, krange);
+    SG950_LAUNCH((narrow_kernel<TA, TB, true, true>), grid, block, 0, stream, p, krange);
   } else if (va) {
-    hipLaunchKernelGGL((narrow_kernel<TA, TB, true, false>), grid, block, 0, stream, p, krange);
+    SG950_LAUNCH((narrow_kernel<TA, TB, true, false>), grid, block, 0, stream, p, krange);
   } else if (vb) {
-    hipLaunchKernelGGL((narrow_kernel<TA, TB, false, true>), grid, block, 0, stream, p, krange);
+    SG950_LAUNCH((narrow_kernel<TA, TB, false, true>), grid, block, 0, stream, p, krange);
   } else {
-    hipLaunchKernelGGL((narrow_kernel<TA, TB, false, false>), grid, block, 0, stream, p, krange);
+    SG950_LAUNCH((narrow_kernel<TA, TB, false, false>), grid, block, 0, stream, p, krange);
   }
 }
 }  // namespace

@@ -200,11 +200,17 @@ __device__ __forceinline__ void read_sched_operands(Operands<T> &o, const float 
 //
 // SHORTM (A not transposed): M may be below BM; the tile then starts at row 0,
 // rows from M on read row M - 1 of A and are not stored.
+//
+// TAIL (one batch slice): workgroups from tl.dp_tiles on each take one K
+// range of a tile of the last round (TailArgs); the partial tiles meet in a
+// fixed order, so the result does not depend on which range finishes last.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD, bool TA,
-          bool TB, bool RAGGED, bool SPLITK, bool SHORTM = false>
+          bool TB, bool RAGGED, bool SPLITK, bool SHORTM = false, bool TAIL = false>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Problem p, int tiles_m,
                                                                                int tiles_n, int group_m,
-                                                                               int k_per_split) {
+                                                                               int k_per_split,
+                                                                               TailArgs tl) {
+  static_assert(!(TAIL && (SPLITK || SHORTM)), "the tail form is its own split");
   select_slice(p);
   if constexpr (SPLITK) {
     const int kb = (int)blockIdx.y * k_per_split;
@@ -226,7 +232,28 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
   __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_STAGE];
 
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+  int tail_t = -1, sidx = 0;  // TAIL: tile of the last round and K range, or -1 (whole tile)
+  if constexpr (TAIL) {
+    const int b = (int)blockIdx.x;
+    int id;
+    if (b < tl.dp_tiles) {
+      id = xcd_remap(b, tl.dp_tiles);
+    } else {
+      const int j = b - tl.dp_tiles;
+      tail_t = j / tl.splits;
+      sidx = j - tail_t * tl.splits;
+      id = tl.dp_tiles + tail_t;
+      const int nkf = p.K / BK;  // whole slabs; the last range also takes the rest
+      const int kb = (int)((long long)sidx * nkf / tl.splits) * BK;
+      const int ke = (sidx + 1 == tl.splits) ? p.K : (int)((long long)(sidx + 1) * nkf / tl.splits) * BK;
+      p.A += TA ? (size_t)kb * (size_t)p.lda : (size_t)kb;
+      p.B += TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb;
+      p.K = ke - kb;
+    }
+    grouped_tile(id, tiles_m, tiles_n, group_m, tm, tn);
+  } else {
+    grouped_tile(xcd_remap(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   // shifted inside C (with CLAMPM and M < BM: from row 0)
   const int ms = CLAMPM ? max(0, min(m0, p.M - BM)) : min(m0, p.M - BM), ns = min(n0, p.N - BN);
@@ -344,6 +371,67 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
       __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
     }
     o = nxt;
+  }
+  if constexpr (TAIL) {
+    if (tail_t >= 0) {
+      // Partial tile out in register order (value e of thread t at e*NT + t:
+      // every store instruction of a wave writes 256 contiguous bytes), then
+      // count this range in.  The workgroup that counts last reads every
+      // partial back (its own included: the same bits), adds them in range
+      // order 0, 1, ..., splits-1, resets the counter for the next call and
+      // stores the tile below like a whole one.  No workgroup waits for
+      // another.
+      //
+      // Coherence across the eight XCDs (each with its own L2) without
+      // writing back or invalidating whole caches: the partials are stored
+      // and loaded as agent-scope atomics (coherent at the device level, not
+      // through an XCD's L2), every wave waits until its stores are
+      // acknowledged before the barrier, and only then does one thread count
+      // the range in with a device-scope atomic add; the last one's loads
+      // come after it has seen the count.
+      constexpr int NREG = T::FM * T::FN * kRegs;
+      const size_t tile_part = (size_t)NREG * NT;
+      float *mine = tl.part + ((size_t)tail_t * tl.splits + sidx) * tile_part + tid;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < kRegs; ++r)
+            __hip_atomic_store(mine + (size_t)((i * T::FN + j) * kRegs + r) * NT, acc[i][j][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __shared__ int tail_last;
+      __builtin_amdgcn_s_waitcnt(0);  // every memory operation of this wave complete
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned before =
+            __hip_atomic_fetch_add(tl.flags + tail_t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tail_last = (before + 1u == (unsigned)tl.splits);
+      }
+      __syncthreads();
+      if (!tail_last) return;
+      const float *part0 = tl.part + (size_t)tail_t * tl.splits * tile_part + tid;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int r = 0; r < kRegs; ++r)
+            acc[i][j][r] = __hip_atomic_load(part0 + (size_t)((i * T::FN + j) * kRegs + r) * NT, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      for (int sp = 1; sp < tl.splits; ++sp) {
+        const float *ps = part0 + (size_t)sp * tile_part;
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < kRegs; ++r)
+              acc[i][j][r] += __hip_atomic_load(ps + (size_t)((i * T::FN + j) * kRegs + r) * NT, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid == 0) __hip_atomic_store(tl.flags + tail_t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // Epilogue: C = alpha*acc + beta*C for the rows and columns of this tile
   // (a shifted tile also computed some of its neighbour's).
@@ -483,12 +571,60 @@ static int sched_splits(long long tiles, int K, int &k_per_split) {
   return (int)splits;
 }
 
+// Workspace layout of the tail form: the per-tile counters first (at most
+// kTailMaxTiles of them, in kTailFlagBytes), then the partial tiles.  The
+// partials of one call are capped at kTailPartBytes, which bounds the
+// workspace any problem needs.
+constexpr long long kTailMaxTiles = 1024;
+constexpr long long kTailFlagBytes = 4096;
+constexpr long long kTailPartBytes = 32LL << 20;
+constexpr long long kTailWorkspaceBytes = kTailFlagBytes + kTailPartBytes;
+constexpr int kTailCus = 256;  // compute units of an MI355X
+
+// The tail plan of a grid of `tiles` output tiles (one batch slice) for a
+// tile family that runs `slots` workgroups per CU: whole rounds of tiles run
+// whole; the tiles of a last, partial round are each split into enough K
+// ranges to fill the CUs' slots -- at most kTailMaxSplits (the workgroup
+// that finishes a tile last reads every partial), each range at least four
+// whole slabs, within the workspace cap.  splits == 1: no tail form (a
+// whole number of rounds, or too short a K).
+constexpr int kTailMaxSplits = 8;
+struct TailPlan {
+  int dp_tiles = 0, tail_tiles = 0, splits = 1;
+  int max_range = 0;    // K depth of the deepest range
+  long long bytes = 0;  // workspace needed
+};
+inline TailPlan tail_plan(long long tiles, int K, int slots, long long tile_floats, int BK) {
+  TailPlan t;
+  const long long P = (long long)kTailCus * slots;
+  const long long rem = tiles % P;
+  if (tiles < 1 || rem == 0 || rem > kTailMaxTiles) return t;
+  long long splits = P / rem;
+  const long long nkf = K / BK;
+  if (splits > nkf / 4) splits = nkf / 4;
+  if (splits > kTailMaxSplits) splits = kTailMaxSplits;
+  const long long cap = kTailPartBytes / (rem * tile_floats * 4);
+  if (splits > cap) splits = cap;
+  if (splits < 2) return t;
+  t.dp_tiles = (int)(tiles - rem);
+  t.tail_tiles = (int)rem;
+  t.splits = (int)splits;
+  // slabs of the deepest range (a middle one, or the last with K's rest)
+  const long long mid = (nkf + splits - 1) / splits;
+  const long long last_k = K - (long long)((splits - 1) * nkf / splits) * BK;
+  t.max_range = (int)(mid * BK > last_k ? mid * BK : last_k);
+  t.bytes = kTailFlagBytes + rem * splits * tile_floats * 4;
+  return t;
+}
+
 // Launches sched_kernel when its preconditions hold, else `fallback` (a
 // variant of the same tile family that accepts every problem).  SPLIT: K may
 // be split over workgroups when the tiles leave CUs idle.  SHORTM: M may be
-// below BM when A is not transposed.
+// below BM when A is not transposed.  TAILOK: with a workspace large enough
+// (and one batch slice) the last partial round of tiles takes the tail form
+// (TailArgs), `slots` workgroups of this family fitting on a CU.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MINW, int BPAD,
-          bool SPLIT = false, bool SHORTM = false>
+          bool SPLIT = false, bool SHORTM = false, bool TAILOK = false, int SLOTS = 1>
 static int launch_sched(const Problem &p, hipStream_t stream,
                         int (*fallback)(const Problem &, hipStream_t)) {
   if (!sched_ok<BM, BN, BK, SHORTM>(p)) return fallback(p, stream);
@@ -497,6 +633,20 @@ static int launch_sched(const Problem &p, hipStream_t stream,
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
   int k_per_split = p.K;
   const int splits = SPLIT ? sched_splits<BK>(tiles_m * tiles_n * p.batch, p.K, k_per_split) : 1;
+  TailArgs tl;
+  TailPlan tp;
+  if constexpr (TAILOK) {
+    if (p.batch == 1 && p.ws != nullptr) {
+      tp = tail_plan(tiles_m * tiles_n, p.K, SLOTS, (long long)BM * BN, BK);
+      if (tp.splits > 1 && (unsigned long long)tp.bytes <= p.ws_bytes) {
+        tl.dp_tiles = tp.dp_tiles;
+        tl.splits = tp.splits;
+        tl.flags = reinterpret_cast<unsigned *>(p.ws);
+        tl.part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
+      }
+    }
+  }
+  const bool tail = TAILOK && tl.splits > 1;
   if (splits > 1) {
     if (splits > 65535) return -1;
     // C = beta*C first; the split workgroups then add into it.
@@ -504,22 +654,32 @@ static int launch_sched(const Problem &p, hipStream_t stream,
   }
   // Every range but the last is a multiple of BK; the last decides.
   const bool ragged = (p.K - (splits - 1) * k_per_split) % BK != 0;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits, (unsigned)p.batch);
+  const long long gx = tail ? (long long)tp.dp_tiles + (long long)tp.tail_tiles * tp.splits
+                            : tiles_m * tiles_n;
+  if (gx > (long long)INT_MAX) return -1;
+  const dim3 grid((unsigned)gx, (unsigned)splits, (unsigned)p.batch);
   const dim3 block(WAVES_M * WAVES_N * 64);
   const int tm = (int)tiles_m, tn = (int)tiles_n, group_m = 8;
   // The row-clamping form only where M is below the tile (A untransposed).
   const bool short_m = SHORTM && p.M < BM;
 #define SG950_SCHED_K(TA_, TB_, RG_, SK_)                                                                       \
   do {                                                                                                        \
-    if constexpr (SHORTM && !(TA_)) {                                                                         \
-      if (short_m) {                                                                                          \
-        hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_, true>), \
-                           grid, block, 0, stream, p, tm, tn, group_m, k_per_split);                          \
+    if constexpr (TAILOK && !(SK_)) {                                                                         \
+      if (tail) {                                                                                             \
+        SG950_LAUNCH((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, false, false, true>), \
+                     grid, block, 0, stream, p, tm, tn, group_m, k_per_split, tl);                           \
         break;                                                                                                \
       }                                                                                                       \
     }                                                                                                         \
-    hipLaunchKernelGGL((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_>), grid,  \
-                       block, 0, stream, p, tm, tn, group_m, k_per_split);                                     \
+    if constexpr (SHORTM && !(TA_)) {                                                                         \
+      if (short_m) {                                                                                          \
+        SG950_LAUNCH((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_, true>), \
+                           grid, block, 0, stream, p, tm, tn, group_m, k_per_split, tl);                      \
+        break;                                                                                                \
+      }                                                                                                       \
+    }                                                                                                         \
+    SG950_LAUNCH((sched_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, MINW, BPAD, TA_, TB_, RG_, SK_>), grid,  \
+                       block, 0, stream, p, tm, tn, group_m, k_per_split, tl);                                 \
   } while (0)
 #define SG950_SCHED(TA_, TB_)                       \
   do {                                              \

@@ -269,13 +269,13 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
 #define SG950_FULLK(MR_)                                                                        \
   do {                                                                                          \
     if (fva && fvb)                                                                             \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true, true>), fgrid, fblock, 0, stream, p);  \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, true>), fgrid, fblock, 0, stream, p);  \
     else if (fvb)                                                                               \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false, true>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, true>), fgrid, fblock, 0, stream, p); \
     else if (fva)                                                                               \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, true, false>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, false>), fgrid, fblock, 0, stream, p); \
     else                                                                                        \
-      hipLaunchKernelGGL((skinny_fullk_kernel<MR_, false, false>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, false>), fgrid, fblock, 0, stream, p); \
   } while (0)
     if (p.M <= 1) {
       SG950_FULLK(1);
@@ -301,11 +301,11 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
 #define SG950_SKINNY(MR_)                                                                     \
   do {                                                                                        \
     if (p.tb)                                                                                 \
-      hipLaunchKernelGGL((skinny_kernel<MR_, false, true>), grid, block, 0, stream, p, kc); \
+      SG950_LAUNCH((skinny_kernel<MR_, false, true>), grid, block, 0, stream, p, kc); \
     else if (vb)                                                                              \
-      hipLaunchKernelGGL((skinny_kernel<MR_, true, false>), grid, block, 0, stream, p, kc); \
+      SG950_LAUNCH((skinny_kernel<MR_, true, false>), grid, block, 0, stream, p, kc); \
     else                                                                                      \
-      hipLaunchKernelGGL((skinny_kernel<MR_, false, false>), grid, block, 0, stream, p, kc); \
+      SG950_LAUNCH((skinny_kernel<MR_, false, false>), grid, block, 0, stream, p, kc); \
   } while (0)
   if (p.M <= 1) {
     SG950_SKINNY(1);

@@ -182,15 +182,15 @@ static void launch_valu_t(const Problem &p, dim3 grid, hipStream_t stream, int t
   // The C alignment only changes the epilogue, so it is folded into the
   // fully aligned case rather than doubling the instantiations.
   if (va && vb && vc) {
-    hipLaunchKernelGGL((valu_kernel<TA, TB, true, true, true>), grid, block, 0, stream, p, tm, tn, gm);
+    SG950_LAUNCH((valu_kernel<TA, TB, true, true, true>), grid, block, 0, stream, p, tm, tn, gm);
   } else if (va && vb) {
-    hipLaunchKernelGGL((valu_kernel<TA, TB, true, true, false>), grid, block, 0, stream, p, tm, tn, gm);
+    SG950_LAUNCH((valu_kernel<TA, TB, true, true, false>), grid, block, 0, stream, p, tm, tn, gm);
   } else if (va) {
-    hipLaunchKernelGGL((valu_kernel<TA, TB, true, false, false>), grid, block, 0, stream, p, tm, tn, gm);
+    SG950_LAUNCH((valu_kernel<TA, TB, true, false, false>), grid, block, 0, stream, p, tm, tn, gm);
   } else if (vb) {
-    hipLaunchKernelGGL((valu_kernel<TA, TB, false, true, false>), grid, block, 0, stream, p, tm, tn, gm);
+    SG950_LAUNCH((valu_kernel<TA, TB, false, true, false>), grid, block, 0, stream, p, tm, tn, gm);
   } else {
-    hipLaunchKernelGGL((valu_kernel<TA, TB, false, false, false>), grid, block, 0, stream, p, tm, tn, gm);
+    SG950_LAUNCH((valu_kernel<TA, TB, false, false, false>), grid, block, 0, stream, p, tm, tn, gm);
   }
 }
 

@@ -49,7 +49,11 @@
  *   - beta == 1 with alpha == 0 or K == 0: nothing is enqueued.
  *
  * Errors.  Every function returns SGEMM_OK (0) or a negative status; nothing
- * aborts or prints.  Argument errors are detected before any HIP call.
+ * aborts or prints.  Argument errors are detected before any HIP call, and
+ * so are grids too large to launch (SGEMM_ERR_GRID): every launch a call
+ * needs, for every chunk of a large batch, is checked against the HIP grid
+ * limits before the first one is enqueued, so an error never leaves C partly
+ * updated.  SGEMM_ERR_LAUNCH reports a launch the runtime rejected anyway.
  */
 #ifndef SGEMM_GFX950_H
 #define SGEMM_GFX950_H
@@ -59,7 +63,7 @@ extern "C" {
 #endif
 
 #define SGEMM_OK 0
-#define SGEMM_ERR_DIM (-1)     /* M, N, K or batch negative, or a grid too large */
+#define SGEMM_ERR_DIM (-1)     /* M, N, K or batch negative */
 #define SGEMM_ERR_LD (-2)      /* a leading dimension shorter than the stored row */
 #define SGEMM_ERR_PTR (-3)     /* a matrix that must be read or written is NULL */
 #define SGEMM_ERR_LAUNCH (-4)  /* the HIP runtime rejected a kernel launch */
@@ -67,6 +71,9 @@ extern "C" {
 #define SGEMM_ERR_VARIANT (-6) /* sgemm_ex: variant index out of range */
 #define SGEMM_ERR_OP (-7)      /* sgemm_op: opA or opB not SGEMM_OP_N / SGEMM_OP_T */
 #define SGEMM_ERR_STRIDE (-8)  /* batched: a negative stride, or slices of C overlap */
+#define SGEMM_ERR_GRID (-9)    /* the problem needs a launch grid beyond the HIP limits;
+                                  nothing was enqueued */
+#define SGEMM_ERR_WORKSPACE (-10) /* a workspace that is not 16-byte aligned */
 
 /* Operand orientation for sgemm_op: use the matrix as stored, or its transpose. */
 #define SGEMM_OP_N 0
@@ -154,14 +161,81 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
                              int ldb, long long strideB, float beta, float *C, int ldc,
                              long long strideC, int batch, void *stream, int variant);
 
-/* Number of kernel variants, and a stable name for each ("" when out of range). */
+/*
+ * Strided batched SGEMM with a caller workspace.  Everything is as for
+ * sgemm_strided_batched(), except that the call may use `workspace`
+ * (workspace_bytes bytes of device memory on the current device, 16-byte
+ * aligned, or NULL for none) to split the last, partial round of output
+ * tiles over K.  A grid whose tiles fill the CUs' workgroup slots a whole
+ * number of times and a bit more leaves most CUs idle in its last round
+ * ((4095, 4097, 1023): 1056 tiles of 128x128 for 512 slots); with a
+ * workspace the tiles of that round are split into K ranges that fill the
+ * slots, the partial tiles go to the workspace, and the workgroup that
+ * finishes a tile's ranges last adds them in range order and writes the
+ * tile of C.  The pages name splitting K as the way to fill the GPU when the
+ * output tiles cannot ("The road to a fast GEMM", "Where to go next").
+ *
+ * Results are bitwise repeatable (each output is one sum in a fixed order; no
+ * atomics touch C), in either atomics mode.  The automatic choice takes the
+ * split form only for a single matrix (batch == 1), when the predicted rate
+ * is higher and the workspace holds its partial tiles; otherwise the call
+ * runs as without a workspace.
+ *
+ * The workspace must be zero-filled before its first use (e.g. allocated
+ * with hipMalloc and cleared with hipMemset once); each call that uses it
+ * leaves it ready for the next (the counters it holds are back at zero when
+ * the call's kernels finish).  The caller owns it; calls that use one
+ * workspace must not overlap in time (same stream, or synchronised).
+ * A workspace that is not 16-byte aligned gives SGEMM_ERR_WORKSPACE; one that
+ * is too small is not an error (the split form is not taken).
+ */
+int sgemm_strided_batched_ws(int opA, int opB, int M, int N, int K, float alpha,
+                             const float *A, int lda, long long strideA, const float *B, int ldb,
+                             long long strideB, float beta, float *C, int ldc, long long strideC,
+                             int batch, void *workspace, unsigned long long workspace_bytes,
+                             void *stream);
+
+/* As sgemm_strided_batched_ws() with an explicit kernel variant (-1 = automatic). */
+int sgemm_strided_batched_ws_ex(int opA, int opB, int M, int N, int K, float alpha,
+                                const float *A, int lda, long long strideA, const float *B,
+                                int ldb, long long strideB, float beta, float *C, int ldc,
+                                long long strideC, int batch, void *workspace,
+                                unsigned long long workspace_bytes, void *stream, int variant);
+
+/* The variant sgemm_strided_batched_ws() would run with a workspace of
+ * workspace_bytes bytes (no launch, no HIP call; see sgemm_select_variant). */
+int sgemm_strided_batched_ws_select_variant(int opA, int opB, int M, int N, int K, float alpha,
+                                            const float *A, int lda, long long strideA,
+                                            const float *B, int ldb, long long strideB,
+                                            float beta, const float *C, int ldc,
+                                            long long strideC, int batch,
+                                            unsigned long long workspace_bytes);
+
+/*
+ * Bytes of workspace the automatic choice of sgemm_strided_batched_ws() can
+ * use for this problem (packed leading dimensions): 0 when it would not take
+ * the split form, at most 4 KiB + 32 MiB for any problem, or a negative
+ * SGEMM_ERR_* status for invalid operations or sizes.
+ */
+long long sgemm_workspace_size(int opA, int opB, int M, int N, int K, int batch);
+
+/* Number of kernel variants, and a stable name for each ("" when out of range).
+ * The variants are the kernel versions sgemm_ex() can force, as the pages'
+ * benchmark walks its table of kernel versions ("The road to a fast GEMM",
+ * "The complete code"). */
 int sgemm_num_variants(void);
 const char *sgemm_variant_name(int variant);
 
 /*
  * The variant sgemm() would run for this problem (no launch, no HIP call), or
- * a negative SGEMM_ERR_* status for invalid arguments.  Returns -100 when the
- * problem needs no GEMM kernel (M or N zero, or alpha == 0 or K == 0).
+ * a negative SGEMM_ERR_* status for invalid arguments or a problem too large
+ * to launch.  Returns -100 when the problem needs no GEMM kernel (M or N
+ * zero, or alpha == 0 or K == 0).  Takes every argument sgemm() takes except
+ * the stream: alpha because alpha == 0 needs no GEMM kernel, the pointers
+ * because their alignment selects the load paths.  The pointers are not
+ * dereferenced.  Its variant index names the registry of sgemm_variant_name,
+ * the per-shape kernel table of the build (the pages keep such a registry
+ * of their kernel versions, "The road to a fast GEMM", "The complete code").
  */
 int sgemm_select_variant(int M, int N, int K, float alpha, const float *A,
                          int lda, const float *B, int ldb, float beta,
@@ -178,11 +252,14 @@ int sgemm_strided_batched_select_variant(int opA, int opB, int M, int N, int K, 
                                          const float *B, int ldb, long long strideB, float beta,
                                          const float *C, int ldc, long long strideC, int batch);
 
-/* Short English description of a status code (never NULL). */
+/* Short English description of a status code (never NULL).  The pages check
+ * every runtime call with a macro that reports the error text ("The road to
+ * a fast GEMM", "The complete code"); this is that text for the library's own
+ * status codes. */
 const char *sgemm_status_string(int status);
 
-/* Interface version, currently 4 (2 added sgemm_op, 3 the strided batches, 4
- * the atomics mode). */
+/* Interface version, currently 5 (2 added sgemm_op, 3 the strided batches, 4
+ * the atomics mode, 5 the workspace entry points and SGEMM_ERR_GRID). */
 int sgemm_version(void);
 
 /*

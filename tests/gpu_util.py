@@ -43,7 +43,7 @@ class DevMatrix:
 
 
 def run(A, B, C=None, alpha=1.0, beta=0.0, *, variant=-1, lds=(None, None, None),
-        offsets=(0, 0, 0), check_outside=False, trans_a=False, trans_b=False):
+        offsets=(0, 0, 0), check_outside=False, trans_a=False, trans_b=False, workspace=None):
     """Runs the HIP SGEMM on device copies; returns C as numpy (float32).
 
     A and B are the matrices as stored: with trans_a, A is K x M and op(A) is
@@ -57,7 +57,7 @@ def run(A, B, C=None, alpha=1.0, beta=0.0, *, variant=-1, lds=(None, None, None)
     dB = DevMatrix(B, lds[1], offsets[1])
     dC = DevMatrix(C, lds[2], offsets[2])
     sg.gemm(dA.view, dB.view, dC.view, alpha, beta, variant=variant, trans_a=trans_a,
-            trans_b=trans_b)
+            trans_b=trans_b, workspace=workspace)
     torch.cuda.synchronize()
     out = dC.numpy()
     if check_outside:

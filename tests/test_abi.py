@@ -56,7 +56,7 @@ def test_variant_registry(lib):
     assert names[0] == "simple"
     assert any(x.startswith("mfma32") for x in names) and any(x.startswith("valu") for x in names)
     assert sg.sgemm_variant_name(n) == "" and sg.sgemm_variant_name(-1) == ""
-    assert sg.sgemm_version() == 4
+    assert sg.sgemm_version() == 5
 
 
 FAKE = 0x1000  # never dereferenced: every call below fails or returns before any HIP call
@@ -344,6 +344,11 @@ def test_ceiling_argument_checks(lib):
     assert sg.sgemm_ceiling_fma(1, 0, FAKE)[0] == -1
     assert sg.sgemm_ceiling_copy(FAKE, FAKE, 6, 1) == -1
     assert sg.sgemm_ceiling_copy(FAKE + 4, FAKE, 8, 1) == -1
+    assert sg.sgemm_ceiling_read(FAKE, 6, 1, FAKE) == -1
+    assert sg.sgemm_ceiling_read(FAKE + 4, 8, 1, FAKE) == -1
+    assert sg.sgemm_ceiling_read(FAKE, 8, 0, FAKE) == -1
+    assert sg.sgemm_ceiling_read(FAKE, 8, 1, None) == -1
+    assert sg.sgemm_ceiling_empty(0) == -1
 
 
 def test_no_device_is_reported_not_crashed(lib):
@@ -511,3 +516,70 @@ def test_select_fuzz_valid_and_stable(lib):
                 assert not sg.sgemm_variant_name(v).endswith("_splitk"), (ta, tb, M, N, K, batch)
     finally:
         sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
+
+
+# ---------------------------------------------------------------- launch planning
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+def test_scale_any_width_is_not_a_grid_error(lib):
+    """alpha = 0 (or K = 0) scales C by beta with a grid-stride kernel, so a C
+    wider than 65535 blocks of 64 columns is valid: the call gets past the
+    launch plan to the device check (no GPU here: SGEMM_ERR_DEVICE)."""
+    if not _no_gpu():
+        pytest.skip("a GPU is present")
+    N = 5_000_000
+    assert sg.sgemm(1, N, 0, 1.0, None, 1, None, N, 0.5, FAKE, N, 0) == sg.SGEMM_ERR_DEVICE
+    assert sg.sgemm(3, N, 7, 0.0, None, 7, None, N, 2.0, FAKE, N, 0) == sg.SGEMM_ERR_DEVICE
+    # the one-lane kernel strides too: forced on a very wide problem
+    simple = sg.variant_names().index("simple")
+    assert sg.sgemm_ex(1, N, 4, 1.0, FAKE, 4, FAKE, N, 0.0, FAKE, N, 0, simple) == sg.SGEMM_ERR_DEVICE
+
+
+def test_grid_too_large_is_reported_before_any_launch(lib):
+    """A problem whose tile grid exceeds the HIP limits (2^32 work-items along
+    x) returns SGEMM_ERR_GRID from the launch plan, before the device is
+    touched -- for the automatic choice, a forced variant, the choice query,
+    and a batch split into several chunks of 65535 slices."""
+    M = N = 1 << 20
+    st = sg.sgemm(M, N, 1024, 1.0, FAKE, 1024, FAKE, N, 0.0, FAKE, N, 0)
+    assert st == sg.SGEMM_ERR_GRID, st
+    assert sg.sgemm_select_variant(M, N, 1024, 1.0, FAKE, 1024, FAKE, N, 0.0, FAKE, N) == sg.SGEMM_ERR_GRID
+    v = sg.variant_names().index("mfma16_64x64x16_2x2")
+    assert sg.sgemm_ex(M, N, 64, 1.0, FAKE, 64, FAKE, N, 0.0, FAKE, N, 0, v) == sg.SGEMM_ERR_GRID
+    # 70000 slices: two chunks, each with the same oversized grid
+    Mb, Nb = 1 << 19, 1 << 19
+    args = (0, 0, Mb, Nb, 64, 1.0, FAKE, 64, 0, FAKE, Nb, 0, 0.0, FAKE, Nb, Mb * Nb, 70000)
+    assert sg.sgemm_strided_batched_ex(*args, 0, v) == sg.SGEMM_ERR_GRID
+    assert "nothing was enqueued" in sg.sgemm_status_string(sg.SGEMM_ERR_GRID)
+
+
+def test_large_batch_within_limits_passes_the_plan(lib):
+    """Just inside the limits the plan passes (no GPU here: the device check
+    answers)."""
+    if not _no_gpu():
+        pytest.skip("a GPU is present")
+    args = (0, 0, 64, 64, 64, 1.0, FAKE, 64, 4096, FAKE, 64, 4096, 0.0, FAKE, 64, 4096, 200000)
+    assert sg.sgemm_strided_batched(*args, 0) == sg.SGEMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("which", ["A", "B", "C"])
+def test_strided_one_row_view_is_rejected(which):
+    """A one-row view whose elements are not adjacent (column stride != 1) is
+    not a row-major matrix: the binding refuses it instead of reading or
+    writing its row as if it were packed."""
+    import torch
+    base = torch.zeros(4, 512)
+    strided = base[:1, ::8]                      # shape (1, 64), strides (512, 8)
+    assert strided.shape == (1, 64) and strided.stride() == (512, 8)
+    A = torch.zeros(1, 64) if which != "A" else strided
+    B = torch.zeros(64, 64)
+    C = torch.zeros(1, 64) if which != "C" else strided
+    if which == "B":
+        B = torch.zeros(1, 512)[:, ::8]          # K = 1 row of B, strided
+        A = torch.zeros(1, 1)
+    with pytest.raises(ValueError, match="row-major"):
+        sg.gemm(A, B, C)
