@@ -27,13 +27,15 @@ from ._lib import (EXPORTS, LIBRARY, SGEMM_ATOMICS_ALLOWED,  # noqa: F401
                    sgemm_status_string, sgemm_strided_batched, sgemm_strided_batched_ex,
                    sgemm_strided_batched_select_variant, sgemm_strided_batched_ws,
                    sgemm_strided_batched_ws_ex, sgemm_strided_batched_ws_select_variant,
-                   sgemm_variant_name, sgemm_version, sgemm_workspace_size, SGEMM_ERR_WORKSPACE)
+                   sgemm_variant_name, sgemm_version, sgemm_workspace_size, SGEMM_ERR_WORKSPACE,
+                   sgemm_strided_batched_noalloc)
 
 __all__ = ["gemm", "gemm_batched", "variant_names", "sgemm", "sgemm_ex", "sgemm_op",
            "sgemm_op_ex", "sgemm_op_select_variant", "sgemm_strided_batched",
            "sgemm_strided_batched_ex", "sgemm_strided_batched_select_variant", "sgemm_num_variants",
            "sgemm_strided_batched_ws", "sgemm_strided_batched_ws_ex",
            "sgemm_strided_batched_ws_select_variant", "sgemm_workspace_size", "workspace",
+           "sgemm_strided_batched_noalloc",
            "sgemm_variant_name", "sgemm_select_variant", "sgemm_status_string",
            "sgemm_version", "sgemm_set_atomics_mode", "sgemm_get_atomics_mode",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy",

@@ -39,6 +39,7 @@ EXPORTS = ("sgemm", "sgemm_ex", "sgemm_op", "sgemm_op_ex", "sgemm_strided_batche
            "sgemm_status_string", "sgemm_version", "sgemm_set_atomics_mode",
            "sgemm_get_atomics_mode", "sgemm_strided_batched_ws", "sgemm_strided_batched_ws_ex",
            "sgemm_strided_batched_ws_select_variant", "sgemm_workspace_size",
+           "sgemm_strided_batched_noalloc",
            "sgemm_ceiling_mfma", "sgemm_ceiling_fma", "sgemm_ceiling_copy", "sgemm_ceiling_read",
            "sgemm_ceiling_empty")
 
@@ -80,6 +81,8 @@ def _declare(lib):
     lib.sgemm_strided_batched_ws_ex.restype = c_int
     lib.sgemm_strided_batched_ws_select_variant.argtypes = batched + [u64]
     lib.sgemm_strided_batched_ws_select_variant.restype = c_int
+    lib.sgemm_strided_batched_noalloc.argtypes = batched + [vp]
+    lib.sgemm_strided_batched_noalloc.restype = c_int
     lib.sgemm_workspace_size.argtypes = [c_int] * 6
     lib.sgemm_workspace_size.restype = ctypes.c_longlong
     lib.sgemm_num_variants.argtypes = []
@@ -191,6 +194,13 @@ def sgemm_strided_batched_ws_select_variant(opA, opB, M, N, K, alpha, A, lda, st
     return load().sgemm_strided_batched_ws_select_variant(opA, opB, M, N, K, alpha, A, lda,
                                                           strideA, B, ldb, strideB, beta, C, ldc,
                                                           strideC, batch, workspace_bytes)
+
+
+def sgemm_strided_batched_noalloc(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta,
+                                  C, ldc, strideC, batch, stream=0) -> int:
+    """sgemm_strided_batched_ws on the library's static scratch (allocates nothing)."""
+    return load().sgemm_strided_batched_noalloc(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                                strideB, beta, C, ldc, strideC, batch, stream)
 
 
 def sgemm_workspace_size(opA, opB, M, N, K, batch=1) -> int:

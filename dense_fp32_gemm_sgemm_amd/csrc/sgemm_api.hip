@@ -12,6 +12,7 @@
 #include <atomic>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 namespace sg950 {
 namespace {
@@ -582,6 +583,71 @@ long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
   return 0;
 }
 
+// Scratch of the entry point that allocates nothing
+// (sgemm_strided_batched_noalloc): the workspace of the split tail form as a
+// file-scope device array, 4 KiB of counters plus 32 MiB of partial tiles --
+// the most any problem's split can use.  Every GPU the library runs on holds
+// its own copy from module load to process end.  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once, with that device current.
+constexpr unsigned long long kScratchBytes = (unsigned long long)kTailWorkspaceBytes;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device; set once
+
+// The device address of this device's scratch (set up on the first call on
+// the device), or nullptr when the runtime cannot give it.  The counters
+// must start at zero: the array is zero at load, every call that uses it
+// leaves them zero, and the set-up clears them once more with a kernel on
+// `s` (a kernel, not a memset, so a captured first call replays cleanly).
+void *device_scratch(int dev, hipStream_t s) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    // zero the counters: kTailFlagBytes of zero floats (zero bits) through
+    // the C-scaling kernel with beta = 0
+    Problem z{};
+    z.M = 1;
+    z.N = (int)(kTailFlagBytes / 4);
+    z.beta = 0.0f;
+    z.C = reinterpret_cast<float *>(ptr);
+    z.ldc = z.N;
+    z.batch = 1;
+    if (launch_scale(z, s) != 0 || hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+int run_noalloc(int opA, int opB, int M, int N, int K, float alpha, const float *A, int lda,
+                long long sa, const float *B, int ldb, long long sb, float beta, float *C, int ldc,
+                long long sc, int batch, void *stream) {
+  int st = check_args(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0 || batch == 0) return SGEMM_OK;
+  // The scratch a call may use: the split plan of the variant the choice
+  // takes with kScratchBytes available (never more, as plans are capped at
+  // the workspace maximum); a call that would need more is refused.
+  if (alpha != 0.0f && K > 0) {
+    const Problem p{M,   N,   K,   alpha, beta, A, lda, B, ldb, C, ldc, opA == SGEMM_OP_T, opB == SGEMM_OP_T,
+                    sa,  sb,  sc,  batch, reinterpret_cast<void *>(256), kScratchBytes};
+    const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
+    for (const TailFamily &tf : kTailFamilies)
+      if (tf.variant == v && (unsigned long long)family_tail_plan(tf, p).bytes > kScratchBytes)
+        return SGEMM_ERR_WORKSPACE;
+  }
+  st = check_device();
+  if (st != SGEMM_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SGEMM_ERR_DEVICE;
+  void *ws = device_scratch(dev, reinterpret_cast<hipStream_t>(stream));
+  if (ws == nullptr) return SGEMM_ERR_LAUNCH;
+  return run(opA, opB, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc, batch, ws, kScratchBytes,
+             stream, -1);
+}
+
 }  // namespace
 }  // namespace sg950
 
@@ -653,6 +719,14 @@ int sgemm_strided_batched_ws_select_variant(int opA, int opB, int M, int N, int 
                        strideC, batch, workspace_bytes);
 }
 
+int sgemm_strided_batched_noalloc(int opA, int opB, int M, int N, int K, float alpha,
+                                  const float *A, int lda, long long strideA, const float *B,
+                                  int ldb, long long strideB, float beta, float *C, int ldc,
+                                  long long strideC, int batch, void *stream) {
+  return sg950::run_noalloc(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                            strideC, batch, stream);
+}
+
 long long sgemm_workspace_size(int opA, int opB, int M, int N, int K, int batch) {
   return sg950::workspace_size(opA, opB, M, N, K, batch);
 }
@@ -695,7 +769,8 @@ const char *sgemm_status_string(int status) {
     case SGEMM_ERR_OP: return "invalid operation (opA and opB must be SGEMM_OP_N or SGEMM_OP_T)";
     case SGEMM_ERR_STRIDE: return "invalid batch stride (negative, or slices of C overlap)";
     case SGEMM_ERR_GRID: return "problem too large for the launch grid of its kernel (nothing was enqueued)";
-    case SGEMM_ERR_WORKSPACE: return "workspace not 16-byte aligned";
+    case SGEMM_ERR_WORKSPACE:
+      return "workspace not 16-byte aligned, or the call needs more scratch than the library's static buffer";
     default: return "unknown status";
   }
 }

@@ -73,7 +73,8 @@ extern "C" {
 #define SGEMM_ERR_STRIDE (-8)  /* batched: a negative stride, or slices of C overlap */
 #define SGEMM_ERR_GRID (-9)    /* the problem needs a launch grid beyond the HIP limits;
                                   nothing was enqueued */
-#define SGEMM_ERR_WORKSPACE (-10) /* a workspace that is not 16-byte aligned */
+#define SGEMM_ERR_WORKSPACE (-10) /* a workspace that is not 16-byte aligned, or (no-alloc
+                                     entry point) a call needing more than the static scratch */
 
 /* Operand orientation for sgemm_op: use the matrix as stored, or its transpose. */
 #define SGEMM_OP_N 0
@@ -210,6 +211,29 @@ int sgemm_strided_batched_ws_select_variant(int opA, int opB, int M, int N, int 
                                             float beta, const float *C, int ldc,
                                             long long strideC, int batch,
                                             unsigned long long workspace_bytes);
+
+/*
+ * sgemm_strided_batched_ws() for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is the library's own static scratch, 4 KiB +
+ * 32 MiB per GPU, held from module load until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating routine).
+ *
+ * Everything else is as for sgemm_strided_batched_ws() with that workspace:
+ * the same automatic choice, results bitwise equal to it.  The split plans
+ * are capped to fit the scratch, so no problem size needs more; a call that
+ * would is refused with SGEMM_ERR_WORKSPACE before anything is enqueued.
+ *
+ * The first call on a device looks up the device's scratch address and
+ * clears its counters with a small kernel on `stream` (one-time set-up);
+ * every call leaves the counters at zero.  All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (on different streams, or
+ * from several threads without ordering) race and give wrong results.
+ */
+int sgemm_strided_batched_noalloc(int opA, int opB, int M, int N, int K, float alpha,
+                                  const float *A, int lda, long long strideA, const float *B,
+                                  int ldb, long long strideB, float beta, float *C, int ldc,
+                                  long long strideC, int batch, void *stream);
 
 /*
  * Bytes of workspace the automatic choice of sgemm_strided_batched_ws() can
