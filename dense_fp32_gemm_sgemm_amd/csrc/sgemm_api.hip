@@ -69,7 +69,7 @@ struct Variant {
 // Stable order: tests and benchmarks address variants by index and name.
 const Variant kVariants[] = {
     {"simple", launch_simple},
-    {"valu_128x128x16", launch_valu_128x128},
+    {"valu_128x256x16", launch_valu_128x256},
     {"mfma32_256x256x32_4x2", launch_mfma32_256x256x32_4x2},
     {"mfma32_256x256x16_4x2", launch_mfma32_256x256x16_4x2},
     {"mfma32_128x128x32_2x2", launch_mfma32_128x128x32_2x2},
@@ -218,7 +218,9 @@ constexpr long long kCus = 256;  // compute units of an MI355X
 
 // Tile families of the ordered slab loop, for the choice among them.  Rates
 // are the steady TFLOP/s of each family measured on MI355X over the shape
-// sweeps with whole rounds of tiles (at K >= 2048 and at K = 1024); a shape
+// sweeps with whole rounds of tiles (at K >= 2048 and at K <= 1024: the
+// median of measured / (area share x busy share), device time per call from
+// back-to-back graph replays, so no host launch gap inflates short calls); a shape
 // gets rate x (share of the tiles' area inside C) x (share of the CU time
 // the tiles keep busy).  The busiest CU holds n = ceil(tiles / 256) tiles;
 // a family that fits s workgroups on a CU runs them s at a time at the
@@ -232,12 +234,12 @@ struct TileFamily {
   bool short_m;       // also runs M < bm (A untransposed)
 };
 constexpr TileFamily kTileFamilies[] = {
-    {kMfma32_256x256x32_w4_sched, 256, 256, 148.0, 140.0, 1, {0.0, 0.0, 0.0}, false},
-    {kMfma16_128x128x32_w4_sched, 128, 128, 145.0, 140.0, 2, {0.0, 0.95, 0.0}, false},
-    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 133.0, 1, {0.0, 0.0, 0.0}, false},
-    {kMfma16_128x64x64_w8_sched, 128, 64, 133.0, 126.0, 1, {0.0, 0.0, 0.0}, false},
-    {kMfma16_64x64x64_w8_sched, 64, 64, 131.0, 127.0, 2, {0.0, 0.92, 0.0}, false},
-    {kMfma16_32x64x64_w4_sched, 32, 64, 120.0, 112.0, 3, {0.0, 0.75, 0.93}, true},
+    {kMfma32_256x256x32_w4_sched, 256, 256, 147.5, 141.0, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_128x128x32_w4_sched, 128, 128, 146.5, 140.0, 2, {0.0, 0.95, 0.0}, false},
+    {kMfma16_128x128x64_w8_sched, 128, 128, 141.0, 131.5, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_128x64x64_w8_sched, 128, 64, 135.0, 122.5, 1, {0.0, 0.0, 0.0}, false},
+    {kMfma16_64x64x64_w8_sched, 64, 64, 132.5, 123.5, 2, {0.0, 0.92, 0.0}, false},
+    {kMfma16_32x64x64_w4_sched, 32, 64, 124.0, 112.5, 3, {0.0, 0.75, 0.93}, true},
 };
 // The same loops with K split over workgroups (atomics after a beta-scaling
 // launch), priced by the unsplit family's rate at the range depth.
@@ -315,26 +317,30 @@ double split_rate(const SplitFamily &sf, const Problem &p) {
 // tiles (workspace entry points only): whole rounds at the family's steady
 // rate, and the last round's tiles split into K ranges that fill the slots,
 // each range at the rate a split of that depth keeps.
+// (whole_round: taken only after at least one whole round of tiles -- the
+// 64x64 tail form never beat the other choices on a grid of a single,
+// partial round, where its predicted rate ran 5-30% high.)
 struct TailFamily {
   int variant;
   TileFamily base;
   int bk;
+  bool whole_round;
 };
 constexpr TailFamily kTailFamilies[] = {
-    {kMfma16_128x128x32_w4_sched_tail, kTileFamilies[1], 32},
-    {kMfma16_128x128x64_w8_sched_tail, kTileFamilies[2], 64},
-    {kMfma16_128x64x64_w8_sched_tail, kTileFamilies[3], 64},
-    {kMfma16_64x64x64_w8_sched_tail, kTileFamilies[4], 64},
+    {kMfma16_128x128x32_w4_sched_tail, kTileFamilies[1], 32, false},
+    {kMfma16_128x128x64_w8_sched_tail, kTileFamilies[2], 64, false},
+    {kMfma16_128x64x64_w8_sched_tail, kTileFamilies[3], 64, false},
+    {kMfma16_64x64x64_w8_sched_tail, kTileFamilies[4], 64, true},
 };
 
 // Share of the rate a tail range of depth k (K values) keeps when its tile
 // was split `splits` ways: the range's own slabs against those plus a fixed
-// cost (its pipeline's start, about 140 values of k) and the partial tiles
-// written and read back (about 19 per split).  Fitted to the tail forms on
-// MI355X: 0.74 for 512-deep ranges of 64x64 tiles in two (1024^3), 0.78 for
-// 768-deep ranges of 128x128 tiles in four (3000^3), 0.43 for 191-deep
-// ranges of 128x128 tiles in seven ((4095, 4097, 1023)).
-double tail_efficiency(double k, int splits) { return k / (k + 143.0 + 18.5 * splits); }
+// cost (its pipeline's start, about 120 values of k) and the partial tiles
+// written and read back (about 20 per split).  Least-squares fit (in log
+// rate) to the 195 tail-form timings of the tile-choice table on MI355X
+// (device time per call); e.g. 0.45 for 191-deep ranges of 128x128 tiles in
+// seven ((4095, 4097, 1023)), 0.80 for 768-deep ranges in four (3000^3).
+double tail_efficiency(double k, int splits) { return k / (k + 120.0 + 20.0 * splits); }
 
 TailPlan family_tail_plan(const TailFamily &tf, const Problem &p) {
   return tail_plan(family_tiles(tf.base, p), p.K, tf.base.slots, (long long)tf.base.bm * tf.base.bn, tf.bk);
@@ -350,6 +356,7 @@ double tail_rate(const TailFamily &tf, const Problem &p) {
   if (p.batch != 1 || p.ws == nullptr) return 0.0;
   const TailPlan tp = family_tail_plan(tf, p);
   if (tp.splits < 2 || (unsigned long long)tp.bytes > p.ws_bytes) return 0.0;
+  if (tf.whole_round && tp.dp_tiles == 0) return 0.0;
   const TileFamily &f = tf.base;
   const long long tiles = family_tiles(f, p);
   const double whole = (double)tp.dp_tiles / (double)kCus;  // tiles per CU in whole rounds

@@ -18,8 +18,8 @@ int launch_simple(const Problem &p, hipStream_t stream);
 // C = beta*C over every batch slice (zeros without reading C when beta == 0).
 int launch_scale(const Problem &p, hipStream_t stream);
 
-// Register-tiled VALU kernel: 128x128 tile, 8x8 outputs per thread.
-int launch_valu_128x128(const Problem &p, hipStream_t stream);
+// Register-tiled VALU kernel: 128x256 tile, 8x16 outputs per thread.
+int launch_valu_128x256(const Problem &p, hipStream_t stream);
 
 // Matrix-core kernels, named <instruction>_<BM>x<BN>x<BK>_<waves M>x<waves N>;
 // _pipe: software-pipelined slab order; _w4: registers capped for four waves

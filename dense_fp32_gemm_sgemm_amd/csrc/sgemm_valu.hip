@@ -3,20 +3,30 @@
 // The vector-ALU counterpart of the matrix-core kernel, following the ladder
 // of "The road to a fast GEMM" (sections "v4: two-dimensional register
 // tiling", "v5: vectorized loads" and the double-buffering exercise) and the
-// tuning notes of the Tinyforge README (deeper K-slab, padded shared tile),
-// re-shaped for gfx950:
-//   * a 256-thread workgroup owns a 128 x 128 tile of C; each thread owns an
-//     8 x 8 block of it, kept in 64 accumulator registers and updated as an
-//     outer product: per k, 8 values of A and 8 of B feed 64 FMAs;
+// tuning notes of the Tinyforge README (register tiling as the main step,
+// a deeper K-slab, a padded shared tile), re-shaped for gfx950:
+//   * a 256-thread workgroup owns a 128 x 256 tile of C; each thread owns an
+//     8 x 16 block of it in 128 accumulator registers, updated as an outer
+//     product: per k, 8 values of A and 16 of B feed 128 FMAs;
 //   * both tiles are stored k-major in LDS (As[k][m], Bs[k][n]) so a thread's
-//     8 A values are two 16-byte reads, like its 8 B values (an operand whose
-//     memory rows run along K is transposed on its way into LDS);
-//   * a thread's 8 rows are {4*ty .. 4*ty+3} and {64+4*ty .. 64+4*ty+3} (and
-//     likewise its 8 columns), so the 16 lanes that read one LDS row at a time
-//     touch 16 consecutive 16-byte chunks: no bank conflicts on the reads;
-//   * two LDS buffers alternate with one barrier per K-slab of 16.
-// Its ceiling is the plain v_fma_f32 rate (half the FP32 peak, which needs
-// packed FMA; packed FP32 instructions are disabled in this build).
+//     8 A values are two 16-byte reads and its 16 B values four (an operand
+//     whose memory rows run along K is transposed on its way into LDS);
+//   * a thread's 8 rows are {4*ty .. 4*ty+3} and {64+4*ty .. 64+4*ty+3} and
+//     its 16 columns {4*tx + 64*c .. +3} (c = 0..3), so the 16 lanes that
+//     read one LDS row at a time touch 16 consecutive 16-byte chunks: no bank
+//     conflicts on the reads;
+//   * two LDS buffers alternate with one barrier per K-slab of 16; the global
+//     loads of the next slab are in flight while this one is multiplied, and
+//     a ragged last slab is the only one that checks k against K.
+// Why 8 x 16: LDS returns 128 bytes per clock to a CU, and every FMA needs
+// its operands from LDS once per k.  An 8 x 8 block reads (8 + 8) * 4 bytes
+// per 64 FMAs, 1 byte per lane-FMA -- at the measured vector FMA rate of
+// gfx950 (about 105 lane-FMAs per clock per CU, 129 TFLOP/s with unpacked
+// v_fma_f32) that is 82% of the LDS bandwidth; 8 x 16 needs 0.75 bytes, and
+// the 128 accumulators still leave room for two workgroups per CU.
+// Ceiling: the unpacked v_fma_f32 rate (packed FP32 instructions are switched
+// off in this build); the matrix cores, at 155 TFLOP/s measured for FP32,
+// are the main path.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
 #include "sgemm_tiles.hpp"
@@ -27,14 +37,15 @@
 namespace sg950 {
 
 namespace {
-constexpr int kBM = 128, kBN = 128, kBK = 16, kThreads = 256;
-constexpr int kAPitch = kBM + 4;  // k-major A row pitch (floats)
-constexpr int kBPitch = kBN + 4;  // B row pitch (floats)
+constexpr int kBM = 128, kBN = 256, kBK = 16, kThreads = 256;
+constexpr int kTM = 8, kTN = 16;      // outputs per thread
+constexpr int kAPitch = kBM + 4;      // k-major A row pitch (floats)
+constexpr int kBPitch = kBN + 4;      // B row pitch (floats)
 }  // namespace
 
 template <bool TA, bool TB, bool VA, bool VB, bool VC>
-__global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, int tiles_n,
-                                                        int group_m) {
+__global__ __launch_bounds__(kThreads, 2) void valu_kernel(Problem p, int tiles_m, int tiles_n,
+                                                           int group_m) {
   select_slice(p);
   __shared__ __attribute__((aligned(16))) float As[2 * kBK * kAPitch];
   __shared__ __attribute__((aligned(16))) float Bs[2 * kBK * kBPitch];
@@ -72,15 +83,15 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, 
     b_st[i] = TB ? LB::col_of(tid, i) * kBPitch + LB::row_of(tid, i)
                  : LB::row_of(tid, i) * kBPitch + LB::col_of(tid, i);
 
-  float acc[8][8];
+  float acc[kTM][kTN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < kTN; ++j) acc[i][j] = 0.0f;
 
   const int K = p.K;
   const int nk = (K + kBK - 1) / kBK;
-  const bool ragged = (K % kBK) != 0;
+  const int nfull = K / kBK;  // slabs that lie wholly inside K
 
   auto stage = [&](float *as, float *bs) {
 #pragma unroll
@@ -102,58 +113,78 @@ __global__ __launch_bounds__(kThreads) void valu_kernel(Problem p, int tiles_m, 
       }
     }
   };
-
-  if (ragged && nk == 1) {
-    la.template load<true>(0, K);
-    lb.template load<true>(0, K);
-  } else {
-    la.template load<false>(0, K);
-    lb.template load<false>(0, K);
-  }
-  stage(As, Bs);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool has_next = kt + 1 < nk;
-    if (has_next) {
-      const int k1 = (kt + 1) * kBK;
-      if (ragged && kt + 2 == nk) {
-        la.template load<true>(k1, K);
-        lb.template load<true>(k1, K);
-      } else {
-        la.template load<false>(k1, K);
-        lb.template load<false>(k1, K);
-      }
+  auto load = [&](int kt) {
+    if (kt < nfull) {
+      la.template load<false>(kt * kBK, K);
+      lb.template load<false>(kt * kBK, K);
+    } else {
+      la.template load<true>(kt * kBK, K);
+      lb.template load<true>(kt * kBK, K);
     }
+  };
+  // The outer products of one slab from LDS stage `cur`.  The operands of
+  // step k+1 are read while step k is multiplied, and a scheduling fence
+  // after every step keeps the compiler from hoisting the reads of further
+  // steps (which would need more registers than the accumulators leave).
+  auto read_ops = [&](const float *as, const float *bs, int k, float (&a)[kTM], float (&b)[kTN]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(as + k * kAPitch + 64 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * h + e] = v[e];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(bs + k * kBPitch + 64 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[4 * c + e] = v[e];
+    }
+  };
+  auto multiply = [&](int cur) {
     const float *as = As + cur * kBK * kAPitch + 4 * ty;
     const float *bs = Bs + cur * kBK * kBPitch + 4 * tx;
+    float a[kTM], b[kTN];
+    read_ops(as, bs, 0, a, b);
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
-      const floatx4 a0 = *reinterpret_cast<const floatx4 *>(as + k * kAPitch);
-      const floatx4 a1 = *reinterpret_cast<const floatx4 *>(as + k * kAPitch + 64);
-      const floatx4 b0 = *reinterpret_cast<const floatx4 *>(bs + k * kBPitch);
-      const floatx4 b1 = *reinterpret_cast<const floatx4 *>(bs + k * kBPitch + 64);
-      const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      float an[kTM], bn[kTN];
+      if (k + 1 < kBK) read_ops(as, bs, k + 1, an, bn);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kTM; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < kTN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      if (k + 1 < kBK) {
+#pragma unroll
+        for (int i = 0; i < kTM; ++i) a[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) b[j] = bn[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (has_next) stage(As + (cur ^ 1) * kBK * kAPitch, Bs + (cur ^ 1) * kBK * kBPitch);
+  };
+
+  load(0);
+  stage(As, Bs);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int cur = kt & 1;
+    load(kt + 1);  // in flight while this slab is multiplied
+    multiply(cur);
+    stage(As + (cur ^ 1) * kBK * kAPitch, Bs + (cur ^ 1) * kBK * kBPitch);
     __syncthreads();
   }
+  multiply((nk - 1) & 1);
 
-  // Epilogue: rows 4*ty + {0..3} and 64 + 4*ty + {0..3}; columns likewise with
-  // tx.  Whole in-range 4-column groups of an aligned C use 16-byte accesses.
+  // Epilogue: rows 4*ty + {0..3} and 64 + 4*ty + {0..3}; columns 4*tx + 64*c
+  // + {0..3}.  Whole in-range 4-column groups of an aligned C use 16-byte
+  // accesses.
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kTM; ++i) {
     const int row = m0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + (i - 4));
     if (row >= p.M) continue;
     float *crow = p.C + (size_t)row * (size_t)p.ldc;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 4; ++h) {
       const int col = n0 + h * 64 + 4 * tx;
       if (VC && col + 3 < p.N) {
         floatx4 *c4 = reinterpret_cast<floatx4 *>(crow + col);
@@ -194,7 +225,7 @@ static void launch_valu_t(const Problem &p, dim3 grid, hipStream_t stream, int t
   }
 }
 
-int launch_valu_128x128(const Problem &p, hipStream_t stream) {
+int launch_valu_128x256(const Problem &p, hipStream_t stream) {
   const long long tiles_m = ((long long)p.M + kBM - 1) / kBM;
   const long long tiles_n = ((long long)p.N + kBN - 1) / kBN;
   if (tiles_m * tiles_n > (long long)INT_MAX) return -1;
