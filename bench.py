@@ -659,6 +659,10 @@ def main(argv=None):
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "RUN_LOG"),
                     help="print a markdown table of kernel-only times from a rocprofv3 kernel "
                          "trace and the JSON lines of the run it traced (no GPU needed)")
+    ap.add_argument("--choice-table", action="store_true",
+                    help="every scored tile family on each tile-choice shape (device time)")
+    ap.add_argument("--choice-table-md", metavar="RUN_LOG",
+                    help="format the JSON lines of a --choice-table run as a markdown table")
     ap.add_argument("--counter-summary", nargs=2, metavar=("COUNTER_CSV", "RUN_LOG"),
                     help="per-job mean counters from a rocprofv3 counter_collection.csv and the "
                          "JSON lines of the run it profiled (no GPU needed)")
@@ -670,6 +674,9 @@ def main(argv=None):
     if args.counter_summary:
         for rec in counter_summary(*args.counter_summary):
             print(json.dumps(rec))
+        return 0
+    if args.choice_table_md:
+        sys.stdout.write(choice_table_md(args.choice_table_md))
         return 0
 
     if args.traffic_from:
@@ -699,6 +706,8 @@ def main(argv=None):
 
     if args.few_rows:
         return few_rows(args)
+    if args.choice_table:
+        return choice_table(args)
     if (args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib
             or args.shapes_from):
         return run_modes(args)
@@ -922,6 +931,99 @@ def run_modes(args):
         del prob
         _torch().cuda.empty_cache()
     return 0
+
+
+# The tile families the automatic choice scores, with their tile sizes and
+# whether they also run fewer rows than the tile (A untransposed); the tail
+# forms need the workspace entry point.
+CHOICE_FAMILIES = (
+    ("256x256", "mfma32_256x256x32_2x2_sched", 256, 256, False),
+    ("128x128 w4", "mfma16_128x128x32_2x2_sched", 128, 128, False),
+    ("128x128 w8", "mfma16_128x128x64_4x2_sched", 128, 128, False),
+    ("128x64", "mfma16_128x64x64_4x2_sched", 128, 64, False),
+    ("64x64", "mfma16_64x64x64_4x2_sched", 64, 64, False),
+    ("64x64 split-K", "mfma16_64x64x64_4x2_sched_splitk", 64, 64, False),
+    ("32x64", "mfma16_32x64x64_2x2_sched", 32, 64, True),
+    ("32x64 split-K", "mfma16_32x64x64_2x2_sched_splitk", 32, 64, True),
+    ("128x128 w4 tail", "mfma16_128x128x32_2x2_sched_tail", 128, 128, False),
+    ("128x128 w8 tail", "mfma16_128x128x64_4x2_sched_tail", 128, 128, False),
+    ("128x64 tail", "mfma16_128x64x64_4x2_sched_tail", 128, 64, False),
+    ("64x64 tail", "mfma16_64x64x64_4x2_sched_tail", 64, 64, False),
+)
+
+
+def choice_table(args):
+    """Every scored tile family (device time, graph replays) on each shape of
+    workloads.TILE_CHOICE_SHAPES, with the automatic choices of the plain and
+    the workspace entry points: one JSON line per shape."""
+    import dense_fp32_gemm_sgemm_amd as sg
+    from workloads import TILE_CHOICE_SHAPES
+    torch = _torch()
+    names = sg.variant_names()
+    for M, N, K, ops in TILE_CHOICE_SHAPES:
+        prob = Problem(M, N, K, ops=ops, ws=True)
+        rec = {"mode": "choice", "M": M, "N": N, "K": K, "ops": ops, "tflops": {}}
+        for label, vname, bm, bn, short_m in CHOICE_FAMILIES:
+            if not ((M >= bm or (short_m and ops[0] == "N")) and N >= bn):
+                continue  # the family's loop does not run this shape
+            v = names.index(vname)
+            fn = prob.launcher(v)
+            fn()
+            fn()
+            _, per = time_steps(fn, 3, prob.stream)
+            ms, _ = device_ms_per_call(prob.launcher_on(v), min(per), replays=10)
+            rec["tflops"][label] = round(flops(M, N, K) / (ms * 1e-3) / 1e12, 2)
+        rec["auto_ws"] = prob.variant_name(-1)
+        prob.ws = None
+        rec["auto"] = prob.variant_name(-1)
+        print(json.dumps(rec), flush=True)
+        del prob
+        torch.cuda.empty_cache()
+    return 0
+
+
+def _current_choices(M, N, K, ops):
+    """(plain, workspace) automatic choices of the built library for a shape
+    (host-only queries; no GPU needed)."""
+    import dense_fp32_gemm_sgemm_amd as sg
+    ta, tb = int(ops[0] == "T"), int(ops[1] == "T")
+    lda, ldb, f = (M if ta else K), (K if tb else N), 256
+    v = sg.sgemm_strided_batched_select_variant(ta, tb, M, N, K, 1.0, f, lda, 0, f, ldb, 0, 0.0, f, N,
+                                                0, 1)
+    w = sg.sgemm_strided_batched_ws_select_variant(ta, tb, M, N, K, 1.0, f, lda, 0, f, ldb, 0, 0.0, f,
+                                                   N, 0, 1, WS_BYTES)
+    return sg.sgemm_variant_name(v), sg.sgemm_variant_name(w)
+
+
+def choice_table_md(log_path: str) -> str:
+    """The --choice-table JSON lines as a markdown table (best family bold);
+    the two choice columns are those of the library as built now."""
+    labels = [f[0] for f in CHOICE_FAMILIES]
+    short = {f[1]: f[0] for f in CHOICE_FAMILIES}
+    out = ["| M x N x K | ops | " + " | ".join(labels) + " | auto | auto with workspace |",
+           "|---|---|" + "---|" * len(labels) + "---|---|"]
+    with open(log_path) as f:
+        for line in f:
+            if not line.startswith("{"):
+                continue
+            r = json.loads(line)
+            if r.get("mode") != "choice":
+                continue
+            t = r["tflops"]
+            best = max(t.values()) if t else None
+            cells = []
+            for lab in labels:
+                if lab not in t:
+                    cells.append("-")
+                elif t[lab] == best:
+                    cells.append("**%.1f**" % t[lab])
+                else:
+                    cells.append("%.1f" % t[lab])
+            auto, auto_ws = _current_choices(r["M"], r["N"], r["K"], r["ops"])
+            out.append("| %dx%dx%d | %s | %s | %s | %s |" % (
+                r["M"], r["N"], r["K"], r["ops"], " | ".join(cells), short.get(auto, auto),
+                short.get(auto_ws, auto_ws)))
+    return "\n".join(out) + "\n"
 
 
 def trace_summary(trace_csv: str, log_path: str, title: str = "") -> str:

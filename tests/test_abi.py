@@ -428,10 +428,13 @@ def test_atomics_not_allowed_selection(lib):
 
 def test_tile_choice_against_measured_rates(lib):
     """Every shape of the committed tile-family measurements
-    (profiles/tile_choice_mi355x.md, every family timed on an MI355X): the
-    automatic choice is a measured family within 5% of the fastest family.
-    (The split form does not split once the tiles fill 512 slots, so a 5%
-    spread between it and its unsplit twin there is run-to-run noise.)"""
+    (profiles/tile_choice_mi355x.md: every family timed on an MI355X as
+    device time per call): the automatic choice of sgemm() is a measured
+    family within 5% of the fastest family it may take (no split tail),
+    and the choice with a workspace within 5% of the fastest of all --
+    on every shape but at most two, which stay within 10%; the geometric
+    mean of both is at least 0.98 of the fastest."""
+    import math
     import os
     path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
                         "tile_choice_mi355x.md")
@@ -440,8 +443,12 @@ def test_tile_choice_against_measured_rates(lib):
     fam = {"256x256": "mfma32_256x256x32_2x2_sched", "128x128 w4": "mfma16_128x128x32_2x2_sched",
            "128x128 w8": "mfma16_128x128x64_4x2_sched", "128x64": "mfma16_128x64x64_4x2_sched",
            "64x64": "mfma16_64x64x64_4x2_sched", "64x64 split-K": "mfma16_64x64x64_4x2_sched_splitk",
-           "32x64": "mfma16_32x64x64_2x2_sched", "32x64 split-K": "mfma16_32x64x64_2x2_sched_splitk"}
-    checked = 0
+           "32x64": "mfma16_32x64x64_2x2_sched", "32x64 split-K": "mfma16_32x64x64_2x2_sched_splitk",
+           "128x128 w4 tail": "mfma16_128x128x32_2x2_sched_tail",
+           "128x128 w8 tail": "mfma16_128x128x64_4x2_sched_tail",
+           "128x64 tail": "mfma16_128x64x64_4x2_sched_tail", "64x64 tail": "mfma16_64x64x64_4x2_sched_tail"}
+    ws_bytes = 4096 + (32 << 20)
+    fracs, fracs_ws = [], []
     for line in lines:
         cells = [c.strip() for c in line.split("|")[1:-1]]
         if not cells or not cells[0][:1].isdigit():
@@ -449,11 +456,19 @@ def test_tile_choice_against_measured_rates(lib):
         M, N, K = (int(x) for x in cells[0].split("x"))
         ta, tb = (1 if cells[1][0] == "T" else 0), (1 if cells[1][1] == "T" else 0)
         rates = {fam[h]: float(v.replace("*", "")) for h, v in zip(head, cells) if h in fam and v != "-"}
+        plain = {k: v for k, v in rates.items() if not k.endswith("_tail")}
         name = _op_choice(ta, tb, M, N, K)
-        assert name in rates, (cells[0], cells[1], name)
-        assert rates[name] >= 0.95 * max(rates.values()), (cells[0], cells[1], name, rates)
-        checked += 1
-    assert checked >= 40
+        assert name in plain, (cells[0], cells[1], name)
+        fracs.append(plain[name] / max(plain.values()))
+        v = sg.sgemm_strided_batched_ws_select_variant(ta, tb, M, N, K, 1.0, FAKE, M if ta else K, 0, FAKE,
+                                                       K if tb else N, 0, 0.0, FAKE, N, 0, 1, ws_bytes)
+        wname = sg.sgemm_variant_name(v)
+        assert wname in rates, (cells[0], cells[1], wname)
+        fracs_ws.append(rates[wname] / max(rates.values()))
+    assert len(fracs) >= 80
+    for f in (fracs, fracs_ws):
+        assert min(f) >= 0.90 and sum(1 for x in f if x < 0.95) <= 2, sorted(f)[:4]
+        assert math.exp(sum(math.log(x) for x in f) / len(f)) >= 0.98
 
 
 def test_few_tiles_with_long_k_always_split(lib):

@@ -32,6 +32,44 @@ RAGGED_SHAPES = ((4095, 4097, 1023), (8192, 1024, 8192), (1024, 8192, 256),
 SHARD_SHAPES = ((512, 4096, 4096), (2048, 1024, 4096))
 
 
+# Shapes (M, N, K, op(A)op(B)) on which every scored tile family is timed to
+# fit and check the automatic tile choice: tile counts just past whole
+# rounds, M just past a multiple of 64, few rows with a long K, mid-size
+# squares, one GPU's share of a split 4096^3, and a last round left partial.
+TILE_CHOICE_SHAPES = (
+    (4095, 4097, 1023, "NN"), (4096, 4096, 1023, "NN"), (4096, 4097, 1024, "NN"),
+    (4095, 4097, 4095, "NN"), (2047, 2049, 2047, "NN"), (8191, 1025, 8191, "NN"),
+    (4096, 4096, 1024, "NN"), (1023, 8193, 257, "NN"), (2047, 4097, 4095, "NN"),
+    (3000, 3000, 3000, "NN"), (3072, 3072, 3072, "NN"), (6144, 1024, 4096, "NN"),
+    (2048, 2048, 512, "NN"), (10000, 10000, 1000, "NN"), (5000, 5000, 5000, "NN"),
+    (3584, 3584, 3584, "NN"), (2560, 2560, 2560, "NN"), (1536, 1536, 1536, "NN"),
+    (96, 16384, 4096, "NN"), (256, 16384, 4096, "NN"), (448, 4096, 8192, "NN"),
+    (192, 16384, 4096, "NN"), (4095, 4097, 1023, "NT"), (4095, 4097, 1023, "TN"),
+    (4095, 4097, 1023, "TT"), (96, 8192, 8192, "NN"), (96, 4096, 4096, "NN"),
+    (96, 2048, 8192, "NN"), (192, 8192, 8192, "NN"), (320, 8192, 8192, "NN"),
+    (320, 4096, 4096, "NN"), (384, 4096, 4096, "NN"), (1024, 1536, 8192, "NN"),
+    (1536, 1024, 4096, "NN"), (512, 512, 512, "NN"), (1024, 1024, 1024, "NN"),
+    (256, 4096, 4096, "NN"), (160, 4096, 4096, "NN"), (352, 8192, 8192, "NN"),
+    (48, 16384, 4096, "NN"), (128, 8192, 8192, "NN"), (4096, 4096, 4096, "NN"),
+    (768, 768, 768, "NN"), (1000, 1000, 1000, "NN"), (48, 8192, 8192, "NN"),
+    (48, 4096, 4096, "NN"), (40, 16384, 4096, "NN"), (56, 8192, 8192, "NN"),
+    (33, 8192, 8192, "NN"), (64, 8192, 8192, "NN"), (48, 4096, 16384, "NN"),
+    (64, 4096, 4096, "NN"), (40, 4096, 4096, "NN"), (48, 2048, 8192, "NN"),
+    (64, 2048, 8192, "NN"), (36, 1024, 8192, "NN"), (64, 4096, 16384, "NN"),
+    (48, 1024, 4096, "NN"), (64, 1024, 4096, "NN"), (200, 300, 2048, "NN"),
+    (96, 700, 2048, "NN"), (64, 700, 2048, "NN"), (200, 700, 2048, "NN"),
+    (300, 1000, 1024, "NN"), (128, 1024, 1024, "NN"), (256, 512, 1024, "NN"),
+    (128, 2048, 1024, "NN"), (512, 256, 1024, "NN"), (200, 1500, 1024, "NN"),
+    (128, 1024, 1536, "NN"), (300, 1000, 1536, "NN"), (1500, 3000, 2000, "NN"),
+    (700, 5000, 3000, "NN"), (3000, 700, 5000, "NN"), (2500, 2500, 1500, "NN"),
+    (6000, 3000, 1000, "NN"), (1200, 1200, 8000, "NN"), (800, 9000, 2000, "NN"),
+    (5000, 1500, 3000, "NN"), (384, 6000, 6000, "NN"), (2200, 4400, 700, "NN"),
+    (512, 4096, 4096, "NN"), (2048, 1024, 4096, "NN"), (2048, 2048, 2048, "NN"),
+    (8192, 1024, 8192, "NN"), (1024, 8192, 256, "NN"), (2944, 2944, 1000, "NN"),
+    (4097, 4097, 4097, "NN"), (6000, 6000, 2000, "NN"),
+)
+
+
 @dataclass(frozen=True)
 class Workload:
     """One GEMM problem: shape, scalars, value kind and seed."""
