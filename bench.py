@@ -610,6 +610,30 @@ def time_call(prob: Problem, variant: int, steps: int, warmup: int, job: int, co
     return rec
 
 
+def read_floor(nbytes: float, cold: bool = True, grids=(2, 4, 8, 16)):
+    """The read-only stream kernel over `nbytes` (rounded up to 16 bytes):
+    device microseconds per launch, best over the grids (workgroups per CU)
+    -- warm (one buffer, re-read) or cold (rotated over copies that together
+    exceed 1.5 GiB, as the cold GEMM timings are).  The attainable HBM time
+    for a call that must stream that many bytes once."""
+    torch = _torch()
+    import dense_fp32_gemm_sgemm_amd as sg
+    n = int(-(-nbytes // 16)) * 4                      # floats, a multiple of 4
+    copies = int(min(256, -(-1.5 * 2 ** 30 // (4 * n)))) if cold else 1
+    buf = torch.ones(n * copies, dtype=torch.float32, device="cuda")
+    sink = torch.empty(NUM_CUS * 16 * 256, dtype=torch.float32, device="cuda")
+    best = None
+    for per_cu in grids:
+        def fn(h, i, per_cu=per_cu):
+            assert sg.sgemm_ceiling_read(buf.data_ptr() + 4 * n * (i % copies), n, NUM_CUS * per_cu,
+                                         sink.data_ptr(), h) == 0
+        ms, _ = device_ms_per_call(fn, 4 * n / 5e12 * 1e3, copies=copies)
+        best = ms if best is None else min(best, ms)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best * 1e3
+
+
 def bench_problem(prob: Problem, steps: int, warmup: int, variant=-1):
     fn = prob.launcher(variant)
     for _ in range(warmup):
@@ -650,6 +674,11 @@ def main(argv=None):
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--ws", action="store_true",
                     help="non-contract modes: call the workspace entry point (4 KiB + 32 MiB workspace)")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="with --cold: also time the read-only stream kernel over each "
+                         "problem's algorithmic bytes, cold (the attainable HBM time at that size)")
+    ap.add_argument("--read-ladder", action="store_true",
+                    help="time the read-only stream kernel warm and cold over 4 MiB .. 1 GiB")
     ap.add_argument("--cold", action="store_true",
                     help="non-contract modes: also time on rotated operand copies past the 256 MB cache")
     ap.add_argument("--shapes-from", metavar="FILE",
@@ -706,6 +735,14 @@ def main(argv=None):
 
     if args.few_rows:
         return few_rows(args)
+    if args.read_ladder:
+        for mib in (4, 16, 64, 256, 1024):
+            nb = mib * 2 ** 20
+            warm, cold = read_floor(nb, cold=False), read_floor(nb, cold=True)
+            print(json.dumps({"mode": "read_ladder", "mib": mib, "us_warm": round(warm, 3),
+                              "us_cold": round(cold, 3), "gbs_warm": round(nb / warm / 1e3, 1),
+                              "gbs_cold": round(nb / cold / 1e3, 1)}), flush=True)
+        return 0
     if args.choice_table:
         return choice_table(args)
     if (args.sweep or args.variants or args.shape or args.profile or args.matrix or args.copy_calib
@@ -919,6 +956,11 @@ def run_modes(args):
                "hbm_gbs_device": round(nb / (us * 1e-6) / 1e9, 1)}
         if "us_cold" in t:
             rec["hbm_gbs_cold"] = round(nb / (t["us_cold"] * 1e-6) / 1e9, 1)
+            if args.read_floor:
+                # the read-only stream over the same bytes, cold: what any
+                # kernel that reads them once can reach at this size
+                rec["us_read_cold"] = round(read_floor(nb, cold=True), 3)
+                rec["frac_of_read_cold"] = round(rec["us_read_cold"] / t["us_cold"], 4)
         # judged on the cold time where the bytes bind, else the warm one
         roof = binding_roof(work, nb, us, ceil)
         if roof["bound"] == "hbm" and "us_cold" in t:

@@ -33,6 +33,20 @@ int launch_skinny_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// The same for the fixed-order split few-rows form (which falls back to the
+// few-rows kernel without a workspace).
+int launch_skinny_fixed_any(const Problem &p, hipStream_t s) {
+  for (int r = 0; r < p.M; r += 8) {
+    Problem q = p;
+    q.M = (p.M - r < 8) ? p.M - r : 8;
+    q.A = p.ta ? p.A + r : p.A + (size_t)r * (size_t)p.lda;
+    q.C = p.C + (size_t)r * (size_t)p.ldc;
+    const int rc = launch_skinny_fixed(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 // The few-columns kernel covers N <= 16; as a forced variant on a wider
 // problem it runs on column blocks of 16.
 int launch_narrow_any(const Problem &p, hipStream_t s) {
@@ -103,6 +117,7 @@ const Variant kVariants[] = {
     {"mfma16_128x128x64_4x2_sched_tail", launch_mfma16_128x128x64_4x2_sched_tail},
     {"mfma16_128x64x64_4x2_sched_tail", launch_mfma16_128x64x64_4x2_sched_tail},
     {"mfma16_64x64x64_4x2_sched_tail", launch_mfma16_64x64x64_4x2_sched_tail},
+    {"skinny_fixed_m8", launch_skinny_fixed_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -142,6 +157,7 @@ enum VariantId {
   kMfma16_128x128x64_w8_sched_tail = 32,
   kMfma16_128x64x64_w8_sched_tail = 33,
   kMfma16_64x64x64_w8_sched_tail = 34,
+  kSkinnyFixed = 35,
 };
 
 constexpr int kNoKernel = -100;
@@ -405,11 +421,30 @@ int choose_variant(const Problem &p, bool atomics) {
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
+    // With a workspace that holds it: the fixed-order split few-rows form
+    // where K is long for the columns (at least 2N, and N*K from 2^21 at one
+    // or two rows, 2^22 up to four, 2^23 up to eight with K <= 16384), or
+    // the columns very many and K short -- measured cold (operands rotated
+    // past the last-level cache): (1, 2048, 16384) 33 against 63 us,
+    // (1, 1024, 4096) 9.9 against 16, (8, 4096, 16384) 62 against 75,
+    // (1, 65536, 2048) 86.5 against 103.
+    if (valu_ok && batch == 1 && p.ws != nullptr) {
+      const long long need = skinny_fixed_bytes(p);
+      const long long min_nk = p.M <= 2 ? (1LL << 21) : (p.M <= 4 ? (1LL << 22) : (1LL << 23));
+      const bool long_k = p.K >= 2LL * p.N && nk >= min_nk && (p.M <= 4 || p.K <= 16384);
+      if (need > 0 && (unsigned long long)need <= p.ws_bytes && (long_k || (p.N >= 32768 && p.K <= 2048)))
+        return kSkinnyFixed;
+    }
     if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&
         (p.M <= 2 || p.N >= 4096))
       return kSkinny;
     const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
                               : nb >= (p.M <= 16 ? 1024 : 2048);
+    // (a K of 16N or more leaves the few-rows matrix-core kernel too few
+    // column strips for its long K: the split form of the vector-unit kernel
+    // instead, (1, 1024, 65536) 72 against 222 us cold, (8, 1024, 16384) 52
+    // against 67)
+    if (fewrows && valu_ok && atomics && batch == 1 && p.K >= 16LL * p.N) return kSkinny;
     if (fewrows) return kFewRows;
     if (valu_ok && (atomics || skinny_full_k(p))) return kSkinny;
   }
@@ -585,6 +620,7 @@ long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
                   opA == SGEMM_OP_T, opB == SGEMM_OP_T, 0, 0, 0, 1,
                   reinterpret_cast<void *>(256), (unsigned long long)kTailWorkspaceBytes};
   const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
+  if (v == kSkinnyFixed) return skinny_fixed_bytes(p);
   for (const TailFamily &tf : kTailFamilies)
     if (tf.variant == v) return family_tail_plan(tf, p).bytes;
   return 0;

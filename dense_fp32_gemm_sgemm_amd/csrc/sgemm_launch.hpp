@@ -73,6 +73,16 @@ int launch_mfma16_64x64x64_4x2_sched_tail(const Problem &p, hipStream_t stream);
 // M > 8.
 int launch_skinny(const Problem &p, hipStream_t stream);
 
+// Few rows of C (M <= 8), one batch slice, B untransposed, with a workspace:
+// B streamed in 1 KiB row segments by (column strip, K chunk) workgroups, the
+// chunks' partial strips added in a fixed order by the strip's last chunk
+// (one launch, no atomics on C).  Without a workspace that holds
+// skinny_fixed_bytes(p), or where the form does not apply, launch_skinny.
+// Returns -1 for M > 8.
+int launch_skinny_fixed(const Problem &p, hipStream_t stream);
+// Workspace bytes that form needs for p (0: the form does not apply).
+long long skinny_fixed_bytes(const Problem &p);
+
 // Few columns of C (N <= 16): streams A, the matrix cores accumulate 16 x 16
 // blocks, K split over the waves of a workgroup, one launch.  Returns -1 for
 // N > 16.

@@ -4,7 +4,7 @@
 // With M <= 8 a GEMM does 2*M FLOP per element of B it reads, below the
 // MI355X ridge point (about 20 FLOP/byte): the whole of B has to stream from
 // HBM once, and the kernel's job is to keep enough loads in flight on every
-// CU.  Two kernels:
+// CU.  Three forms:
 //
 //   * full-K strips (moderate B): a workgroup owns 32 columns of C and runs
 //     the whole K for them -- a lane loads 4 columns of 4 consecutive rows of
@@ -25,11 +25,19 @@
 //     otherwise).  A's values are the same for every lane and are read
 //     through the scalar path.
 //
+//   * fixed-order split (one batch slice, with a caller's workspace): the
+//     split-K grid without the atomics -- each K chunk's partial strip goes
+//     to the workspace and the strip's last chunk adds them in chunk order
+//     and writes C once.  One launch, deterministic; taken where K is long
+//     for the columns (the full-K strips then leave CUs idle) or the columns
+//     are very many.
+//
 // The second launch of the split form costs about 4 us on an MI355X, a fifth
 // of a (1, 4096, 4096) product; the full-K form avoids it whenever the column
 // strips alone give enough workgroups.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
+#include "sgemm_sched.hpp"
 
 #include <climits>
 
@@ -241,6 +249,193 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
       store_out(p.C + (size_t)r * (size_t)p.ldc + c, s, p.alpha, p.beta);
     }
   }
+}
+
+// Fixed-order split form (one batch slice, B untransposed, a workspace).
+// The grid is (column strips of 256, K chunks): each workgroup streams a
+// chunk of rows of B as 1 KiB row segments (lane l: columns 4l..4l+3 of the
+// strip, its wave: every fourth row of the chunk, eight rows in flight), so
+// HBM sees long runs of each row instead of 128-byte pieces at a 4*N-byte
+// stride.  The four waves' sums meet in LDS in a fixed order; the chunk's
+// partial strip goes to the workspace as agent-scope stores (coherent across
+// the XCDs), the chunk counts itself in with a device-scope atomic, and the
+// chunk that counts last adds the strip's partials in chunk order and writes
+// C = alpha*sum + beta*C.  One launch, no atomics on C, bitwise repeatable.
+constexpr int kFixedUnroll = 8;  // rows of B in flight per wave
+
+template <int MR, bool VB>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_fixed_kernel(Problem p, int kchunk,
+                                                                        unsigned *flags, float *part) {
+  __shared__ float red[kSkinnyWaves][MR][kSkinnyCols];
+  __shared__ int last_chunk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int strip = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
+  const int c0 = strip * kSkinnyCols + 4 * lane;
+  const int kb = chunk * kchunk;
+  const int ke = min(p.K, kb + kchunk);
+  // Columns past N read the last column (VB, N a multiple of 4: the last
+  // quad) -- in bounds, never stored -- so the loads carry no branch.
+  const int cv = min(c0, p.N - 4);
+  int cc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cc[e] = min(c0 + e, p.N - 1);
+  const size_t ldb = (size_t)p.ldb;
+  const size_t sa_r = p.ta ? 1 : (size_t)p.lda, sa_k = p.ta ? (size_t)p.lda : 1;
+  auto load_b = [&](int k) -> floatx4 {
+    const float *brow = p.B + (size_t)k * ldb;
+    if constexpr (VB) {
+      return *reinterpret_cast<const floatx4 *>(brow + cv);
+    } else {
+      return floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
+    }
+  };
+  // rows of A past M read row M - 1 (their sums are never stored)
+  auto load_a = [&](int r, int k) -> float { return p.A[(size_t)min(r, p.M - 1) * sa_r + (size_t)k * sa_k]; };
+
+  float acc[MR][4];
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
+  // wave w takes rows kb + w, kb + w + 4, ...
+  int k = kb + w;
+  for (; k + kSkinnyWaves * (kFixedUnroll - 1) < ke; k += kSkinnyWaves * kFixedUnroll) {
+    floatx4 b[kFixedUnroll];
+    float a[kFixedUnroll][MR];
+#pragma unroll
+    for (int u = 0; u < kFixedUnroll; ++u) {
+      b[u] = load_b(k + kSkinnyWaves * u);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) a[u][r] = load_a(r, k + kSkinnyWaves * u);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch issued before the first use
+#pragma unroll
+    for (int u = 0; u < kFixedUnroll; ++u)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a[u][r], b[u][e], acc[r][e]);
+  }
+  for (; k < ke; k += kSkinnyWaves) {
+    const floatx4 b = load_b(k);
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const float a = load_a(r, k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(a, b[e], acc[r][e]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[w][r][4 * lane + e] = acc[r][e];
+  __syncthreads();
+  // thread t: column t of the strip, the waves' sums in order
+  const size_t strip_part = (size_t)nchunks * MR * kSkinnyCols;
+  float *mine = part + (size_t)strip * strip_part + (size_t)chunk * MR * kSkinnyCols + tid;
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    float s = red[0][r][tid];
+#pragma unroll
+    for (int q = 1; q < kSkinnyWaves; ++q) s += red[q][r][tid];
+    __hip_atomic_store(mine + r * kSkinnyCols, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every memory operation of this wave complete
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned before = __hip_atomic_fetch_add(flags + strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_chunk = (before + 1u == (unsigned)nchunks);
+  }
+  __syncthreads();
+  if (!last_chunk) return;
+  // The strip's last chunk: partials added in chunk order, eight chunks'
+  // loads in flight at a time.
+  const int col = strip * kSkinnyCols + tid;
+  const float *pcol = part + (size_t)strip * strip_part + tid;
+  float sum[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) sum[r] = 0.0f;
+  for (int c = 0; c < nchunks; c += 8) {
+    float v[8][MR];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+        v[u][r] = (c + u < nchunks) ? __hip_atomic_load(pcol + (size_t)(c + u) * MR * kSkinnyCols + r * kSkinnyCols,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < MR; ++r)
+        if (c + u < nchunks) sum[r] = (c + u == 0) ? v[u][r] : sum[r] + v[u][r];
+  }
+  if (tid == 0) __hip_atomic_store(flags + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (col < p.N) {
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+      if (r < p.M) store_out(p.C + (size_t)r * (size_t)p.ldc + col, sum[r], p.alpha, p.beta);
+  }
+}
+
+// Chunks of the fixed-order split form: about two workgroups per CU, each
+// chunk a multiple of 32 rows (the waves' batches) and at least 128.
+static int skinny_fixed_kchunk(const Problem &p, long long strips) {
+  long long chunks = 512 / (strips > 0 ? strips : 1);
+  if (chunks < 1) chunks = 1;
+  long long kc = ((long long)p.K + chunks - 1) / chunks;
+  if (kc < 128) kc = 128;
+  kc = (kc + 31) / 32 * 32;
+  return (int)kc;
+}
+
+// Workspace bytes of the fixed-order split form for this problem (counters
+// first, then the partial strips), or 0 when the form does not apply.
+long long skinny_fixed_bytes(const Problem &p) {
+  if (p.M < 1 || p.M > 8 || p.tb || p.batch != 1) return 0;
+  const long long strips = ((long long)p.N + kSkinnyCols - 1) / kSkinnyCols;
+  if (strips > kTailMaxTiles) return 0;
+  const int kc = skinny_fixed_kchunk(p, strips);
+  const long long chunks = ((long long)p.K + kc - 1) / kc;
+  const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
+  const long long bytes = kTailFlagBytes + strips * chunks * mr * kSkinnyCols * 4;
+  return bytes <= kTailWorkspaceBytes ? bytes : 0;
+}
+
+// The fixed-order split form when it applies and the workspace holds it,
+// otherwise the other few-rows forms (M <= 8).
+int launch_skinny_fixed(const Problem &p, hipStream_t stream) {
+  if (p.M > 8) return -1;
+  const long long need = skinny_fixed_bytes(p);
+  if (need == 0 || p.ws == nullptr || (unsigned long long)need > p.ws_bytes) return launch_skinny(p, stream);
+  const long long strips = ((long long)p.N + kSkinnyCols - 1) / kSkinnyCols;
+  const int kc = skinny_fixed_kchunk(p, strips);
+  const long long chunks = ((long long)p.K + kc - 1) / kc;
+  const dim3 grid((unsigned)strips, (unsigned)chunks, 1u);
+  const dim3 block(kSkinnyWaves * 64);
+  unsigned *flags = reinterpret_cast<unsigned *>(p.ws);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
+  const bool vb = b_vec_ok(p);
+#define SG950_FIXED(MR_)                                                                                  \
+  do {                                                                                                    \
+    if (vb)                                                                                               \
+      SG950_LAUNCH((skinny_fixed_kernel<MR_, true>), grid, block, 0, stream, p, kc, flags, part);  \
+    else                                                                                                  \
+      SG950_LAUNCH((skinny_fixed_kernel<MR_, false>), grid, block, 0, stream, p, kc, flags, part); \
+  } while (0)
+  if (p.M <= 1) {
+    SG950_FIXED(1);
+  } else if (p.M <= 2) {
+    SG950_FIXED(2);
+  } else if (p.M <= 4) {
+    SG950_FIXED(4);
+  } else {
+    SG950_FIXED(8);
+  }
+#undef SG950_FIXED
+  return 0;
 }
 
 // K rows per workgroup: enough workgroups (over all batch slices) for about

@@ -175,6 +175,11 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
  * finishes a tile's ranges last adds them in range order and writes the
  * tile of C.  The pages name splitting K as the way to fill the GPU when the
  * output tiles cannot ("The road to a fast GEMM", "Where to go next").
+ * Problems with at most 8 rows of an untransposed B (matrix-vector-like,
+ * bound by streaming B) use the workspace the same way where K is long for
+ * the columns or the columns very many: B is split into (256-column strip,
+ * K chunk) workgroups whose partial strips the strip's last chunk adds in
+ * chunk order.
  *
  * Results are bitwise repeatable (each output is one sum in a fixed order; no
  * atomics touch C), in either atomics mode.  The automatic choice takes the
