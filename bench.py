@@ -813,7 +813,7 @@ def main(argv=None):
 
 FEW_ROWS_M = (1, 4, 8, 12, 16, 20, 24, 32)
 FEW_ROWS_NK = ((4096, 4096), (8192, 8192), (16384, 16384), (1024, 4096), (2048, 2048),
-               (4096, 1024), (4096, 16384), (65536, 1024))
+               (4096, 1024), (4096, 16384), (65536, 1024), (1024, 16384))
 
 
 def few_rows(args):
@@ -844,6 +844,19 @@ def few_rows(args):
                     rec["reps_" + key] = t["graph_reps"]
                     if "us_cold" in t:
                         rec["us_cold_auto"] = t["us_cold"]
+                if args.ws:
+                    # the workspace entry point's automatic choice (timed only
+                    # where it differs from the plain one)
+                    pw = Problem(M, N, K, ops=ops, ws=True)
+                    rec["auto_ws"] = pw.variant_name(-1)
+                    if rec["auto_ws"] != rec["auto"]:
+                        t = time_call(pw, -1, args.steps, min(args.warmup, args.steps), job, cold=args.cold)
+                        rec["jobs"]["auto_ws"] = job
+                        job += 1
+                        rec["us_device_auto_ws"] = t["us_device"]
+                        if "us_cold" in t:
+                            rec["us_cold_auto_ws"] = t["us_cold"]
+                    del pw
                 nb = min_bytes(M, N, K)
                 rec["auto_gbs_device"] = round(nb / (rec["us_device_auto"] * 1e-6) / 1e9, 1)
                 if "us_cold_auto" in rec:
