@@ -44,6 +44,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -674,6 +675,15 @@ def main(argv=None):
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--ws", action="store_true",
                     help="non-contract modes: call the workspace entry point (4 KiB + 32 MiB workspace)")
+    ap.add_argument("--counters-md", nargs="+", metavar="JSON",
+                    help="format --counter-summary outputs of several passes as one markdown table")
+    ap.add_argument("--times", nargs="+", metavar="JSONL",
+                    help="with --counters-md: timing runs (--sweep / --shapes-from) giving device times")
+    ap.add_argument("--sweep-md", nargs="+", metavar="JSONL",
+                    help="format a --sweep run (and optionally its --ws run) as a markdown table")
+    ap.add_argument("--few-rows-md", metavar="JSONL", help="format a --few-rows run as a markdown table")
+    ap.add_argument("--variants-md", nargs="+", metavar="JSONL",
+                    help="format --variants / --matrix / --shape runs as a shape x variant table")
     ap.add_argument("--read-floor", action="store_true",
                     help="with --cold: also time the read-only stream kernel over each "
                          "problem's algorithmic bytes, cold (the attainable HBM time at that size)")
@@ -703,6 +713,18 @@ def main(argv=None):
     if args.counter_summary:
         for rec in counter_summary(*args.counter_summary):
             print(json.dumps(rec))
+        return 0
+    if args.counters_md:
+        sys.stdout.write(counters_md(args.counters_md, args.times))
+        return 0
+    if args.sweep_md:
+        sys.stdout.write(sweep_md(*args.sweep_md))
+        return 0
+    if args.variants_md:
+        sys.stdout.write(variants_md(args.variants_md))
+        return 0
+    if args.few_rows_md:
+        sys.stdout.write(few_rows_md(args.few_rows_md))
         return 0
     if args.choice_table_md:
         sys.stdout.write(choice_table_md(args.choice_table_md))
@@ -912,6 +934,7 @@ def run_modes(args):
             for _ in range(args.warmup):
                 fn()
             torch_ = _torch()
+            wake(0.1, fn)  # clocks up before the timed calls
             torch_.cuda.synchronize()
             _mark(args.job0 + j, 1)(prob.stream.cuda_stream)
             _, per = time_steps(fn, args.steps, prob.stream)
@@ -962,7 +985,8 @@ def run_modes(args):
         t = time_call(prob, v, steps, min(args.warmup, steps), args.job0 + j, cold=cold)
         us = t["us_device"]
         rec = {"mode": mode, "ops": args.ops, "batch": args.batch, "M": M, "N": N, "K": K,
-               "beta": args.beta, "variant": name, "workspace": bool(args.ws), "steps": steps, **t,
+               "beta": args.beta, "variant": name, "forced": v >= 0, "workspace": bool(args.ws), "steps": steps,
+               **t,
                "tflops_device": round(work / (us * 1e-6) / 1e12, 3),
                "tflops_launch": round(work / (t["us_launch"] * 1e-6) / 1e12, 3),
                "ai_flop_per_byte": round(work / nb, 2),
@@ -1078,6 +1102,168 @@ def choice_table_md(log_path: str) -> str:
             out.append("| %dx%dx%d | %s | %s | %s | %s |" % (
                 r["M"], r["N"], r["K"], r["ops"], " | ".join(cells), short.get(auto, auto),
                 short.get(auto_ws, auto_ws)))
+    return "\n".join(out) + "\n"
+
+
+def _jsonl(path: str, mode=None) -> list:
+    out = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                r = json.loads(line)
+                if mode is None or r.get("mode") == mode:
+                    out.append(r)
+    return out
+
+
+def sweep_md(sweep_path: str, ws_path: str = None) -> str:
+    """A --sweep run (with --cold, --vendor, --read-floor) as a markdown
+    table: device time per call, launch-inclusive time, cold time, the
+    binding roof and the fraction of it, the same-size cold read floor, the
+    vendor stopwatch; with ws_path the workspace entry point's run beside."""
+    ceil = (_jsonl(sweep_path, "ceilings") or [{}])[0]
+    ws = {(r["M"], r["N"], r["K"]): r for r in _jsonl(ws_path, "sweep")} if ws_path else {}
+    out = []
+    if ceil:
+        out.append("Measured ceilings of this run: MFMA 32x32x2 %.1f TFLOP/s, 16x16x4 %.1f, v_fma_f32 %.1f; "
+                   "HBM read-only stream %.0f GB/s (2 GiB), copy %.0f GB/s; dispatch floor %.2f us.\n"
+                   % (ceil["mfma_f32_32x32x2_tflops"], ceil["mfma_f32_16x16x4_tflops"],
+                      ceil["valu_fma_f32_tflops"], ceil["hbm_read_gbs"], ceil["hbm_copy_gbs"],
+                      ceil["dispatch_floor_us"]))
+    head = ("| M x N x K | variant | device us | TFLOP/s | launch us | cold us | bound | floor us | "
+            "frac of bound | frac of datasheet | read floor cold us | vendor device us | vendor / ours |")
+    if ws:
+        head += " workspace variant | ws device us | ws TFLOP/s |"
+    out += [head, "|" + "---|" * (head.count("|") - 1)]
+    for r in _jsonl(sweep_path, "sweep"):
+        key = (r["M"], r["N"], r["K"])
+        floor = r["floor_us"][r["bound"]]
+        vend = r.get("torch_mm_us_device")
+        row = "| %dx%dx%d | %s | %.2f | %.2f | %.2f | %s | %s%s | %.2f | %.3f | %.3f | %s | %s | %s |" % (
+            key + (r["variant"], r["us_device"], r["tflops_device"], r["us_launch"],
+                   "%.2f" % r["us_cold"] if "us_cold" in r else "-", r["bound"],
+                   " (cold)" if r.get("judged_on") == "us_cold" else "", floor, r["frac_of_bound"],
+                   r["frac_datasheet"], "%.2f" % r["us_read_cold"] if "us_read_cold" in r else "-",
+                   "%.2f" % vend if vend else "-",
+                   "%.2f" % (vend / r["us_device"]) if vend else "-"))
+        if ws:
+            w = ws.get(key)
+            row += (" %s | %.2f | %.2f |" % (w["variant"], w["us_device"], w["tflops_device"]) if w
+                    else " - | - | - |")
+        out.append(row)
+    return "\n".join(out) + "\n"
+
+
+def variants_md(paths) -> str:
+    """Timing records of --variants / --matrix / --shape / --sweep runs as a
+    shape x variant table of TFLOP/s (device time per call), with the
+    automatic choice (records not forced) in the last columns; the best
+    forced variant of each row in bold."""
+    rows, names = {}, []
+    for path in paths:
+        for r in _jsonl(path):
+            if "us_device" not in r or "M" not in r:
+                continue
+            key = (r.get("batch", 1), r["M"], r["N"], r["K"], r.get("ops", "NN"))
+            d = rows.setdefault(key, {"forced": {}, "auto": None})
+            if r.get("forced", True) and r.get("mode") != "sweep":
+                d["forced"][r["variant"]] = r["tflops_device"]
+                if r["variant"] not in names:
+                    names.append(r["variant"])
+            else:
+                d["auto"] = (r["variant"], r["tflops_device"])
+    out = ["| batch x M x N x K | ops | " + " | ".join(names) + " | auto | auto TFLOP/s | auto / best |",
+           "|---|---|" + "---|" * len(names) + "---|---|---|"]
+    for key in sorted(rows, key=lambda k: (k[4], k[0] * k[1] * k[2] * k[3], k)):
+        d = rows[key]
+        best = max(d["forced"].values()) if d["forced"] else None
+        cells = []
+        for n in names:
+            v = d["forced"].get(n)
+            cells.append("-" if v is None else ("**%.2f**" % v if v == best else "%.2f" % v))
+        a = d["auto"]
+        out.append("| %s%dx%dx%d | %s | %s | %s | %s | %s |" % (
+            "%d x " % key[0] if key[0] != 1 else "", key[1], key[2], key[3], key[4], " | ".join(cells),
+            a[0] if a else "-", "%.2f" % a[1] if a else "-",
+            "%.3f" % (a[1] / best) if a and best else "-"))
+    return "\n".join(out) + "\n"
+
+
+def few_rows_md(path: str) -> str:
+    """A --few-rows run as a markdown table of device times (graph replays),
+    with the cold time of the automatic choice(s) and the vendor stopwatch."""
+    out = ["| M x N x K | B | auto | auto us | auto cold us | cold GB/s | skinny_m8 | pipe_splitk | "
+           "fewrows_m32 | workspace auto | ws us | ws cold us | vendor us | vendor / best auto |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    ratios = []
+    for r in _jsonl(path, "few-rows"):
+        d = lambda k: r.get("us_device_" + k)
+        auto_ws = r.get("auto_ws", r["auto"])
+        best = min(x for x in (d("auto"), r.get("us_device_auto_ws")) if x)
+        vend = r.get("torch_mm_us_device")
+        if vend:
+            ratios.append(vend / best)
+        out.append("| %dx%dx%d | %s | %s | %.2f | %s | %s | %.2f | %.2f | %.2f | %s | %s | %s | %s | %s |" % (
+            r["M"], r["N"], r["K"], r["ops"], r["auto"], d("auto"),
+            "%.2f" % r["us_cold_auto"] if "us_cold_auto" in r else "-",
+            "%.0f" % r["auto_gbs_cold"] if "auto_gbs_cold" in r else "-",
+            d("skinny_m8"), d("mfma16_64x64x64_4x2_pipe_splitk"), d("fewrows_m32"),
+            auto_ws if auto_ws != r["auto"] else "(same)",
+            "%.2f" % r["us_device_auto_ws"] if "us_device_auto_ws" in r else "-",
+            "%.2f" % r["us_cold_auto_ws"] if "us_cold_auto_ws" in r else "-",
+            "%.2f" % vend if vend else "-", "%.2f" % (vend / best) if vend else "-"))
+    if ratios:
+        g = math.exp(sum(math.log(x) for x in ratios) / len(ratios))
+        out.append("")
+        out.append("Vendor time / best automatic choice (device time): geometric mean %.3f over %d shapes; "
+                   "%d below 0.9, %d above 1.1." % (g, len(ratios), sum(x < 0.9 for x in ratios),
+                                                   sum(x > 1.1 for x in ratios)))
+    return "\n".join(out) + "\n"
+
+
+def counters_md(paths, times_path=None, copy_fetch_scale=2.0, clock_ghz=2.38) -> str:
+    """The --counter-summary outputs of several passes over the same jobs
+    (one JSON list per pass) as one markdown table per job: matrix-core busy
+    (the deterministic busy count against the profiled dispatch's cycles,
+    and against the unprofiled device time when a --sweep / --shapes-from
+    run gives it), HBM-side bytes against the algorithmic ones, L2 hit rate,
+    LDS bank conflicts."""
+    jobs = {}
+    for path in paths:
+        with open(path) as f:
+            text = f.read().strip()
+        recs = json.loads(text) if text.startswith("[") else [json.loads(l) for l in text.splitlines() if l]
+        for r in recs:
+            d = jobs.setdefault(r["job"], {"M": r["M"], "N": r["N"], "K": r["K"], "variant": r["variant"],
+                                           "c": {}})
+            d["c"].update(r["counters"])
+    dev = {}
+    for tp in ([times_path] if isinstance(times_path, str) else (times_path or [])):
+        for r in _jsonl(tp):
+            if "us_device" in r and "M" in r:
+                dev[(r["M"], r["N"], r["K"], r.get("variant"))] = r["us_device"]
+    out = ["| M x N x K | variant | MFMA busy (profiled) | device us | MFMA busy (device time) | "
+           "fetch MB | reads MB (A+B) | fetch / reads | write MB | C MB | L2 hit | LDS conflict cycles |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for job in sorted(jobs):
+        d = jobs[job]
+        M, N, K, c = d["M"], d["N"], d["K"], d["c"]
+        ideal = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4 * NUM_CUS)  # cycles per SIMD
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / 8                            # per XCD
+        us = dev.get((M, N, K, d["variant"]))
+        fetch = c.get("FETCH_SIZE", 0.0) * 1024 * copy_fetch_scale / 1e6
+        write = c.get("WRITE_SIZE", 0.0) * 1024 / 1e6
+        reads = 4.0 * (M * K + K * N) / 1e6
+        cmb = 4.0 * M * N / 1e6
+        hit, miss = c.get("TCC_HIT_sum"), c.get("TCC_MISS_sum")
+        conf, act = c.get("SQ_LDS_BANK_CONFLICT"), c.get("SQ_LDS_IDX_ACTIVE")
+        out.append("| %dx%dx%d | %s | %s | %s | %s | %.1f | %.1f | %.2f | %.1f | %.1f | %s | %s |" % (
+            M, N, K, d["variant"], "%.1f%%" % (100 * ideal / cyc) if cyc else "-",
+            "%.2f" % us if us else "-", "%.1f%%" % (100 * ideal / (us * 1e3 * clock_ghz)) if us else "-",
+            fetch, reads, fetch / reads if reads else 0.0, write, cmb,
+            "%.1f%%" % (100 * hit / (hit + miss)) if hit is not None and miss is not None else "-",
+            "%.1f%%" % (100 * conf / act) if conf is not None and act else "-"))
     return "\n".join(out) + "\n"
 
 

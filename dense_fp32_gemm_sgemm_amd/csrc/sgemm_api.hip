@@ -421,6 +421,23 @@ int choose_variant(const Problem &p, bool atomics) {
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
+    // A K of 16N or more: too few columns for the streaming kernels' strips
+    // and a long K each; split-K 64x64 tiles spread it over the CUs
+    // ((1, 1024, 16384) 23.2 us against 36.2 on the vector-unit kernel's
+    // split form, (8, 1024, 16384) 23.9 against 45.9) -- except at four rows
+    // or fewer with K above 16384, where the fixed-order split (with a
+    // workspace: (1, 1024, 65536) 53 against 78.5 us cold) or, for 2048
+    // columns and more and K from 65536, the vector-unit kernel's split form
+    // ((1, 2048, 65536) 101 against 151) stream B better.
+    if (valu_ok && atomics && batch == 1 && p.K >= 16LL * p.N) {
+      const long long need = skinny_fixed_bytes(p);
+      const bool fixed_better = p.ws != nullptr && p.M <= 4 && p.K > 16384 && need > 0 &&
+                                (unsigned long long)need <= p.ws_bytes;
+      if (!fixed_better) {
+        if (p.M <= 4 && p.N >= 2048 && p.K >= 65536) return kSkinny;
+        return kMfma16_64x64x64_w8_pipe_splitk;
+      }
+    }
     // With a workspace that holds it: the fixed-order split few-rows form
     // where K is long for the columns (at least 2N, and N*K from 2^21 at one
     // or two rows, 2^22 up to four, 2^23 up to eight with K <= 16384), or
@@ -440,11 +457,6 @@ int choose_variant(const Problem &p, bool atomics) {
       return kSkinny;
     const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
                               : nb >= (p.M <= 16 ? 1024 : 2048);
-    // (a K of 16N or more leaves the few-rows matrix-core kernel too few
-    // column strips for its long K: the split form of the vector-unit kernel
-    // instead, (1, 1024, 65536) 72 against 222 us cold, (8, 1024, 16384) 52
-    // against 67)
-    if (fewrows && valu_ok && atomics && batch == 1 && p.K >= 16LL * p.N) return kSkinny;
     if (fewrows) return kFewRows;
     if (valu_ok && (atomics || skinny_full_k(p))) return kSkinny;
   }
