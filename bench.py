@@ -822,7 +822,7 @@ def main(argv=None):
         line["measured_ceilings"] = {k: round(v, 2) for k, v in ceilings.items()}
         line["pct_of_measured_mfma_f32"] = round(100.0 * value / 1e3 / mf, 2)
         # above 100: the matrix cores outrun unpacked v_fma_f32 (packed FP32
-        # vector instructions are switched off in this build)
+        # vector instructions are switched off in the library's compile flags)
         line["pct_of_measured_valu_f32"] = round(100.0 * value / 1e3 / ceilings["valu_fma_f32_tflops"], 2)
         line["pct_of_datasheet_fp32"] = round(100.0 * value / 1e3 / PEAK_FP32_TFLOPS, 2)
     print(json.dumps(line), flush=True)

@@ -25,7 +25,7 @@
 // v_fma_f32) that is 82% of the LDS bandwidth; 8 x 16 needs 0.75 bytes, and
 // the 128 accumulators still leave room for two workgroups per CU.
 // Ceiling: the unpacked v_fma_f32 rate (packed FP32 instructions are switched
-// off in this build); the matrix cores, at 155 TFLOP/s measured for FP32,
+// off in the library's compile flags); the matrix cores, at 155 TFLOP/s measured for FP32,
 // are the main path.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"

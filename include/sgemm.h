@@ -109,8 +109,8 @@ int sgemm_ex(int M, int N, int K, float alpha, const float *A, int lda,
 
 /*
  * C = alpha * op(A) * op(B) + beta * C with op(X) = X (SGEMM_OP_N) or its
- * transpose (SGEMM_OP_T); op(A) is M x K and op(B) is K x N.  The pages name
- * "any transpose" as part of what a general SGEMM library covers (Tinyforge
+ * transpose (SGEMM_OP_T); op(A) is M x K and op(B) is K x N.  The pages count
+ * transposed operands among what a general SGEMM library covers (Tinyforge
  * README, the comparison with the vendor library) and use the transposition
  * identity to call a column-major library from row-major code ("Optimizing
  * SGEMM in CUDA", "cuBLAS implementation"; "The road to a fast GEMM", the

@@ -158,7 +158,8 @@ def test_batched_select_small_slices(lib):
     """Many small slices leave the one-lane kernel for tiled ones; tiles that
     would mostly lie outside a slice are not chosen."""
     assert _batched_choice(1, 127, 129, 17) == "simple"
-    assert _batched_choice(1, 128, 128, 128) == "mfma16_64x64x64_4x2_sched"
+    # few 64x64 tiles with a short K: 32x64 tiles (3.5 against 4.5 us, device time)
+    assert _batched_choice(1, 128, 128, 128) == "mfma16_32x64x64_2x2_sched"
     assert _batched_choice(1, 256, 256, 65536) == "mfma16_64x64x64_4x2_pipe_splitk"
     assert _batched_choice(1024, 128, 128, 128) == "mfma32_128x128x16_2x2_w4"
     assert _batched_choice(256, 256, 256, 256) == "mfma32_256x256x32_2x2_sched"
