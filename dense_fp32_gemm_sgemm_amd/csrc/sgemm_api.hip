@@ -47,6 +47,19 @@ int launch_skinny_fixed_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// The same for the few-rows kernel's workspace form.
+int launch_skinny_ws_any(const Problem &p, hipStream_t s) {
+  for (int r = 0; r < p.M; r += 8) {
+    Problem q = p;
+    q.M = (p.M - r < 8) ? p.M - r : 8;
+    q.A = p.ta ? p.A + r : p.A + (size_t)r * (size_t)p.lda;
+    q.C = p.C + (size_t)r * (size_t)p.ldc;
+    const int rc = launch_skinny_ws(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 // The few-columns kernel covers N <= 16; as a forced variant on a wider
 // problem it runs on column blocks of 16.
 int launch_narrow_any(const Problem &p, hipStream_t s) {
@@ -118,6 +131,7 @@ const Variant kVariants[] = {
     {"mfma16_128x64x64_4x2_sched_tail", launch_mfma16_128x64x64_4x2_sched_tail},
     {"mfma16_64x64x64_4x2_sched_tail", launch_mfma16_64x64x64_4x2_sched_tail},
     {"skinny_fixed_m8", launch_skinny_fixed_any},
+    {"skinny_m8_ws", launch_skinny_ws_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -158,6 +172,7 @@ enum VariantId {
   kMfma16_128x64x64_w8_sched_tail = 33,
   kMfma16_64x64x64_w8_sched_tail = 34,
   kSkinnyFixed = 35,
+  kSkinnyWs = 36,
 };
 
 constexpr int kNoKernel = -100;
@@ -445,20 +460,27 @@ int choose_variant(const Problem &p, bool atomics) {
     // past the last-level cache): (1, 2048, 16384) 33 against 63 us,
     // (1, 1024, 4096) 9.9 against 16, (8, 4096, 16384) 62 against 75,
     // (1, 65536, 2048) 86.5 against 103.
+    // With a workspace, up to four rows and a full-K strip grid of fewer
+    // workgroups than CUs, the strips split over K instead
+    // (`skinny_m8_ws`), which fills the CUs' memory queues: cold (1, 4096,
+    // 4096) 15.1 against 19.5 us, (1, 2048, 8192) 15.8 against 34.5.
+    const long long split_need = skinny_split_bytes(p);
+    const bool ws_split = valu_ok && p.M <= 4 && batch == 1 && p.ws != nullptr && split_need > 0 &&
+                          (unsigned long long)split_need <= p.ws_bytes;
     if (valu_ok && batch == 1 && p.ws != nullptr) {
       const long long need = skinny_fixed_bytes(p);
       const long long min_nk = p.M <= 2 ? (1LL << 21) : (p.M <= 4 ? (1LL << 22) : (1LL << 23));
       const bool long_k = p.K >= 2LL * p.N && nk >= min_nk && (p.M <= 4 || p.K <= 16384);
       if (need > 0 && (unsigned long long)need <= p.ws_bytes && (long_k || (p.N >= 32768 && p.K <= 2048)))
-        return kSkinnyFixed;
+        return ws_split ? kSkinnyWs : kSkinnyFixed;
     }
     if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&
         (p.M <= 2 || p.N >= 4096))
-      return kSkinny;
+      return ws_split ? kSkinnyWs : kSkinny;
     const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
                               : nb >= (p.M <= 16 ? 1024 : 2048);
     if (fewrows) return kFewRows;
-    if (valu_ok && (atomics || skinny_full_k(p))) return kSkinny;
+    if (valu_ok && (atomics || skinny_full_k(p))) return ws_split ? kSkinnyWs : kSkinny;
   }
   // 64x64 tiles with 16-deep slabs, split over K when atomics are allowed.
   const int m16 = atomics ? kMfma16_64x64x16_splitk : kMfma16_64x64x16;
@@ -638,6 +660,7 @@ long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
                   reinterpret_cast<void *>(256), (unsigned long long)kTailWorkspaceBytes};
   const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
   if (v == kSkinnyFixed) return skinny_fixed_bytes(p);
+  if (v == kSkinnyWs) return skinny_split_bytes(p);
   for (const TailFamily &tf : kTailFamilies)
     if (tf.variant == v) return family_tail_plan(tf, p).bytes;
   return 0;

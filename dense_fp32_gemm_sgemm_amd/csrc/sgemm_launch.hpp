@@ -83,6 +83,14 @@ int launch_skinny_fixed(const Problem &p, hipStream_t stream);
 // Workspace bytes that form needs for p (0: the form does not apply).
 long long skinny_fixed_bytes(const Problem &p);
 
+// Few rows of C (M <= 8), one batch slice, B untransposed, with a workspace:
+// the full-K strip kernel with K split over up to four ranges when its strips
+// alone give fewer workgroups than CUs (partial strips added in range order
+// by the last range); otherwise launch_skinny.  Returns -1 for M > 8.
+int launch_skinny_ws(const Problem &p, hipStream_t stream);
+// Workspace bytes of that split (0: it does not apply).
+long long skinny_split_bytes(const Problem &p);
+
 // Few columns of C (N <= 16): streams A, the matrix cores accumulate 16 x 16
 // blocks, K split over the waves of a workgroup, one launch.  Returns -1 for
 // N > 16.

@@ -123,6 +123,7 @@ constexpr int kFullKCq = 8;                  // 16-byte column quads per workgro
 constexpr int kFullKCols = 4 * kFullKCq;     // 32 columns
 constexpr int kFullKWaves = 4;
 constexpr int kFullKUnroll = 2;              // sweeps (4 rows each) in flight per lane
+constexpr int kFullKMaxSplits = 4;           // K ranges of the split form
 
 // Full-K strip kernel (op(B) untransposed).  Lane l takes column quad
 // cq = l % 8 and row slot rr = l / 8.  In sweep i, wave w covers the 32 rows
@@ -131,9 +132,23 @@ constexpr int kFullKUnroll = 2;              // sweeps (4 rows each) in flight p
 // read the last column (or quad) instead -- in bounds, never stored -- so the
 // loads carry no branch and the unrolled ones issue together.  Rows of B left
 // after the last whole sweep are taken one per slot, rows past K skipped.
-template <int MR, bool VA, bool VB>
-__global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem p) {
+//
+// SPLIT (one batch slice, with a workspace): blockIdx.y takes the kchunk rows
+// of B from blockIdx.y * kchunk, so that the strips times the ranges give
+// every CU a workgroup (a strip grid of fewer workgroups than CUs leaves
+// half the chip's memory requests unissued, which a cold read from HBM
+// feels most); each range's partial strip goes to the workspace as
+// agent-scope stores and the strip's last range adds them in range order.
+template <int MR, bool VA, bool VB, bool SPLIT = false>
+__global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem p, int kchunk, unsigned *flags,
+                                                                         float *part) {
   select_slice(p);
+  if constexpr (SPLIT) {
+    const int kb = (int)blockIdx.y * kchunk;
+    p.A += p.ta ? (size_t)kb * (size_t)p.lda : (size_t)kb;
+    p.B += (size_t)kb * (size_t)p.ldb;
+    p.K = min(p.K - kb, kchunk);
+  }
   __shared__ float red[kFullKWaves][MR][kFullKCols];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -238,7 +253,53 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
       for (int e = 0; e < 4; ++e) red[w][r][4 * cq + e] = acc[r][e];
   }
   __syncthreads();
-  if (threadIdx.x < kFullKCols) {
+  if constexpr (SPLIT) {
+    // Partial strip out (value r of thread t at r * 32 + t), wait until the
+    // stores are acknowledged, count the range in; the last range reads the
+    // partials back in range order, resets the counter and stores C.
+    const int strip = blockIdx.x, sidx = blockIdx.y, splits = gridDim.y;
+    constexpr int kPart = MR * kFullKCols;
+    if (threadIdx.x < kFullKCols) {
+      float *mine = part + ((size_t)strip * splits + sidx) * kPart + threadIdx.x;
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        float s = red[0][r][threadIdx.x];
+#pragma unroll
+        for (int q = 1; q < kFullKWaves; ++q) s += red[q][r][threadIdx.x];
+        __hip_atomic_store(mine + r * kFullKCols, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __shared__ int last_range;
+    __builtin_amdgcn_s_waitcnt(0);  // every memory operation of this wave complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned before = __hip_atomic_fetch_add(flags + strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_range = (before + 1u == (unsigned)splits);
+    }
+    __syncthreads();
+    if (!last_range) return;
+    if (threadIdx.x < kFullKCols) {
+      const int c = strip * kFullKCols + threadIdx.x;
+      const float *p0 = part + (size_t)strip * splits * kPart + threadIdx.x;
+      float v[kFullKMaxSplits][MR];
+#pragma unroll
+      for (int sp = 0; sp < kFullKMaxSplits; ++sp)
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+          v[sp][r] = sp < splits ? __hip_atomic_load(p0 + (size_t)sp * kPart + r * kFullKCols, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.0f;
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        float s = v[0][r];
+#pragma unroll
+        for (int sp = 1; sp < kFullKMaxSplits; ++sp)
+          if (sp < splits) s += v[sp][r];
+        if (r < p.M && c < p.N) store_out(p.C + (size_t)r * (size_t)p.ldc + c, s, p.alpha, p.beta);
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(flags + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x < kFullKCols) {
     const int c = blockIdx.x * kFullKCols + threadIdx.x;
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
@@ -464,13 +525,13 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
 #define SG950_FULLK(MR_)                                                                        \
   do {                                                                                          \
     if (fva && fvb)                                                                             \
-      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, true>), fgrid, fblock, 0, stream, p);  \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, true>), fgrid, fblock, 0, stream, p, p.K, nullptr, nullptr);  \
     else if (fvb)                                                                               \
-      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, true>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, true>), fgrid, fblock, 0, stream, p, p.K, nullptr, nullptr); \
     else if (fva)                                                                               \
-      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, false>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, false>), fgrid, fblock, 0, stream, p, p.K, nullptr, nullptr); \
     else                                                                                        \
-      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, false>), fgrid, fblock, 0, stream, p); \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, false>), fgrid, fblock, 0, stream, p, p.K, nullptr, nullptr); \
   } while (0)
     if (p.M <= 1) {
       SG950_FULLK(1);
@@ -512,6 +573,70 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
     SG950_SKINNY(8);
   }
 #undef SG950_SKINNY
+  return 0;
+}
+
+// The full-K strip kernel with K split over up to four ranges through a
+// workspace (one batch slice, B untransposed), when its strips alone give
+// fewer workgroups than CUs; otherwise launch_skinny.  Returns -1 for M > 8.
+static int skinny_fullk_split_plan(const Problem &p, int &splits, int &kchunk, long long &bytes) {
+  splits = 1;
+  const long long fstrips = ((long long)p.N + kFullKCols - 1) / kFullKCols;
+  if (p.M < 1 || p.M > 8 || p.tb || p.batch != 1 || fstrips < 64 || fstrips >= 256 || fstrips > 1024 ||
+      (long long)p.N * p.K > (1LL << 26))
+    return 0;
+  constexpr int kSweep = kFullKWaves * 32;
+  int want = (int)((256 + fstrips - 1) / fstrips);
+  if (want > kFullKMaxSplits) want = kFullKMaxSplits;
+  if (p.K < want * 4 * kSweep) return 0;  // at least four sweeps per range
+  kchunk = (p.K + want - 1) / want;
+  kchunk = (kchunk + kSweep - 1) / kSweep * kSweep;
+  splits = (p.K + kchunk - 1) / kchunk;
+  const int mr = p.M <= 1 ? 1 : (p.M <= 2 ? 2 : (p.M <= 4 ? 4 : 8));
+  bytes = kTailFlagBytes + fstrips * splits * mr * kFullKCols * 4;
+  return splits > 1 ? 1 : 0;
+}
+
+long long skinny_split_bytes(const Problem &p) {
+  int splits = 1, kchunk = 0;
+  long long bytes = 0;
+  return skinny_fullk_split_plan(p, splits, kchunk, bytes) ? bytes : 0;
+}
+
+int launch_skinny_ws(const Problem &p, hipStream_t stream) {
+  if (p.M > 8) return -1;
+  int splits = 1, kchunk = 0;
+  long long bytes = 0;
+  if (!skinny_fullk_split_plan(p, splits, kchunk, bytes) || p.ws == nullptr ||
+      (unsigned long long)bytes > p.ws_bytes)
+    return launch_skinny(p, stream);
+  const long long fstrips = ((long long)p.N + kFullKCols - 1) / kFullKCols;
+  const dim3 fgrid((unsigned)fstrips, (unsigned)splits, 1u);
+  const dim3 fblock(kFullKWaves * 64);
+  unsigned *flags = reinterpret_cast<unsigned *>(p.ws);
+  float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
+  const bool fvb = b_vec_ok(p), fva = !p.ta && a_vec_ok(p);
+#define SG950_FULLKS(MR_)                                                                                \
+  do {                                                                                                   \
+    if (fva && fvb)                                                                                      \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, true, true>), fgrid, fblock, 0, stream, p, kchunk, flags, part);  \
+    else if (fvb)                                                                                        \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, true, true>), fgrid, fblock, 0, stream, p, kchunk, flags, part); \
+    else if (fva)                                                                                        \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, true, false, true>), fgrid, fblock, 0, stream, p, kchunk, flags, part); \
+    else                                                                                                 \
+      SG950_LAUNCH((skinny_fullk_kernel<MR_, false, false, true>), fgrid, fblock, 0, stream, p, kchunk, flags, part); \
+  } while (0)
+  if (p.M <= 1) {
+    SG950_FULLKS(1);
+  } else if (p.M <= 2) {
+    SG950_FULLKS(2);
+  } else if (p.M <= 4) {
+    SG950_FULLKS(4);
+  } else {
+    SG950_FULLKS(8);
+  }
+#undef SG950_FULLKS
   return 0;
 }
 

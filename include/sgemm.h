@@ -176,10 +176,11 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
  * tile of C.  The pages name splitting K as the way to fill the GPU when the
  * output tiles cannot ("The road to a fast GEMM", "Where to go next").
  * Problems with at most 8 rows of an untransposed B (matrix-vector-like,
- * bound by streaming B) use the workspace the same way where K is long for
- * the columns or the columns very many: B is split into (256-column strip,
- * K chunk) workgroups whose partial strips the strip's last chunk adds in
- * chunk order.
+ * bound by streaming B) use the workspace the same way: the 32-column strips
+ * of the full-K kernel split into up to four K ranges when the strips alone
+ * leave CUs idle (up to four rows), or, where K is long for the columns or
+ * the columns very many, (256-column strip, K chunk) workgroups; either
+ * way the partials are added in range order by the last range.
  *
  * Results are bitwise repeatable (each output is one sum in a fixed order; no
  * atomics touch C), in either atomics mode.  The automatic choice takes the

@@ -135,7 +135,7 @@ def test_fixed_form_in_a_graph():
         assert counters_zero(ws)
 
 
-@pytest.mark.parametrize("shape", [(1, 2048, 16384), (4, 1024, 4096), (1, 65536, 2048), (8, 2048, 16384)],
+@pytest.mark.parametrize("shape", [(1, 1024, 8192), (4, 1024, 4096), (1, 65536, 2048), (8, 2048, 16384)],
                          ids=lambda s: "%dx%dx%d" % s)
 def test_automatic_choice_with_workspace_takes_fixed_form(shape):
     """Through the workspace entry point's automatic choice these shapes
@@ -158,4 +158,99 @@ def test_automatic_choice_with_workspace_takes_fixed_form(shape):
     C3 = run(Ai, Bi, workspace=ws)
     ref, _ = oracle.gemm(Ai, Bi)
     assert oracle.exact_match(C3, ref)
+    assert counters_zero(ws)
+
+
+# The full-K strip kernel split over K through the workspace (skinny_m8_ws):
+# strip counts from 64 to 255 (two to four ranges), ragged N (a partial last
+# strip, N not a multiple of 4: element loads), ragged last range, M 1..8.
+VWS = sg.variant_names().index("skinny_m8_ws")
+WS_SPLIT_SHAPES = [(1, 4096, 4096), (2, 2048, 2048), (4, 4096, 4096), (8, 4096, 2048), (3, 4000, 3000),
+                   (1, 2050, 4099), (6, 8000, 4096)]
+
+
+@pytest.mark.parametrize("shape", WS_SPLIT_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_split_full_k_against_oracle(shape):
+    M, N, K = shape
+    ws = new_ws()
+    say("split full-K few-rows", shape)
+    A, B, _ = draw(M, N, K, seed=M * 5 + N + K)
+    C1 = run(A, B, variant=VWS, workspace=ws)
+    assert counters_zero(ws), "counters left set"
+    ref, den = oracle.gemm(A, B)
+    err = oracle.normalized_error(C1, ref, den)
+    assert err <= TOL, "%s: normalized error %.3g" % (shape, err)
+    C2 = run(A, B, variant=VWS, workspace=ws)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32)), "not bitwise repeatable"
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K + 2, kind="int", with_c=True)
+    C3 = run(Ai, Bi, Ci, 1.0, 1.0, variant=VWS, workspace=ws)
+    ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0)
+    assert oracle.exact_match(C3, ref), "%s: integer result differs" % (shape,)
+    assert counters_zero(ws)
+
+
+def test_split_full_k_transposed_a_padded_and_graph():
+    """Transposed A with alpha/beta, padded and misaligned operands with a
+    NaN C (nothing outside C written), and a captured graph replayed with
+    eager work between the replays."""
+    ws = new_ws()
+    M, N, K = 5, 3000, 2500
+    A, B, Cin = draw(M, N, K, seed=43, with_c=True)
+    say("split full-K transposed A")
+    C = run(np.ascontiguousarray(A.T), B, Cin, -1.25, 0.75, variant=VWS, workspace=ws, trans_a=True)
+    ref, den = oracle.gemm(A, B, Cin, -1.25, 0.75)
+    assert oracle.normalized_error(C, ref, den) <= TOL
+    M, N, K = 2, 3001, 2600
+    A, B, _ = draw(M, N, K, seed=44)
+    say("split full-K padded")
+    C = run(A, B, None, 1.0, 0.0, variant=VWS, lds=(K + 3, N + 1, N + 5), offsets=(1, 3, 2),
+            check_outside=True, workspace=ws)
+    ref, den = oracle.gemm(A, B)
+    assert oracle.normalized_error(C, ref, den) <= TOL
+    assert counters_zero(ws)
+    M, N, K = 1, 4096, 4096
+    Ai, Bi, Ci = draw(M, N, K, seed=45, kind="int", with_c=True)
+    ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0)
+    dA, dB, dC0 = (torch.from_numpy(x).cuda() for x in (Ai, Bi, Ci))
+    out = torch.empty_like(dC0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.add(dC0, 0.0, out=out)
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=VWS, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        torch.add(dC0, 0.0, out=out)
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=VWS, workspace=ws)
+    say("split full-K graph")
+    for i in range(3):
+        junk = torch.randn(4096, device="cuda")
+        float(junk.abs().sum())
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref), "replay %d" % i
+        assert counters_zero(ws)
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (2, 2048, 2048), (1, 2048, 8192), (4, 4096, 4096)],
+                         ids=lambda s: "%dx%dx%d" % s)
+def test_automatic_choice_with_workspace_takes_split_full_k(shape):
+    """Through the workspace entry point's automatic choice these shapes take
+    the split full-K form; results meet the oracle and repeat bit for bit."""
+    M, N, K = shape
+    need = sg.sgemm_workspace_size(0, 0, M, N, K, 1)
+    v = sg.sgemm_strided_batched_ws_select_variant(0, 0, M, N, K, 1.0, 256, K, 0, 256, N, 0, 0.0, 256, N, 0, 1,
+                                                   WS_BYTES)
+    say("auto split full-K", shape, sg.sgemm_variant_name(v), need)
+    assert v == VWS and 4096 < need <= WS_BYTES
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    A, B, _ = draw(M, N, K, seed=N + K + 7)
+    C1 = run(A, B, workspace=ws)
+    ref, den = oracle.gemm(A, B)
+    assert oracle.normalized_error(C1, ref, den) <= TOL
+    C2 = run(A, B, workspace=ws)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
     assert counters_zero(ws)
