@@ -1142,7 +1142,7 @@ def sweep_md(sweep_path: str, ws_path: str = None) -> str:
     head = ("| M x N x K | variant | device us | TFLOP/s | launch us | cold us | bound | floor us | "
             "frac of bound | frac of datasheet | read floor cold us | vendor device us | vendor / ours |")
     if ws:
-        head += " workspace variant | ws device us | ws TFLOP/s |"
+        head += " workspace variant | ws device us | ws TFLOP/s | ws cold us |"
     out += [head, "|" + "---|" * (head.count("|") - 1)]
     for r in _jsonl(sweep_path, "sweep"):
         key = (r["M"], r["N"], r["K"])
@@ -1157,8 +1157,9 @@ def sweep_md(sweep_path: str, ws_path: str = None) -> str:
                    "%.2f" % (vend / r["us_device"]) if vend else "-"))
         if ws:
             w = ws.get(key)
-            row += (" %s | %.2f | %.2f |" % (w["variant"], w["us_device"], w["tflops_device"]) if w
-                    else " - | - | - |")
+            row += (" %s | %.2f | %.2f | %s |" % (w["variant"], w["us_device"], w["tflops_device"],
+                                                   "%.2f" % w["us_cold"] if "us_cold" in w else "-") if w
+                    else " - | - | - | - |")
         out.append(row)
     return "\n".join(out) + "\n"
 
