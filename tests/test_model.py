@@ -145,3 +145,76 @@ def test_counter_summary_means_per_job(tmp_path):
     assert [o["job"] for o in out] == [0, 1]
     assert out[0]["counters"]["X"] == 20.0 and out[0]["dispatches"] == 2 and out[0]["M"] == 1
     assert out[1]["counters"]["X"] == 5.0
+
+
+def _jsonl(path, recs):
+    path.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    return str(path)
+
+
+def test_sweep_md_binding_roof_and_vendor_ratio(tmp_path):
+    """The sweep table keeps each record's roof, its fraction, the cold read
+    floor and vendor / ours; the workspace run's columns join by shape."""
+    ceil = {"mode": "ceilings", "mfma_f32_32x32x2_tflops": 155.0, "mfma_f32_16x16x4_tflops": 141.0,
+            "valu_fma_f32_tflops": 128.0, "hbm_copy_gbs": 4500.0, "hbm_read_gbs": 5900.0,
+            "dispatch_floor_us": 1.5}
+    rec = {"mode": "sweep", "M": 1, "N": 4096, "K": 4096, "variant": "skinny_m8", "us_device": 12.0,
+           "tflops_device": 2.8, "us_launch": 14.0, "us_cold": 20.0, "bound": "hbm", "judged_on": "us_cold",
+           "floor_us": {"mfma": 0.2, "hbm": 11.4, "latency": 1.5}, "frac_of_bound": 0.57,
+           "frac_datasheet": 0.011, "us_read_cold": 11.6, "torch_mm_us_device": 18.0}
+    ws = dict(rec, variant="skinny_m8_ws", us_device=13.0, us_cold=15.0)
+    md = bench.sweep_md(_jsonl(tmp_path / "s.jsonl", [ceil, rec]), _jsonl(tmp_path / "w.jsonl", [ws]))
+    row = [l for l in md.splitlines() if l.startswith("| 1x4096x4096")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[6] == "hbm (cold)" and cells[8] == "0.570" and cells[10] == "11.60"
+    assert cells[12] == "1.50"                       # vendor 18 / ours 12
+    assert cells[13:] == ["skinny_m8_ws", "13.00", "2.80", "15.00"]
+
+
+def test_few_rows_md_ratio_uses_the_better_choice(tmp_path):
+    rec = {"mode": "few-rows", "M": 1, "N": 4096, "K": 4096, "ops": "NN", "auto": "skinny_m8",
+           "auto_ws": "skinny_m8_ws", "us_device_auto": 12.0, "us_device_auto_ws": 10.0,
+           "us_cold_auto": 20.0, "auto_gbs_cold": 3355.0, "us_device_skinny_m8": 12.0,
+           "us_device_mfma16_64x64x64_4x2_pipe_splitk": 23.0, "us_device_fewrows_m32": 15.0,
+           "torch_mm_us_device": 15.0}
+    md = bench.few_rows_md(_jsonl(tmp_path / "f.jsonl", [rec]))
+    row = [l for l in md.splitlines() if l.startswith("| 1x4096x4096")][0]
+    assert row.rstrip().endswith("| 15.00 | 1.50 |")   # vendor 15 / min(12, 10)
+    assert "geometric mean 1.500 over 1 shapes" in md
+
+
+def test_variants_md_marks_best_forced_and_auto_ratio(tmp_path):
+    recs = [{"M": 64, "N": 64, "K": 64, "variant": "a", "forced": True, "us_device": 2.0, "tflops_device": 1.0},
+            {"M": 64, "N": 64, "K": 64, "variant": "b", "forced": True, "us_device": 1.0, "tflops_device": 2.0},
+            {"M": 64, "N": 64, "K": 64, "variant": "b", "forced": False, "us_device": 1.0,
+             "tflops_device": 1.9}]
+    md = bench.variants_md([_jsonl(tmp_path / "v.jsonl", recs)])
+    row = [l for l in md.splitlines() if l.startswith("| 64x64x64")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[2:] == ["1.00", "**2.00**", "b", "1.90", "0.950"]
+
+
+def test_counters_md_busy_fetch_and_hit_rate(tmp_path):
+    """MFMA busy from the deterministic busy count (2MNK / 64 per SIMD), fetch
+    scaled by the copy calibration, L2 hit rate and LDS conflict share."""
+    M = N = K = 1024
+    busy = 2.0 * M * N * K / 64                     # summed over the 1024 SIMDs
+    base = {"job": 0, "M": M, "N": N, "K": K, "variant": "v", "dispatches": 1}
+    passes = [dict(base, counters={"SQ_VALU_MFMA_BUSY_CYCLES": busy, "GRBM_GUI_ACTIVE": 8 * 40000.0,
+                                   "SQ_LDS_BANK_CONFLICT": 10.0, "SQ_LDS_IDX_ACTIVE": 100.0}),
+              dict(base, counters={"FETCH_SIZE": 1000.0}), dict(base, counters={"WRITE_SIZE": 4096.0}),
+              dict(base, counters={"TCC_HIT_sum": 3.0, "TCC_MISS_sum": 1.0})]
+    paths = []
+    for i, p in enumerate(passes):
+        f = tmp_path / ("p%d.json" % i)
+        f.write_text(json.dumps([p]))
+        paths.append(str(f))
+    times = _jsonl(tmp_path / "t.jsonl", [{"M": M, "N": N, "K": K, "variant": "v", "us_device": 20.0}])
+    md = bench.counters_md(paths, times)
+    row = [l for l in md.splitlines() if l.startswith("| 1024x1024x1024")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    ideal = busy / 1024                             # 32768 cycles
+    assert cells[2] == "%.1f%%" % (100 * ideal / 40000.0)
+    assert cells[3] == "20.00" and cells[4] == "%.1f%%" % (100 * ideal / (20.0 * 1e3 * 2.38))
+    assert cells[5] == "2.0"                        # 1000 KiB x 1024 x 2.0 / 1e6
+    assert cells[10] == "75.0%" and cells[11] == "10.0%"
