@@ -669,6 +669,8 @@ def main(argv=None):
     ap.add_argument("--few-rows", action="store_true",
                     help="few-rows grid (M <= 32, both orientations of B): the automatic choice, "
                          "the three candidate kernels and the vendor BLAS")
+    ap.add_argument("--rows", type=int, nargs="+", metavar="M",
+                    help="with --few-rows: only these row counts of the grid")
     ap.add_argument("--vendor", action="store_true",
                     help="with --sweep/--shape: also time torch.mm in strict FP32 (context only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -849,7 +851,7 @@ def few_rows(args):
     cands = [names.index(n) for n in ("skinny_m8", "mfma16_64x64x64_4x2_pipe_splitk", "fewrows_m32")]
     ceil = _sweep_ceilings(args)
     job = args.job0
-    for M in FEW_ROWS_M:
+    for M in (args.rows or FEW_ROWS_M):
         for N, K in FEW_ROWS_NK:
             for ops in ("NN", "NT"):
                 prob = Problem(M, N, K, ops=ops)

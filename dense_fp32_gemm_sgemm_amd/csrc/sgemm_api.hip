@@ -88,6 +88,19 @@ int launch_fewrows_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// The same for its workspace form.
+int launch_fewrows_ws_any(const Problem &p, hipStream_t s) {
+  for (int r = 0; r < p.M; r += 32) {
+    Problem q = p;
+    q.M = (p.M - r < 32) ? p.M - r : 32;
+    q.A = p.ta ? p.A + r : p.A + (size_t)r * (size_t)p.lda;
+    q.C = p.C + (size_t)r * (size_t)p.ldc;
+    const int rc = launch_fewrows_ws(q, s);
+    if (rc != 0) return rc;
+  }
+  return 0;
+}
+
 struct Variant {
   const char *name;
   Launcher launch;
@@ -132,6 +145,7 @@ const Variant kVariants[] = {
     {"mfma16_64x64x64_4x2_sched_tail", launch_mfma16_64x64x64_4x2_sched_tail},
     {"skinny_fixed_m8", launch_skinny_fixed_any},
     {"skinny_m8_ws", launch_skinny_ws_any},
+    {"fewrows_m32_ws", launch_fewrows_ws_any},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -173,6 +187,7 @@ enum VariantId {
   kMfma16_64x64x64_w8_sched_tail = 34,
   kSkinnyFixed = 35,
   kSkinnyWs = 36,
+  kFewRowsWs = 37,
 };
 
 constexpr int kNoKernel = -100;
@@ -436,6 +451,26 @@ int choose_variant(const Problem &p, bool atomics) {
   if (p.M <= 32 && p.N >= 64 && nk >= (1LL << 20) && !rows32_tiles) {
     const long long nb = (long long)p.N * batch;  // columns over the batch
     const bool valu_ok = !p.tb && p.M <= 8;
+    // With a workspace, up to four rows and a full-K strip grid of fewer
+    // workgroups than CUs, the vector-unit kernel's strips split over K
+    // (`skinny_m8_ws`), which fills the CUs' memory queues: cold (1, 4096,
+    // 4096) 15.1 against 19.5 us, (1, 2048, 8192) 15.8 against 34.5.
+    const long long split_need = skinny_split_bytes(p);
+    const bool ws_split = valu_ok && p.M <= 4 && batch == 1 && p.ws != nullptr && split_need > 0 &&
+                          (unsigned long long)split_need <= p.ws_bytes;
+    // Otherwise, with a workspace that holds it, the matrix-core few-rows
+    // kernel split over K (`fewrows_m32_ws`, up to 2048 columns): up to 16
+    // rows from 64 strips of 16 columns (1009 columns) at a K up to 32768
+    // (as far as measured), or from fewer at a K up to 4096 (with fewer
+    // strips than 64 a longer K fills too few CUs); above 16 rows where the
+    // unsplit kernel is chosen below.
+    // Cold, operands rotated past the last-level cache: (8, 1024, 8192)
+    // 13.7 us against 31.3 on the fixed-order vector-unit form, (16, 1024,
+    // 8192) 15.0 against 39.9 unsplit, (4, 1024, 4096) with B transposed 8.1
+    // against 11.1 on split 64x64 tiles.
+    const long long few_need = fewrows_split_bytes(p);
+    const bool few_ws = !ws_split && p.ws != nullptr && few_need > 0 && (unsigned long long)few_need <= p.ws_bytes;
+    if (few_ws && p.M <= 16 && p.K <= (p.N > 1008 ? 32768 : 4096)) return kFewRowsWs;
     // A K of 16N or more: too few columns for the streaming kernels' strips
     // and a long K each; split-K 64x64 tiles spread it over the CUs
     // ((1, 1024, 16384) 23.2 us against 36.2 on the vector-unit kernel's
@@ -459,14 +494,8 @@ int choose_variant(const Problem &p, bool atomics) {
     // the columns very many and K short -- measured cold (operands rotated
     // past the last-level cache): (1, 2048, 16384) 33 against 63 us,
     // (1, 1024, 4096) 9.9 against 16, (8, 4096, 16384) 62 against 75,
-    // (1, 65536, 2048) 86.5 against 103.
-    // With a workspace, up to four rows and a full-K strip grid of fewer
-    // workgroups than CUs, the strips split over K instead
-    // (`skinny_m8_ws`), which fills the CUs' memory queues: cold (1, 4096,
-    // 4096) 15.1 against 19.5 us, (1, 2048, 8192) 15.8 against 34.5.
-    const long long split_need = skinny_split_bytes(p);
-    const bool ws_split = valu_ok && p.M <= 4 && batch == 1 && p.ws != nullptr && split_need > 0 &&
-                          (unsigned long long)split_need <= p.ws_bytes;
+    // (1, 65536, 2048) 86.5 against 103; the strips split over K where
+    // `ws_split` holds.
     if (valu_ok && batch == 1 && p.ws != nullptr) {
       const long long need = skinny_fixed_bytes(p);
       const long long min_nk = p.M <= 2 ? (1LL << 21) : (p.M <= 4 ? (1LL << 22) : (1LL << 23));
@@ -477,9 +506,13 @@ int choose_variant(const Problem &p, bool atomics) {
     if (valu_ok && p.M <= 4 && p.N >= 2048 && p.K >= 2048 && (long long)p.N * p.K <= (1LL << 26) &&
         (p.M <= 2 || p.N >= 4096))
       return ws_split ? kSkinnyWs : kSkinny;
-    const bool fewrows = p.tb ? (p.M <= 16 ? nb >= 2048 : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
-                              : nb >= (p.M <= 16 ? 1024 : 2048);
-    if (fewrows) return kFewRows;
+    // (B transposed, up to 16 rows: from 1024 columns at a K up to 2048,
+    // (8, 1024, 1024) 4.8 against 8.8 us on split 64x64 tiles.)
+    const bool fewrows =
+        p.tb ? (p.M <= 16 ? (nb >= 2048 || (batch == 1 && p.N >= 1024 && p.K <= 2048))
+                          : (nb >= 8192 || (nb >= 2048 && p.K <= 4096)))
+             : nb >= (p.M <= 16 ? 1024 : 2048);
+    if (fewrows) return few_ws ? kFewRowsWs : kFewRows;
     if (valu_ok && (atomics || skinny_full_k(p))) return ws_split ? kSkinnyWs : kSkinny;
   }
   // 64x64 tiles with 16-deep slabs, split over K when atomics are allowed.
@@ -661,6 +694,7 @@ long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
   const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
   if (v == kSkinnyFixed) return skinny_fixed_bytes(p);
   if (v == kSkinnyWs) return skinny_split_bytes(p);
+  if (v == kFewRowsWs) return fewrows_split_bytes(p);
   for (const TailFamily &tf : kTailFamilies)
     if (tf.variant == v) return family_tail_plan(tf, p).bytes;
   return 0;

@@ -35,6 +35,7 @@
 // deterministic.
 #include "sgemm_common.hpp"
 #include "sgemm_launch.hpp"
+#include "sgemm_sched.hpp"
 
 #include <climits>
 
@@ -43,14 +44,28 @@ namespace sg950 {
 namespace {
 constexpr int kFewWaves = 8;   // waves per workgroup, each a K range
 constexpr int kFewUnroll = 8;  // steps whose loads are in flight together
+constexpr int kFewMaxSplits = 4;  // K chunks of the split form
 }  // namespace
 
 // NR: 16-row blocks of C (M <= 16 NR).  CPL: column blocks per lane (the
 // strip is 16 CPL columns).  VB: an untransposed B's rows hold whole
 // CPL-column groups (N % CPL == 0), so a lane's columns are one load.
-template <int NR, int CPL, bool TA, bool TB, bool VB>
-__global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange) {
+//
+// SPLIT (one batch slice, with a workspace): blockIdx.y takes the kchunk
+// values of K from blockIdx.y * kchunk (the eight waves split that chunk),
+// so that strips x chunks give every CU a workgroup where the strips alone
+// cannot; each chunk's partial blocks go to the workspace as agent-scope
+// stores and the strip's last chunk adds them in chunk order and stores C.
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SPLIT = false>
+__global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange, int kchunk,
+                                                                 unsigned *flags, float *part) {
   select_slice(p);
+  if constexpr (SPLIT) {
+    const int kb = (int)blockIdx.y * kchunk;
+    p.A += TA ? (size_t)kb * (size_t)p.lda : (size_t)kb;
+    p.B += TB ? (size_t)kb : (size_t)kb * (size_t)p.ldb;
+    p.K = min(p.K - kb, kchunk);
+  }
   constexpr int NB = CPL;       // 16 x 16 blocks per wave and row block
   constexpr int NC = 16 * CPL;  // columns per workgroup
   __shared__ floatx4 red[kFewWaves][NR * NB][64];
@@ -307,6 +322,58 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
     for (int e = 0; e < NB; ++e) red[w][rb * NB + e][lane] = acc[rb][e];
   __syncthreads();
+  if constexpr (SPLIT) {
+    // Block b's wave sum (block b by wave b mod 8, over the waves in order)
+    // to the workspace: value r of lane l of block b at (b * 64 + l) * 4 + r.
+    constexpr int kPart = NR * NB * 256;
+    const int strip = (int)blockIdx.x, sidx = (int)blockIdx.y, splits = (int)gridDim.y;
+    float *mine = part + ((size_t)strip * splits + sidx) * kPart;
+    for (int blk = w; blk < NR * NB; blk += kFewWaves) {
+      floatx4 s = red[0][blk][lane];
+#pragma unroll
+      for (int q = 1; q < kFewWaves; ++q) {
+        const floatx4 v = red[q][blk][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] += v[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __hip_atomic_store(mine + (blk * 64 + lane) * 4 + r, s[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __shared__ int last_chunk;
+    __builtin_amdgcn_s_waitcnt(0);  // every memory operation of this wave complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned before = __hip_atomic_fetch_add(flags + strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_chunk = (before + 1u == (unsigned)splits);
+    }
+    __syncthreads();
+    if (!last_chunk) return;
+    const float *p0 = part + (size_t)strip * splits * kPart;
+    for (int blk = w; blk < NR * NB; blk += kFewWaves) {
+      const int rb = blk / NB, e = blk % NB;
+      float v[kFewMaxSplits][4];
+#pragma unroll
+      for (int sp = 0; sp < kFewMaxSplits; ++sp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[sp][r] = sp < splits ? __hip_atomic_load(p0 + (size_t)sp * kPart + (blk * 64 + lane) * 4 + r,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.0f;
+      const int col = TB ? n0 + 16 * e + li : n0 + CPL * li + e;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s = v[0][r];
+#pragma unroll
+        for (int sp = 1; sp < kFewMaxSplits; ++sp)
+          if (sp < splits) s += v[sp][r];
+        const int row = 16 * rb + 4 * sl + r;
+        if (col < p.N && row < p.M) store_out(p.C + (size_t)row * (size_t)p.ldc + col, s, p.alpha, p.beta);
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(flags + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   // Block b of the NR x NB is summed by wave b mod 8, over the waves in
   // order; no barrier after this point.
   for (int blk = w; blk < NR * NB; blk += kFewWaves) {
@@ -329,45 +396,52 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 }
 
 namespace {
-template <int NR, int CPL, bool TA, bool TB, bool VB>
-void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange) {
-  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB>), grid, dim3(kFewWaves * 64), 0, stream, p,
-                     krange);
+// (SP: the split form; kchunk, flags and part are its arguments)
+struct FewSplit {
+  int kchunk = 0;
+  unsigned *flags = nullptr;
+  float *part = nullptr;
+};
+
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SP>
+void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange, const FewSplit &fs) {
+  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB, SP>), grid, dim3(kFewWaves * 64), 0, stream, p, krange,
+               fs.kchunk, fs.flags, fs.part);
 }
 
-template <int NR, int CPL, bool TB>
-void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int krange, bool vb) {
+template <int NR, int CPL, bool TB, bool SP>
+void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int krange, bool vb, const FewSplit &fs) {
   if (p.ta) {
     if (vb)
-      launch_fewrows_t<NR, CPL, true, TB, true>(p, grid, stream, krange);
+      launch_fewrows_t<NR, CPL, true, TB, true, SP>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, true, TB, false>(p, grid, stream, krange);
+      launch_fewrows_t<NR, CPL, true, TB, false, SP>(p, grid, stream, krange, fs);
   } else {
     if (vb)
-      launch_fewrows_t<NR, CPL, false, TB, true>(p, grid, stream, krange);
+      launch_fewrows_t<NR, CPL, false, TB, true, SP>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, false, TB, false>(p, grid, stream, krange);
+      launch_fewrows_t<NR, CPL, false, TB, false, SP>(p, grid, stream, krange, fs);
   }
 }
 
-template <int NR>
-void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl) {
+template <int NR, bool SP>
+void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl, const FewSplit &fs) {
   if (p.tb) {
     if (cpl == 4)
-      launch_fewrows_ta<NR, 4, true>(p, grid, stream, krange, false);
+      launch_fewrows_ta<NR, 4, true, SP>(p, grid, stream, krange, false, fs);
     else if (cpl == 2)
-      launch_fewrows_ta<NR, 2, true>(p, grid, stream, krange, false);
+      launch_fewrows_ta<NR, 2, true, SP>(p, grid, stream, krange, false, fs);
     else
-      launch_fewrows_ta<NR, 1, true>(p, grid, stream, krange, false);
+      launch_fewrows_ta<NR, 1, true, SP>(p, grid, stream, krange, false, fs);
     return;
   }
   const bool vb = p.N % cpl == 0;
   if (cpl == 4)
-    launch_fewrows_ta<NR, 4, false>(p, grid, stream, krange, vb);
+    launch_fewrows_ta<NR, 4, false, SP>(p, grid, stream, krange, vb, fs);
   else if (cpl == 2)
-    launch_fewrows_ta<NR, 2, false>(p, grid, stream, krange, vb);
+    launch_fewrows_ta<NR, 2, false, SP>(p, grid, stream, krange, vb, fs);
   else
-    launch_fewrows_ta<NR, 1, false>(p, grid, stream, krange, vb);
+    launch_fewrows_ta<NR, 1, false, SP>(p, grid, stream, krange, vb, fs);
 }
 }  // namespace
 
@@ -390,10 +464,62 @@ int launch_fewrows(const Problem &p, hipStream_t stream) {
   int krange = (p.K + kFewWaves - 1) / kFewWaves;
   krange = (krange + 15) / 16 * 16;
   const dim3 grid((unsigned)blocks, 1u, (unsigned)p.batch);
+  const FewSplit none;
   if (p.M > 16)
-    launch_fewrows_nr<2>(p, grid, stream, krange, cpl);
+    launch_fewrows_nr<2, false>(p, grid, stream, krange, cpl, none);
   else
-    launch_fewrows_nr<1>(p, grid, stream, krange, cpl);
+    launch_fewrows_nr<1, false>(p, grid, stream, krange, cpl, none);
+  return 0;
+}
+
+// The split form's plan: one column block per lane (the strips are then as
+// many as they can be) and as many K chunks as keep strips x chunks within
+// one workgroup per CU (at most four, each at least 128 values of K per
+// wave).  Only for 128 strips (2048 columns) or fewer: with more, two chunks
+// already overfill the CUs, and a second round of workgroups costs more
+// than the unsplit strips' shortfall of memory parallelism (cold, (8, 3072,
+// 2048) 12.5 against 11.5 us unsplit, (16, 4000, 4096) 22.1 against 19.5).
+static bool fewrows_split_plan(const Problem &p, int &splits, int &kchunk, long long &bytes) {
+  splits = 1;
+  if (p.M < 1 || p.M > 32 || p.batch != 1) return false;
+  const long long strips = ((long long)p.N + 15) / 16;
+  if (strips > 128) return false;
+  int want = (int)(256 / strips);
+  if (want > kFewMaxSplits) want = kFewMaxSplits;
+  if (p.K < want * kFewWaves * 128) want = p.K / (kFewWaves * 128);
+  if (want < 2) return false;
+  kchunk = (p.K + want - 1) / want;
+  kchunk = (kchunk + 16 * kFewWaves - 1) / (16 * kFewWaves) * (16 * kFewWaves);
+  splits = (p.K + kchunk - 1) / kchunk;
+  const int nr = p.M > 16 ? 2 : 1;
+  bytes = kTailFlagBytes + strips * splits * nr * 256LL * 4;
+  return splits > 1;
+}
+
+long long fewrows_split_bytes(const Problem &p) {
+  int splits = 1, kchunk = 0;
+  long long bytes = 0;
+  return fewrows_split_plan(p, splits, kchunk, bytes) ? bytes : 0;
+}
+
+int launch_fewrows_ws(const Problem &p, hipStream_t stream) {
+  if (p.M < 1 || p.M > 32) return -1;
+  int splits = 1, kchunk = 0;
+  long long bytes = 0;
+  if (!fewrows_split_plan(p, splits, kchunk, bytes) || p.ws == nullptr || (unsigned long long)bytes > p.ws_bytes)
+    return launch_fewrows(p, stream);
+  const long long strips = ((long long)p.N + 15) / 16;
+  int krange = (kchunk + kFewWaves - 1) / kFewWaves;
+  krange = (krange + 15) / 16 * 16;
+  FewSplit fs;
+  fs.kchunk = kchunk;
+  fs.flags = reinterpret_cast<unsigned *>(p.ws);
+  fs.part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
+  const dim3 grid((unsigned)strips, (unsigned)splits, 1u);
+  if (p.M > 16)
+    launch_fewrows_nr<2, true>(p, grid, stream, krange, 1, fs);
+  else
+    launch_fewrows_nr<1, true>(p, grid, stream, krange, 1, fs);
   return 0;
 }
 

@@ -175,12 +175,15 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
  * finishes a tile's ranges last adds them in range order and writes the
  * tile of C.  The pages name splitting K as the way to fill the GPU when the
  * output tiles cannot ("The road to a fast GEMM", "Where to go next").
- * Problems with at most 8 rows of an untransposed B (matrix-vector-like,
- * bound by streaming B) use the workspace the same way: the 32-column strips
- * of the full-K kernel split into up to four K ranges when the strips alone
- * leave CUs idle (up to four rows), or, where K is long for the columns or
- * the columns very many, (256-column strip, K chunk) workgroups; either
- * way the partials are added in range order by the last range.
+ * Problems with few rows (matrix-vector-like, bound by streaming B) use the
+ * workspace the same way.  At most 8 rows of an untransposed B: the
+ * 32-column strips of the full-K kernel split into up to four K ranges when
+ * the strips alone leave CUs idle (up to four rows), or, where K is long for
+ * the columns or the columns very many, (256-column strip, K chunk)
+ * workgroups.  Up to 32 rows and 2048 columns, either orientation of B: the
+ * 16-column strips of the matrix-core few-rows kernel split into up to four
+ * K chunks, as many as keep one workgroup per CU.  Either way the partials
+ * are added in range order by the last range.
  *
  * Results are bitwise repeatable (each output is one sum in a fixed order; no
  * atomics touch C), in either atomics mode.  The automatic choice takes the

@@ -291,6 +291,51 @@ def test_select_few_rows(lib):
     assert _op_choice(0, 0, 12, 1024, 256, batch=8) == "fewrows_m32"   # strips over the batch
 
 
+def _ws_choice(ta, tb, M, N, K, ws_bytes=4096 + (32 << 20), batch=1):
+    return sg.sgemm_variant_name(sg.sgemm_strided_batched_ws_select_variant(
+        ta, tb, M, N, K, 1.0, FAKE, M if ta else K, M * K, FAKE, K if tb else N, K * N, 0.0, FAKE, N, M * N,
+        batch, ws_bytes))
+
+
+def test_select_few_rows_split_through_workspace(lib):
+    """With a workspace, the matrix-core few-rows kernel split over K: up to
+    16 rows from 1009 columns (64 strips of 16) at a K up to 32768, from fewer
+    columns at a K up to 4096; above 16 rows where the unsplit kernel would be
+    chosen.  Never beyond 2048 columns, never in a batch, never where the
+    vector-unit strips split over K or 32-row tiles are chosen."""
+    assert _ws_choice(0, 0, 8, 1024, 8192) == "fewrows_m32_ws"      # was the fixed-order VALU form
+    assert _ws_choice(0, 0, 16, 1024, 8192) == "fewrows_m32_ws"     # was unsplit
+    assert _ws_choice(0, 1, 4, 1024, 4096) == "fewrows_m32_ws"      # was split 64x64 tiles
+    assert _ws_choice(0, 0, 1, 1500, 16384) == "fewrows_m32_ws"
+    assert _ws_choice(1, 0, 12, 2048, 2048) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 8, 512, 4096) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 32, 2048, 4096) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 1, 2048, 4096) == "skinny_m8_ws"        # vector-unit strips split first
+    assert _ws_choice(0, 0, 8, 3072, 4096) == "fewrows_m32"         # beyond 2048 columns
+    assert _ws_choice(0, 0, 8, 512, 8192) != "fewrows_m32_ws"       # too few strips for a long K
+    assert _ws_choice(0, 0, 4, 1024, 65536) == "skinny_fixed_m8"    # beyond the measured K
+    assert _ws_choice(0, 0, 8, 1024, 1024) == "fewrows_m32"         # K too short to split
+    assert _ws_choice(0, 0, 32, 1024, 4096) != "fewrows_m32_ws"     # 32-row tiles fill C
+    assert _ws_choice(0, 0, 24, 2048, 16384) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _ws_choice(0, 1, 16, 1024, 4096) == "mfma16_32x64x64_2x2_sched_splitk"
+    assert _ws_choice(0, 0, 8, 1024, 8192, ws_bytes=4096) == "fewrows_m32"   # workspace too small
+    assert _ws_choice(0, 0, 8, 1024, 8192, batch=2) != "fewrows_m32_ws"
+    # 64 strips x 4 chunks of 2048, one 16-row block of 256 floats per lane
+    assert sg.sgemm_workspace_size(0, 0, 8, 1024, 8192, 1) == 4096 + 64 * 4 * 1024
+    # 128 strips x 2 chunks, two 16-row blocks
+    assert sg.sgemm_workspace_size(0, 0, 32, 2048, 4096, 1) == 4096 + 128 * 2 * 2 * 1024
+    try:   # the split sums in a fixed order: allowed without atomics
+        assert sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_NOT_ALLOWED) == sg.SGEMM_OK
+        assert _ws_choice(0, 0, 8, 1024, 8192) == "fewrows_m32_ws"
+    finally:
+        sg.sgemm_set_atomics_mode(sg.SGEMM_ATOMICS_ALLOWED)
+    # without a workspace, B transposed and up to 16 rows: the unsplit
+    # few-rows kernel from 1024 columns at a K up to 2048
+    assert _op_choice(0, 1, 8, 1024, 1024) == "fewrows_m32"
+    assert _op_choice(0, 1, 16, 1024, 2048) == "fewrows_m32"
+    assert _op_choice(0, 1, 8, 1024, 4096) == "mfma16_64x64x64_4x2_pipe_splitk"
+
+
 def test_select_split_k_below_one_round(lib):
     """Fewer 64x64 tiles than CUs with a long K: K is split over workgroups
     ((64, 8192, 8192): 84 us split against 139 us on 128 tiles); from 32 to

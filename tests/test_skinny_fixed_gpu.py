@@ -135,7 +135,7 @@ def test_fixed_form_in_a_graph():
         assert counters_zero(ws)
 
 
-@pytest.mark.parametrize("shape", [(1, 1024, 8192), (4, 1024, 4096), (1, 65536, 2048), (8, 2048, 16384)],
+@pytest.mark.parametrize("shape", [(1, 512, 32768), (4, 1024, 65536), (1, 65536, 2048), (8, 4096, 16384)],
                          ids=lambda s: "%dx%dx%d" % s)
 def test_automatic_choice_with_workspace_takes_fixed_form(shape):
     """Through the workspace entry point's automatic choice these shapes
@@ -253,4 +253,91 @@ def test_automatic_choice_with_workspace_takes_split_full_k(shape):
     assert oracle.normalized_error(C1, ref, den) <= TOL
     C2 = run(A, B, workspace=ws)
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+    assert counters_zero(ws)
+
+
+# The matrix-core few-rows kernel split over K through the workspace
+# (fewrows_m32_ws): 65 to 128 strips of 16 columns (two to four K chunks),
+# both orientations of B, one and two 16-row blocks, ragged N and K; past
+# 2048 columns the plain kernel.
+VFW = sg.variant_names().index("fewrows_m32_ws")
+FEW_SPLIT_CASES = [((16, 2048, 2048), False), ((16, 2048, 2048), True), ((8, 1024, 4096), False),
+                   ((32, 2048, 3000), True), ((20, 1500, 2200), False), ((3, 1030, 8200), True),
+                   ((8, 520, 4100), False), ((6, 3000, 4096), False)]
+
+
+@pytest.mark.parametrize("case", FEW_SPLIT_CASES, ids=lambda c: "%dx%dx%d-%s" % (c[0] + ("NT" if c[1] else "NN",)))
+def test_fewrows_split_against_oracle(case):
+    (M, N, K), tb = case
+    ws = new_ws()
+    say("few-rows matrix-core split", (M, N, K), tb)
+    A, B, _ = draw(M, N, K, seed=M * 3 + N + K)
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    C1 = run(A, Bs, variant=VFW, workspace=ws, trans_b=tb)
+    assert counters_zero(ws), "counters left set"
+    ref, den = oracle.gemm(A, B)
+    err = oracle.normalized_error(C1, ref, den)
+    assert err <= TOL, "%s: normalized error %.3g" % ((M, N, K), err)
+    C2 = run(A, Bs, variant=VFW, workspace=ws, trans_b=tb)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32)), "not bitwise repeatable"
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K + 3, kind="int", with_c=True)
+    Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+    C3 = run(Ai, Bis, Ci, 1.0, 1.0, variant=VFW, workspace=ws, trans_b=tb)
+    ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0)
+    assert oracle.exact_match(C3, ref), "%s: integer result differs" % ((M, N, K),)
+    assert counters_zero(ws)
+
+
+def test_fewrows_split_transposed_a_padded():
+    """Transposed A with alpha/beta; padded, misaligned operands with a NaN
+    C (nothing outside C written); rows past 32 in blocks of 32."""
+    ws = new_ws()
+    M, N, K = 12, 1600, 4100
+    A, B, Cin = draw(M, N, K, seed=46, with_c=True)
+    say("few-rows split transposed A")
+    C = run(np.ascontiguousarray(A.T), B, Cin, 0.5, -2.0, variant=VFW, workspace=ws, trans_a=True)
+    ref, den = oracle.gemm(A, B, Cin, 0.5, -2.0)
+    assert oracle.normalized_error(C, ref, den) <= TOL
+    M, N, K = 24, 1999, 2100
+    A, B, _ = draw(M, N, K, seed=47)
+    say("few-rows split padded")
+    C = run(A, B, None, 1.0, 0.0, variant=VFW, lds=(K + 3, N + 1, N + 5), offsets=(1, 3, 2),
+            check_outside=True, workspace=ws)
+    ref, den = oracle.gemm(A, B)
+    assert oracle.normalized_error(C, ref, den) <= TOL
+    M, N, K = 40, 2048, 2048
+    Ai, Bi, _ = draw(M, N, K, seed=48, kind="int")
+    say("few-rows split row blocks")
+    C = run(Ai, Bi, variant=VFW, workspace=ws)
+    ref, _ = oracle.gemm(Ai, Bi)
+    assert oracle.exact_match(C, ref)
+    assert counters_zero(ws)
+
+
+@pytest.mark.parametrize("case", [((8, 1024, 8192), False), ((16, 1024, 8192), False), ((4, 1024, 4096), True),
+                                  ((32, 2048, 4096), False), ((1, 1500, 16384), False)],
+                         ids=lambda c: "%dx%dx%d-%s" % (c[0] + ("NT" if c[1] else "NN",)))
+def test_automatic_choice_with_workspace_takes_fewrows_split(case):
+    """Through the workspace entry point's automatic choice these shapes take
+    the matrix-core few-rows kernel split over K, with the workspace size the
+    library reports; results meet the oracle and repeat bit for bit."""
+    (M, N, K), tb = case
+    need = sg.sgemm_workspace_size(0, 1 if tb else 0, M, N, K, 1)
+    v = sg.sgemm_strided_batched_ws_select_variant(0, 1 if tb else 0, M, N, K, 1.0, 256, K, 0, 256,
+                                                   K if tb else N, 0, 0.0, 256, N, 0, 1, WS_BYTES)
+    say("auto few-rows split", (M, N, K), tb, sg.sgemm_variant_name(v), need)
+    assert v == VFW and 4096 < need <= WS_BYTES
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    A, B, _ = draw(M, N, K, seed=N + K + 11)
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    C1 = run(A, Bs, workspace=ws, trans_b=tb)
+    ref, den = oracle.gemm(A, B)
+    assert oracle.normalized_error(C1, ref, den) <= TOL
+    C2 = run(A, Bs, workspace=ws, trans_b=tb)
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+    Ai, Bi, _ = draw(M, N, K, seed=N + K + 12, kind="int")
+    Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+    C3 = run(Ai, Bis, workspace=ws, trans_b=tb)
+    ref, _ = oracle.gemm(Ai, Bi)
+    assert oracle.exact_match(C3, ref)
     assert counters_zero(ws)
