@@ -469,8 +469,22 @@ int choose_variant(const Problem &p, bool atomics) {
     // 8192) 15.0 against 39.9 unsplit, (4, 1024, 4096) with B transposed 8.1
     // against 11.1 on split 64x64 tiles.
     const long long few_need = fewrows_split_bytes(p);
-    const bool few_ws = !ws_split && p.ws != nullptr && few_need > 0 && (unsigned long long)few_need <= p.ws_bytes;
+    const bool few_fits = p.ws != nullptr && few_need > 0 && (unsigned long long)few_need <= p.ws_bytes;
+    const bool few_ws = !ws_split && p.N <= 2048 && few_fits;
     if (few_ws && p.M <= 16 && p.K <= (p.N > 1008 ? 32768 : 4096)) return kFewRowsWs;
+    // Past 2048 columns (wider strips, at most 128 of them), with B
+    // untransposed, where the unsplit kernel's grid fills less than 80% of
+    // its last round of workgroups (3072 columns: 192 strips, 6144: 384) and
+    // K is at least 4096 -- ahead of the vector-unit strips split over K as
+    // well; up to eight rows only while N*K <= 2^26 (beyond it the
+    // fixed-order vector-unit split streams B better: (4, 6144, 16384) 69 us
+    // against 78).  Cold: (16, 6144, 4096) 25.4 against 46.6 us unsplit,
+    // (16, 3072, 8192) 31.3 against 45.0, (1, 3072, 8192) 25.0 against 29.9
+    // on the vector-unit split, (8, 6144, 8192) 42.8 against 78.9.  (With B
+    // transposed the unsplit kernel keeps up: the split ran slower cold.)
+    if (few_fits && !p.tb && p.N > 2048 && p.K >= 4096 && (p.M > 8 || (long long)p.N * p.K <= (1LL << 26)) &&
+        fewrows_round_fill_pct(p) < 80)
+      return kFewRowsWs;
     // A K of 16N or more: too few columns for the streaming kernels' strips
     // and a long K each; split-K 64x64 tiles spread it over the CUs
     // ((1, 1024, 16384) 23.2 us against 36.2 on the vector-unit kernel's

@@ -445,18 +445,27 @@ void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int kran
 }
 }  // namespace
 
-int launch_fewrows(const Problem &p, hipStream_t stream) {
-  if (p.M < 1 || p.M > 32) return -1;
-  // Column blocks per lane: the most that still give the strips at least one
-  // workgroup per CU over the batch.
-  int cpl = 1;
+// Column blocks per lane of the unsplit kernel: the most that still give the
+// strips at least one workgroup per CU over the batch.
+static int fewrows_cpl(const Problem &p) {
   for (int c = 4; c >= 2; c /= 2) {
     const long long strips = ((long long)p.N + 16 * c - 1) / (16 * c);
-    if (strips * p.batch >= 256) {
-      cpl = c;
-      break;
-    }
+    if (strips * p.batch >= 256) return c;
   }
+  return 1;
+}
+
+int fewrows_round_fill_pct(const Problem &p) {
+  const int c = fewrows_cpl(p);
+  const long long units = ((long long)p.N + 16 * c - 1) / (16 * c) * (long long)p.batch;
+  if (units <= 0) return 0;
+  const long long rounds = (units + 255) / 256;
+  return (int)(units * 100 / (rounds * 256));
+}
+
+int launch_fewrows(const Problem &p, hipStream_t stream) {
+  if (p.M < 1 || p.M > 32) return -1;
+  const int cpl = fewrows_cpl(p);
   const int nc = 16 * cpl;
   const long long blocks = ((long long)p.N + nc - 1) / nc;
   if (blocks > INT_MAX) return -1;
@@ -472,17 +481,24 @@ int launch_fewrows(const Problem &p, hipStream_t stream) {
   return 0;
 }
 
-// The split form's plan: one column block per lane (the strips are then as
-// many as they can be) and as many K chunks as keep strips x chunks within
-// one workgroup per CU (at most four, each at least 128 values of K per
-// wave).  Only for 128 strips (2048 columns) or fewer: with more, two chunks
-// already overfill the CUs, and a second round of workgroups costs more
-// than the unsplit strips' shortfall of memory parallelism (cold, (8, 3072,
-// 2048) 12.5 against 11.5 us unsplit, (16, 4000, 4096) 22.1 against 19.5).
-static bool fewrows_split_plan(const Problem &p, int &splits, int &kchunk, long long &bytes) {
+// The split form's plan: the fewest column blocks per lane (1, 2 or 4) that
+// give at most 128 strips, so that at least two K chunks fit one round of
+// workgroups, and as many chunks as keep strips x chunks within one
+// workgroup per CU (at most four, each at least 128 values of K per wave).
+// Up to 2048 columns that is one block per lane, the strips as many as they
+// can be; past 8192 columns there is no plan.  (16-column strips past 2048
+// columns, two chunks each, overfill the CUs and lose to the unsplit kernel:
+// cold, (8, 3072, 2048) 12.5 against 11.5 us, (16, 4000, 4096) 22.1 against
+// 19.5.)
+static bool fewrows_split_plan(const Problem &p, int &splits, int &kchunk, long long &bytes, int &cpl) {
   splits = 1;
+  cpl = 1;
   if (p.M < 1 || p.M > 32 || p.batch != 1) return false;
-  const long long strips = ((long long)p.N + 15) / 16;
+  long long strips = ((long long)p.N + 15) / 16;
+  while (strips > 128 && cpl < 4) {
+    cpl *= 2;
+    strips = ((long long)p.N + 16 * cpl - 1) / (16 * cpl);
+  }
   if (strips > 128) return false;
   int want = (int)(256 / strips);
   if (want > kFewMaxSplits) want = kFewMaxSplits;
@@ -492,23 +508,24 @@ static bool fewrows_split_plan(const Problem &p, int &splits, int &kchunk, long 
   kchunk = (kchunk + 16 * kFewWaves - 1) / (16 * kFewWaves) * (16 * kFewWaves);
   splits = (p.K + kchunk - 1) / kchunk;
   const int nr = p.M > 16 ? 2 : 1;
-  bytes = kTailFlagBytes + strips * splits * nr * 256LL * 4;
+  bytes = kTailFlagBytes + strips * splits * nr * cpl * 256LL * 4;
   return splits > 1;
 }
 
 long long fewrows_split_bytes(const Problem &p) {
-  int splits = 1, kchunk = 0;
+  int splits = 1, kchunk = 0, cpl = 1;
   long long bytes = 0;
-  return fewrows_split_plan(p, splits, kchunk, bytes) ? bytes : 0;
+  return fewrows_split_plan(p, splits, kchunk, bytes, cpl) ? bytes : 0;
 }
 
 int launch_fewrows_ws(const Problem &p, hipStream_t stream) {
   if (p.M < 1 || p.M > 32) return -1;
-  int splits = 1, kchunk = 0;
+  int splits = 1, kchunk = 0, cpl = 1;
   long long bytes = 0;
-  if (!fewrows_split_plan(p, splits, kchunk, bytes) || p.ws == nullptr || (unsigned long long)bytes > p.ws_bytes)
+  if (!fewrows_split_plan(p, splits, kchunk, bytes, cpl) || p.ws == nullptr ||
+      (unsigned long long)bytes > p.ws_bytes)
     return launch_fewrows(p, stream);
-  const long long strips = ((long long)p.N + 15) / 16;
+  const long long strips = ((long long)p.N + 16 * cpl - 1) / (16 * cpl);
   int krange = (kchunk + kFewWaves - 1) / kFewWaves;
   krange = (krange + 15) / 16 * 16;
   FewSplit fs;
@@ -517,9 +534,9 @@ int launch_fewrows_ws(const Problem &p, hipStream_t stream) {
   fs.part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
   const dim3 grid((unsigned)strips, (unsigned)splits, 1u);
   if (p.M > 16)
-    launch_fewrows_nr<2, true>(p, grid, stream, krange, 1, fs);
+    launch_fewrows_nr<2, true>(p, grid, stream, krange, cpl, fs);
   else
-    launch_fewrows_nr<1, true>(p, grid, stream, krange, 1, fs);
+    launch_fewrows_nr<1, true>(p, grid, stream, krange, cpl, fs);
   return 0;
 }
 

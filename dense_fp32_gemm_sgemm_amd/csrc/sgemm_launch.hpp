@@ -101,14 +101,17 @@ int launch_narrow(const Problem &p, hipStream_t stream);
 // M outside 1..32.
 int launch_fewrows(const Problem &p, hipStream_t stream);
 
-// The same kernel, one batch slice, with a workspace: K split over up to
-// four workgroups per column strip when the strips alone give fewer
-// workgroups than CUs, the chunks' partial blocks added in chunk order by
-// the strip's last chunk; otherwise launch_fewrows.  Returns -1 for M outside
-// 1..32.
+// The same kernel, one batch slice, with a workspace: at most 128 column
+// strips (16, 32 or 64 columns; up to 8192 columns in all), each split into
+// two to four K chunks so that strips x chunks fill at most one workgroup
+// per CU, the chunks' partial blocks added in chunk order by the strip's
+// last chunk; otherwise launch_fewrows.  Returns -1 for M outside 1..32.
 int launch_fewrows_ws(const Problem &p, hipStream_t stream);
 // Workspace bytes of that split (0: it does not apply).
 long long fewrows_split_bytes(const Problem &p);
+// How full (percent) the last round of 256 workgroups is on the unsplit
+// kernel's grid.
+int fewrows_round_fill_pct(const Problem &p);
 
 // Operand alignment classes: an operand may be read with 16-byte vector
 // loads when its base is 16-byte aligned and its leading dimension is a

@@ -180,10 +180,11 @@ int sgemm_strided_batched_ex(int opA, int opB, int M, int N, int K, float alpha,
  * 32-column strips of the full-K kernel split into up to four K ranges when
  * the strips alone leave CUs idle (up to four rows), or, where K is long for
  * the columns or the columns very many, (256-column strip, K chunk)
- * workgroups.  Up to 32 rows and 2048 columns, either orientation of B: the
- * 16-column strips of the matrix-core few-rows kernel split into up to four
- * K chunks, as many as keep one workgroup per CU.  Either way the partials
- * are added in range order by the last range.
+ * workgroups.  Up to 32 rows and 8192 columns: the strips of the
+ * matrix-core few-rows kernel (16 columns, or 32 or 64 past 2048 columns,
+ * at most 128 of them) split into two to four K chunks, as many as keep one
+ * workgroup per CU.  Either way the partials are added in range order by
+ * the last range.
  *
  * Results are bitwise repeatable (each output is one sum in a fixed order; no
  * atomics touch C), in either atomics mode.  The automatic choice takes the

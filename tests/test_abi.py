@@ -311,7 +311,23 @@ def test_select_few_rows_split_through_workspace(lib):
     assert _ws_choice(0, 0, 8, 512, 4096) == "fewrows_m32_ws"
     assert _ws_choice(0, 0, 32, 2048, 4096) == "fewrows_m32_ws"
     assert _ws_choice(0, 0, 1, 2048, 4096) == "skinny_m8_ws"        # vector-unit strips split first
-    assert _ws_choice(0, 0, 8, 3072, 4096) == "fewrows_m32"         # beyond 2048 columns
+    assert _ws_choice(0, 0, 8, 4096, 4096) == "fewrows_m32"         # 256 strips: a whole round
+    assert _ws_choice(0, 1, 8, 3072, 4096) == "fewrows_m32"         # B transposed: unsplit past 2048
+    # past 2048 columns, B untransposed, K >= 4096, the unsplit grid's last
+    # round under 80% full: the split on wider strips, ahead of the vector-unit
+    # strips split over K; up to eight rows only while N*K <= 2^26
+    assert _ws_choice(0, 0, 16, 6144, 4096) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 1, 3072, 8192) == "fewrows_m32_ws"
+    assert _ws_choice(1, 0, 24, 3072, 4096) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 16, 6144, 16384) == "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 4, 6144, 16384) != "fewrows_m32_ws"
+    assert _ws_choice(0, 0, 8, 3072, 2048) != "fewrows_m32_ws"      # K below 4096
+    assert _ws_choice(0, 0, 1, 4096, 4096) == "skinny_m8_ws"        # 256 strips: a whole round
+    assert _ws_choice(0, 0, 8, 9000, 8192) != "fewrows_m32_ws"      # past 8192 columns: no plan
+    assert _ws_choice(0, 0, 24, 6144, 8192) == "mfma16_32x64x64_2x2_sched_splitk"   # 32-row tiles
+    # 96 strips of 32 columns x 2 chunks; 96 strips of 64 columns x 2 chunks
+    assert sg.sgemm_workspace_size(0, 0, 16, 3072, 8192, 1) == 4096 + 96 * 2 * 2 * 1024
+    assert sg.sgemm_workspace_size(0, 0, 16, 6144, 4096, 1) == 4096 + 96 * 2 * 4 * 1024
     assert _ws_choice(0, 0, 8, 512, 8192) != "fewrows_m32_ws"       # too few strips for a long K
     assert _ws_choice(0, 0, 4, 1024, 65536) == "skinny_fixed_m8"    # beyond the measured K
     assert _ws_choice(0, 0, 8, 1024, 1024) == "fewrows_m32"         # K too short to split

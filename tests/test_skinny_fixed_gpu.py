@@ -257,13 +257,16 @@ def test_automatic_choice_with_workspace_takes_split_full_k(shape):
 
 
 # The matrix-core few-rows kernel split over K through the workspace
-# (fewrows_m32_ws): 65 to 128 strips of 16 columns (two to four K chunks),
-# both orientations of B, one and two 16-row blocks, ragged N and K; past
-# 2048 columns the plain kernel.
+# (fewrows_m32_ws): 33 to 128 strips of 16 columns (two to four K chunks),
+# wider strips past 2048 columns (two or four column blocks per lane), both
+# orientations of B, one and two 16-row blocks, ragged N and K; past 8192
+# columns the plain kernel.
 VFW = sg.variant_names().index("fewrows_m32_ws")
 FEW_SPLIT_CASES = [((16, 2048, 2048), False), ((16, 2048, 2048), True), ((8, 1024, 4096), False),
                    ((32, 2048, 3000), True), ((20, 1500, 2200), False), ((3, 1030, 8200), True),
-                   ((8, 520, 4100), False), ((6, 3000, 4096), False)]
+                   ((8, 520, 4100), False), ((6, 3000, 4096), False), ((16, 4096, 4096), True),
+                   ((24, 8000, 2048), False), ((5, 4100, 3000), False), ((9, 6000, 8192), True),
+                   ((8, 9000, 2048), False)]
 
 
 @pytest.mark.parametrize("case", FEW_SPLIT_CASES, ids=lambda c: "%dx%dx%d-%s" % (c[0] + ("NT" if c[1] else "NN",)))
@@ -315,7 +318,8 @@ def test_fewrows_split_transposed_a_padded():
 
 
 @pytest.mark.parametrize("case", [((8, 1024, 8192), False), ((16, 1024, 8192), False), ((4, 1024, 4096), True),
-                                  ((32, 2048, 4096), False), ((1, 1500, 16384), False)],
+                                  ((32, 2048, 4096), False), ((1, 1500, 16384), False),
+                                  ((16, 6144, 4096), False), ((1, 3072, 8192), False)],
                          ids=lambda c: "%dx%dx%d-%s" % (c[0] + ("NT" if c[1] else "NN",)))
 def test_automatic_choice_with_workspace_takes_fewrows_split(case):
     """Through the workspace entry point's automatic choice these shapes take
