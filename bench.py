@@ -1008,11 +1008,11 @@ def run_modes(args):
                 # kernel that reads them once can reach at this size
                 rec["us_read_cold"] = round(read_floor(nb, cold=True), 3)
                 rec["frac_of_read_cold"] = round(rec["us_read_cold"] / t["us_cold"], 4)
-        # judged on the cold time where the bytes bind, else the warm one
+        # rated on the cold time where the bytes bind, else the warm one
         roof = binding_roof(work, nb, us, ceil)
         if roof["bound"] == "hbm" and "us_cold" in t:
             roof = binding_roof(work, nb, t["us_cold"], ceil)
-            roof["judged_on"] = "us_cold"
+            roof["rated_on"] = "us_cold"
         rec.update(roof)
         if args.vendor and args.batch == 1 and v == -1:
             rec.update(vendor_context(prob, steps, min(args.warmup, steps)))
@@ -1153,7 +1153,7 @@ def sweep_md(sweep_path: str, ws_path: str = None) -> str:
         row = "| %dx%dx%d | %s | %.2f | %.2f | %.2f | %s | %s%s | %.2f | %.3f | %.3f | %s | %s | %s |" % (
             key + (r["variant"], r["us_device"], r["tflops_device"], r["us_launch"],
                    "%.2f" % r["us_cold"] if "us_cold" in r else "-", r["bound"],
-                   " (cold)" if r.get("judged_on") == "us_cold" else "", floor, r["frac_of_bound"],
+                   " (cold)" if r.get("rated_on") == "us_cold" else "", floor, r["frac_of_bound"],
                    r["frac_datasheet"], "%.2f" % r["us_read_cold"] if "us_read_cold" in r else "-",
                    "%.2f" % vend if vend else "-",
                    "%.2f" % (vend / r["us_device"]) if vend else "-"))

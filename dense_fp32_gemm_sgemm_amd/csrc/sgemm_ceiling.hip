@@ -1,5 +1,5 @@
 // sgemm_ceiling.hip -- microbenchmarks that measure the ceilings SGEMM is
-// judged against on this GPU.
+// measured against on this GPU.
 //
 // The Tinyforge README (results table and the note below it) makes the point
 // that a percentage of a datasheet peak can be wrong by tens of percent and

@@ -159,7 +159,7 @@ def test_sweep_md_binding_roof_and_vendor_ratio(tmp_path):
             "valu_fma_f32_tflops": 128.0, "hbm_copy_gbs": 4500.0, "hbm_read_gbs": 5900.0,
             "dispatch_floor_us": 1.5}
     rec = {"mode": "sweep", "M": 1, "N": 4096, "K": 4096, "variant": "skinny_m8", "us_device": 12.0,
-           "tflops_device": 2.8, "us_launch": 14.0, "us_cold": 20.0, "bound": "hbm", "judged_on": "us_cold",
+           "tflops_device": 2.8, "us_launch": 14.0, "us_cold": 20.0, "bound": "hbm", "rated_on": "us_cold",
            "floor_us": {"mfma": 0.2, "hbm": 11.4, "latency": 1.5}, "frac_of_bound": 0.57,
            "frac_datasheet": 0.011, "us_read_cold": 11.6, "torch_mm_us_device": 18.0}
     ws = dict(rec, variant="skinny_m8_ws", us_device=13.0, us_cold=15.0)
