@@ -56,7 +56,26 @@ constexpr int kFewMaxSplits = 4;  // K chunks of the split form
 // so that strips x chunks give every CU a workgroup where the strips alone
 // cannot; each chunk's partial blocks go to the workspace as agent-scope
 // stores and the strip's last chunk adds them in chunk order and stores C.
-template <int NR, int CPL, bool TA, bool TB, bool VB, bool SPLIT = false>
+// W consecutive floats of B; NTL: as non-temporal loads, which do not keep
+// the lines in the caches.
+template <bool NTL, int W>
+__device__ __forceinline__ void load_b_words(float *dst, const float *src) {
+  if constexpr (NTL) {
+    if constexpr (W == 4) {
+      const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(src));
+      dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+    } else if constexpr (W == 2) {
+      const floatx2 v = __builtin_nontemporal_load(reinterpret_cast<const floatx2 *>(src));
+      dst[0] = v[0]; dst[1] = v[1];
+    } else {
+      dst[0] = __builtin_nontemporal_load(src);
+    }
+  } else {
+    __builtin_memcpy(dst, src, W * sizeof(float));
+  }
+}
+
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SPLIT = false, bool NTL = false>
 __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange, int kchunk,
                                                                  unsigned *flags, float *part) {
   select_slice(p);
@@ -98,10 +117,10 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
       Cols b;
       if constexpr (VB) {
         // Whole groups: a group past N repeats the last one (never stored).
-        __builtin_memcpy(b.v, row + min(c0, p.N - CPL), sizeof(b.v));
+        load_b_words<NTL, CPL>(b.v, row + min(c0, p.N - CPL));
       } else {
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) b.v[e] = row[min(c0 + e, p.N - 1)];
+        for (int e = 0; e < CPL; ++e) load_b_words<NTL, 1>(&b.v[e], row + min(c0 + e, p.N - 1));
       }
       return b;
     };
@@ -227,9 +246,9 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
     for (int c = 0; c < CPL; ++c) brow[c] = p.B + (size_t)min(n0 + 16 * c + li, p.N - 1) * ldb;
     auto load_b4 = [&](int c, int k) -> floatx4 {
-      floatx4 v;
-      __builtin_memcpy(&v, brow[c] + k, sizeof(v));
-      return v;
+      float w[4];
+      load_b_words<NTL, 4>(w, brow[c] + k);
+      return floatx4{w[0], w[1], w[2], w[3]};
     };
     auto load_a4 = [&](int r, int k) -> floatx4 {
       if constexpr (!TA) {
@@ -403,30 +422,30 @@ struct FewSplit {
   float *part = nullptr;
 };
 
-template <int NR, int CPL, bool TA, bool TB, bool VB, bool SP>
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SP, bool NTL = false>
 void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange, const FewSplit &fs) {
-  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB, SP>), grid, dim3(kFewWaves * 64), 0, stream, p, krange,
+  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB, SP, NTL>), grid, dim3(kFewWaves * 64), 0, stream, p, krange,
                fs.kchunk, fs.flags, fs.part);
 }
 
-template <int NR, int CPL, bool TB, bool SP>
+template <int NR, int CPL, bool TB, bool SP, bool NTL = false>
 void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int krange, bool vb, const FewSplit &fs) {
   if (p.ta) {
     if (vb)
-      launch_fewrows_t<NR, CPL, true, TB, true, SP>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, true, TB, true, SP, NTL>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, true, TB, false, SP>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, true, TB, false, SP, NTL>(p, grid, stream, krange, fs);
   } else {
     if (vb)
-      launch_fewrows_t<NR, CPL, false, TB, true, SP>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, false, TB, true, SP, NTL>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, false, TB, false, SP>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, false, TB, false, SP, NTL>(p, grid, stream, krange, fs);
   }
 }
 
-template <int NR, bool SP>
+template <int NR, bool SP, bool NTL = false>
 void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl, const FewSplit &fs) {
-  if (p.tb) {
+  if (p.tb) {  // (non-temporal loads only for an untransposed B)
     if (cpl == 4)
       launch_fewrows_ta<NR, 4, true, SP>(p, grid, stream, krange, false, fs);
     else if (cpl == 2)
@@ -437,11 +456,11 @@ void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int kran
   }
   const bool vb = p.N % cpl == 0;
   if (cpl == 4)
-    launch_fewrows_ta<NR, 4, false, SP>(p, grid, stream, krange, vb, fs);
+    launch_fewrows_ta<NR, 4, false, SP, NTL>(p, grid, stream, krange, vb, fs);
   else if (cpl == 2)
-    launch_fewrows_ta<NR, 2, false, SP>(p, grid, stream, krange, vb, fs);
+    launch_fewrows_ta<NR, 2, false, SP, NTL>(p, grid, stream, krange, vb, fs);
   else
-    launch_fewrows_ta<NR, 1, false, SP>(p, grid, stream, krange, vb, fs);
+    launch_fewrows_ta<NR, 1, false, SP, NTL>(p, grid, stream, krange, vb, fs);
 }
 }  // namespace
 
@@ -474,10 +493,26 @@ int launch_fewrows(const Problem &p, hipStream_t stream) {
   krange = (krange + 15) / 16 * 16;
   const dim3 grid((unsigned)blocks, 1u, (unsigned)p.batch);
   const FewSplit none;
-  if (p.M > 16)
-    launch_fewrows_nr<2, false>(p, grid, stream, krange, cpl, none);
-  else
-    launch_fewrows_nr<1, false>(p, grid, stream, krange, cpl, none);
+  // An untransposed B of 512 MiB or more (twice the last-level cache) is
+  // read with non-temporal loads: no call finds it in a cache anyway, and
+  // streaming past the caches runs 9-14% faster ((1, 16384, 16384) 175 against
+  // 192 us, (16, 16384, 8192) 88.8 against 95.9).  Below that they lose when
+  // B stays cached between calls ((1, 4096, 16384) 69.9 against 49.2 us), and
+  // with B transposed always (each line is read in two halves by successive
+  // loads, the second of which then misses: (16, 16384, 8192) 156 against
+  // 126 us).
+  const bool ntl = !p.tb && (long long)p.N * p.K * p.batch >= (1LL << 27);
+  if (p.M > 16) {
+    if (ntl)
+      launch_fewrows_nr<2, false, true>(p, grid, stream, krange, cpl, none);
+    else
+      launch_fewrows_nr<2, false>(p, grid, stream, krange, cpl, none);
+  } else {
+    if (ntl)
+      launch_fewrows_nr<1, false, true>(p, grid, stream, krange, cpl, none);
+    else
+      launch_fewrows_nr<1, false>(p, grid, stream, krange, cpl, none);
+  }
   return 0;
 }
 

@@ -658,6 +658,32 @@ def test_few_rows_matrix_core_kernel(shape):
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "few rows %s %s%s int" % (shape, ta, tb))
 
 
+@pytest.mark.parametrize("shape", [(4, 16384, 8192), (3, 8201, 16400), (20, 16384, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_matrix_core_kernel_streaming_b(shape):
+    """An untransposed B of 512 MiB or more goes through the matrix-core
+    few-rows kernel's non-temporal loads: four-column vector loads, one-column
+    loads (N odd), two 16-row blocks (M = 20), a padded / misaligned copy;
+    real data to 1e-5 and integer data exactly."""
+    M, N, K = shape
+    assert N * K >= 1 << 27
+    v = VNAMES.index("fewrows_m32")
+    A, B, Cin = draw(M, N, K, seed=M + N, with_c=True)
+    say("few rows streaming B", shape)
+    C = run(A, B, Cin, 1.5, 0.5, variant=v, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "few rows streaming %s" % (shape,))
+    if M == 4:
+        say("few rows streaming B padded", shape)
+        C = run(A, B, Cin, 1.5, 0.5, variant=v, lds=(K + 3, N + 1, N + 2), offsets=(1, 3, 2),
+                check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "few rows streaming %s padded" % (shape,))
+    del A, B
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + 1, kind="int", with_c=True)
+    say("few rows streaming B int", shape)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "few rows streaming %s int" % (shape,))
+
+
 @pytest.mark.parametrize("batch,N", [(16, 1000), (8, 1000), (16, 1001), (3, 130)],
                          ids=lambda x: str(x))
 def test_few_rows_matrix_core_kernel_batched(batch, N):

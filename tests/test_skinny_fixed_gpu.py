@@ -317,6 +317,42 @@ def test_fewrows_split_transposed_a_padded():
     assert counters_zero(ws)
 
 
+@pytest.mark.parametrize("case", [((16, 1024, 4096), False), ((24, 6144, 4096), False), ((8, 2048, 2048), True)],
+                         ids=lambda c: "%dx%dx%d-%s" % (c[0] + ("NT" if c[1] else "NN",)))
+def test_fewrows_split_in_a_graph(case):
+    """The matrix-core few-rows split (16-column strips, and 64-column strips
+    past 2048 columns) captured in a HIP graph replays exactly, with eager
+    work between the replays (each replay's last chunks reset the counters)."""
+    (M, N, K), tb = case
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N, kind="int", with_c=True)
+    ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0)
+    Bs = np.ascontiguousarray(Bi.T) if tb else Bi
+    dA, dB, dC0 = (torch.from_numpy(x).cuda() for x in (Ai, Bs, Ci))
+    out = torch.empty_like(dC0)
+    ws = new_ws()
+    say("few-rows split in a graph", (M, N, K), tb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.add(dC0, 0.0, out=out)
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=VFW, workspace=ws, trans_b=tb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        torch.add(dC0, 0.0, out=out)
+        sg.gemm(dA, dB, out, 1.0, 1.0, variant=VFW, workspace=ws, trans_b=tb)
+    for i in range(3):
+        junk = torch.randn(4096, device="cuda")
+        float(junk.abs().sum())
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref), "replay %d" % i
+        assert counters_zero(ws)
+
+
 @pytest.mark.parametrize("case", [((8, 1024, 8192), False), ((16, 1024, 8192), False), ((4, 1024, 4096), True),
                                   ((32, 2048, 4096), False), ((1, 1500, 16384), False),
                                   ((16, 6144, 4096), False), ((1, 3072, 8192), False)],
