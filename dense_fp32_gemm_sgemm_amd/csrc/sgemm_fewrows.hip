@@ -75,7 +75,9 @@ __device__ __forceinline__ void load_b_words(float *dst, const float *src) {
   }
 }
 
-template <int NR, int CPL, bool TA, bool TB, bool VB, bool SPLIT = false, bool NTL = false>
+// NTL (B untransposed): B read with non-temporal loads.  ILV (B transposed):
+// the waves take batches of K groups in turn rather than one range each.
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SPLIT = false, bool NTL = false, bool ILV = false>
 __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int krange, int kchunk,
                                                                  unsigned *flags, float *part) {
   select_slice(p);
@@ -260,16 +262,15 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
         return floatx4{q[0], q[lda], q[2 * lda], q[3 * lda]};
       }
     };
-    // Groups of 16 k: slot sl takes k = kb + 16t + 4sl .. + 3.  A lane's A
-    // vector serves all CPL column blocks, its B vector all NR row blocks.
+    // Groups of 16 k: in group g slot sl takes k = 16g + 4sl .. + 3.  A
+    // lane's A vector serves all CPL column blocks, its B vector all NR row
+    // blocks.
     constexpr int UN = (kFewUnroll / (NR * CPL)) > 1 ? kFewUnroll / (NR * CPL) : 2;
-    const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
-    int t = 0;
-    for (; t + UN <= nfull; t += UN) {
+    auto batch = [&](int g0) {  // groups g0 .. g0 + UN - 1, loads first
       floatx4 a[UN][NR], b[UN][CPL];
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const int k = kb + 16 * (t + u) + 4 * sl;
+        const int k = 16 * (g0 + u) + 4 * sl;
 #pragma unroll
         for (int r = 0; r < NR; ++r) a[u][r] = load_a4(r, k);
 #pragma unroll
@@ -285,9 +286,9 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
               acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][r][e], b[u][c][e], acc[r][c], 0, 0, 0);
-    }
-    for (; t < nfull; ++t) {
-      const int k = kb + 16 * t + 4 * sl;
+    };
+    auto one = [&](int g) {
+      const int k = 16 * g + 4 * sl;
       floatx4 b[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) b[c] = load_b4(c, k);
@@ -300,18 +301,18 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
           for (int c = 0; c < CPL; ++c)
             acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[c][e], acc[r][c], 0, 0, 0);
       }
-    }
-    // The rest of the range (fewer than 16 k): element by element, k < ke only.
-    const int kt = kb + 16 * nfull;
-    if (kt < ke) {
+    };
+    // Fewer than 16 k from kt to kend: element by element, k < kend only
+    // (kt itself stands in for the k past kend, whose values are replaced).
+    auto tail = [&](int kt, int kend) {
       floatx4 b[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = kt + 4 * sl + e;
-          const bool in = k < ke;
-          b[c][e] = in ? brow[c][in ? k : kb] : 0.0f;
+          const bool in = k < kend;
+          b[c][e] = in ? brow[c][in ? k : kt] : 0.0f;
         }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = kt + 4 * sl + e;
-          const bool in = k < ke;
-          const int kk = in ? k : kb;
+          const bool in = k < kend;
+          const int kk = in ? k : kt;
           const float av = TA ? p.A[(size_t)kk * lda + arow[r]] : p.A[(size_t)arow[r] * lda + kk];
           a[e] = in ? av : 0.0f;
         }
@@ -330,6 +331,25 @@ __global__ __launch_bounds__(kFewWaves * 64) void fewrows_kernel(Problem p, int 
           for (int c = 0; c < CPL; ++c)
             acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[c][e], acc[r][c], 0, 0, 0);
       }
+    };
+    if constexpr (ILV) {
+      // Batches of UN groups dealt to the waves in turn, so that the eight
+      // waves read neighbouring bytes of each row of B together; the groups
+      // after the last whole batch and the ragged end go to the wave next
+      // in turn.
+      const int G = p.K / 16, nch = G / UN, rw = nch % kFewWaves;
+      for (int c = w; c < nch; c += kFewWaves) batch(c * UN);
+      if (w == rw) {
+        for (int g = nch * UN; g < G; ++g) one(g);
+        if (16 * G < p.K) tail(16 * G, p.K);
+      }
+    } else {
+      const int g0 = kb / 16;  // (krange is a multiple of 16)
+      const int nfull = (ke > kb) ? (ke - kb) / 16 : 0;
+      int t = 0;
+      for (; t + UN <= nfull; t += UN) batch(g0 + t);
+      for (; t < nfull; ++t) one(g0 + t);
+      if (kb + 16 * nfull < ke) tail(kb + 16 * nfull, ke);
     }
   }
 
@@ -422,36 +442,36 @@ struct FewSplit {
   float *part = nullptr;
 };
 
-template <int NR, int CPL, bool TA, bool TB, bool VB, bool SP, bool NTL = false>
+template <int NR, int CPL, bool TA, bool TB, bool VB, bool SP, bool NTL = false, bool ILV = false>
 void launch_fewrows_t(const Problem &p, dim3 grid, hipStream_t stream, int krange, const FewSplit &fs) {
-  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB, SP, NTL>), grid, dim3(kFewWaves * 64), 0, stream, p, krange,
+  SG950_LAUNCH((fewrows_kernel<NR, CPL, TA, TB, VB, SP, NTL, ILV>), grid, dim3(kFewWaves * 64), 0, stream, p, krange,
                fs.kchunk, fs.flags, fs.part);
 }
 
-template <int NR, int CPL, bool TB, bool SP, bool NTL = false>
+template <int NR, int CPL, bool TB, bool SP, bool NTL = false, bool ILV = false>
 void launch_fewrows_ta(const Problem &p, dim3 grid, hipStream_t stream, int krange, bool vb, const FewSplit &fs) {
   if (p.ta) {
     if (vb)
-      launch_fewrows_t<NR, CPL, true, TB, true, SP, NTL>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, true, TB, true, SP, NTL, ILV>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, true, TB, false, SP, NTL>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, true, TB, false, SP, NTL, ILV>(p, grid, stream, krange, fs);
   } else {
     if (vb)
-      launch_fewrows_t<NR, CPL, false, TB, true, SP, NTL>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, false, TB, true, SP, NTL, ILV>(p, grid, stream, krange, fs);
     else
-      launch_fewrows_t<NR, CPL, false, TB, false, SP, NTL>(p, grid, stream, krange, fs);
+      launch_fewrows_t<NR, CPL, false, TB, false, SP, NTL, ILV>(p, grid, stream, krange, fs);
   }
 }
 
-template <int NR, bool SP, bool NTL = false>
+template <int NR, bool SP, bool NTL = false, bool ILV = false>
 void launch_fewrows_nr(const Problem &p, dim3 grid, hipStream_t stream, int krange, int cpl, const FewSplit &fs) {
   if (p.tb) {  // (non-temporal loads only for an untransposed B)
     if (cpl == 4)
-      launch_fewrows_ta<NR, 4, true, SP>(p, grid, stream, krange, false, fs);
+      launch_fewrows_ta<NR, 4, true, SP, false, ILV>(p, grid, stream, krange, false, fs);
     else if (cpl == 2)
-      launch_fewrows_ta<NR, 2, true, SP>(p, grid, stream, krange, false, fs);
+      launch_fewrows_ta<NR, 2, true, SP, false, ILV>(p, grid, stream, krange, false, fs);
     else
-      launch_fewrows_ta<NR, 1, true, SP>(p, grid, stream, krange, false, fs);
+      launch_fewrows_ta<NR, 1, true, SP, false, ILV>(p, grid, stream, krange, false, fs);
     return;
   }
   const bool vb = p.N % cpl == 0;
@@ -501,15 +521,30 @@ int launch_fewrows(const Problem &p, hipStream_t stream) {
   // with B transposed always (each line is read in two halves by successive
   // loads, the second of which then misses: (16, 16384, 8192) 156 against
   // 126 us).
-  const bool ntl = !p.tb && (long long)p.N * p.K * p.batch >= (1LL << 27);
+  const long long nk = (long long)p.N * p.K * p.batch;
+  const bool ntl = !p.tb && nk >= (1LL << 27);
+  // A transposed B of 256 MiB or more: the waves take batches of groups in
+  // turn instead of one contiguous K range each, so a workgroup's reads of
+  // each row of B arrive together.  With one range per wave the reads kept
+  // fewer requests in flight at a longer latency (30.5k at 2210 cycles
+  // against 34.7k at 1860 for B untransposed, (16, 16384, 8192)): (16,
+  // 16384, 8192) 125.6 -> 110.4 us, (1, 16384, 8192) 127 -> 102, (8, 8192,
+  // 8192) cold 88 -> 62.  Smaller, it measured within a few percent either
+  // way ((1, 4096, 4096) 12.1 against 12.7 us, (16, 4096, 4096) cold 20.4
+  // against 19.2).
+  const bool ilv = p.tb && nk >= (1LL << 26);
   if (p.M > 16) {
     if (ntl)
       launch_fewrows_nr<2, false, true>(p, grid, stream, krange, cpl, none);
+    else if (ilv)
+      launch_fewrows_nr<2, false, false, true>(p, grid, stream, krange, cpl, none);
     else
       launch_fewrows_nr<2, false>(p, grid, stream, krange, cpl, none);
   } else {
     if (ntl)
       launch_fewrows_nr<1, false, true>(p, grid, stream, krange, cpl, none);
+    else if (ilv)
+      launch_fewrows_nr<1, false, false, true>(p, grid, stream, krange, cpl, none);
     else
       launch_fewrows_nr<1, false>(p, grid, stream, krange, cpl, none);
   }

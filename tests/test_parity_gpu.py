@@ -684,6 +684,32 @@ def test_few_rows_matrix_core_kernel_streaming_b(shape):
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "few rows streaming %s int" % (shape,))
 
 
+@pytest.mark.parametrize("shape,ta", [((16, 8192, 8192), False), ((20, 8200, 8193), True),
+                                      ((3, 65536, 1024), False)],
+                         ids=lambda x: "x".join(map(str, x)) if isinstance(x, tuple) else ("TA" if x else "NA"))
+def test_few_rows_matrix_core_kernel_streaming_bt(shape, ta):
+    """A transposed B of 256 MiB or more: the waves take batches of K groups
+    in turn (the last whole batch, the groups after it and a ragged end on
+    the wave next in turn); A as stored or transposed, two 16-row blocks
+    (M = 20), one to four column blocks per lane; real data to 1e-5 and
+    integer data exactly."""
+    M, N, K = shape
+    assert N * K >= 1 << 26
+    v = VNAMES.index("fewrows_m32")
+    A, B, Cin = draw(M, N, K, seed=M + N + 5, with_c=True)
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T)
+    say("few rows streaming B^T", shape, ta)
+    C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=True, check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "few rows streaming B^T %s" % (shape,))
+    del A, B, Bs
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + 6, kind="int", with_c=True)
+    Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+    say("few rows streaming B^T int", shape, ta)
+    C = run(Ais, np.ascontiguousarray(Bi.T), Ci, 1.0, 1.0, variant=v, trans_a=ta, trans_b=True)
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "few rows streaming B^T %s int" % (shape,))
+
+
 @pytest.mark.parametrize("batch,N", [(16, 1000), (8, 1000), (16, 1001), (3, 130)],
                          ids=lambda x: str(x))
 def test_few_rows_matrix_core_kernel_batched(batch, N):
