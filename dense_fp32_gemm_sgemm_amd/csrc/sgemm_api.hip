@@ -473,17 +473,22 @@ int choose_variant(const Problem &p, bool atomics) {
     const bool few_ws = !ws_split && p.N <= 2048 && few_fits;
     if (few_ws && p.M <= 16 && p.K <= (p.N > 1008 ? 32768 : 4096)) return kFewRowsWs;
     // Past 2048 columns (wider strips, at most 128 of them), with B
-    // untransposed, where the unsplit kernel's grid fills less than 80% of
-    // its last round of workgroups (3072 columns: 192 strips, 6144: 384) and
-    // K is at least 4096 -- ahead of the vector-unit strips split over K as
-    // well; up to eight rows only while N*K <= 2^26 (beyond it the
-    // fixed-order vector-unit split streams B better: (4, 6144, 16384) 69 us
-    // against 78).  Cold: (16, 6144, 4096) 25.4 against 46.6 us unsplit,
-    // (16, 3072, 8192) 31.3 against 45.0, (1, 3072, 8192) 25.0 against 29.9
-    // on the vector-unit split, (8, 6144, 8192) 42.8 against 78.9.  (With B
-    // transposed the unsplit kernel keeps up: the split ran slower cold.)
+    // untransposed and K at least 4096, where the unsplit kernel's grid
+    // fills less than 80% of its last round of workgroups (3072 columns: 192
+    // strips, 6144: 384) -- ahead of the vector-unit strips split over K as
+    // well -- or, above four rows, where its strips are 16 columns wide (up
+    // to about 8192 columns: each row of B read in half lines); up to eight
+    // rows only while N*K <= 2^26 (beyond it the fixed-order vector-unit
+    // split streams B better: (4, 6144, 16384) 69 us against 78).  Cold:
+    // (16, 6144, 4096) 25.4 against 46.6 us unsplit, (16, 3072, 8192) 31.3
+    // against 45.0, (1, 3072, 8192) 25.0 against 29.9 on the vector-unit
+    // split, (8, 6144, 8192) 42.8 against 78.9, (16, 4096, 16384) 64.8
+    // against 85.3, (24, 4096, 4096) 23.2 against 28.4; at four rows or
+    // fewer and 4096 columns the vector-unit split stays ahead ((4, 4096,
+    // 4096) 16.5 against 19.8).  (With B transposed the unsplit kernel keeps
+    // up: the split ran slower cold.)
     if (few_fits && !p.tb && p.N > 2048 && p.K >= 4096 && (p.M > 8 || (long long)p.N * p.K <= (1LL << 26)) &&
-        fewrows_round_fill_pct(p) < 80)
+        (fewrows_round_fill_pct(p) < 80 || (p.M > 4 && fewrows_strip_cols(p) == 16)))
       return kFewRowsWs;
     // A K of 16N or more: too few columns for the streaming kernels' strips
     // and a long K each; split-K 64x64 tiles spread it over the CUs

@@ -494,6 +494,8 @@ static int fewrows_cpl(const Problem &p) {
   return 1;
 }
 
+int fewrows_strip_cols(const Problem &p) { return 16 * fewrows_cpl(p); }
+
 int fewrows_round_fill_pct(const Problem &p) {
   const int c = fewrows_cpl(p);
   const long long units = ((long long)p.N + 16 * c - 1) / (16 * c) * (long long)p.batch;

@@ -110,8 +110,9 @@ int launch_fewrows_ws(const Problem &p, hipStream_t stream);
 // Workspace bytes of that split (0: it does not apply).
 long long fewrows_split_bytes(const Problem &p);
 // How full (percent) the last round of 256 workgroups is on the unsplit
-// kernel's grid.
+// kernel's grid, and the columns of its strips (16, 32 or 64).
 int fewrows_round_fill_pct(const Problem &p);
+int fewrows_strip_cols(const Problem &p);
 
 // Operand alignment classes: an operand may be read with 16-byte vector
 // loads when its base is 16-byte aligned and its leading dimension is a

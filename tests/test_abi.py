@@ -311,11 +311,14 @@ def test_select_few_rows_split_through_workspace(lib):
     assert _ws_choice(0, 0, 8, 512, 4096) == "fewrows_m32_ws"
     assert _ws_choice(0, 0, 32, 2048, 4096) == "fewrows_m32_ws"
     assert _ws_choice(0, 0, 1, 2048, 4096) == "skinny_m8_ws"        # vector-unit strips split first
-    assert _ws_choice(0, 0, 8, 4096, 4096) == "fewrows_m32"         # 256 strips: a whole round
+    assert _ws_choice(0, 0, 8, 8192, 4096) == "fewrows_m32"         # 256 strips of 32: a whole round
+    assert _ws_choice(0, 0, 8, 4096, 4096) == "fewrows_m32_ws"      # unsplit strips of 16 columns
+    assert _ws_choice(0, 0, 4, 4096, 4096) == "skinny_m8_ws"        # up to 4 rows: the VALU split
     assert _ws_choice(0, 1, 8, 3072, 4096) == "fewrows_m32"         # B transposed: unsplit past 2048
     # past 2048 columns, B untransposed, K >= 4096, the unsplit grid's last
-    # round under 80% full: the split on wider strips, ahead of the vector-unit
-    # strips split over K; up to eight rows only while N*K <= 2^26
+    # round under 80% full (or, above four rows, its strips 16 columns wide):
+    # the split on wider strips, ahead of the vector-unit strips split over
+    # K; up to eight rows only while N*K <= 2^26
     assert _ws_choice(0, 0, 16, 6144, 4096) == "fewrows_m32_ws"
     assert _ws_choice(0, 0, 1, 3072, 8192) == "fewrows_m32_ws"
     assert _ws_choice(1, 0, 24, 3072, 4096) == "fewrows_m32_ws"
