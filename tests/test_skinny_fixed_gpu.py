@@ -135,7 +135,7 @@ def test_fixed_form_in_a_graph():
         assert counters_zero(ws)
 
 
-@pytest.mark.parametrize("shape", [(1, 512, 32768), (4, 1024, 65536), (1, 65536, 2048), (8, 4096, 16384)],
+@pytest.mark.parametrize("shape", [(1, 512, 32768), (4, 1024, 65536), (1, 65536, 2048), (8, 5000, 16384)],
                          ids=lambda s: "%dx%dx%d" % s)
 def test_automatic_choice_with_workspace_takes_fixed_form(shape):
     """Through the workspace entry point's automatic choice these shapes
