@@ -8,7 +8,9 @@
 //
 // A workgroup owns a strip of columns of C and all of its rows (one or two
 // 16-row blocks, sharing every load of B); its eight waves take eight
-// contiguous K ranges.  Each wave accumulates 16 x 16 blocks
+// contiguous K ranges (a transposed B of 256 MiB or more: batches of K groups
+// in turn, so that the waves read neighbouring bytes of each row of B
+// together).  Each wave accumulates 16 x 16 blocks
 // with v_mfma_f32_16x16x4f32, whose lane l supplies A[l%16][slot l/16] and
 // B[slot][l%16] for the four k slots of one instruction; the k behind a slot
 // is free to choose as long as A and B agree on it:
@@ -26,7 +28,9 @@
 //
 // Loads of eight steps are issued before their first use (with B
 // untransposed and four or more blocks per wave, one group's loads are
-// issued before the previous group's matrix instructions).  Rows past M read
+// issued before the previous group's matrix instructions); an untransposed
+// B of 512 MiB or more, which no call finds in a cache, is read with
+// non-temporal loads.  Rows past M read
 // row M-1 and columns past N read column N-1 (in bounds, never stored); k
 // past the end of a wave's range is skipped by selection, so a NaN or Inf
 // outside the matrices cannot leak in.  The eight waves' blocks are added
