@@ -1044,7 +1044,18 @@ CHOICE_FAMILIES = (
     ("128x128 w8 tail", "mfma16_128x128x64_4x2_sched_tail", 128, 128, False),
     ("128x64 tail", "mfma16_128x64x64_4x2_sched_tail", 128, 64, False),
     ("64x64 tail", "mfma16_64x64x64_4x2_sched_tail", 64, 64, False),
+    ("edge split", "edge_split", 1, 1, False),
 )
+
+
+def has_thin_edge(M, N, K):
+    """Whether the library's edge split applies: K of about 1024 or more and
+    a dimension that overruns some tile family's tiles by 1 to 16 (rows:
+    tiles of 256, 128, 64 or 32; columns: 256, 128 or 64)."""
+    if K < 1000:
+        return False
+    return (any(M > t and 1 <= M % t <= 16 for t in (256, 128, 64, 32)) or
+            any(N > t and 1 <= N % t <= 16 for t in (256, 128, 64)))
 
 
 def choice_table(args):
@@ -1061,6 +1072,8 @@ def choice_table(args):
         for label, vname, bm, bn, short_m in CHOICE_FAMILIES:
             if not ((M >= bm or (short_m and ops[0] == "N")) and N >= bn):
                 continue  # the family's loop does not run this shape
+            if vname == "edge_split" and not has_thin_edge(M, N, K):
+                continue  # (it would run the automatic choice whole)
             v = names.index(vname)
             fn = prob.launcher(v)
             fn()

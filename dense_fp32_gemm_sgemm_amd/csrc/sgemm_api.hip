@@ -74,6 +74,9 @@ int launch_narrow_any(const Problem &p, hipStream_t s) {
   return 0;
 }
 
+// A thin edge of C split off (defined with the automatic choice below).
+int launch_edge_split(const Problem &p, hipStream_t s);
+
 // The matrix-core few-rows kernel covers M <= 32; as a forced variant on a
 // taller problem it runs on row blocks of 32.
 int launch_fewrows_any(const Problem &p, hipStream_t s) {
@@ -146,6 +149,7 @@ const Variant kVariants[] = {
     {"skinny_fixed_m8", launch_skinny_fixed_any},
     {"skinny_m8_ws", launch_skinny_ws_any},
     {"fewrows_m32_ws", launch_fewrows_ws_any},
+    {"edge_split", launch_edge_split},
 };
 constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -188,6 +192,7 @@ enum VariantId {
   kSkinnyFixed = 35,
   kSkinnyWs = 36,
   kFewRowsWs = 37,
+  kEdgeSplit = 38,
 };
 
 constexpr int kNoKernel = -100;
@@ -424,6 +429,85 @@ bool skinny_full_k(const Problem &p) {
   return !p.tb && ((long long)p.N + 31) / 32 * p.batch >= 64 && (long long)p.N * p.K <= (1LL << 26);
 }
 
+// Edge split: a dimension of C that overruns a family's tiles by a thin edge
+// (1 to 16 rows or columns) costs that family a whole extra row or column
+// of tiles -- at (4095, 4097, 1023) the 256x256 tiles number 16 x 17, one
+// round of 256 and a second of 16 one-column tiles.  Splitting the edge off
+// leaves the bulk to the tiles (whole rounds) and gives the thin strip to
+// the few-columns or few-rows kernel, one launch after the other on the
+// stream.  side 0: columns (keep = the bulk's N), 1: rows (keep = its M).
+struct EdgePlan {
+  int side = -1;
+  int keep = 0;
+  double rate = 0.0;  // predicted TFLOP/s of the two launches together
+};
+
+// The bulk (thin = false) or the thin strip of C and the operands it reads.
+Problem edge_part(const Problem &p, int side, int keep, bool thin) {
+  Problem q = p;
+  if (side == 0) {
+    if (!thin) {
+      q.N = keep;
+    } else {
+      q.N = p.N - keep;
+      q.C = p.C + keep;
+      q.B = p.tb ? p.B + (size_t)keep * (size_t)p.ldb : p.B + keep;
+    }
+  } else {
+    if (!thin) {
+      q.M = keep;
+    } else {
+      q.M = p.M - keep;
+      q.C = p.C + (size_t)keep * (size_t)p.ldc;
+      q.A = p.ta ? p.A + keep : p.A + (size_t)keep * (size_t)p.lda;
+    }
+  }
+  return q;
+}
+
+// Microseconds a thin strip takes: a launch and a stream over its operands at
+// 4 TB/s, slower when its long side is short of 4096 (the few-columns and
+// few-rows kernels spread over that side).  Measured (us, alone, warm):
+// (4095, 1, 1023) 6.5 (model 7.2), (8191, 1, 8191) 55 (70), (512, 1, 4096)
+// 12.0 (19.8), (2047, 1, 4095) 14.9 (19.8), (1, 8192, 1024) 5.8 (11.4).
+double thin_us(const Problem &t) {
+  const double bytes = 4.0 * ((double)t.M * t.K + (double)t.K * t.N + (double)t.M * t.N) * (double)t.batch;
+  const double side = (double)(t.M > t.N ? t.M : t.N) * (double)t.batch;
+  return 3.0 + bytes / (4.0e6 * fmin(1.0, side / 4096.0));
+}
+
+// depth 1: the bulk may itself split its other edge off (both dimensions
+// thin, as at (4097, 4097, 4097)); it then goes through the automatic choice
+// again, which takes that second split by the same prediction.
+EdgePlan edge_plan(const Problem &p, int depth = 1) {
+  EdgePlan best;
+  // (the family rates are fitted from a K of about 1024 up: at (1023, 8193,
+  // 257) the split ran 64 against 75 TFLOP/s on whole 64x64 tiles)
+  if (p.K < 1000) return best;
+  const double flops = 2.0 * (double)p.M * p.N * p.K * (double)p.batch;
+  for (const TileFamily &f : kTileFamilies) {
+    for (int side = 0; side < 2; ++side) {
+      const int dim = side == 0 ? p.N : p.M, tile = side == 0 ? f.bn : f.bm;
+      const int r = dim % tile;
+      if (r < 1 || r > 16 || dim <= tile) continue;
+      const Problem bulk = edge_part(p, side, dim - r, false);
+      if (!family_fits(f, bulk)) continue;
+      double rb = family_rate(f, bulk);
+      if (depth > 0) rb = fmax(rb, edge_plan(bulk, depth - 1).rate);
+      if (rb <= 0.0) continue;
+      const double t = 2.0 * (double)bulk.M * bulk.N * bulk.K * (double)bulk.batch / (rb * 1e6) +
+                       thin_us(edge_part(p, side, dim - r, true));
+      const double rate = flops / (t * 1e6);
+      if (rate > best.rate) {
+        best.side = side;
+        best.keep = dim - r;
+        best.rate = rate;
+      }
+    }
+  }
+  return best;
+}
+
 // The automatic choice.  atomics: whether variants that add partial sums into
 // C with atomics (an order the hardware decides) may be taken.
 int choose_variant(const Problem &p, bool atomics) {
@@ -600,11 +684,26 @@ int choose_variant(const Problem &p, bool atomics) {
     const double r = tail_rate(tf, p);
     if (r > best_rate) best_rate = r, best = tf.variant;
   }
+  // A thin edge split off, where that is predicted faster by 3% or more.
+  const EdgePlan ep = edge_plan(p);
+  if (ep.side >= 0 && ep.rate > 1.03 * best_rate) return kEdgeSplit;
   // No family's tile fits C (fewer than 32 rows with A transposed, or fewer
   // than 64 columns): few tiles with a long K still split K over workgroups.
   if (best_rate < 0.0 && atomics && ((t64 < cus / 2 && p.K >= 1024) || (t64 < cus && p.K >= 2048)))
     return kMfma16_64x64x64_w8_pipe_splitk;
   return best;
+}
+
+// The edge split: the bulk and the thin strip, each through the automatic
+// choice, one after the other on the stream.  Without a thin edge (as a
+// forced variant) the whole problem goes through the automatic choice.
+int launch_edge_split(const Problem &p, hipStream_t s) {
+  const bool atomics = g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED;
+  const EdgePlan ep = edge_plan(p);
+  if (ep.side < 0) return kVariants[choose_variant(p, atomics)].launch(p, s);
+  const Problem bulk = edge_part(p, ep.side, ep.keep, false), thin = edge_part(p, ep.side, ep.keep, true);
+  if (kVariants[choose_variant(bulk, atomics)].launch(bulk, s) != 0) return -1;
+  return kVariants[choose_variant(thin, atomics)].launch(thin, s);
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other
@@ -698,6 +797,26 @@ int select(int opA, int opB, int M, int N, int K, float alpha, const float *A, i
   return plan_fits(p, v, false) ? v : SGEMM_ERR_GRID;
 }
 
+// Workspace variant v uses on this problem (0: none); the edge split's two
+// launches run one after the other and share it.
+long long variant_ws_bytes(const Problem &p, int v) {
+  if (v == kSkinnyFixed) return skinny_fixed_bytes(p);
+  if (v == kSkinnyWs) return skinny_split_bytes(p);
+  if (v == kFewRowsWs) return fewrows_split_bytes(p);
+  if (v == kEdgeSplit) {
+    const bool atomics = g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED;
+    const EdgePlan ep = edge_plan(p);
+    if (ep.side < 0) return variant_ws_bytes(p, choose_variant(p, atomics));
+    const Problem bulk = edge_part(p, ep.side, ep.keep, false), thin = edge_part(p, ep.side, ep.keep, true);
+    const long long a = variant_ws_bytes(bulk, choose_variant(bulk, atomics));
+    const long long b = variant_ws_bytes(thin, choose_variant(thin, atomics));
+    return a > b ? a : b;
+  }
+  for (const TailFamily &tf : kTailFamilies)
+    if (tf.variant == v) return family_tail_plan(tf, p).bytes;
+  return 0;
+}
+
 // Workspace the automatic choice of the workspace entry points would use for
 // this problem (0: none), or a negative status for invalid sizes.
 long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
@@ -710,13 +829,7 @@ long long workspace_size(int opA, int opB, int M, int N, int K, int batch) {
   const Problem p{M,    N,   K,   1.0f, 0.0f, fake, lda, fake, ldb, const_cast<float *>(fake), N,
                   opA == SGEMM_OP_T, opB == SGEMM_OP_T, 0, 0, 0, 1,
                   reinterpret_cast<void *>(256), (unsigned long long)kTailWorkspaceBytes};
-  const int v = choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED);
-  if (v == kSkinnyFixed) return skinny_fixed_bytes(p);
-  if (v == kSkinnyWs) return skinny_split_bytes(p);
-  if (v == kFewRowsWs) return fewrows_split_bytes(p);
-  for (const TailFamily &tf : kTailFamilies)
-    if (tf.variant == v) return family_tail_plan(tf, p).bytes;
-  return 0;
+  return variant_ws_bytes(p, choose_variant(p, g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED));
 }
 
 // Scratch of the entry point that allocates nothing

@@ -178,24 +178,28 @@ def test_select_128_tiles(lib):
     assert _batched_choice(1, 2048, 2048, 2048) == "mfma16_128x128x64_4x2_sched"
     assert _batched_choice(2, 2048, 2048, 2048) == "mfma16_128x128x32_2x2_sched"
     assert _batched_choice(1, 256, 16384, 4096) == "mfma16_128x128x64_4x2_sched"
-    assert _batched_choice(1, 10000, 10000, 1000) == "mfma16_128x128x32_2x2_sched"
+    assert _batched_choice(1, 10000, 10000, 1000) == "edge_split"   # 16-row and -column edges: 136.9 vs 134.6
 
 
 def test_select_last_round_tail(lib):
-    """A tile count just past whole rounds of the 256 CUs (an odd M or N adds
-    a row or column of tiles) leaves the last round nearly empty: smaller
-    tiles then win (measured, TFLOP/s: (2047, 2049, 2047) 106 on 32x64 tiles
-    and 102 on 64x64 against 68 on 128x128, (4095, 4097, 4095) 123 vs 117,
-    (8191, 1025, 8191) 117 vs 105 on 128x64, 3000^3 126 vs 104,
-    (6144, 1024, 4096) 135 vs 108 on 128x128), in every orientation."""
-    f64 = "mfma16_64x64x64_4x2_sched"
+    """A tile count just past whole rounds of the 256 CUs leaves the last
+    round nearly empty.  Where a thin edge of 1 to 16 rows or columns adds
+    that row or column of tiles, the edge is split off to the few-columns or
+    few-rows kernel and the bulk keeps the large tiles (measured, TFLOP/s:
+    (4095, 4097, 1023) 129.9 against 118.9 on 64x64 tiles, (4095, 4097, 4095)
+    143.8 vs 125.9, (2047, 2049, 2047) 121.7 vs 108.5 on 32x64, (8191, 1025,
+    8191) 134.4 vs 118.8), in every orientation; otherwise smaller tiles win
+    (3000^3 126 vs 104 on 128x128, (6144, 1024, 4096) 135 vs 108)."""
     for shape in ((4095, 4097, 4095), (8191, 1025, 8191), (2047, 4097, 4095), (4096, 4097, 1024),
-                  (3000, 3000, 3000), (3072, 3072, 3072)):
-        assert _batched_choice(1, *shape) == f64, shape
+                  (2047, 2049, 2047), (4097, 4095, 1023), (4097, 4097, 4097)):
+        assert _batched_choice(1, *shape) == "edge_split", shape
     for ta in (0, 1):
         for tb in (0, 1):
-            assert _op_choice(ta, tb, 4095, 4097, 1023) == f64
-    assert _batched_choice(1, 2047, 2049, 2047) == "mfma16_32x64x64_2x2_sched"
+            assert _op_choice(ta, tb, 4095, 4097, 1023) == "edge_split"
+    # no thin edge (3000 = 11 x 256 + 184), or K below the fitted depths
+    for shape in ((3000, 3000, 3000), (3072, 3072, 3072)):
+        assert _batched_choice(1, *shape) == "mfma16_64x64x64_4x2_sched", shape
+    assert _batched_choice(1, 1023, 8193, 257) == "mfma16_64x64x64_4x2_sched"
     assert _batched_choice(1, 6144, 1024, 4096) == "mfma16_128x64x64_4x2_sched"
     # whole rounds keep the large tiles
     assert _batched_choice(1, 4096, 4096, 1023) == "mfma32_256x256x32_2x2_sched"
@@ -511,7 +515,8 @@ def test_tile_choice_against_measured_rates(lib):
            "32x64": "mfma16_32x64x64_2x2_sched", "32x64 split-K": "mfma16_32x64x64_2x2_sched_splitk",
            "128x128 w4 tail": "mfma16_128x128x32_2x2_sched_tail",
            "128x128 w8 tail": "mfma16_128x128x64_4x2_sched_tail",
-           "128x64 tail": "mfma16_128x64x64_4x2_sched_tail", "64x64 tail": "mfma16_64x64x64_4x2_sched_tail"}
+           "128x64 tail": "mfma16_128x64x64_4x2_sched_tail", "64x64 tail": "mfma16_64x64x64_4x2_sched_tail",
+           "edge split": "edge_split"}
     ws_bytes = 4096 + (32 << 20)
     fracs, fracs_ws = [], []
     for line in lines:

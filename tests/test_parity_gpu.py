@@ -933,9 +933,9 @@ def test_rectangular_and_ragged(w):
 # row count sits just past a multiple of 64, where the automatic choice takes
 # smaller tiles (32x64, 64x64, 128x64, K split or not); the automatic path,
 # with the selection pinned so the intended kernel is the one checked.
-TAIL_SHAPES = [((2047, 2049, 2047), "mfma16_32x64x64_2x2_sched"),
+TAIL_SHAPES = [((2047, 2049, 2047), "edge_split"),
                ((3000, 3000, 3000), "mfma16_64x64x64_4x2_sched"),
-               ((8191, 1025, 8191), "mfma16_64x64x64_4x2_sched"),
+               ((8191, 1025, 8191), "edge_split"),
                ((6144, 1024, 4096), "mfma16_128x64x64_4x2_sched"),
                ((96, 8192, 8192), "mfma16_32x64x64_2x2_sched_splitk"),
                ((160, 4096, 4096), "mfma16_32x64x64_2x2_sched_splitk"),
@@ -962,6 +962,85 @@ def test_last_round_tail_shapes(shape, expect):
     assert oracle.exact_match(C[rows], ref), "tail %s int rows" % (shape,)
     ref, _ = oracle.gemm(Ai, Bi, cols=cols)
     assert oracle.exact_match(C[:, cols], ref), "tail %s int cols" % (shape,)
+
+
+# The edge split: a thin edge of 1 to 16 columns (or rows) split off to the
+# few-columns (few-rows) kernel, the bulk on whole rounds of large tiles.
+EDGE_SHAPES = [((4095, 4097, 1023), "NN"), ((4095, 4097, 1023), "NT"), ((4095, 4097, 1023), "TN"),
+               ((4095, 4097, 1023), "TT"), ((4097, 4097, 4097), "NN"), ((1025, 1024, 1024), "NN"),
+               ((1025, 1024, 1024), "TT"), ((2047, 2049, 2047), "NT")]
+
+
+@pytest.mark.parametrize("shape,ops", EDGE_SHAPES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple)
+                         else v)
+def test_edge_split_automatic(shape, ops):
+    """The automatic choice takes the edge split (both edges at (4097, 4097,
+    4097); a one-row edge at (1025, 1024, 1024)), in every orientation, with
+    alpha and beta: whole rows and columns of real data to 1e-5 (every
+    element for the smaller shapes), and integer data exactly."""
+    M, N, K = shape
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    lda, ldb = (M if ta else K), (K if tb else N)
+    v = sg.sgemm_strided_batched_select_variant(int(ta), int(tb), M, N, K, 1.0, 256, lda, 0, 256, ldb, 0,
+                                                0.5, 256, N, 0, 1)
+    assert sg.sgemm_variant_name(v) == "edge_split", sg.sgemm_variant_name(v)
+    A, B, Cin = draw(M, N, K, seed=M + 2 * N + K, with_c=True)
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T) if tb else B
+    say("edge split", shape, ops)
+    C = run(As, Bs, Cin, 1.5, 0.5, trans_a=ta, trans_b=tb, check_outside=True)
+    if M * N * K > 2 ** 32:
+        _sampled_check(A, B, C, 1.5, 0.5, Cin, 160, 160, M, "edge split %s %s" % (shape, ops))
+        # the thin edge itself, whole
+        ref, den = oracle.gemm(A, B, Cin, 1.5, 0.5, cols=np.arange(N - N % 64, N))
+        assert oracle.normalized_error(C[:, N - N % 64:], ref, den) <= TOL
+    else:
+        check_real(C, A, B, Cin, 1.5, 0.5, "edge split %s %s" % (shape, ops))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + 2 * N + K + 1, kind="int", with_c=True)
+    Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+    Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+    C = run(Ais, Bis, Ci, 1.0, 1.0, trans_a=ta, trans_b=tb)
+    if M * N * K > 2 ** 32:
+        rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 96)), np.arange(M - M % 64, M)]))
+        cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 96)), np.arange(N - N % 64, N)]))
+        ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0, rows=rows)
+        assert oracle.exact_match(C[rows], ref), "edge split %s %s int rows" % (shape, ops)
+        ref, _ = oracle.gemm(Ai, Bi, Ci, 1.0, 1.0, cols=cols)
+        assert oracle.exact_match(C[:, cols], ref), "edge split %s %s int cols" % (shape, ops)
+    else:
+        check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "edge split %s %s int" % (shape, ops))
+
+
+def test_edge_split_padded_batched_and_workspace():
+    """The edge split forced on padded, misaligned operands (nothing outside C
+    written); over a strided batch with gaps between the slices; and through
+    the workspace entry point, whose choice it is as well."""
+    v = VNAMES.index("edge_split")
+    M, N, K = 1031, 1030, 1100
+    A, B, Cin = draw(M, N, K, seed=77, with_c=True)
+    say("edge split padded")
+    C = run(A, B, Cin, 1.5, 0.5, variant=v, lds=(K + 3, N + 1, N + 5), offsets=(1, 3, 2), check_outside=True)
+    check_real(C, A, B, Cin, 1.5, 0.5, "edge split padded")
+    rng = np.random.default_rng(78)
+    batch, M, N, K = 3, 1025, 1024, 1024
+    Ai = rng.integers(-4, 5, (batch, M, K)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (batch, K, N)).astype(np.float32)
+    Ci = rng.integers(-4, 5, (batch, M, N)).astype(np.float32)
+    say("edge split batched")
+    out = run_batched(Ai, Bi, Ci, 1.0, 1.0, variant=v, gap=3)
+    check_batched(out, Ai, Bi, Ci, 1.0, 1.0, "edge split batched", exact=True)
+    M, N, K = 4095, 4097, 1023
+    ws = torch.zeros(4096 + (32 << 20), dtype=torch.uint8, device="cuda")
+    w = sg.sgemm_strided_batched_ws_select_variant(0, 0, M, N, K, 1.0, 256, K, 0, 256, N, 0, 0.0, 256, N, 0, 1,
+                                                   ws.numel())
+    assert sg.sgemm_variant_name(w) == "edge_split"
+    Ai, Bi, _ = draw(M, N, K, seed=79, kind="int")
+    say("edge split workspace")
+    C = run(Ai, Bi, workspace=ws)
+    cols = np.unique(np.concatenate([np.arange(0, N, 61), np.arange(N - 64, N)]))
+    ref, _ = oracle.gemm(Ai, Bi, cols=cols)
+    assert oracle.exact_match(C[:, cols], ref)
+    assert bool((ws[:4096] == 0).all().item())
 
 
 # Shapes whose default choice adds partial sums with atomics: K-split tiles

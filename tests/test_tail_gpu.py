@@ -137,11 +137,14 @@ def test_workspace_reused_across_shapes_and_too_small():
 
 
 def test_automatic_choice_with_workspace():
-    """The automatic choice of the workspace entry point takes a split form
-    where the last round is partial -- (4095, 4097, 1023) -- and its results
-    meet the oracle (every element), integer copies exactly; 1024^3 through
-    the same entry point likewise, whatever it chooses."""
-    shapes = [(w.M, w.N, w.K, w.seed) for w in ragged_workloads() if w.M == 4095]
+    """The automatic choice of the workspace entry point takes the tail form
+    where the last round is partial and no thin edge can be split off --
+    3000^3 -- and the edge split at (4095, 4097, 1023), whose 4097 columns
+    overrun the tiles by one; results meet the oracle (every element),
+    integer copies exactly; 1024^3 through the same entry point likewise,
+    whatever it chooses."""
+    shapes = [(3000, 3000, 3000, 31)]
+    shapes += [(w.M, w.N, w.K, w.seed) for w in ragged_workloads() if w.M == 4095]
     shapes += [(w.M, w.N, w.K, w.seed) for w in sweep_workloads() if w.M == 1024]
     for M, N, K, seed in shapes:
         need = sg.sgemm_workspace_size(0, 0, M, N, K, 1)
@@ -149,8 +152,10 @@ def test_automatic_choice_with_workspace():
                                                        256, N, 0, 1, WS_BYTES)
         say("auto ws", (M, N, K), sg.sgemm_variant_name(v), need)
         assert need <= WS_BYTES
-        if M == 4095:
+        if M == 3000:
             assert sg.sgemm_variant_name(v).endswith("_tail") and need > 4096
+        if M == 4095:
+            assert sg.sgemm_variant_name(v) == "edge_split"
         ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
         A, B, _ = draw(M, N, K, seed=seed)
         C = run(A, B, workspace=ws)

@@ -48,7 +48,7 @@ def _both(A, B, Cin, alpha, beta, batch=1):
 
 
 # Two calls in a row, the second smaller: both take the split tail form.
-SHAPES = [(4095, 4097, 1023), (1536, 1536, 1536)]
+SHAPES = [(3000, 3000, 3000), (1536, 1536, 1536)]
 
 
 @pytest.mark.parametrize("kind", ["real", "int"])
