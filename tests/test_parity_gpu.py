@@ -1011,6 +1011,36 @@ def test_edge_split_automatic(shape, ops):
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "edge split %s %s int" % (shape, ops))
 
 
+# Shapes the automatic choice gives the edge split, drawn once with a seeded
+# generator over M, N = (4..24) x (64, 128 or 256) + (1..16 or 0), K 1000-2600
+# and every orientation.
+EDGE_RANDOM = [(1293, 6152, 1114, "NT"), (1024, 5122, 1438, "TT"), (2947, 2825, 2373, "NT"),
+               (6144, 6154, 1999, "TN"), (3072, 4105, 1229, "NN"), (5387, 3854, 2393, "NN"),
+               (2053, 5888, 1615, "TN"), (4864, 2572, 2592, "NN"), (4864, 3333, 2311, "NN"),
+               (4610, 1798, 1047, "NN")]
+
+
+@pytest.mark.parametrize("case", EDGE_RANDOM, ids=lambda c: "%dx%dx%d-%s" % c)
+def test_edge_split_random_shapes(case):
+    """Integer data exactly on sampled rows and columns, the edges whole."""
+    M, N, K, ops = case
+    ta, tb = ops[0] == "T", ops[1] == "T"
+    v = sg.sgemm_strided_batched_select_variant(int(ta), int(tb), M, N, K, 1.0, 256, M if ta else K, 0, 256,
+                                                K if tb else N, 0, 0.0, 256, N, 0, 1)
+    assert sg.sgemm_variant_name(v) == "edge_split"
+    Ai, Bi, _ = draw(M, N, K, seed=M * 7 + N + K, kind="int")
+    Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+    Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+    say("edge split random", case)
+    C = run(Ais, Bis, trans_a=ta, trans_b=tb, check_outside=True)
+    rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 48)), np.arange(M - M % 64, M), [M - 1]]))
+    cols = np.unique(np.concatenate([np.arange(0, N, max(1, N // 48)), np.arange(N - N % 64, N), [N - 1]]))
+    ref, _ = oracle.gemm(Ai, Bi, rows=rows)
+    assert oracle.exact_match(C[rows], ref), "%s rows" % (case,)
+    ref, _ = oracle.gemm(Ai, Bi, cols=cols)
+    assert oracle.exact_match(C[:, cols], ref), "%s cols" % (case,)
+
+
 def test_edge_split_padded_batched_and_workspace():
     """The edge split forced on padded, misaligned operands (nothing outside C
     written); over a strided batch with gaps between the slices; and through
