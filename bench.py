@@ -1361,9 +1361,11 @@ def trace_summary(trace_csv: str, log_path: str, title: str = "") -> str:
 
 
 def counter_summary(counter_csv: str, log_path: str) -> list:
-    """Per job of a traced run (--profile / --sweep): the mean of each
-    counter over the job's GEMM dispatches (separators and C-scaling
-    launches left out), from a rocprofv3 counter_collection.csv."""
+    """Per job of a traced run (--profile / --sweep): each counter summed
+    over the GEMM dispatches of a call (a call can launch two kernels, as
+    the edge split does) and averaged over the job's timed calls
+    (separators and C-scaling launches left out), from a rocprofv3
+    counter_collection.csv."""
     import csv
     with open(counter_csv) as f:
         rows = list(csv.DictReader(f))
@@ -1391,17 +1393,20 @@ def counter_summary(counter_csv: str, log_path: str) -> list:
             continue
         if cur is None or "scale_kernel" in name:
             continue
-        d = per.setdefault(cur, {"kernel": name, "vals": {}, "dispatches": set()})
+        d = per.setdefault(cur, {"kernel": name, "kernels": [], "vals": {}, "dispatches": set()})
         d["dispatches"].add(r["Dispatch_Id"])
+        if name not in d["kernels"]:
+            d["kernels"].append(name)
         d["vals"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     out = []
     for job in sorted(per):
         r = recs.get(job, {})
         d = per[job]
+        calls = int(r.get("steps") or len(d["dispatches"]))
         out.append({"job": job, "M": r.get("M"), "N": r.get("N"), "K": r.get("K"),
-                    "variant": r.get("variant"), "kernel": d["kernel"],
-                    "dispatches": len(d["dispatches"]),
-                    "counters": {k: sum(v) / len(v) for k, v in d["vals"].items()}})
+                    "variant": r.get("variant"), "kernel": d["kernel"], "kernels": d["kernels"],
+                    "dispatches": len(d["dispatches"]), "calls": calls,
+                    "counters": {k: sum(v) / calls for k, v in d["vals"].items()}})
     return out
 
 

@@ -137,14 +137,30 @@ def test_counter_summary_means_per_job(tmp_path):
                      "Workgroup_Size_X": 64, "Grid_Size_X": 64 * bench.mark_code(job, 2),
                      "Counter_Name": "X", "Counter_Value": 0})
         did += 1
+    # job 2: two calls of two kernels each (the edge split): summed per call
+    rows.append({"Dispatch_Id": did, "Kernel_Name": sep, "Start_Timestamp": 0, "End_Timestamp": 1,
+                 "Workgroup_Size_X": 64, "Grid_Size_X": 64 * bench.mark_code(2, 1),
+                 "Counter_Name": "X", "Counter_Value": 0})
+    did += 1
+    for v in (10.0, 1.0, 12.0, 1.0):
+        rows.append({"Dispatch_Id": did, "Kernel_Name": "void sg950::sched_kernel<1>()" if v > 1 else
+                     "void sg950::narrow_kernel<false>()", "Start_Timestamp": 0, "End_Timestamp": 1,
+                     "Workgroup_Size_X": 256, "Grid_Size_X": 256, "Counter_Name": "X", "Counter_Value": v})
+        did += 1
+    rows.append({"Dispatch_Id": did, "Kernel_Name": sep, "Start_Timestamp": 0, "End_Timestamp": 1,
+                 "Workgroup_Size_X": 64, "Grid_Size_X": 64 * bench.mark_code(2, 2),
+                 "Counter_Name": "X", "Counter_Value": 0})
     p = tmp_path / "cc.csv"
     _write_trace(p, rows, counters=True)
     log = tmp_path / "run.log"
-    log.write_text(json.dumps({"job": 0, "M": 1, "N": 2, "K": 3, "variant": "v"}) + "\n")
+    log.write_text(json.dumps({"job": 0, "M": 1, "N": 2, "K": 3, "variant": "v"}) + "\n" +
+                   json.dumps({"job": 2, "M": 4, "N": 5, "K": 6, "variant": "edge_split", "steps": 2}) + "\n")
     out = bench.counter_summary(str(p), str(log))
-    assert [o["job"] for o in out] == [0, 1]
+    assert [o["job"] for o in out] == [0, 1, 2]
     assert out[0]["counters"]["X"] == 20.0 and out[0]["dispatches"] == 2 and out[0]["M"] == 1
     assert out[1]["counters"]["X"] == 5.0
+    assert out[2]["counters"]["X"] == 12.0 and out[2]["dispatches"] == 4 and out[2]["calls"] == 2
+    assert len(out[2]["kernels"]) == 2
 
 
 def _jsonl(path, recs):
