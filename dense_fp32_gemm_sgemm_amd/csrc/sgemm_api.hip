@@ -489,7 +489,9 @@ EdgePlan edge_plan(const Problem &p, int depth = 1) {
     for (int side = 0; side < 2; ++side) {
       const int dim = side == 0 ? p.N : p.M, tile = side == 0 ? f.bn : f.bm;
       const int r = dim % tile;
-      if (r < 1 || r > 16 || dim <= tile) continue;
+      // (the few-columns kernel takes up to 16 columns, the few-rows kernels
+      // up to 32 rows)
+      if (r < 1 || r > (side == 0 ? 16 : 32) || dim <= tile) continue;
       const Problem bulk = edge_part(p, side, dim - r, false);
       if (!family_fits(f, bulk)) continue;
       double rb = family_rate(f, bulk);

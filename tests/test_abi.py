@@ -193,6 +193,12 @@ def test_select_last_round_tail(lib):
     for shape in ((4095, 4097, 4095), (8191, 1025, 8191), (2047, 4097, 4095), (4096, 4097, 1024),
                   (2047, 2049, 2047), (4097, 4095, 1023), (4097, 4097, 4097)):
         assert _batched_choice(1, *shape) == "edge_split", shape
+    # row edges up to 32 go to the few-rows kernels ((4120, 4096, 2048) 143.3
+    # against 122.9 TFLOP/s on 64x64 tiles, (2080, 2048, 2048) 128.1 vs 110.3)
+    for shape in ((4120, 4096, 2048), (4128, 4096, 1024), (2080, 2048, 2048), (1056, 1024, 2048)):
+        assert _batched_choice(1, *shape) == "edge_split", shape
+    # a column edge of 32 is not thin (the few-columns kernel takes 16)
+    assert _batched_choice(1, 4128, 4128, 2048) != "edge_split"
     for ta in (0, 1):
         for tb in (0, 1):
             assert _op_choice(ta, tb, 4095, 4097, 1023) == "edge_split"
