@@ -1050,13 +1050,12 @@ CHOICE_FAMILIES = (
 
 def has_thin_edge(M, N, K):
     """Whether the library's edge split applies: K of about 1024 or more and
-    a dimension that overruns some tile family's tiles by a thin edge (rows:
-    1 to 32 past tiles of 256, 128, 64 or 32; columns: 1 to 16 past 256, 128
-    or 64)."""
+    a dimension that overruns some tile family's tiles by a thin edge of 1
+    to 32 (rows: tiles of 256, 128, 64 or 32; columns: 256, 128 or 64)."""
     if K < 1000:
         return False
     return (any(M > t and 1 <= M % t <= 32 for t in (256, 128, 64, 32)) or
-            any(N > t and 1 <= N % t <= 16 for t in (256, 128, 64)))
+            any(N > t and 1 <= N % t <= 32 for t in (256, 128, 64)))
 
 
 def choice_table(args):

@@ -430,7 +430,7 @@ bool skinny_full_k(const Problem &p) {
 }
 
 // Edge split: a dimension of C that overruns a family's tiles by a thin edge
-// (1 to 16 rows or columns) costs that family a whole extra row or column
+// (1 to 32 rows or columns) costs that family a whole extra row or column
 // of tiles -- at (4095, 4097, 1023) the 256x256 tiles number 16 x 17, one
 // round of 256 and a second of 16 one-column tiles.  Splitting the edge off
 // leaves the bulk to the tiles (whole rounds) and gives the thin strip to
@@ -465,6 +465,17 @@ Problem edge_part(const Problem &p, int side, int keep, bool thin) {
   return q;
 }
 
+// The thin strip as launches: a column edge wider than the few-columns
+// kernel's 16 goes as two strips (16 columns, then the rest).  Returns how
+// many of out[] it filled.
+int thin_parts(const Problem &p, int side, int keep, Problem (&out)[2]) {
+  out[0] = edge_part(p, side, keep, true);
+  if (side != 0 || out[0].N <= 16) return 1;
+  out[1] = edge_part(p, side, keep + 16, true);
+  out[0].N = 16;
+  return 2;
+}
+
 // Microseconds a thin strip takes: a launch and a stream over its operands at
 // 4 TB/s, slower when its long side is short of 4096 (the few-columns and
 // few-rows kernels spread over that side).  Measured (us, alone, warm):
@@ -489,16 +500,18 @@ EdgePlan edge_plan(const Problem &p, int depth = 1) {
     for (int side = 0; side < 2; ++side) {
       const int dim = side == 0 ? p.N : p.M, tile = side == 0 ? f.bn : f.bm;
       const int r = dim % tile;
-      // (the few-columns kernel takes up to 16 columns, the few-rows kernels
-      // up to 32 rows)
-      if (r < 1 || r > (side == 0 ? 16 : 32) || dim <= tile) continue;
+      // (edges of up to 32: the few-rows kernels take 32 rows, the
+      // few-columns kernel 16 columns a launch)
+      if (r < 1 || r > 32 || dim <= tile) continue;
       const Problem bulk = edge_part(p, side, dim - r, false);
       if (!family_fits(f, bulk)) continue;
       double rb = family_rate(f, bulk);
       if (depth > 0) rb = fmax(rb, edge_plan(bulk, depth - 1).rate);
       if (rb <= 0.0) continue;
-      const double t = 2.0 * (double)bulk.M * bulk.N * bulk.K * (double)bulk.batch / (rb * 1e6) +
-                       thin_us(edge_part(p, side, dim - r, true));
+      Problem parts[2];
+      const int np = thin_parts(p, side, dim - r, parts);
+      double t = 2.0 * (double)bulk.M * bulk.N * bulk.K * (double)bulk.batch / (rb * 1e6);
+      for (int i = 0; i < np; ++i) t += thin_us(parts[i]);
       const double rate = flops / (t * 1e6);
       if (rate > best.rate) {
         best.side = side;
@@ -703,9 +716,13 @@ int launch_edge_split(const Problem &p, hipStream_t s) {
   const bool atomics = g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED;
   const EdgePlan ep = edge_plan(p);
   if (ep.side < 0) return kVariants[choose_variant(p, atomics)].launch(p, s);
-  const Problem bulk = edge_part(p, ep.side, ep.keep, false), thin = edge_part(p, ep.side, ep.keep, true);
+  const Problem bulk = edge_part(p, ep.side, ep.keep, false);
   if (kVariants[choose_variant(bulk, atomics)].launch(bulk, s) != 0) return -1;
-  return kVariants[choose_variant(thin, atomics)].launch(thin, s);
+  Problem parts[2];
+  const int np = thin_parts(p, ep.side, ep.keep, parts);
+  for (int i = 0; i < np; ++i)
+    if (kVariants[choose_variant(parts[i], atomics)].launch(parts[i], s) != 0) return -1;
+  return 0;
 }
 
 std::atomic<int> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other
@@ -809,10 +826,15 @@ long long variant_ws_bytes(const Problem &p, int v) {
     const bool atomics = g_atomics_mode.load() == SGEMM_ATOMICS_ALLOWED;
     const EdgePlan ep = edge_plan(p);
     if (ep.side < 0) return variant_ws_bytes(p, choose_variant(p, atomics));
-    const Problem bulk = edge_part(p, ep.side, ep.keep, false), thin = edge_part(p, ep.side, ep.keep, true);
-    const long long a = variant_ws_bytes(bulk, choose_variant(bulk, atomics));
-    const long long b = variant_ws_bytes(thin, choose_variant(thin, atomics));
-    return a > b ? a : b;
+    const Problem bulk = edge_part(p, ep.side, ep.keep, false);
+    long long need = variant_ws_bytes(bulk, choose_variant(bulk, atomics));
+    Problem parts[2];
+    const int np = thin_parts(p, ep.side, ep.keep, parts);
+    for (int i = 0; i < np; ++i) {
+      const long long b = variant_ws_bytes(parts[i], choose_variant(parts[i], atomics));
+      if (b > need) need = b;
+    }
+    return need;
   }
   for (const TailFamily &tf : kTailFamilies)
     if (tf.variant == v) return family_tail_plan(tf, p).bytes;

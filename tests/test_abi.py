@@ -184,7 +184,8 @@ def test_select_128_tiles(lib):
 def test_select_last_round_tail(lib):
     """A tile count just past whole rounds of the 256 CUs leaves the last
     round nearly empty.  Where a thin edge of 1 to 16 rows or columns adds
-    that row or column of tiles, the edge is split off to the few-columns or
+    that row or column of tiles (1 to 32 rows or columns), the edge is split
+    off to the few-columns or
     few-rows kernel and the bulk keeps the large tiles (measured, TFLOP/s:
     (4095, 4097, 1023) 129.9 against 118.9 on 64x64 tiles, (4095, 4097, 4095)
     143.8 vs 125.9, (2047, 2049, 2047) 121.7 vs 108.5 on 32x64, (8191, 1025,
@@ -197,8 +198,13 @@ def test_select_last_round_tail(lib):
     # against 122.9 TFLOP/s on 64x64 tiles, (2080, 2048, 2048) 128.1 vs 110.3)
     for shape in ((4120, 4096, 2048), (4128, 4096, 1024), (2080, 2048, 2048), (1056, 1024, 2048)):
         assert _batched_choice(1, *shape) == "edge_split", shape
-    # a column edge of 32 is not thin (the few-columns kernel takes 16)
-    assert _batched_choice(1, 4128, 4128, 2048) != "edge_split"
+    # column edges of 17 to 32 go as two few-columns strips ((4096, 4120,
+    # 2048) 141.9 against 127.2 on 64x64 tiles, (4128, 4128, 2048) 137.3 vs
+    # 128.4, (2048, 2080, 2048) 123.3 vs 114.7 on 32x64); (1024, 1056, 2048)
+    # keeps 32x64 tiles (83.4 against 81.7 split)
+    for shape in ((4128, 4128, 2048), (4096, 4120, 2048), (2048, 2080, 2048), (4095, 4127, 1023)):
+        assert _batched_choice(1, *shape) == "edge_split", shape
+    assert _batched_choice(1, 1024, 1056, 2048) != "edge_split"
     for ta in (0, 1):
         for tb in (0, 1):
             assert _op_choice(ta, tb, 4095, 4097, 1023) == "edge_split"
