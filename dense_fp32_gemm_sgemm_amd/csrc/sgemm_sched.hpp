@@ -467,13 +467,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
       }
     }
   } else if constexpr (PERMB) {
-    // FN consecutive columns per lane and row: one vector store when they are
-    // FN-float aligned in memory (then a group lies wholly on one side of n0,
-    // since n0 - ns is a multiple of FN), else one store per column of the
-    // tile's own.
+    // FN consecutive columns per lane and row: one vector store (a group from
+    // n0 on lies wholly inside the tile).  Like the slab loads, the vector
+    // accesses go through copies that need only 4-byte alignment, so a leading
+    // dimension or shift that is not a multiple of FN keeps them: one store per
+    // column instead would touch each cache line FN times.
     const int colq = ns + wn * T::WTN + T::FN * li;
-    const bool cvec = (reinterpret_cast<uintptr_t>(p.C) % (4 * T::FN) == 0) && (p.ldc % T::FN == 0) &&
-                      (ns % T::FN == 0);
+    const bool cvec = (reinterpret_cast<uintptr_t>(p.C) & 3) == 0;
     if (colq >= n0) {
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
@@ -488,21 +488,23 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINW) void sched_kernel(Prob
 #pragma unroll
               for (int j = 0; j < 4; ++j) v[j] = p.alpha * acc[i][j][r];
               if (p.beta != 0.0f) {
-                const floatx4 old = *reinterpret_cast<const floatx4 *>(c);
+                floatx4 old;
+                __builtin_memcpy(&old, c, sizeof(old));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = fmaf(p.beta, old[j], v[j]);
               }
-              *reinterpret_cast<floatx4 *>(c) = v;
+              __builtin_memcpy(c, &v, sizeof(v));
             } else {
               floatx2 v;
 #pragma unroll
               for (int j = 0; j < 2; ++j) v[j] = p.alpha * acc[i][j][r];
               if (p.beta != 0.0f) {
-                const floatx2 old = *reinterpret_cast<const floatx2 *>(c);
+                floatx2 old;
+                __builtin_memcpy(&old, c, sizeof(old));
 #pragma unroll
                 for (int j = 0; j < 2; ++j) v[j] = fmaf(p.beta, old[j], v[j]);
               }
-              *reinterpret_cast<floatx2 *>(c) = v;
+              __builtin_memcpy(c, &v, sizeof(v));
             }
           } else {
 #pragma unroll

@@ -289,6 +289,33 @@ def test_sched_path_ragged_k_and_unaligned(variant, shape):
         check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], shape, ta, tb))
 
 
+@pytest.mark.parametrize("variant", SCHED, ids=[VNAMES[v] for v in SCHED])
+def test_sched_misaligned_c_rows(variant):
+    """Rows of C that do not start on a 16-byte boundary keep the vector
+    stores of the ordered loop's epilogue: an odd N (the last tile shifted
+    back by an odd number of columns), an odd leading dimension of C and a C
+    that starts one float into its buffer, every operand orientation, beta
+    != 0 (the old C read as a vector too); real to 1e-5, integer data
+    exactly, nothing outside C written."""
+    for (M, N, K) in ((300, 263, 64), (257, 301, 96)):
+        for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+            A, B, Cin = draw(M, N, K, seed=M + 3 * N + K, with_c=True)
+            As = np.ascontiguousarray(A.T) if ta else A
+            Bs = np.ascontiguousarray(B.T) if tb else B
+            say("sched misaligned C", VNAMES[variant], (M, N, K), ta, tb)
+            C = run(As, Bs, Cin, -1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb, check_outside=True)
+            check_real(C, A, B, Cin, -1.5, 0.5, "%s %s %s%s" % (VNAMES[variant], (M, N, K), ta, tb))
+            C = run(As, Bs, Cin, -1.5, 0.5, variant=variant, trans_a=ta, trans_b=tb,
+                    lds=(None, None, N + 1), offsets=(0, 0, 1), check_outside=True)
+            check_real(C, A, B, Cin, -1.5, 0.5, "%s %s %s%s ldc+1" % (VNAMES[variant], (M, N, K), ta, tb))
+            Ai, Bi, Ci = draw(M, N, K, seed=M + 3 * N + K, kind="int", with_c=True)
+            Ais = np.ascontiguousarray(Ai.T) if ta else Ai
+            Bis = np.ascontiguousarray(Bi.T) if tb else Bi
+            C = run(Ais, Bis, Ci, 1.0, 1.0, variant=variant, trans_a=ta, trans_b=tb,
+                    lds=(None, None, N + 1), offsets=(0, 0, 1))
+            check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s %s %s%s int" % (VNAMES[variant], (M, N, K), ta, tb))
+
+
 @pytest.mark.parametrize("shape", [(64, 64, 4096), (100, 130, 3001), (70, 200, 1290), (128, 192, 2048)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_sched_split_k(shape):
