@@ -33,8 +33,12 @@ constexpr int kNarrowWaves = 8;   // waves per workgroup, each a K range
 constexpr int kNarrowUnroll = 8;  // groups of 16 k whose loads are in flight
 }  // namespace
 
-// VA: A rows (or, with TA, its stored rows along M) allow 16-byte loads.
-// VB: op(B) with TB stored N x K allows 16-byte loads along K.
+// VA: A untransposed, its rows read as 16-byte vectors along K.
+// VB: B transposed (stored N x K), its rows read as 16-byte vectors along K.
+// The vectors go through copies that need only 4-byte alignment, which a
+// global load of 16 bytes also needs: a leading dimension that is not a
+// multiple of 4 keeps them (four single loads instead stream A at about
+// half the rate).
 template <bool TA, bool TB, bool VA, bool VB>
 __global__ __launch_bounds__(kNarrowWaves * 64) void narrow_kernel(Problem p, int krange) {
   select_slice(p);
@@ -51,7 +55,9 @@ __global__ __launch_bounds__(kNarrowWaves * 64) void narrow_kernel(Problem p, in
   // Four consecutive k of this lane's row of op(A), and of its column of op(B).
   auto load_a = [&](int k) -> floatx4 {
     if constexpr (!TA && VA) {
-      return *reinterpret_cast<const floatx4 *>(p.A + (size_t)row * lda + k);
+      floatx4 v;
+      __builtin_memcpy(&v, p.A + (size_t)row * lda + k, sizeof(v));
+      return v;
     } else if constexpr (!TA) {
       const float *q = p.A + (size_t)row * lda + k;
       return floatx4{q[0], q[1], q[2], q[3]};
@@ -62,7 +68,9 @@ __global__ __launch_bounds__(kNarrowWaves * 64) void narrow_kernel(Problem p, in
   };
   auto load_b = [&](int k) -> floatx4 {
     if constexpr (TB && VB) {
-      return *reinterpret_cast<const floatx4 *>(p.B + (size_t)col * ldb + k);
+      floatx4 v;
+      __builtin_memcpy(&v, p.B + (size_t)col * ldb + k, sizeof(v));
+      return v;
     } else if constexpr (TB) {
       const float *q = p.B + (size_t)col * ldb + k;
       return floatx4{q[0], q[1], q[2], q[3]};
@@ -138,13 +146,9 @@ namespace {
 template <bool TA, bool TB>
 void launch_narrow_t(const Problem &p, dim3 grid, hipStream_t stream, int krange) {
   const dim3 block(kNarrowWaves * 64);
-  // 16-byte loads along K need 16-byte aligned rows: an aligned base, a
-  // leading dimension and batch stride that are multiples of 4 (the K ranges
-  // and groups start at multiples of 4).
-  const bool va = !TA && (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 && p.lda % 4 == 0 &&
-                  (p.batch <= 1 || p.sa % 4 == 0);
-  const bool vb = TB && (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 4 == 0 &&
-                  (p.batch <= 1 || p.sb % 4 == 0);
+  // 16-byte loads along K at any 4-byte aligned address.
+  const bool va = !TA && (reinterpret_cast<uintptr_t>(p.A) & 3) == 0;
+  const bool vb = TB && (reinterpret_cast<uintptr_t>(p.B) & 3) == 0;
   if (va && vb) {
     SG950_LAUNCH((narrow_kernel<TA, TB, true, true>), grid, block, 0, stream, p, krange);
   } else if (va) {

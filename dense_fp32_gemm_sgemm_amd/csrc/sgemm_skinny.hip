@@ -44,6 +44,19 @@
 namespace sg950 {
 
 constexpr int kSkinnyCols = 256;  // columns of B per workgroup
+
+// Four consecutive floats are read as one 16-byte vector through a copy,
+// which needs only the 4-byte alignment of any float (as does the global
+// load itself): a leading dimension that is not a multiple of 4 keeps the
+// vectors.  What decides is the shape: a quad of columns of an untransposed
+// B (N a multiple of 4, so the quad past the edge can be replaced by the
+// last whole one), four consecutive k of a row of an untransposed A.
+inline bool skinny_b_vec(const Problem &p) {
+  return !p.tb && p.N % 4 == 0 && (reinterpret_cast<uintptr_t>(p.B) & 3) == 0;
+}
+inline bool skinny_a_vec(const Problem &p) {
+  return !p.ta && (reinterpret_cast<uintptr_t>(p.A) & 3) == 0;
+}
 constexpr int kSkinnyWaves = 4;
 
 // TB: B is stored N x K (op(B) = its transpose); its elements are then read
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_kernel(Problem p, in
     } else {
       const float *brow = p.B + (size_t)k * ldb;
       if (vec) {
-        b = *reinterpret_cast<const floatx4 *>(brow + c0);
+        __builtin_memcpy(&b, brow + c0, sizeof(b));
       } else {
         b = floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
       }
@@ -171,7 +184,9 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
   auto load_b = [&](int k) -> floatx4 {
     const float *brow = p.B + (size_t)k * ldb;
     if constexpr (VB) {
-      return *reinterpret_cast<const floatx4 *>(brow + cv);
+      floatx4 v;
+      __builtin_memcpy(&v, brow + cv, sizeof(v));
+      return v;
     } else {
       return floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
     }
@@ -182,7 +197,9 @@ __global__ __launch_bounds__(kFullKWaves * 64) void skinny_fullk_kernel(Problem 
   };
   auto load_a4 = [&](int r, int k) -> floatx4 {
     if constexpr (VA) {
-      return *reinterpret_cast<const floatx4 *>(p.A + (size_t)min(r, p.M - 1) * sa_r + k);
+      floatx4 v;
+      __builtin_memcpy(&v, p.A + (size_t)min(r, p.M - 1) * sa_r + k, sizeof(v));
+      return v;
     } else {
       return floatx4{load_a(r, k), load_a(r, k + 1), load_a(r, k + 2), load_a(r, k + 3)};
     }
@@ -347,7 +364,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void skinny_fixed_kernel(Problem
   auto load_b = [&](int k) -> floatx4 {
     const float *brow = p.B + (size_t)k * ldb;
     if constexpr (VB) {
-      return *reinterpret_cast<const floatx4 *>(brow + cv);
+      floatx4 v;
+      __builtin_memcpy(&v, brow + cv, sizeof(v));
+      return v;
     } else {
       return floatx4{brow[cc[0]], brow[cc[1]], brow[cc[2]], brow[cc[3]]};
     }
@@ -478,7 +497,7 @@ int launch_skinny_fixed(const Problem &p, hipStream_t stream) {
   const dim3 block(kSkinnyWaves * 64);
   unsigned *flags = reinterpret_cast<unsigned *>(p.ws);
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
-  const bool vb = b_vec_ok(p);
+  const bool vb = skinny_b_vec(p);
 #define SG950_FIXED(MR_)                                                                                  \
   do {                                                                                                    \
     if (vb)                                                                                               \
@@ -521,7 +540,7 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
       fstrips <= INT_MAX) {
     const dim3 fgrid((unsigned)fstrips, 1u, (unsigned)p.batch);
     const dim3 fblock(kFullKWaves * 64);
-    const bool fvb = b_vec_ok(p), fva = !p.ta && a_vec_ok(p);
+    const bool fvb = skinny_b_vec(p), fva = skinny_a_vec(p);
 #define SG950_FULLK(MR_)                                                                        \
   do {                                                                                          \
     if (fva && fvb)                                                                             \
@@ -553,7 +572,7 @@ int launch_skinny(const Problem &p, hipStream_t stream) {
   if (p.beta != 1.0f && launch_scale(p, stream) != 0) return -1;
   const dim3 grid((unsigned)strips, (unsigned)chunks, (unsigned)p.batch);
   const dim3 block(kSkinnyWaves * 64);
-  const bool vb = b_vec_ok(p);
+  const bool vb = skinny_b_vec(p);
 #define SG950_SKINNY(MR_)                                                                     \
   do {                                                                                        \
     if (p.tb)                                                                                 \
@@ -615,7 +634,7 @@ int launch_skinny_ws(const Problem &p, hipStream_t stream) {
   const dim3 fblock(kFullKWaves * 64);
   unsigned *flags = reinterpret_cast<unsigned *>(p.ws);
   float *part = reinterpret_cast<float *>(reinterpret_cast<char *>(p.ws) + kTailFlagBytes);
-  const bool fvb = b_vec_ok(p), fva = !p.ta && a_vec_ok(p);
+  const bool fvb = skinny_b_vec(p), fva = skinny_a_vec(p);
 #define SG950_FULLKS(MR_)                                                                                \
   do {                                                                                                   \
     if (fva && fvb)                                                                                      \

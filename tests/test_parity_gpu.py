@@ -630,6 +630,26 @@ def test_few_rows_full_k_strips(M, NK):
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
 
 
+@pytest.mark.parametrize("shape", [(3, 1024, 4100), (8, 1000, 3001), (1, 2048, 4097)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_few_rows_vector_loads_on_misaligned_rows(shape):
+    """The few-rows kernels forced with N a multiple of 4 but rows of A and B
+    that do not start on 16-byte boundaries (odd leading dimensions, bases
+    one or three floats in): four consecutive floats still go as one vector.
+    K split over workgroups (fewer than 64 strips of 32 columns) and the
+    full-K strips, beta != 0; real to 1e-5, integer data exactly."""
+    M, N, K = shape
+    v = VNAMES.index("skinny_m8")
+    A, B, Cin = draw(M, N, K, seed=M + N + K, with_c=True)
+    say("few rows misaligned", shape)
+    C = run(A, B, Cin, -0.75, 0.5, variant=v, lds=(K + 1, N + 1, N + 3), offsets=(3, 1, 2),
+            check_outside=True)
+    check_real(C, A, B, Cin, -0.75, 0.5, "%s padded" % (shape,))
+    Ai, Bi, Ci = draw(M, N, K, seed=M + N + K, kind="int", with_c=True)
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v, lds=(K + 1, N + 1, N + 3), offsets=(3, 1, 2))
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "%s int padded" % (shape,))
+
+
 @pytest.mark.parametrize("N", [1, 5, 16])
 @pytest.mark.parametrize("MK", [(16, 1), (100, 15), (1000, 33), (333, 4099), (64, 20000)],
                          ids=lambda t: "M%dK%d" % t)
@@ -648,12 +668,17 @@ def test_few_columns_kernel(N, MK):
         C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb, check_outside=True)
         check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d %s%s" % (M, N, K, ta, tb))
     A, B, Cin = draw(M, N, K, seed=M + 3 * N + K, with_c=True)
-    C = run(A, B, Cin, 1.5, 0.5, variant=v, lds=(K + 1, N + 3, N + 2), offsets=(3, 1, 2),
-            check_outside=True)
-    check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d padded" % (M, N, K))
+    for ta, tb in ((False, False), (False, True), (True, False), (True, True)):
+        As = np.ascontiguousarray(A.T) if ta else A
+        Bs = np.ascontiguousarray(B.T) if tb else B
+        C = run(As, Bs, Cin, 1.5, 0.5, variant=v, trans_a=ta, trans_b=tb,
+                lds=(As.shape[1] + 1, Bs.shape[1] + 3, N + 2), offsets=(3, 1, 2), check_outside=True)
+        check_real(C, A, B, Cin, 1.5, 0.5, "M=%d N=%d K=%d %s%s padded" % (M, N, K, ta, tb))
     Ai, Bi, Ci = draw(M, N, K, seed=M + 3 * N + K, kind="int", with_c=True)
     C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v)
     check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int" % (M, N, K))
+    C = run(Ai, Bi, Ci, 1.0, 1.0, variant=v, lds=(K + 1, N + 3, N + 2), offsets=(3, 1, 2))
+    check_exact(C, Ai, Bi, Ci, 1.0, 1.0, "M=%d N=%d K=%d int padded" % (M, N, K))
 
 
 @pytest.mark.parametrize("shape", [(9, 100, 33), (16, 1000, 1000), (1, 4099, 5), (12, 4096, 1),

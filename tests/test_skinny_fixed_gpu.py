@@ -77,13 +77,15 @@ def test_fixed_form_alpha_beta_and_transposed_a(trans_a):
     assert counters_zero(ws)
 
 
-def test_fixed_form_padded_misaligned_and_nan_c():
-    """Odd leading dimensions and 4-byte aligned operands (B read element by
-    element) with a NaN-filled C and beta = 0; nothing outside C written."""
-    M, N, K = 3, 777, 1234
+@pytest.mark.parametrize("N", [777, 776])
+def test_fixed_form_padded_misaligned_and_nan_c(N):
+    """Odd leading dimensions and 4-byte aligned operands with a NaN-filled C
+    and beta = 0 (N = 777: B read element by element; N = 776: as 16-byte
+    vectors off 16-byte boundaries); nothing outside C written."""
+    M, K = 3, 1234
     ws = new_ws()
     A, B, _ = draw(M, N, K, seed=8)
-    say("fixed few-rows padded")
+    say("fixed few-rows padded", N)
     C = run(A, B, None, 1.0, 0.0, variant=V, lds=(K + 3, N + 1, N + 5), offsets=(1, 3, 2),
             check_outside=True, workspace=ws)
     ref, den = oracle.gemm(A, B)
