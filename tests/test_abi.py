@@ -680,3 +680,23 @@ def test_strided_one_row_view_is_rejected(which):
         A = torch.zeros(1, 1)
     with pytest.raises(ValueError, match="row-major"):
         sg.gemm(A, B, C)
+
+
+def test_edge_split_only_where_the_benchmark_times_it(lib):
+    """The tile-choice benchmark times the edge split only where a thin edge
+    exists (bench.has_thin_edge); the automatic choice must never take it
+    anywhere else, or its tables would miss the chosen form.  Seeded shapes
+    around tile boundaries, every orientation."""
+    import random
+    import bench
+    rng = random.Random(7)
+    seen = 0
+    for _ in range(400):
+        M = rng.choice((32, 64, 128, 256)) * rng.randint(2, 40) + rng.randint(-40, 40)
+        N = rng.choice((64, 128, 256)) * rng.randint(2, 40) + rng.randint(-40, 40)
+        K = rng.choice((257, 999, 1000, 1023, 2048, 4097))
+        ta, tb = rng.randint(0, 1), rng.randint(0, 1)
+        if _op_choice(ta, tb, M, N, K) == "edge_split":
+            seen += 1
+            assert bench.has_thin_edge(M, N, K), (ta, tb, M, N, K)
+    assert seen >= 20, seen
