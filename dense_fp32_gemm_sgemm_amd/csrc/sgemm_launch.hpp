@@ -114,10 +114,14 @@ long long fewrows_split_bytes(const Problem &p);
 int fewrows_round_fill_pct(const Problem &p);
 int fewrows_strip_cols(const Problem &p);
 
-// Operand alignment classes: an operand may be read with 16-byte vector
-// loads when its base is 16-byte aligned and its leading dimension is a
-// multiple of four; when its rows run along M or N (A transposed, B not) the
-// row length must be one too, so a vector never crosses the end of a row.
+// Operand alignment classes of the plain-loop and VALU kernels, which read
+// vectors through 16-byte typed pointers: an operand may be read with
+// 16-byte vector loads when its base is 16-byte aligned and its leading
+// dimension is a multiple of four; when its rows run along M or N (A
+// transposed, B not) the row length must be one too, so a vector never
+// crosses the end of a row.  (The ordered-loop and streaming kernels copy
+// their vectors instead, which needs only 4-byte alignment: the global loads
+// and stores themselves need no more.)
 inline bool a_vec_ok(const Problem &p) {
   return ((reinterpret_cast<uintptr_t>(p.A) & 15) == 0) && (p.lda % 4 == 0) &&
          (!p.ta || p.M % 4 == 0) && (p.batch <= 1 || p.sa % 4 == 0);
