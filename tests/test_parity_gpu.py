@@ -1020,14 +1020,17 @@ def test_last_round_tail_shapes(shape, expect):
 # few-columns (few-rows) kernel, the bulk on whole rounds of large tiles.
 EDGE_SHAPES = [((4095, 4097, 1023), "NN"), ((4095, 4097, 1023), "NT"), ((4095, 4097, 1023), "TN"),
                ((4095, 4097, 1023), "TT"), ((4097, 4097, 4097), "NN"), ((1025, 1024, 1024), "NN"),
-               ((1025, 1024, 1024), "TT"), ((2047, 2049, 2047), "NT")]
+               ((1025, 1024, 1024), "TT"), ((2047, 2049, 2047), "NT"),
+               # column edges of 32 and 24: two few-columns strips (16, then the rest)
+               ((2048, 2080, 2048), "NN"), ((4096, 4120, 2048), "TN")]
 
 
 @pytest.mark.parametrize("shape,ops", EDGE_SHAPES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple)
                          else v)
 def test_edge_split_automatic(shape, ops):
     """The automatic choice takes the edge split (both edges at (4097, 4097,
-    4097); a one-row edge at (1025, 1024, 1024)), in every orientation, with
+    4097); a one-row edge at (1025, 1024, 1024); column edges of 24 and 32 in
+    two strips), in every orientation, with
     alpha and beta: whole rows and columns of real data to 1e-5 (every
     element for the smaller shapes), and integer data exactly."""
     M, N, K = shape
